@@ -1,0 +1,481 @@
+/*
+ * moe_oracle.c -- CPU oracle for the routed MoE layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, fp64 statement of
+ * what the layer computes.  It is used by the tests, by the GPU smoke check and
+ * by the CPU-baseline leg of the benchmark, and by nothing else.  It shares no
+ * code, header, table or constant with the HIP library: it does not include
+ * any header of that library and that library does not include this file.
+ *
+ * Sources (page title, then section / equation):
+ *   [MM]  CANN operator page "mega_moe": §计算公式 (inputs X, E, G, W1, W2 and
+ *         output Y), §约定 (SiLU, round-to-nearest), §计算过程 -> EP Dispatch,
+ *         Expert Compute (Linear1, SwiGLU, Linear2), Token Combine, and the
+ *         A8W8 block (per-token activation scale, per-output-channel weight
+ *         scales, requantisation of the SwiGLU output before Linear2).
+ *   [V4]  "Megatron-LM 的 MoE 并行：以 DeepSeek-V4 为例": §模型与入口 (the
+ *         layer equation y_t = F_s(x_t) + sum_{e in I_t} g_{t,e} F_e(x_t)),
+ *         §路由张量 (gating linear [n,h]->[n,E]; a = sqrt(softplus(l));
+ *         I_t = TopK(a + beta); g = alpha * a / sum_{I_t} a; the bias is used
+ *         for selection only), §Hash 路由 (a token-id table replaces only the
+ *         selection), §计数与重排 (per-expert counts; the first permute copies
+ *         each token once per selected expert), §ETP 里的矩阵 (SwiGLU expert
+ *         F(X) = (SiLU(X Wg) * X Wu) Wd).
+ *   [MD]  "Megatron 分布式训练全维度并行技术文档": §4.1 (router W_gate in
+ *         [H,E]) and §4.2 (G(x) = TopK(softmax(x W_gate)), the top-k
+ *         probabilities used directly as mixing weights).
+ *
+ * Readings taken where the pages leave a step open (each also listed in the
+ * design notes of the repository):
+ *   - top-k order: key descending, ties to the lower expert id;
+ *   - row order inside an expert block: ascending flat assignment index
+ *     t*k + j (a stable counting sort), one fixed order as [MM] allows;
+ *   - SwiGLU split: the first `inter` columns of Linear1 are the gate, the
+ *     last `inter` are the up projection ([MM] Expert Compute);
+ *   - fp8 (e4m3fn, OCP) replaces INT8 in the A8W8 block: the constant 127
+ *     becomes 448, round-to-nearest-even with saturation; a zero row gets
+ *     scale 1 and code 0;
+ *   - the per-token activation quantisation of X is an integer decision
+ *     taken from an input, so it is done in fp32 (the kernel's precision),
+ *     everything else is fp64.
+ *
+ * Element codes for tensors handed in: 0 = fp32, 1 = bf16 (raw 16-bit words),
+ * 2 = fp8 e4m3fn (raw bytes).  All arrays are host memory, row major.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_FP8 2
+
+#define ORC_SIGMOID 0
+#define ORC_SOFTMAX 1
+#define ORC_SQRT_SOFTPLUS 2
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the top half of an IEEE binary32 word. */
+static double bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* OCP e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; exponent field 0 is subnormal. */
+double oracle_e4m3_decode(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int ex = (code >> 3) & 0xF;
+  int man = code & 0x7;
+  double v;
+  if (ex == 0xF && man == 0x7) return NAN;
+  if (ex == 0)
+    v = ldexp((double)man / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)man / 8.0, ex - 7);
+  return sign ? -v : v;
+}
+
+/* Nearest e4m3fn value to v, ties to the code with an even mantissa, values
+ * beyond the largest finite magnitude (448) saturate to it.  Found by a
+ * binary search over the 127 non-negative finite codes, whose values increase
+ * with the code. */
+uint8_t oracle_e4m3_encode(double v) {
+  if (isnan(v)) return 0x7F;
+  uint8_t sign = (v < 0.0 || (v == 0.0 && signbit(v))) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+  int lo = 0, hi = 0x7E; /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (oracle_e4m3_decode((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  double dlo = a - oracle_e4m3_decode((uint8_t)lo);
+  double dhi = oracle_e4m3_decode((uint8_t)hi) - a;
+  int pick;
+  if (dlo < dhi)
+    pick = lo;
+  else if (dhi < dlo)
+    pick = hi;
+  else
+    pick = (lo & 1) ? hi : lo; /* tie: even mantissa */
+  return (uint8_t)(sign | pick);
+}
+
+/* Values of all 256 e4m3 codes, filled from oracle_e4m3_decode on first use
+ * so that the inner loops below do a table read instead of the decode. */
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+static void e4m3_table_init(void) {
+  if (e4m3_table_ready) return;
+  for (int c = 0; c < 256; ++c) e4m3_table[c] = oracle_e4m3_decode((uint8_t)c);
+  e4m3_table_ready = 1;
+}
+
+static double elem(const void* base, int dt, size_t i) {
+  if (dt == ORC_F32) return (double)((const float*)base)[i];
+  if (dt == ORC_BF16) return bf16_value(((const uint16_t*)base)[i]);
+  return e4m3_table[((const uint8_t*)base)[i]];
+}
+
+/* ------------------------------------------------------------------ */
+/* Routing  ([V4] §路由张量, §Hash 路由; [MD] §4.2)                     */
+/* ------------------------------------------------------------------ */
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+static double softplus(double z) { return z > 0 ? z + log1p(exp(-z)) : log1p(exp(z)); }
+
+/* Gating linear: logits[t,e] = sum_c X[t,c] * Wg[c,e] (+ gate_bias[e]). */
+void oracle_gate_logits(int T, int hidden, int E, int dt, const void* X, const void* Wg,
+                        const double* gate_bias, double* logits) {
+  e4m3_table_init();
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    double* l = logits + (size_t)t * E;
+    for (int e = 0; e < E; ++e) l[e] = 0.0;
+    for (int c = 0; c < hidden; ++c) {
+      double xc = elem(X, dt, (size_t)t * hidden + c);
+      for (int e = 0; e < E; ++e) l[e] += xc * elem(Wg, dt, (size_t)c * E + e);
+    }
+    for (int e = 0; e < E; ++e) l[e] += gate_bias ? gate_bias[e] : 0.0;
+  }
+}
+
+/* Affinity a[t,e] from the logits: sigmoid, softmax over the experts, or
+ * sqrt(softplus). */
+void oracle_affinity(int T, int E, int score_fn, const double* logits, double* aff) {
+  for (int t = 0; t < T; ++t) {
+    const double* l = logits + (size_t)t * E;
+    double* a = aff + (size_t)t * E;
+    if (score_fn == ORC_SOFTMAX) {
+      double m = l[0];
+      for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+      double z = 0.0;
+      for (int e = 0; e < E; ++e) z += exp(l[e] - m);
+      for (int e = 0; e < E; ++e) a[e] = exp(l[e] - m) / z;
+    } else if (score_fn == ORC_SQRT_SOFTPLUS) {
+      for (int e = 0; e < E; ++e) a[e] = sqrt(softplus(l[e]));
+    } else {
+      for (int e = 0; e < E; ++e) a[e] = sigmoid(l[e]);
+    }
+  }
+}
+
+/* Top-k selection on keys[T,E]: the k largest keys, listed by key descending,
+ * equal keys in ascending expert id.  margin[t] = k-th largest key minus the
+ * (k+1)-th (INFINITY when k == E). */
+void oracle_topk(int T, int E, int k, const double* keys, int32_t* ids, double* margin) {
+  char* taken = (char*)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const double* key = keys + (size_t)t * E;
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j <= k && j < E; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || key[e] > key[best])) best = e;
+      if (j < k) {
+        ids[(size_t)t * k + j] = best;
+        taken[best] = 1;
+      } else if (margin) {
+        margin[t] = key[ids[(size_t)t * k + k - 1]] - key[best];
+      }
+    }
+    if (margin && k >= E) margin[t] = INFINITY;
+  }
+  free(taken);
+}
+
+/* Full router.  Score routing: keys = a + beta (beta only selects), ids =
+ * TopK(keys).  Hash routing (token_ids and tid2eid both given): ids[t,:] =
+ * tid2eid[token_ids[t], :], beta unused.  In both cases the mixing weight is
+ * taken from the unbiased affinity: G = alpha * a / sum_{selected} a when
+ * renorm, else alpha * a.  keys_out / margin_out may be NULL. */
+void oracle_route(int T, int hidden, int E, int k, int dt, const void* X, const void* Wg,
+                  const double* gate_bias, const double* beta, int score_fn, int renorm,
+                  double alpha, const int32_t* token_ids, const int32_t* tid2eid,
+                  int32_t* ids, double* G, double* logits_out, double* keys_out,
+                  double* margin_out) {
+  double* logits = (double*)malloc(sizeof(double) * (size_t)T * E);
+  double* aff = (double*)malloc(sizeof(double) * (size_t)T * E);
+  double* keys = (double*)malloc(sizeof(double) * (size_t)T * E);
+  oracle_gate_logits(T, hidden, E, dt, X, Wg, gate_bias, logits);
+  oracle_affinity(T, E, score_fn, logits, aff);
+  int hash = (token_ids != NULL && tid2eid != NULL);
+  for (size_t i = 0; i < (size_t)T * E; ++i)
+    keys[i] = aff[i] + ((beta && !hash) ? beta[i % (size_t)E] : 0.0);
+  if (hash) {
+    for (int t = 0; t < T; ++t) {
+      for (int j = 0; j < k; ++j) ids[(size_t)t * k + j] = tid2eid[(size_t)token_ids[t] * k + j];
+      if (margin_out) margin_out[t] = INFINITY;
+    }
+  } else {
+    oracle_topk(T, E, k, keys, ids, margin_out);
+  }
+  for (int t = 0; t < T; ++t) {
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += aff[(size_t)t * E + ids[(size_t)t * k + j]];
+    for (int j = 0; j < k; ++j) {
+      double a = aff[(size_t)t * E + ids[(size_t)t * k + j]];
+      G[(size_t)t * k + j] = renorm ? alpha * a / denom : alpha * a;
+    }
+  }
+  if (logits_out) memcpy(logits_out, logits, sizeof(double) * (size_t)T * E);
+  if (keys_out) memcpy(keys_out, keys, sizeof(double) * (size_t)T * E);
+  free(logits);
+  free(aff);
+  free(keys);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dispatch  ([MM] EP Dispatch; [V4] §计数与重排)                        */
+/* ------------------------------------------------------------------ */
+
+/* counts[e] = number of assignments (t,j) with ids[t,j] == e; offsets is the
+ * exclusive prefix sum (E+1 entries).  Each assignment gets the destination
+ * row dst_row[t*k+j] = offsets[e] + (number of earlier assignments, in flat
+ * order t*k+j, to the same expert); src_tok[row] = t.  Returns the number of
+ * assignments whose expert id is outside [0,E) (those get dst_row = -1). */
+int oracle_dispatch(int T, int k, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                    int32_t* dst_row, int32_t* src_tok) {
+  int bad = 0;
+  if (E <= 0 || T < 0 || k <= 0) return -1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (size_t i = 0; i < (size_t)T * k; ++i) {
+    int e = ids[i];
+    if (e < 0 || e >= E)
+      ++bad;
+    else
+      ++counts[e];
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+  for (size_t i = 0; i < (size_t)T * k; ++i) {
+    int e = ids[i];
+    if (e < 0 || e >= E) {
+      dst_row[i] = -1;
+      continue;
+    }
+    int r = offsets[e] + fill[e]++;
+    dst_row[i] = r;
+    src_tok[r] = (int32_t)(i / (size_t)k);
+  }
+  free(fill);
+  return bad;
+}
+
+/* ------------------------------------------------------------------ */
+/* Expert FFN  ([MM] Expert Compute; [V4] §ETP 里的矩阵)                 */
+/* ------------------------------------------------------------------ */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* out[0:hidden] = (SiLU(x W1[:, :f]) * (x W1[:, f:])) W2 for one row x,
+ * W1 [hidden, 2f] and W2 [f, hidden] of element type wdt. */
+static void swiglu_row(int hidden, int f, const double* x, int wdt, const void* W1,
+                       const void* W2, double* h1, double* out) {
+  for (int n = 0; n < 2 * f; ++n) h1[n] = 0.0;
+  for (int c = 0; c < hidden; ++c) {
+    double xc = x[c];
+    if (xc == 0.0) continue;
+    for (int n = 0; n < 2 * f; ++n) h1[n] += xc * elem(W1, wdt, (size_t)c * 2 * f + n);
+  }
+  for (int n = 0; n < f; ++n) h1[n] = silu(h1[n]) * h1[f + n];
+  for (int o = 0; o < hidden; ++o) out[o] = 0.0;
+  for (int n = 0; n < f; ++n) {
+    double u = h1[n];
+    for (int o = 0; o < hidden; ++o) out[o] += u * elem(W2, wdt, (size_t)n * hidden + o);
+  }
+}
+
+/* Per-token activation quantisation of the A8W8 block, e4m3 form:
+ * s = max|x| / 448, q = RNE_sat(x / s), computed in fp32 (see header). */
+void oracle_quantize_row_f32(int n, const float* x, uint8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    amax = a > amax ? a : amax;
+  }
+  float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  for (int i = 0; i < n; ++i) q[i] = oracle_e4m3_encode((double)(x[i] / s));
+  *scale = s;
+}
+
+/* The A8W8 (e4m3) expert: x arrives quantised (q_x, s_x).  Linear1 runs on
+ * codes, dequantised per output channel and per token; SwiGLU in fp64; the
+ * SwiGLU output is requantised per row (s_a = max|A|/448) before Linear2,
+ * whose result is dequantised the same way. */
+static void swiglu_row_fp8(int hidden, int f, const uint8_t* qx, double sx, const uint8_t* Wq1,
+                           const float* s_w1, const uint8_t* Wq2, const float* s_w2,
+                           double* h1, double* out) {
+  for (int n = 0; n < 2 * f; ++n) h1[n] = 0.0;
+  for (int c = 0; c < hidden; ++c) {
+    double xc = oracle_e4m3_decode(qx[c]);
+    if (xc == 0.0) continue;
+    for (int n = 0; n < 2 * f; ++n)
+      h1[n] += xc * e4m3_table[Wq1[(size_t)c * 2 * f + n]];
+  }
+  for (int n = 0; n < 2 * f; ++n) h1[n] = h1[n] * (double)s_w1[n] * sx;
+  double amax = 0.0;
+  for (int n = 0; n < f; ++n) {
+    h1[n] = silu(h1[n]) * h1[f + n];
+    amax = fabs(h1[n]) > amax ? fabs(h1[n]) : amax;
+  }
+  double sa = amax > 0.0 ? amax / 448.0 : 1.0;
+  for (int o = 0; o < hidden; ++o) out[o] = 0.0;
+  for (int n = 0; n < f; ++n) {
+    double qa = oracle_e4m3_decode(oracle_e4m3_encode(h1[n] / sa));
+    if (qa == 0.0) continue;
+    for (int o = 0; o < hidden; ++o)
+      out[o] += qa * e4m3_table[Wq2[(size_t)n * hidden + o]];
+  }
+  for (int o = 0; o < hidden; ++o) out[o] = out[o] * (double)s_w2[o] * sa;
+}
+
+/* Everything that describes one layer.  Pointers are host memory. */
+typedef struct {
+  int T, hidden, E, k, inter, has_shared;
+  int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3 */
+  const void* X;        /* [T,hidden]: fp32 (precision 0) or bf16 */
+  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes */
+  const void* W2;       /* [E,f,hidden] */
+  const float* w1_scale; /* [E,2f], e4m3 only */
+  const float* w2_scale; /* [E,hidden], e4m3 only */
+  const void* Ws1;      /* shared [hidden,2f] or NULL */
+  const void* Ws2;      /* shared [f,hidden] */
+  const float* ws1_scale;
+  const float* ws2_scale;
+} oracle_layer;
+
+static int w_dt(int precision) {
+  return precision == 0 ? ORC_F32 : (precision == 1 ? ORC_BF16 : ORC_FP8);
+}
+
+/* F_e(x_t) for one token and one expert (e == E selects the shared expert). */
+static void expert_of_token(const oracle_layer* L, int t, int e, double* xbuf, uint8_t* qbuf,
+                            float* fbuf, double* h1, double* out) {
+  int h = L->hidden, f = L->inter;
+  int shared = (e == L->E);
+  const char* W1 = shared ? (const char*)L->Ws1 : (const char*)L->W1;
+  const char* W2 = shared ? (const char*)L->Ws2 : (const char*)L->W2;
+  size_t wb = (L->precision == 0) ? 4 : (L->precision == 1 ? 2 : 1);
+  if (!shared) {
+    W1 += (size_t)e * h * 2 * f * wb;
+    W2 += (size_t)e * f * h * wb;
+  }
+  int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16;
+  if (L->precision == 2) {
+    for (int c = 0; c < h; ++c) fbuf[c] = (float)elem(L->X, xdt, (size_t)t * h + c);
+    float sx;
+    oracle_quantize_row_f32(h, fbuf, qbuf, &sx);
+    const float* s1 = shared ? L->ws1_scale : L->w1_scale + (size_t)e * 2 * f;
+    const float* s2 = shared ? L->ws2_scale : L->w2_scale + (size_t)e * h;
+    swiglu_row_fp8(h, f, qbuf, (double)sx, (const uint8_t*)W1, s1, (const uint8_t*)W2, s2, h1,
+                   out);
+  } else {
+    for (int c = 0; c < h; ++c) xbuf[c] = elem(L->X, xdt, (size_t)t * h + c);
+    swiglu_row(h, f, xbuf, w_dt(L->precision), W1, W2, h1, out);
+  }
+}
+
+/* The layer equation of [V4] §模型与入口, token by token:
+ *   y_t = F_s(x_t) + sum_j G[t,j] * F_{ids[t,j]}(x_t)
+ * for the tokens listed in tok[0..ntok) (all tokens when tok == NULL).
+ * Y is [ntok, hidden] fp64. */
+void oracle_layer_tokens(const oracle_layer* L, const int32_t* ids, const double* G, int ntok,
+                         const int32_t* tok, double* Y) {
+  int h = L->hidden, f = L->inter;
+  e4m3_table_init();
+#pragma omp parallel
+  {
+    double* xbuf = (double*)malloc(sizeof(double) * h);
+    uint8_t* qbuf = (uint8_t*)malloc((size_t)h);
+    float* fbuf = (float*)malloc(sizeof(float) * h);
+    double* h1 = (double*)malloc(sizeof(double) * 2 * f);
+    double* fe = (double*)malloc(sizeof(double) * h);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < ntok; ++i) {
+      int t = tok ? tok[i] : i;
+      double* y = Y + (size_t)i * h;
+      for (int o = 0; o < h; ++o) y[o] = 0.0;
+      for (int j = 0; j < L->k; ++j) {
+        int e = ids[(size_t)t * L->k + j];
+        if (e < 0 || e >= L->E) continue;
+        expert_of_token(L, t, e, xbuf, qbuf, fbuf, h1, fe);
+        double g = G[(size_t)t * L->k + j];
+        for (int o = 0; o < h; ++o) y[o] += g * fe[o];
+      }
+      if (L->has_shared) {
+        expert_of_token(L, t, L->E, xbuf, qbuf, fbuf, h1, fe);
+        for (int o = 0; o < h; ++o) y[o] += fe[o];
+      }
+    }
+    free(xbuf);
+    free(qbuf);
+    free(fbuf);
+    free(h1);
+    free(fe);
+  }
+}
+
+/* The staged form of [MM]: the rows of the dispatched matrix are the tokens
+ * src_tok[r]; row r belongs to the expert whose block [offsets[e],
+ * offsets[e+1]) holds it.  Yp[r] = F_e(x_{src_tok[r]}) for the listed rows
+ * (all T*k rows when rows == NULL).  Yp is [nrows, hidden] fp64.  With
+ * has_shared, rows T*k .. T*k+T-1 stand for the shared expert applied to token
+ * r - T*k (src_tok is not read for them). */
+void oracle_expert_rows(const oracle_layer* L, const int32_t* offsets, const int32_t* src_tok,
+                        int nrows, const int32_t* rows, double* Yp) {
+  int h = L->hidden, f = L->inter;
+  e4m3_table_init();
+#pragma omp parallel
+  {
+    double* xbuf = (double*)malloc(sizeof(double) * h);
+    uint8_t* qbuf = (uint8_t*)malloc((size_t)h);
+    float* fbuf = (float*)malloc(sizeof(float) * h);
+    double* h1 = (double*)malloc(sizeof(double) * 2 * f);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < nrows; ++i) {
+      int r = rows ? rows[i] : i;
+      int routed = L->T * L->k;
+      if (r >= routed) {
+        expert_of_token(L, r - routed, L->E, xbuf, qbuf, fbuf, h1, Yp + (size_t)i * h);
+        continue;
+      }
+      int e = 0;
+      while (e < L->E && offsets[e + 1] <= r) ++e;
+      expert_of_token(L, src_tok[r], e, xbuf, qbuf, fbuf, h1, Yp + (size_t)i * h);
+    }
+    free(xbuf);
+    free(qbuf);
+    free(fbuf);
+    free(h1);
+  }
+}
+
+/* Token Combine of [MM]: y[t] = sum_j G[t,j] * Yp[dst_row[t,j]] (+ Ys[t]),
+ * j ascending.  Yp is [T*k, hidden], Ys [T, hidden] or NULL, all fp64. */
+void oracle_combine(int T, int k, int hidden, const double* Yp, const int32_t* dst_row,
+                    const double* G, const double* Ys, double* Y) {
+  for (int t = 0; t < T; ++t) {
+    double* y = Y + (size_t)t * hidden;
+    for (int o = 0; o < hidden; ++o) y[o] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int r = dst_row[(size_t)t * k + j];
+      if (r < 0) continue;
+      double g = G[(size_t)t * k + j];
+      for (int o = 0; o < hidden; ++o) y[o] += g * Yp[(size_t)r * hidden + o];
+    }
+    if (Ys)
+      for (int o = 0; o < hidden; ++o) y[o] += Ys[(size_t)t * hidden + o];
+  }
+}

@@ -1,0 +1,406 @@
+"""Pins of the CPU oracle against facts the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example printed on a page, a closed form, a library routine (numpy / scipy /
+torch's float8 cast), a brute-force dense formulation, or an invariant of the
+definition.  The planted-mistake test at the end shows that a plausible slip
+in the oracle is caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+from tests.helpers import bits, oracle_layer, oracle_route
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ helpers
+def _np_swiglu(x, W1, W2):
+    """Dense SwiGLU FFN with numpy fp64 matmuls (x [n,h], W1 [h,2f], W2 [f,h])."""
+    f = W1.shape[1] // 2
+    H = x @ W1
+    g, u = H[:, :f], H[:, f:]
+    return (g / (1.0 + np.exp(-g)) * u) @ W2
+
+
+def _rand_ids(rng, T, k, E):
+    """k distinct expert ids per token."""
+    return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16)
+
+
+# ------------------------------------------------------------------ dispatch
+def test_four_token_split_example():
+    """The worked split of §计数与重排 (DeepSeek-V4 blog post)."""
+    g = json.load(open(os.path.join(GOLDEN, "four_token_split.json")))
+    E, k, L = g["experts"], g["topk"], g["experts_per_rank"]
+    names = list(g["tokens"])
+    ids = np.array([g["tokens"][n] for n in names], np.int32)
+    d = oracle.dispatch(ids, E)
+    assert d["counts"].tolist() == g["expected"]["global_counts"]
+    splits = []
+    for toks in g["rank_tokens"]:
+        local = np.array([g["tokens"][n] for n in toks], np.int32)
+        cnt = oracle.dispatch(local, E)["counts"]
+        splits.append([int(cnt[j * L:(j + 1) * L].sum()) for j in range(E // L)])
+        assert sum(splits[-1]) == len(toks) * k
+    assert splits == g["expected"]["input_splits"]
+    out = [[splits[src][dst] for src in range(len(splits))] for dst in range(len(splits))]
+    assert out == g["expected"]["output_splits"]
+    assert [sum(o) for o in out] == g["expected"]["received_rows"]
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (7, 2, 8), (64, 6, 384), (333, 4, 17), (0, 2, 4)])
+def test_dispatch_invariants(T, k, E):
+    rng = np.random.default_rng(T * 131 + k * 7 + E)
+    ids = _rand_ids(rng, T, k, E) if T else np.zeros((0, k), np.int32)
+    d = oracle.dispatch(ids, E)
+    counts, offs, dst, src = d["counts"], d["offsets"], d["dst_row"], d["src_tok"]
+    # counts sum to T*k and agree with numpy's bincount
+    assert counts.sum() == T * k
+    assert np.array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    assert offs[0] == 0 and np.array_equal(np.diff(offs), counts)
+    # dst_row is a bijection onto [0, T*k) and lands in the expert's block
+    assert np.array_equal(np.sort(dst), np.arange(T * k))
+    e_of = ids.ravel()
+    assert np.all(dst >= offs[e_of]) and np.all(dst < offs[e_of + 1])
+    # the source token of each row is the token of the assignment
+    assert np.array_equal(src[dst], np.arange(T * k) // max(k, 1))
+    # stable: within an expert block, rows follow ascending flat index
+    for e in range(E):
+        flat = np.nonzero(e_of == e)[0]
+        assert np.array_equal(dst[flat], offs[e] + np.arange(len(flat)))
+
+
+def test_dispatch_flags_bad_ids():
+    ids = np.array([[0, 5], [1, -1]], np.int32)
+    d = oracle.dispatch(ids, 4)
+    assert d["bad"] == 2
+    assert d["dst_row"][1] == -1 and d["dst_row"][3] == -1
+    assert d["counts"].tolist() == [1, 1, 0, 0]
+
+
+def test_permute_then_unpermute_is_identity():
+    rng = np.random.default_rng(3)
+    T, k, E, h = 50, 3, 9, 16
+    X = rng.standard_normal((T, h))
+    ids = _rand_ids(rng, T, k, E)
+    d = oracle.dispatch(ids, E)
+    Xp = X[d["src_tok"]]                       # permute (with duplication)
+    back = Xp[d["dst_row"]].reshape(T, k, h)   # unpermute each copy
+    for j in range(k):
+        assert np.array_equal(back[:, j], X)
+
+
+def test_identity_experts_combine_gives_weight_sum_times_x():
+    rng = np.random.default_rng(4)
+    T, k, E, h = 40, 4, 11, 24
+    X = rng.standard_normal((T, h))
+    ids = _rand_ids(rng, T, k, E)
+    G = rng.random((T, k))
+    d = oracle.dispatch(ids, E)
+    Y = oracle.combine(X[d["src_tok"]], d["dst_row"], G)
+    np.testing.assert_allclose(Y, G.sum(1, keepdims=True) * X, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ routing
+def test_affinity_closed_forms_and_library():
+    l = np.array([[-30.0, -2.5, -1e-3, 0.0, 1e-3, 0.7, 3.0, 40.0]])
+    np.testing.assert_allclose(oracle.affinity(l, "sigmoid"), scipy.special.expit(l), rtol=1e-15)
+    assert oracle.affinity(np.zeros((1, 1)), "sigmoid")[0, 0] == 0.5
+    np.testing.assert_allclose(oracle.affinity(l, "sqrt_softplus"),
+                               np.sqrt(np.logaddexp(0.0, l)), rtol=1e-14)
+    assert math.isclose(oracle.affinity(np.zeros((1, 1)), "sqrt_softplus")[0, 0],
+                        math.sqrt(math.log(2.0)), rel_tol=1e-15)
+    np.testing.assert_allclose(oracle.affinity(l, "softmax"), scipy.special.softmax(l, axis=1),
+                               rtol=1e-13)
+
+
+def test_topk_matches_stable_argsort_and_ties_go_to_lower_id():
+    rng = np.random.default_rng(5)
+    keys = rng.integers(0, 6, size=(200, 13)).astype(np.float64)   # many exact ties
+    for k in (1, 3, 13):
+        ids, margin = oracle.topk(keys, k)
+        ref = np.argsort(-keys, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        if k < 13:
+            srt = -np.sort(-keys, axis=1)
+            np.testing.assert_array_equal(margin, srt[:, k - 1] - srt[:, k])
+
+
+def test_zero_gate_weight_selects_first_k_with_uniform_weights():
+    T, h, E, k = 5, 16, 10, 4
+    X = _bf16(np.random.default_rng(6).standard_normal((T, h)))
+    Wg = _bf16(np.zeros((h, E)))
+    r = oracle.route(bits(X), bits(Wg), k, score="sigmoid", renorm=True, alpha=2.5)
+    assert np.array_equal(r["ids"], np.tile(np.arange(k), (T, 1)))
+    np.testing.assert_allclose(r["G"], 2.5 / k, rtol=1e-15)
+    r = oracle.route(bits(X), bits(Wg), k, score="softmax", renorm=False)
+    np.testing.assert_allclose(r["G"], 1.0 / E, rtol=1e-15)
+
+
+def test_selection_uses_bias_but_weights_use_raw_affinity():
+    rng = np.random.default_rng(7)
+    T, h, E, k = 32, 64, 16, 3
+    X = rng.standard_normal((T, h)).astype(np.float32)
+    Wg = (rng.standard_normal((h, E)) * 0.3).astype(np.float32)
+    beta = np.zeros(E)
+    beta[5] = 10.0
+    r = oracle.route(X, Wg, k, beta=beta, score="sigmoid", renorm=True, alpha=1.7)
+    assert np.all(r["ids"][:, 0] == 5)          # beta dominates the selection
+    a = scipy.special.expit(X.astype(np.float64) @ Wg.astype(np.float64))
+    sel = np.take_along_axis(a, r["ids"].astype(np.int64), axis=1)
+    np.testing.assert_allclose(r["G"], 1.7 * sel / sel.sum(1, keepdims=True), rtol=1e-12)
+    # the biased key would give a visibly different weight for expert 5
+    biased = sel.copy()
+    biased[:, 0] += 10.0
+    assert np.abs(1.7 * biased / biased.sum(1, keepdims=True) - r["G"]).max() > 0.1
+    # without the bias, the selection is the top-k of the raw affinity
+    r0 = oracle.route(X, Wg, k, score="sigmoid")
+    assert np.array_equal(r0["ids"], np.argsort(-a, axis=1, kind="stable")[:, :k])
+
+
+def test_softmax_router_raw_weights():
+    rng = np.random.default_rng(8)
+    T, h, E, k = 20, 32, 8, 2
+    X = rng.standard_normal((T, h)).astype(np.float32)
+    Wg = (rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32)
+    r = oracle.route(X, Wg, k, score="softmax", renorm=False, alpha=1.0)
+    p = scipy.special.softmax(X.astype(np.float64) @ Wg.astype(np.float64), axis=1)
+    np.testing.assert_allclose(r["G"], np.take_along_axis(p, r["ids"].astype(np.int64), 1),
+                               rtol=1e-12)
+    full = oracle.route(X, Wg, E, score="softmax", renorm=False)
+    np.testing.assert_allclose(full["G"].sum(1), 1.0, rtol=1e-13)
+
+
+def test_gate_bias_shifts_logits():
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((6, 8)).astype(np.float32)
+    Wg = rng.standard_normal((8, 5)).astype(np.float32)
+    b = rng.standard_normal(5)
+    np.testing.assert_allclose(oracle.gate_logits(X, Wg, b),
+                               X.astype(np.float64) @ Wg.astype(np.float64) + b, rtol=1e-12)
+
+
+def test_hash_routing_is_a_table_lookup():
+    rng = np.random.default_rng(10)
+    T, h, E, k, V = 30, 16, 12, 3, 50
+    X = rng.standard_normal((T, h)).astype(np.float32)
+    Wg = rng.standard_normal((h, E)).astype(np.float32)
+    tab = _rand_ids(rng, V, k, E)
+    tok = rng.integers(0, V, T).astype(np.int32)
+    beta = rng.standard_normal(E) * 5
+    r = oracle.route(X, Wg, k, beta=beta, token_ids=tok, tid2eid=tab, alpha=2.0)
+    assert np.array_equal(r["ids"], tab[tok])
+    a = scipy.special.expit(X.astype(np.float64) @ Wg.astype(np.float64))
+    sel = np.take_along_axis(a, r["ids"].astype(np.int64), 1)
+    np.testing.assert_allclose(r["G"], 2.0 * sel / sel.sum(1, keepdims=True), rtol=1e-12)
+
+
+# ------------------------------------------------------------------ experts
+def test_single_expert_top1_is_dense_swiglu_plus_shared():
+    rng = np.random.default_rng(11)
+    T, h, f = 9, 32, 16
+    X = rng.standard_normal((T, h)).astype(np.float32)
+    W1 = (rng.standard_normal((1, h, 2 * f)) / math.sqrt(h)).astype(np.float32)
+    W2 = (rng.standard_normal((1, f, h)) / math.sqrt(f)).astype(np.float32)
+    Ws1 = (rng.standard_normal((h, 2 * f)) / math.sqrt(h)).astype(np.float32)
+    Ws2 = (rng.standard_normal((f, h)) / math.sqrt(f)).astype(np.float32)
+    Wg = rng.standard_normal((h, 1)).astype(np.float32)
+    r = oracle.route(X, Wg, 1, alpha=1.0)            # G = a / a = 1
+    np.testing.assert_allclose(r["G"], 1.0, rtol=1e-15)
+    L = oracle.Layer("fp32", X, W1, W2, k=1)
+    x64 = X.astype(np.float64)
+    np.testing.assert_allclose(L.tokens(r["ids"], r["G"]),
+                               _np_swiglu(x64, W1[0].astype(np.float64), W2[0].astype(np.float64)),
+                               rtol=1e-11, atol=1e-12)
+    Ls = oracle.Layer("fp32", X, W1, W2, Ws1=Ws1, Ws2=Ws2, k=1)
+    ref = (_np_swiglu(x64, W1[0].astype(np.float64), W2[0].astype(np.float64))
+           + _np_swiglu(x64, Ws1.astype(np.float64), Ws2.astype(np.float64)))
+    np.testing.assert_allclose(Ls.tokens(r["ids"], r["G"]), ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("score,renorm", [("sigmoid", True), ("softmax", False),
+                                          ("sqrt_softplus", True)])
+def test_k_equals_E_is_the_dense_mixture(score, renorm):
+    """With k = E every expert is selected: the layer is the dense mixture
+    sum_e g_e F_e(x), computed here with numpy matmuls over all experts."""
+    rng = np.random.default_rng(12)
+    T, h, E, f = 12, 24, 5, 8
+    X = rng.standard_normal((T, h)).astype(np.float32)
+    Wg = (rng.standard_normal((h, E)) / math.sqrt(h)).astype(np.float32)
+    W1 = (rng.standard_normal((E, h, 2 * f)) / math.sqrt(h)).astype(np.float32)
+    W2 = (rng.standard_normal((E, f, h)) / math.sqrt(f)).astype(np.float32)
+    alpha = 1.3
+    r = oracle.route(X, Wg, E, score=score, renorm=renorm, alpha=alpha)
+    y = oracle.Layer("fp32", X, W1, W2, k=E).tokens(r["ids"], r["G"])
+    x64 = X.astype(np.float64)
+    logits = x64 @ Wg.astype(np.float64)
+    a = {"sigmoid": scipy.special.expit(logits), "softmax": scipy.special.softmax(logits, 1),
+         "sqrt_softplus": np.sqrt(np.logaddexp(0, logits))}[score]
+    g = alpha * a / a.sum(1, keepdims=True) if renorm else alpha * a
+    dense = sum(g[:, e:e + 1] * _np_swiglu(x64, W1[e].astype(np.float64), W2[e].astype(np.float64))
+                for e in range(E))
+    np.testing.assert_allclose(y, dense, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "v4pro_bf16", "v4pro_fp8", "decode_hash_bf16"])
+def test_token_loop_equals_staged_dispatch_experts_combine(name):
+    """The per-token layer equation (blog §模型与入口) and the staged
+    dispatch / expert / combine definition (mega_moe §计算过程) agree."""
+    inp = synth.make_inputs(name, T=24, hidden=64, inter=32, experts=16 if name != "tiny_fp32" else 8,
+                            zipf=False)
+    wl = inp["workload"]
+    r = oracle_route(inp)
+    L = oracle_layer(inp)
+    d = oracle.dispatch(r["ids"], wl.experts)
+    y_tok = L.tokens(r["ids"], r["G"])
+    Yp = L.expert_rows(d["offsets"], d["src_tok"])
+    Ys = None
+    if wl.shared:
+        Ys = L.expert_rows(d["offsets"], d["src_tok"], rows=np.arange(wl.T * wl.topk,
+                                                                      wl.T * wl.topk + wl.T))
+    y_stg = oracle.combine(Yp, d["dst_row"], r["G"], Ys)
+    np.testing.assert_allclose(y_tok, y_stg, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ fp8
+def test_e4m3_decode_all_codes_match_torch_and_closed_forms():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = ~np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[finite], ref[finite])
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF]) and np.isnan(ours).sum() == 2
+    assert ours[0x7E] == 448.0 and ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9
+    assert ours[0x38] == 1.0 and ours[0xB8] == -1.0
+
+
+def test_e4m3_encode_roundtrip_ties_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+    # ties go to the even mantissa: 1.0625 between 1.0 (0x38) and 1.125 (0x39)
+    assert oracle.e4m3_encode(np.array([1.0625, 1.1875, -1.0625]))[()].tolist() == [0x38, 0x3A, 0xB8]
+    assert oracle.e4m3_encode(np.array([448.0, 463.99, 500.0, 1e30, -1e30])).tolist() == \
+        [0x7E, 0x7E, 0x7E, 0x7E, 0xFE]
+    # random values: nearest-even agrees with torch's float8_e4m3fn cast
+    rng = np.random.default_rng(13)
+    v = np.concatenate([rng.standard_normal(4000) * 50, rng.standard_normal(2000) * 1e-2,
+                        rng.uniform(-448, 448, 2000)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(v.astype(np.float64)), ref)
+
+
+def test_quantize_rows_f32_matches_torch_cast():
+    rng = np.random.default_rng(14)
+    X = (rng.standard_normal((16, 300)) * rng.uniform(0.01, 100, (16, 1))).astype(np.float32)
+    X[3] = 0.0
+    q, s = oracle.quantize_rows_f32(X)
+    amax = np.abs(X).max(1)
+    s_ref = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(s, s_ref)
+    q_ref = torch.from_numpy(X / s_ref[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, q_ref)
+    assert np.all(q[3] == 0) and s[3] == 1.0
+
+
+def test_fp8_expert_is_exact_when_every_quantisation_is_lossless():
+    """inter = 1 makes the SwiGLU output one value per row, whose requantised
+    code is exactly +-448; with X rows holding e4m3 values and max|x| = 448,
+    the activation scale is 1.  The fp8 layer then equals the exact SwiGLU
+    with dequantised weights (code * per-channel scale)."""
+    rng = np.random.default_rng(15)
+    T, h, f, E = 6, 32, 1, 3
+    grid = oracle.e4m3_decode(np.arange(0x30, 0x50, dtype=np.uint8))  # 0.25 .. 8
+    X = rng.choice(grid, size=(T, h)) * rng.choice([-1, 1], size=(T, h))
+    X[:, 0] = 448.0
+    Xb = _bf16(X)
+    assert np.array_equal(Xb.float().numpy(), X.astype(np.float32))  # exact in bf16
+    W1q = rng.integers(0, 0x7E, size=(E, h, 2 * f)).astype(np.uint8) | \
+        (rng.integers(0, 2, size=(E, h, 2 * f)).astype(np.uint8) << 7)
+    W2q = rng.integers(0, 0x7E, size=(E, f, h)).astype(np.uint8)
+    s1 = rng.uniform(1e-4, 1e-3, (E, 2 * f)).astype(np.float32)
+    s2 = rng.uniform(1e-3, 1e-2, (E, h)).astype(np.float32)
+    ids = np.array([[t % E] for t in range(T)], np.int32)
+    G = np.ones((T, 1))
+    L = oracle.Layer("fp8", bits(Xb), W1q, W2q, w1_scale=s1, w2_scale=s2, k=1)
+    y = L.tokens(ids, G)
+    dq1 = oracle.e4m3_decode(W1q) * s1[:, None, :].astype(np.float64)
+    dq2 = oracle.e4m3_decode(W2q) * s2[:, None, :].astype(np.float64)
+    for t in range(T):
+        e = ids[t, 0]
+        ref = _np_swiglu(X[t:t + 1].astype(np.float64), dq1[e], dq2[e])
+        np.testing.assert_allclose(y[t:t + 1], ref, rtol=1e-12)
+
+
+def test_fp8_layer_within_quantisation_error_of_exact_layer():
+    inp = synth.make_inputs("v4pro_fp8", T=16, hidden=256, inter=128, experts=8, zipf=False)
+    wl = inp["workload"]
+    r = oracle_route(inp)
+    y8 = oracle_layer(inp).tokens(r["ids"], r["G"])
+    dq = dict(inp)
+    dq["workload"] = wl.replace(precision="fp32")
+    dq["X"] = inp["X"].float()
+    for w, s in (("W1", "w1_scale"), ("W2", "w2_scale"), ("Ws1", "ws1_scale"), ("Ws2", "ws2_scale")):
+        dq[w] = inp[w].float() * inp[s].unsqueeze(-2)
+        dq[s] = None
+    y = oracle_layer(dq).tokens(r["ids"], r["G"])
+    rel = np.abs(y8 - y).max(1) / np.abs(y).max(1)
+    assert rel.max() < 0.1 and rel.max() > 1e-4   # lossy, but only by the fp8 rounding
+
+
+# ------------------------------------------------------------------ shapes
+def test_workload_shapes_match_the_pages_arithmetic():
+    v4 = synth.WORKLOADS["v4pro_bf16"]
+    assert v4.params_per_expert == 66_060_288          # 3hf, blog §模型与入口
+    ep = synth.WORKLOADS["ep_share_bf16"]
+    assert ep.T * ep.topk == 24_576 and ep.experts == 6  # 6 experts x 4096 rows per EP64 rank
+
+
+def test_zipf_fixture_gives_skewed_load():
+    """Realised load on a fresh batch follows the Zipf target roughly."""
+    inp = synth.make_inputs("v4pro_bf16", T=1024, hidden=512, experts=64, inter=8)
+    r = oracle_route(inp)
+    cnt = np.sort(np.bincount(r["ids"].ravel(), minlength=64))[::-1]
+    assert cnt[0] > 8 * max(cnt[-1], 1)
+    assert cnt[0] > 0.5 * 1024 and cnt.sum() == 6 * 1024
+
+
+# ------------------------------------------------------------------ planted mistake
+def test_pins_catch_a_planted_mistake(tmp_path):
+    """Build a copy of the oracle with the SwiGLU halves swapped (a plausible
+    slip) and check that the dense-SwiGLU pin rejects it."""
+    import ctypes
+    import subprocess
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")).read()
+    bad = src.replace("h1[n] = silu(h1[n]) * h1[f + n];", "h1[n] = silu(h1[f + n]) * h1[n];", 1)
+    assert bad != src
+    c = tmp_path / "bad.c"
+    c.write_text(bad)
+    so = tmp_path / "libbad.so"
+    subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(c), "-lm"])
+    saved = oracle._lib
+    try:
+        oracle._lib = None
+        real = oracle._LIB_PATH
+        oracle._LIB_PATH = str(so)
+        with pytest.raises(AssertionError):
+            test_single_expert_top1_is_dense_swiglu_plus_shared()
+    finally:
+        oracle._LIB_PATH = real
+        oracle._lib = saved
+    del ctypes
