@@ -1,0 +1,197 @@
+/*
+ * moe.h -- C ABI of the routed mixture-of-experts layer forward pass for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, on one GPU's share of T tokens:
+ *   1. gate logits   l = X Wg (+ gate_bias)                        moe_route
+ *   2. affinity a = score(l); selection I_t = TopK(a + beta);
+ *      weights G = alpha * a / sum_{I_t} a (or alpha * a)          moe_route
+ *   3. dispatch: per-expert counts, row map, permuted copy Xp      moe_permute
+ *   4. per-expert Linear1 -> SwiGLU -> Linear2 (grouped GEMM),
+ *      plus the shared expert on every token                       moe_expert_ffn
+ *   5. y_t = sum_j G[t,j] Yp[row(t,j)] + Ys[t]                     moe_combine
+ * and all five in order:                                           moe_forward
+ *
+ * Sources (page title, section):
+ *   - CANN operator page "mega_moe", §计算公式 and §计算过程: the inputs
+ *     X[T,hidden], E[T,topk] (expert ids), G[T,topk] (gate weights),
+ *     W1[experts, hidden, 2*inter], W2[experts, inter, hidden], the output
+ *     Y[T,hidden]; EP Dispatch (rows of X stacked per expert in a fixed order,
+ *     row(i,k) unique), Expert Compute (Linear1, SwiGLU with the first half
+ *     of the Linear1 columns as gate, Linear2), Token Combine, and the A8W8
+ *     block (per-token activation scale, per-output-channel weight scales,
+ *     per-row requantisation of the SwiGLU output before Linear2).
+ *   - "Megatron-LM 的 MoE 并行：以 DeepSeek-V4 为例": §模型与入口 (layer
+ *     equation with the shared expert F_s at weight 1), §路由张量 (affinity,
+ *     selection by a + beta, mixing weight from the unbiased affinity, alpha),
+ *     §Hash 路由 (token-id table replaces the selection only), §计数与重排
+ *     (counts and the duplicating permute).
+ *   - "Megatron 分布式训练全维度并行技术文档" §4.1-§4.2 (router weight
+ *     W_gate in [H, E]; softmax top-k router with raw top-k probabilities).
+ *
+ * Conventions for every entry point:
+ *   - All tensors are device memory, row major, densely packed, allocated
+ *     and owned by the caller.  The library never allocates or frees memory
+ *     and keeps no pointer after a call returns.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  None of them
+ *     reads device memory from the host, except moe_check_device_error.
+ *   - Arguments are validated on the host before any launch; a failed check
+ *     returns a negative moe_status and launches nothing.  A launch failure
+ *     returns MOE_ERR_HIP.
+ *   - Results are deterministic: no atomics decide an order or a sum, so two
+ *     calls with the same inputs give bit-identical outputs.
+ *   - Element types by precision:
+ *       MOE_PREC_F32:  X, Wg, W*, Xp, Yp, Ys, Y fp32.
+ *       MOE_PREC_BF16: X, Wg, W*, Xp, Yp, Ys, Y bf16.
+ *       MOE_PREC_FP8:  X, Wg, Yp, Ys, Y bf16; W1/W2/Ws1/Ws2 OCP e4m3fn codes
+ *                      with fp32 per-output-channel scales; Xp, Xq e4m3fn
+ *                      codes with fp32 per-row scales.
+ *   - Shape limits: 1 <= T; 1 <= topk <= min(16, experts) (the mega_moe
+ *     constraint on top-k); experts <= 512; hidden a multiple of 128 and
+ *     inter a multiple of 64 (the kernels' tile granularity).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a pointer, size or option is out of contract */
+  MOE_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels implement */
+  MOE_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned or too small */
+  MOE_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+  MOE_ERR_DEVICE_DATA = -5  /* device data broke the contract (bad expert id) */
+} moe_status;
+
+typedef enum { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_FP8 = 2 } moe_precision;
+
+typedef enum {
+  MOE_SCORE_SIGMOID = 0,      /* a = 1 / (1 + exp(-l)) */
+  MOE_SCORE_SOFTMAX = 1,      /* a = softmax over the experts of l */
+  MOE_SCORE_SQRT_SOFTPLUS = 2 /* a = sqrt(log(1 + exp(l))) */
+} moe_score_fn;
+
+/* Sizes of one layer invocation. */
+typedef struct {
+  int32_t tokens;     /* T: rows of X */
+  int32_t hidden;     /* h */
+  int32_t experts;    /* E: routed experts */
+  int32_t topk;       /* k: experts per token */
+  int32_t inter;      /* f: SwiGLU width; W1 has 2f columns */
+  int32_t has_shared; /* 1: add the shared expert F_s (weight 1) */
+  int32_t precision;  /* moe_precision */
+} moe_shape;
+
+/* Router options.  Score routing: ids = TopK(a + expert_bias), ordered by
+ * key descending, equal keys by ascending expert id.  Hash routing (both
+ * token_ids and tid2eid non-NULL): ids[t,:] = tid2eid[token_ids[t], :] and
+ * expert_bias is not used.  In both, G[t,j] = alpha * a[ids[t,j]] /
+ * sum_j a[ids[t,j]] when renorm, else alpha * a[ids[t,j]]. */
+typedef struct {
+  int32_t score_fn;          /* moe_score_fn */
+  int32_t renorm;            /* 1: divide by the sum over the selected experts */
+  float alpha;               /* routing scale */
+  const float* expert_bias;  /* [E] fp32 beta, selection only; NULL = 0 */
+  const float* gate_bias;    /* [E] fp32 bias of the gating linear; NULL = 0 */
+  const int32_t* token_ids;  /* [T] token ids in [0, vocab) (hash routing) */
+  const int32_t* tid2eid;    /* [vocab, topk] expert ids (hash routing) */
+  int32_t vocab;             /* rows of tid2eid */
+} moe_route_opts;
+
+/* Expert weights.  W1 [E, hidden, 2*inter], W2 [E, inter, hidden]; shared
+ * Ws1 [hidden, 2*inter], Ws2 [inter, hidden] (NULL without a shared expert).
+ * Scales (MOE_PREC_FP8 only, else ignored): w1_scale [E, 2*inter], w2_scale
+ * [E, hidden], ws1_scale [2*inter], ws2_scale [hidden]. */
+typedef struct {
+  const void* W1;
+  const float* w1_scale;
+  const void* W2;
+  const float* w2_scale;
+  const void* Ws1;
+  const float* ws1_scale;
+  const void* Ws2;
+  const float* ws2_scale;
+} moe_expert_weights;
+
+/* Bytes of device workspace that moe_forward needs for this shape (every
+ * other entry point needs at most as much).  0 if the shape is invalid.  The
+ * workspace must be 256-byte aligned; its contents need no initialisation
+ * and are not meaningful between calls. */
+size_t moe_workspace_size(const moe_shape* shape);
+
+/* Steps 1-2: gating linear, affinity, bias-for-selection top-k, weights.
+ *   X [T, hidden] (fp32 for F32, else bf16), Wg [hidden, E] same type.
+ *   expert_ids [T, topk] int32 out, gate_weights [T, topk] fp32 out.
+ *   keys_out [T, E] fp32 out or NULL: the selection keys a + beta as the
+ *   kernel compared them (for checking near ties).
+ * Hash routing flags token ids outside [0, vocab) in the workspace (see
+ * moe_check_device_error); such tokens get expert id -1 and weight 0. */
+int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+              int32_t* expert_ids, float* gate_weights, float* keys_out, void* workspace,
+              size_t workspace_bytes, hipStream_t stream);
+
+/* Step 3: dispatch (a permutation with duplication).
+ *   counts [E] out: assignments per expert; offsets [E+1] out: exclusive
+ *   prefix sum; dst_row [T*topk] out: destination row of assignment t*k+j
+ *   (rows of one expert are contiguous and ordered by ascending t*k+j);
+ *   src_tok [T*topk] out: token of each destination row; Xp [T*topk, hidden]
+ *   out: Xp[dst_row[i]] = X[i / topk].
+ *   MOE_PREC_FP8: X is bf16 and is quantised per token first (scale =
+ *   max|x| / 448, codes = round-to-nearest-even of x / scale, saturating);
+ *   Xq [T, hidden] e4m3 and x_scale [T] receive that, Xp holds codes and
+ *   xp_scale [T*topk] the scale of each row.  Otherwise xp_scale, Xq and
+ *   x_scale are ignored.
+ * Expert ids outside [0, E) are skipped (dst_row = -1) and flagged. */
+int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,
+                int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
+                float* xp_scale, void* Xq, float* x_scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Step 4: grouped Linear1 -> SwiGLU -> Linear2 over the expert blocks given
+ * by offsets [E+1] (rows offsets[e] .. offsets[e+1]-1 of Xp belong to expert
+ * e), fp32 accumulation.  Yp [T*topk, hidden] out (fp32 for F32, else bf16).
+ * With a shared expert: Xs [T, hidden] is its input (X, or Xq with
+ * xs_scale for FP8) and Ys [T, hidden] its output; else both may be NULL.
+ * The SwiGLU output is held in the workspace in the compute type (fp32 for
+ * FP8, before its per-row e4m3 requantisation). */
+int moe_expert_ffn(const moe_shape* shape, const void* Xp, const float* xp_scale,
+                   const int32_t* offsets, const void* Xs, const float* xs_scale,
+                   const moe_expert_weights* weights, void* Yp, void* Ys, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* Step 5: Y[t] = sum_{j ascending} G[t,j] * Yp[dst_row[t*k+j]] (+ Ys[t]),
+ * fp32 accumulation, rounded once to the output type.  Rows with dst_row < 0
+ * are skipped.  Ys may be NULL. */
+int moe_combine(const moe_shape* shape, const void* Yp, const int32_t* dst_row,
+                const float* gate_weights, const void* Ys, void* Y, hipStream_t stream);
+
+/* Steps 1-5.  With opts != NULL the router runs and writes expert_ids and
+ * gate_weights; with opts == NULL they are inputs (the mega_moe form, which
+ * takes the routing as given) and Wg is not read.  Y [T, hidden] out. */
+int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                const void* Wg, const moe_expert_weights* weights, int32_t* expert_ids,
+                float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Synchronises `stream`, then reports (and clears) the device-side error
+ * flag in the workspace: MOE_ERR_DEVICE_DATA if an earlier moe_permute,
+ * moe_route or moe_forward on this workspace saw an expert id outside
+ * [0, E) or a token id outside [0, vocab); MOE_OK otherwise. */
+int moe_check_device_error(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a moe_status value. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,528 @@
+// grouped_gemm.hip -- the expert FFN of the routed MoE layer as two grouped
+// GEMMs over ragged per-expert row blocks (CANN "mega_moe" page, §计算过程
+// Expert Compute: Linear1, SwiGLU, Linear2, and its A8W8 block; DeepSeek-V4
+// blog post, §ETP 里的矩阵 for F(X) = (SiLU(X Wg) * X Wu) Wd).
+//
+//   Linear1 + SwiGLU:  A[r, n] = SiLU(H[r, n]) * H[r, f + n],  H = Xp[r] W1[e]
+//   Linear2:           Yp[r]  = A[r] W2[e]
+// for every row r of expert e's block [offsets[e], offsets[e+1]); the shared
+// expert is one more segment whose rows are the T tokens themselves (input
+// Xs, output rows T*k.. of A and Ys).
+//
+// Tile schedule (device side, no host sync): tile_off[e] is the prefix sum of
+// ceil(rows_e / BM) over segments 0..E (E = shared).  The grid is an upper
+// bound of m-tiles times the n-tiles; a block maps its id to (m-tile, n-tile),
+// finds its segment by binary search over tile_off, and exits if past the
+// end.  Padding rows are never computed into outputs and are not counted as
+// work.
+//
+// A block is 256 threads (4 waves) computing a BM x BN tile with K-tiles of
+// 128 bytes: 64 bf16 or 128 e4m3 elements.  Rows of X are K-contiguous and
+// go to LDS as they are; weights are [K, N] row-major, so each thread loads
+// a 4 x 16-byte block and writes it transposed (v_perm byte shuffles) so that
+// LDS holds both operands K-contiguous, which is what each MFMA lane reads.
+// LDS is double buffered and the next K-tile is prefetched into registers
+// while the current one is multiplied.
+//   bf16: v_mfma_f32_16x16x32_bf16 (a lane holds 8 K-consecutive elements)
+//   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (32 per lane)
+// For SwiGLU an N-tile of BN columns holds BN/2 gate columns and the
+// matching BN/2 up columns, and each wave owns equal gate/up sub-tiles, so the
+// gate and up accumulators of an output element sit in the same lane.
+//
+// A8W8 (e4m3): H = C * w1_scale[e, n] * x_scale[r]; the SwiGLU output is
+// written in fp32 and requantised per row (scale = max|A[r]| / 448) by
+// requant_kernel; Linear2 dequantises with w2_scale[e, n] * a_scale[r].
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBKBytes = 128;
+constexpr int kRowBytes = kBKBytes + 16;  // padded LDS row
+
+struct GemmArgs {
+  const void* A;         // routed input rows [M, K]
+  const void* A_sh;      // shared-expert input rows [T, K] (or null)
+  const float* a_scale;  // FP8: per routed row
+  const float* a_scale_sh;
+  const void* W;         // [E, K, Nw]
+  const void* W_sh;      // [K, Nw]
+  const float* w_scale;  // FP8: [E, Nw]
+  const float* w_scale_sh;
+  void* out;             // routed rows [M, Nout]
+  void* out_sh;          // shared rows [T, Nout]
+  const int32_t* offsets;
+  const int32_t* tile_off;
+  int E, K, Nw, Nout, f, T, n_tiles;
+};
+
+template <int PREC>
+struct Mfma;
+
+template <>
+struct Mfma<MOE_PREC_BF16> {
+  static constexpr int kEsz = 2;
+  static constexpr int kStepBytes = 64;  // K bytes per MFMA (32 bf16)
+  typedef bf16x8_t frag;
+  __device__ static frag load(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+  __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<MOE_PREC_FP8> {
+  static constexpr int kEsz = 1;
+  static constexpr int kStepBytes = 128;  // K bytes per MFMA (128 e4m3)
+  typedef i32x8_t frag;
+  __device__ static frag load(const char* p) {
+    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p);
+    i32x4_t hi = *reinterpret_cast<const i32x4_t*>(p + 16);
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
+    // formats 0/0 = e4m3 for both operands; E8M0 scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// Transposed store of a 4(k) x 16-byte block: r[q] holds row k0+q.
+template <int ESZ>
+__device__ __forceinline__ void store_bt(char* Bs, int nl, int kbyte, const uint32_t (&r)[4][4]) {
+  if (ESZ == 2) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t d0 = __builtin_amdgcn_perm(r[1][c >> 1], r[0][c >> 1], sel);
+      uint32_t d1 = __builtin_amdgcn_perm(r[3][c >> 1], r[2][c >> 1], sel);
+      *reinterpret_cast<uint2*>(Bs + (nl + c) * kRowBytes + kbyte) = make_uint2(d0, d1);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint32_t b = c & 3;
+      const uint32_t sel = b | ((4u + b) << 8) | (b << 16) | ((4u + b) << 24);
+      uint32_t t01 = __builtin_amdgcn_perm(r[1][c >> 2], r[0][c >> 2], sel);
+      uint32_t t23 = __builtin_amdgcn_perm(r[3][c >> 2], r[2][c >> 2], sel);
+      *reinterpret_cast<uint32_t*>(Bs + (nl + c) * kRowBytes + kbyte) =
+          __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    }
+  }
+}
+
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
+  using M = Mfma<PREC>;
+  constexpr int ESZ = M::kEsz;
+  constexpr int kColsPer16B = 16 / ESZ;           // elements per 16-byte load
+  constexpr int WM = BM / WAVES_M;
+  constexpr int MT = WM / 16;
+  constexpr int NTW = BN / WAVES_N / 16;          // n-tiles per wave
+  constexpr int kAChunks = BM * kBKBytes / 16;
+  constexpr int kAPer = (kAChunks + kThreads - 1) / kThreads;
+  constexpr int kBBlocks = (kBKBytes / ESZ / 4) * (BN / kColsPer16B);
+  constexpr int kBPer = (kBBlocks + kThreads - 1) / kThreads;
+  constexpr int kBColBlocks = BN / kColsPer16B;
+  static_assert(MT >= 1 && NTW >= 1, "tile shape");
+  static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
+
+  __shared__ __attribute__((aligned(16))) char As[2][BM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char Bs[2][BN * kRowBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  // ------------------------------------------------ tile -> segment
+  const int m = blockIdx.x / g.n_tiles;
+  const int nt = blockIdx.x % g.n_tiles;
+  const int E = g.E;
+  if (m >= g.tile_off[E + 1]) return;
+  int lo = 0, hi = E;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (g.tile_off[mid] <= m)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int seg = lo;
+  const bool shared = (seg == E);
+  int row0, row_end;
+  const char* Abase;
+  const char* Wbase;
+  const float* wsc;
+  const float* asc;
+  char* obase;
+  if (!shared) {
+    row0 = g.offsets[seg] + (m - g.tile_off[seg]) * BM;
+    row_end = g.offsets[seg + 1];
+    Abase = static_cast<const char*>(g.A);
+    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * ESZ;
+    wsc = g.w_scale ? g.w_scale + static_cast<size_t>(seg) * g.Nw : nullptr;
+    asc = g.a_scale;
+    obase = static_cast<char*>(g.out);
+  } else {
+    row0 = (m - g.tile_off[E]) * BM;
+    row_end = g.T;
+    Abase = static_cast<const char*>(g.A_sh);
+    Wbase = static_cast<const char*>(g.W_sh);
+    wsc = g.w_scale_sh;
+    asc = g.a_scale_sh;
+    obase = static_cast<char*>(g.out_sh);
+  }
+  const int K = g.K;
+  const size_t a_ld = static_cast<size_t>(K) * ESZ;    // bytes per A row
+  const size_t w_ld = static_cast<size_t>(g.Nw) * ESZ;  // bytes per W row
+
+  // column of LDS row n (0..BN-1) in the weight matrix
+  auto wcol = [&](int nl) -> int {
+    if (SWIGLU) {
+      const int half = BN / 2;
+      return nl < half ? nt * half + nl : g.f + nt * half + (nl - half);
+    }
+    return nt * BN + nl;
+  };
+
+  uint4 ra[kAPer];
+  uint32_t rb[kBPer][4][4];
+  auto gload = [&](int kt) {
+    const size_t kb0 = static_cast<size_t>(kt) * kBKBytes;
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+      int c = tid + q * kThreads;
+      if (kAChunks % kThreads == 0 || c < kAChunks) {
+        int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
+        int row = min(row0 + r, row_end - 1);
+        ra[q] = *reinterpret_cast<const uint4*>(Abase + row * a_ld + kb0 + c16 * 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBPer; ++q) {
+      int b = tid + q * kThreads;
+      if (kBBlocks % kThreads == 0 || b < kBBlocks) {
+        int nb = b % kBColBlocks, kb = b / kBColBlocks;
+        const char* p = Wbase + (static_cast<size_t>(kt) * (kBKBytes / ESZ) + kb * 4) * w_ld +
+                        static_cast<size_t>(wcol(nb * kColsPer16B)) * ESZ;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint4 v = *reinterpret_cast<const uint4*>(p + r * w_ld);
+          rb[q][r][0] = v.x;
+          rb[q][r][1] = v.y;
+          rb[q][r][2] = v.z;
+          rb[q][r][3] = v.w;
+        }
+      }
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < kAPer; ++q) {
+      int c = tid + q * kThreads;
+      if (kAChunks % kThreads == 0 || c < kAChunks) {
+        int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
+        *reinterpret_cast<uint4*>(&As[buf][r * kRowBytes + c16 * 16]) = ra[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBPer; ++q) {
+      int b = tid + q * kThreads;
+      if (kBBlocks % kThreads == 0 || b < kBBlocks) {
+        int nb = b % kBColBlocks, kb = b / kBColBlocks;
+        store_bt<ESZ>(Bs[buf], nb * kColsPer16B, kb * 4 * ESZ, rb[q]);
+      }
+    }
+  };
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // LDS row of this wave's n-tile j
+  auto brow = [&](int j) -> int {
+    if (SWIGLU) {
+      const int half = BN / 2, per = BN / 2 / WAVES_N;
+      return j < NTW / 2 ? wn * per + j * 16 : half + wn * per + (j - NTW / 2) * 16;
+    }
+    return wn * (BN / WAVES_N) + j * 16;
+  };
+
+  const int KT = K * ESZ / kBKBytes;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kBKBytes; ks += M::kStepBytes) {
+      const int koff = ks + (lane >> 4) * (M::kStepBytes / 4);
+      typename M::frag af[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        af[i] = M::load(&As[buf][(wm * WM + i * 16 + (lane & 15)) * kRowBytes + koff]);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        typename M::frag bfr = M::load(&Bs[buf][(brow(j) + (lane & 15)) * kRowBytes + koff]);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][j] = M::mma(af[i], bfr, acc[i][j]);
+      }
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------ epilogue
+  // lane holds column (lane & 15) and rows 4*(lane >> 4) + v of each 16x16 tile
+  const int col_in = lane & 15;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+      if (row >= row_end) continue;
+      const float rs = (PREC == MOE_PREC_FP8) ? asc[row] : 1.0f;
+      if (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < NTW / 2; ++j) {
+          const int nl = brow(j) + col_in;  // gate LDS row; output column inside the tile
+          const int ncol = nt * (BN / 2) + nl;
+          float hg = acc[i][j][v];
+          float hu = acc[i][j + NTW / 2][v];
+          if (PREC == MOE_PREC_FP8) {
+            hg *= wsc[ncol] * rs;
+            hu *= wsc[g.f + ncol] * rs;
+            static_cast<float*>(static_cast<void*>(obase))[static_cast<size_t>(row) * g.Nout + ncol] =
+                silu(hg) * hu;
+          } else {
+            reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+                f32_to_bf16(silu(hg) * hu);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const int ncol = nt * BN + brow(j) + col_in;
+          float y = acc[i][j][v];
+          if (PREC == MOE_PREC_FP8) y *= wsc[ncol] * rs;
+          reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+              f32_to_bf16(y);
+        }
+      }
+    }
+  }
+}
+
+// tile_off[e+1] = tile_off[e] + ceil(rows_e / BM), segment E = shared (T rows).
+__global__ __launch_bounds__(kMaxExperts) void tile_offsets_kernel(const int32_t* __restrict__ offsets,
+                                                                   int E, int T_shared, int BM,
+                                                                   int32_t* __restrict__ tile_off) {
+  __shared__ int32_t s[kMaxExperts];
+  const int e = threadIdx.x;
+  int t = 0;
+  if (e < E) t = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
+  s[e] = t;
+  __syncthreads();
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    int v = (e >= o) ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) tile_off[e + 1] = s[e];
+  if (e == 0) tile_off[0] = 0;
+  if (e == E - 1) tile_off[E + 1] = s[e] + (T_shared + BM - 1) / BM;
+}
+
+// FP8: per-row requantisation of the fp32 SwiGLU output; one block per row.
+__global__ __launch_bounds__(256) void requant_kernel(const float* __restrict__ A, int f,
+                                                      uint8_t* __restrict__ Aq,
+                                                      float* __restrict__ a_scale) {
+  __shared__ float s_red[4];
+  const size_t r = blockIdx.x;
+  const float* a = A + r * f;
+  float amax = 0.0f;
+  for (int c = threadIdx.x * 4; c < f; c += 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(a + c);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (threadIdx.x == 0) a_scale[r] = s;
+  for (int c = threadIdx.x * 4; c < f; c += 256 * 4) {
+    float4 v = *reinterpret_cast<const float4*>(a + c);
+    *reinterpret_cast<uint32_t*>(Aq + r * f + c) = f32x4_to_e4m3x4(v.x / s, v.y / s, v.z / s, v.w / s);
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+// Plain FMA kernels for the fp32 layer (one output element per thread).
+__device__ __forceinline__ int find_segment(const int32_t* offsets, int E, int r) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= r)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void l1_f32_kernel(FfnArgs a, int rows_routed) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int rows = rows_routed + (a.has_shared ? a.T : 0);
+  if (idx >= static_cast<size_t>(rows) * a.f) return;
+  const int r = static_cast<int>(idx / a.f), n = static_cast<int>(idx % a.f);
+  const float* x;
+  const float* W;
+  if (r < rows_routed) {
+    int e = find_segment(a.offsets, a.E, r);
+    x = static_cast<const float*>(a.Xp) + static_cast<size_t>(r) * a.h;
+    W = static_cast<const float*>(a.w.W1) + static_cast<size_t>(e) * a.h * 2 * a.f;
+  } else {
+    x = static_cast<const float*>(a.Xs) + static_cast<size_t>(r - rows_routed) * a.h;
+    W = static_cast<const float*>(a.w.Ws1);
+  }
+  float hg = 0.0f, hu = 0.0f;
+  for (int c = 0; c < a.h; ++c) {
+    hg = fmaf(x[c], W[static_cast<size_t>(c) * 2 * a.f + n], hg);
+    hu = fmaf(x[c], W[static_cast<size_t>(c) * 2 * a.f + a.f + n], hu);
+  }
+  static_cast<float*>(a.A)[idx] = silu(hg) * hu;
+}
+
+__global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int rows = rows_routed + (a.has_shared ? a.T : 0);
+  if (idx >= static_cast<size_t>(rows) * a.h) return;
+  const int r = static_cast<int>(idx / a.h), o = static_cast<int>(idx % a.h);
+  const float* u = static_cast<const float*>(a.A) + static_cast<size_t>(r) * a.f;
+  const float* W;
+  float* out;
+  if (r < rows_routed) {
+    int e = find_segment(a.offsets, a.E, r);
+    W = static_cast<const float*>(a.w.W2) + static_cast<size_t>(e) * a.f * a.h;
+    out = static_cast<float*>(a.Yp) + static_cast<size_t>(r) * a.h;
+  } else {
+    W = static_cast<const float*>(a.w.Ws2);
+    out = static_cast<float*>(a.Ys) + static_cast<size_t>(r - rows_routed) * a.h;
+  }
+  float y = 0.0f;
+  for (int n = 0; n < a.f; ++n) y = fmaf(u[n], W[static_cast<size_t>(n) * a.h + o], y);
+  out[o] = y;
+}
+
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU>
+hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
+  dim3 grid(ub_m * g.n_tiles);
+  hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU>), grid,
+                     dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
+template <int PREC, int BM, int WAVES_M, int WAVES_N>
+hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
+  constexpr int BN = 128;
+  constexpr int ESZ = (PREC == MOE_PREC_FP8) ? 1 : 2;
+  const int rows = a.T * a.k;
+  const int T_sh = a.has_shared ? a.T : 0;
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.offsets, a.E,
+                     T_sh, BM, a.tile_off);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int ub_m = (rows + BM - 1) / BM + (a.E < rows ? a.E : rows) + (T_sh + BM - 1) / BM;
+  const size_t arow_bytes = static_cast<size_t>(a.f) * (PREC == MOE_PREC_FP8 ? 1 : 2);
+
+  GemmArgs g1{};
+  g1.A = a.Xp;
+  g1.A_sh = a.Xs;
+  g1.a_scale = a.xp_scale;
+  g1.a_scale_sh = a.xs_scale;
+  g1.W = a.w.W1;
+  g1.W_sh = a.w.Ws1;
+  g1.w_scale = a.w.w1_scale;
+  g1.w_scale_sh = a.w.ws1_scale;
+  g1.out = a.A;
+  g1.out_sh = static_cast<char*>(a.A) +
+              static_cast<size_t>(rows) * a.f * (PREC == MOE_PREC_FP8 ? 4 : 2);
+  g1.offsets = a.offsets;
+  g1.tile_off = a.tile_off;
+  g1.E = a.E;
+  g1.K = a.h;
+  g1.Nw = 2 * a.f;
+  g1.Nout = a.f;
+  g1.f = a.f;
+  g1.T = a.T;
+  g1.n_tiles = 2 * a.f / BN;
+  err = launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, true>(g1, ub_m, stream);
+  if (err != hipSuccess) return err;
+
+  const void* A2 = a.A;
+  const float* as2 = nullptr;
+  if (PREC == MOE_PREC_FP8) {
+    const int arows = rows + T_sh;
+    hipLaunchKernelGGL(requant_kernel, dim3(arows), dim3(256), 0, stream,
+                       static_cast<const float*>(a.A), a.f, static_cast<uint8_t*>(a.Aq), a.a_scale);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    A2 = a.Aq;
+    as2 = a.a_scale;
+  }
+  GemmArgs g2{};
+  g2.A = A2;
+  g2.A_sh = static_cast<const char*>(A2) + static_cast<size_t>(rows) * arow_bytes;
+  g2.a_scale = as2;
+  g2.a_scale_sh = as2 ? as2 + rows : nullptr;
+  g2.W = a.w.W2;
+  g2.W_sh = a.w.Ws2;
+  g2.w_scale = a.w.w2_scale;
+  g2.w_scale_sh = a.w.ws2_scale;
+  g2.out = a.Yp;
+  g2.out_sh = a.Ys;
+  g2.offsets = a.offsets;
+  g2.tile_off = a.tile_off;
+  g2.E = a.E;
+  g2.K = a.f;
+  g2.Nw = a.h;
+  g2.Nout = a.h;
+  g2.f = a.f;
+  g2.T = a.T;
+  g2.n_tiles = a.h / BN;
+  (void)ESZ;
+  return launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, false>(g2, ub_m, stream);
+}
+
+}  // namespace
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
+  const int rows = a.T * a.k;
+  if (a.precision == MOE_PREC_F32) {
+    const int T_sh = a.has_shared ? a.T : 0;
+    size_t n1 = static_cast<size_t>(rows + T_sh) * a.f;
+    hipLaunchKernelGGL(l1_f32_kernel, dim3((n1 + 255) / 256), dim3(256), 0, stream, a, rows);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    size_t n2 = static_cast<size_t>(rows + T_sh) * a.h;
+    hipLaunchKernelGGL(l2_f32_kernel, dim3((n2 + 255) / 256), dim3(256), 0, stream, a, rows);
+    return hipGetLastError();
+  }
+  // Rows per expert decide the M tile: a decode-sized batch (a few rows per
+  // expert) streams weights with 16-row tiles, a prefill batch uses 128.
+  const bool small = static_cast<long>(rows) < 16L * a.E;
+  if (a.precision == MOE_PREC_BF16)
+    return small ? run_ffn<MOE_PREC_BF16, 16, 1, 4>(a, stream)
+                 : run_ffn<MOE_PREC_BF16, 128, 2, 2>(a, stream);
+  return small ? run_ffn<MOE_PREC_FP8, 16, 1, 4>(a, stream)
+               : run_ffn<MOE_PREC_FP8, 128, 2, 2>(a, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,303 @@
+// moe_api.cpp -- the C ABI of libmoe (declared in include/moe.h): host-side
+// validation, workspace carving and kernel launches.  No entry point reads
+// device memory or synchronises, except moe_check_device_error.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->tokens < 1 || s->hidden < 1 || s->experts < 1 || s->topk < 1 || s->inter < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (s->topk > s->experts || s->topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
+  if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_FP8) return MOE_ERR_INVALID_ARG;
+  if (s->experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->hidden % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->inter % (s->precision == MOE_PREC_FP8 ? 128 : 64) != 0) return MOE_ERR_UNSUPPORTED;
+  // row and element counts must fit the kernels' 32-bit row indices
+  const long long rows = static_cast<long long>(s->tokens) * (s->topk + 1);
+  if (rows > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
+  if (rows * (s->hidden > s->inter ? s->hidden : s->inter) > (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_ws(const moe_shape* s, const void* ws, size_t ws_bytes) {
+  if (!ws || !aligned(ws, kAlign)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < make_layout(*s).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int check_weights(const moe_shape* s, const moe_expert_weights* w) {
+  if (!w || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
+  if (s->precision == MOE_PREC_FP8 && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (s->has_shared) {
+    if (!w->Ws1 || !w->Ws2) return MOE_ERR_INVALID_ARG;
+    if (s->precision == MOE_PREC_FP8 && (!w->ws1_scale || !w->ws2_scale))
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int check_route_opts(const moe_route_opts* o) {
+  if (!o) return MOE_ERR_INVALID_ARG;
+  if (o->score_fn < MOE_SCORE_SIGMOID || o->score_fn > MOE_SCORE_SQRT_SOFTPLUS)
+    return MOE_ERR_INVALID_ARG;
+  if (o->renorm != 0 && o->renorm != 1) return MOE_ERR_INVALID_ARG;
+  if ((o->token_ids == nullptr) != (o->tid2eid == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (o->tid2eid && o->vocab < 1) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+RouteArgs route_args(const moe_shape* s, const moe_route_opts* o, const void* X, const void* Wg,
+                     int32_t* ids, float* G, float* keys, void* ws) {
+  RouteArgs a{};
+  a.T = s->tokens;
+  a.h = s->hidden;
+  a.E = s->experts;
+  a.k = s->topk;
+  a.precision = s->precision;
+  a.score_fn = o->score_fn;
+  a.renorm = o->renorm;
+  a.alpha = o->alpha;
+  a.X = X;
+  a.Wg = Wg;
+  a.beta = o->expert_bias;
+  a.gate_bias = o->gate_bias;
+  a.token_ids = o->token_ids;
+  a.tid2eid = o->tid2eid;
+  a.vocab = o->vocab;
+  a.ids = ids;
+  a.G = G;
+  a.keys = keys;
+  a.flag = at<int32_t>(ws, make_layout(*s).flag);
+  return a;
+}
+
+PermuteArgs permute_args(const moe_shape* s, const int32_t* ids, const void* X, int32_t* counts,
+                         int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
+                         float* xp_scale, void* Xq, float* x_scale, void* ws) {
+  Layout L = make_layout(*s);
+  PermuteArgs a{};
+  a.T = s->tokens;
+  a.h = s->hidden;
+  a.E = s->experts;
+  a.k = s->topk;
+  a.precision = s->precision;
+  a.nblk = L.nblk;
+  a.ids = ids;
+  a.X = X;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.dst_row = dst_row;
+  a.src_tok = src_tok;
+  a.Xp = Xp;
+  a.xp_scale = xp_scale;
+  a.Xq = Xq;
+  a.x_scale = x_scale;
+  a.blk_cnt = at<int32_t>(ws, L.blk_cnt);
+  a.local_rank = at<int32_t>(ws, L.local_rank);
+  a.flag = at<int32_t>(ws, L.flag);
+  return a;
+}
+
+FfnArgs ffn_args(const moe_shape* s, const void* Xp, const float* xp_scale, const int32_t* offsets,
+                 const void* Xs, const float* xs_scale, const moe_expert_weights* w, void* Yp,
+                 void* Ys, void* ws) {
+  Layout L = make_layout(*s);
+  FfnArgs a{};
+  a.T = s->tokens;
+  a.h = s->hidden;
+  a.E = s->experts;
+  a.k = s->topk;
+  a.f = s->inter;
+  a.has_shared = s->has_shared;
+  a.precision = s->precision;
+  a.Xp = Xp;
+  a.xp_scale = xp_scale;
+  a.offsets = offsets;
+  a.Xs = Xs;
+  a.xs_scale = xs_scale;
+  a.w = *w;
+  a.Yp = Yp;
+  a.Ys = Ys;
+  a.A = at<void>(ws, L.A);
+  a.Aq = at<void>(ws, L.Aq);
+  a.a_scale = at<float>(ws, L.a_scale);
+  a.tile_off = at<int32_t>(ws, L.tile_off);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return make_layout(*shape).total;
+}
+
+int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+              int32_t* expert_ids, float* gate_weights, float* keys_out, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_route_opts(opts)) != MOE_OK) return st;
+  if (!X || !Wg || !expert_ids || !gate_weights) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  RouteArgs a = route_args(shape, opts, X, Wg, expert_ids, gate_weights, keys_out, workspace);
+  hipError_t e = launch_clear_flag(a.flag, stream);
+  if (e == hipSuccess) e = launch_route(a, stream);
+  return hip_status(e);
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,
+                int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
+                float* xp_scale, void* Xq, float* x_scale, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!expert_ids || !X || !counts || !offsets || !dst_row || !src_tok || !Xp)
+    return MOE_ERR_INVALID_ARG;
+  if (shape->precision == MOE_PREC_FP8 && (!xp_scale || !Xq || !x_scale))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  PermuteArgs a = permute_args(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp,
+                               xp_scale, Xq, x_scale, workspace);
+  hipError_t e = launch_clear_flag(a.flag, stream);
+  if (e == hipSuccess) e = launch_permute(a, stream);
+  return hip_status(e);
+}
+
+int moe_expert_ffn(const moe_shape* shape, const void* Xp, const float* xp_scale,
+                   const int32_t* offsets, const void* Xs, const float* xs_scale,
+                   const moe_expert_weights* weights, void* Yp, void* Ys, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(shape, weights)) != MOE_OK) return st;
+  if (!Xp || !offsets || !Yp) return MOE_ERR_INVALID_ARG;
+  if (shape->precision == MOE_PREC_FP8 && !xp_scale) return MOE_ERR_INVALID_ARG;
+  if (shape->has_shared) {
+    if (!Xs || !Ys) return MOE_ERR_INVALID_ARG;
+    if (shape->precision == MOE_PREC_FP8 && !xs_scale) return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  FfnArgs a = ffn_args(shape, Xp, xp_scale, offsets, Xs, xs_scale, weights, Yp, Ys, workspace);
+  return hip_status(launch_expert_ffn(a, stream));
+}
+
+int moe_combine(const moe_shape* shape, const void* Yp, const int32_t* dst_row,
+                const float* gate_weights, const void* Ys, void* Y, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!Yp || !dst_row || !gate_weights || !Y) return MOE_ERR_INVALID_ARG;
+  CombineArgs a{};
+  a.T = shape->tokens;
+  a.h = shape->hidden;
+  a.k = shape->topk;
+  a.precision = shape->precision;
+  a.Yp = Yp;
+  a.dst_row = dst_row;
+  a.G = gate_weights;
+  a.Ys = Ys;
+  a.Y = Y;
+  return hip_status(launch_combine(a, stream));
+}
+
+int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                const void* Wg, const moe_expert_weights* weights, int32_t* expert_ids,
+                float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_weights(shape, weights)) != MOE_OK) return st;
+  if (!X || !expert_ids || !gate_weights || !Y) return MOE_ERR_INVALID_ARG;
+  if (opts) {
+    if ((st = check_route_opts(opts)) != MOE_OK) return st;
+    if (!Wg) return MOE_ERR_INVALID_ARG;
+  }
+  if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  const Layout L = make_layout(*shape);
+  void* ws = workspace;
+  const bool fp8 = shape->precision == MOE_PREC_FP8;
+  int32_t* flag = at<int32_t>(ws, L.flag);
+  hipError_t e = launch_clear_flag(flag, stream);
+  if (e == hipSuccess && opts) {
+    RouteArgs r = route_args(shape, opts, X, Wg, expert_ids, gate_weights, nullptr, ws);
+    e = launch_route(r, stream);
+  }
+  if (e == hipSuccess) {
+    PermuteArgs p = permute_args(shape, expert_ids, X, at<int32_t>(ws, L.counts),
+                                 at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.dst_row),
+                                 at<int32_t>(ws, L.src_tok), at<void>(ws, L.Xp),
+                                 fp8 ? at<float>(ws, L.xp_scale) : nullptr,
+                                 fp8 ? at<void>(ws, L.Xq) : nullptr,
+                                 fp8 ? at<float>(ws, L.x_scale) : nullptr, ws);
+    e = launch_permute(p, stream);
+  }
+  if (e == hipSuccess) {
+    FfnArgs f = ffn_args(shape, at<void>(ws, L.Xp), fp8 ? at<float>(ws, L.xp_scale) : nullptr,
+                         at<int32_t>(ws, L.offsets), fp8 ? at<void>(ws, L.Xq) : X,
+                         fp8 ? at<float>(ws, L.x_scale) : nullptr, weights, at<void>(ws, L.Yp),
+                         shape->has_shared ? at<void>(ws, L.Ys) : nullptr, ws);
+    e = launch_expert_ffn(f, stream);
+  }
+  if (e == hipSuccess) {
+    CombineArgs c{};
+    c.T = shape->tokens;
+    c.h = shape->hidden;
+    c.k = shape->topk;
+    c.precision = shape->precision;
+    c.Yp = at<void>(ws, L.Yp);
+    c.dst_row = at<int32_t>(ws, L.dst_row);
+    c.G = gate_weights;
+    c.Ys = shape->has_shared ? at<void>(ws, L.Ys) : nullptr;
+    c.Y = Y;
+    e = launch_combine(c, stream);
+  }
+  return hip_status(e);
+}
+
+int moe_check_device_error(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < kAlign)
+    return MOE_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+  int32_t flag = 0;
+  if (hipMemcpy(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (flag != 0) {
+    const int32_t zero = 0;
+    if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_ERR_DEVICE_DATA;
+  }
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "HIP runtime or launch error";
+    case MOE_ERR_DEVICE_DATA: return "device data out of contract (expert or token id)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// moe_internal.h -- types, device helpers, workspace layout and launcher
+// declarations shared by the HIP kernels and the C ABI of libmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- vectors
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+
+// ---------------------------------------------------------------- numbers
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.  The
+// clamp makes the hardware conversion's out-of-range behaviour irrelevant:
+// every value that reaches it lies in [-448, 448].
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false)) & 0xffu;
+}
+
+// Four fp32 -> four e4m3 codes packed little-endian in one word.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  c = fminf(fmaxf(c, -448.0f), 448.0f);
+  d = fminf(fmaxf(d, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- workspace
+constexpr size_t kAlign = 256;
+constexpr int kPermChunk = 256;  // assignments per dispatch block
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 16;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline size_t act_bytes(int precision) { return precision == MOE_PREC_F32 ? 4 : 2; }
+inline size_t xp_bytes(int precision) {
+  return precision == MOE_PREC_F32 ? 4 : (precision == MOE_PREC_BF16 ? 2 : 1);
+}
+
+// Byte offsets of every region inside the caller's workspace.
+struct Layout {
+  size_t flag;        // int32 error flag (+ padding to 256 B)
+  size_t blk_cnt;     // [nblk, E] int32 per-block expert counts
+  size_t local_rank;  // [T*k] int32 rank of an assignment inside its block
+  size_t tile_off;    // [E+2] int32 m-tile prefix of the grouped GEMM
+  size_t counts, offsets, dst_row, src_tok;  // forward-internal dispatch results
+  size_t Xp, xp_scale, Xq, x_scale;          // forward-internal dispatched rows
+  size_t A;                                  // [T*k + T*S, f] SwiGLU output
+  size_t Aq, a_scale;                        // FP8: requantised SwiGLU output
+  size_t Yp, Ys;                             // forward-internal expert outputs
+  size_t total;
+  int nblk;
+};
+
+inline Layout make_layout(const moe_shape& s) {
+  Layout L{};
+  size_t T = s.tokens, h = s.hidden, E = s.experts, k = s.topk, f = s.inter;
+  size_t rows = T * k, arows = rows + (s.has_shared ? T : 0);
+  L.nblk = static_cast<int>((rows + kPermChunk - 1) / kPermChunk);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.flag = take(kAlign);
+  L.blk_cnt = take(static_cast<size_t>(L.nblk) * E * 4);
+  L.local_rank = take(rows * 4);
+  L.tile_off = take((E + 2) * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.dst_row = take(rows * 4);
+  L.src_tok = take(rows * 4);
+  L.Xp = take(rows * h * xp_bytes(s.precision));
+  bool fp8 = s.precision == MOE_PREC_FP8;
+  L.xp_scale = take(fp8 ? rows * 4 : 0);
+  L.Xq = take(fp8 ? T * h : 0);
+  L.x_scale = take(fp8 ? T * 4 : 0);
+  L.A = take(arows * f * (fp8 ? 4 : act_bytes(s.precision)));
+  L.Aq = take(fp8 ? arows * f : 0);
+  L.a_scale = take(fp8 ? arows * 4 : 0);
+  L.Yp = take(rows * h * act_bytes(s.precision));
+  L.Ys = take(s.has_shared ? T * h * act_bytes(s.precision) : 0);
+  L.total = o;
+  return L;
+}
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are already valid.
+struct RouteArgs {
+  int T, h, E, k, precision, score_fn, renorm;
+  float alpha;
+  const void* X;
+  const void* Wg;
+  const float* beta;
+  const float* gate_bias;
+  const int32_t* token_ids;
+  const int32_t* tid2eid;
+  int vocab;
+  int32_t* ids;
+  float* G;
+  float* keys;
+  int32_t* flag;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+struct PermuteArgs {
+  int T, h, E, k, precision, nblk;
+  const int32_t* ids;
+  const void* X;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* dst_row;
+  int32_t* src_tok;
+  void* Xp;
+  float* xp_scale;
+  void* Xq;
+  float* x_scale;
+  int32_t* blk_cnt;
+  int32_t* local_rank;
+  int32_t* flag;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+
+struct FfnArgs {
+  int T, h, E, k, f, has_shared, precision;
+  const void* Xp;
+  const float* xp_scale;
+  const int32_t* offsets;
+  const void* Xs;
+  const float* xs_scale;
+  moe_expert_weights w;
+  void* Yp;
+  void* Ys;
+  void* A;  // [T*k + T*S, f] (fp32 for FP8)
+  void* Aq;
+  float* a_scale;
+  int32_t* tile_off;
+};
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  int T, h, k, precision;
+  const void* Yp;
+  const int32_t* dst_row;
+  const float* G;
+  const void* Ys;
+  void* Y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream);
+
+}  // namespace moe

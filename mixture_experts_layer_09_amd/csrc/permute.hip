@@ -1,0 +1,210 @@
+// permute.hip -- dispatch of the routed MoE layer: per-expert counts, the
+// destination row of every (token, choice) assignment, and the duplicating
+// row copy X -> Xp (CANN "mega_moe" page, §计算过程 EP Dispatch; DeepSeek-V4
+// blog post, §计数与重排).
+//
+// Three kernels, no global atomics, deterministic:
+//   1. count_rank: block b takes assignments [b*256, (b+1)*256) of the flat
+//      array ids[T*k]; it writes its per-expert counts blk_cnt[b][e] and the
+//      rank of each assignment among the block's earlier assignments to the
+//      same expert (one pass over LDS per thread; broadcast reads).
+//   2. scan: one block turns blk_cnt into counts[e], offsets[e] (exclusive
+//      prefix over experts) and, in place, blk_cnt[b][e] = offsets[e] + sum
+//      of blk_cnt[b'][e] over b' < b (the block's base row for expert e).
+//   3. scatter: one block per token; dst_row[t*k+j] = base + rank, src_tok of
+//      that row = t, and the token row is copied to each of its k rows with
+//      16-byte loads and stores.  For A8W8 the row is quantised to e4m3 once
+//      (scale = max|x| / 448) and the codes are what is copied.
+// Row order inside an expert block is ascending t*k+j: the stable order the
+// pages leave to the implementation ("any fixed order").
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(kPermChunk) void count_rank_kernel(const int32_t* __restrict__ ids,
+                                                                int n, int E,
+                                                                int32_t* __restrict__ blk_cnt,
+                                                                int32_t* __restrict__ local_rank,
+                                                                int32_t* __restrict__ flag) {
+  __shared__ int32_t s_ids[kPermChunk];
+  __shared__ int32_t s_cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  const int base = blockIdx.x * kPermChunk;
+  const int i = base + tid;
+  int e = -1;
+  if (i < n) {
+    e = ids[i];
+    if (e < 0 || e >= E) {
+      flag[0] = 1;  // every writer stores the same value
+      e = -1;
+    }
+  }
+  s_ids[tid] = e;
+  for (int x = tid; x < E; x += kPermChunk) s_cnt[x] = 0;
+  __syncthreads();
+  // rank among earlier assignments of this block to the same expert
+  int rank = 0;
+  for (int j = 0; j < tid; ++j) rank += (s_ids[j] == e) ? 1 : 0;
+  if (i < n) local_rank[i] = (e >= 0) ? rank : -1;
+  // the last assignment of each expert in the block knows the block's count
+  bool last = (e >= 0);
+  for (int j = tid + 1; j < kPermChunk && last; ++j) last = (s_ids[j] != e);
+  if (last) s_cnt[e] = rank + 1;
+  __syncthreads();
+  for (int x = tid; x < E; x += kPermChunk)
+    blk_cnt[static_cast<size_t>(blockIdx.x) * E + x] = s_cnt[x];
+}
+
+// One block of 512 threads; E <= 512, one thread per expert.
+__global__ __launch_bounds__(kMaxExperts) void scan_kernel(int nblk, int E,
+                                                           int32_t* __restrict__ blk_cnt,
+                                                           int32_t* __restrict__ counts,
+                                                           int32_t* __restrict__ offsets) {
+  __shared__ int32_t s[kMaxExperts];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) total += blk_cnt[static_cast<size_t>(b) * E + e];
+  s[e] = (e < E) ? total : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over the experts
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    int v = (e >= o) ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    int off = s[e] - total;
+    counts[e] = total;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = s[e];
+    int run = off;
+    for (int b = 0; b < nblk; ++b) {
+      size_t at = static_cast<size_t>(b) * E + e;
+      int c = blk_cnt[at];
+      blk_cnt[at] = run;
+      run += c;
+    }
+  }
+}
+
+// One block (256 threads) per token.  VEC = 16-byte chunks of a row.
+template <int PREC>
+__global__ __launch_bounds__(256) void scatter_kernel(
+    int T, int h, int E, int k, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ blk_base, const int32_t* __restrict__ local_rank,
+    const void* __restrict__ X, int32_t* __restrict__ dst_row, int32_t* __restrict__ src_tok,
+    void* __restrict__ Xp, float* __restrict__ xp_scale, void* __restrict__ Xq,
+    float* __restrict__ x_scale) {
+  __shared__ int32_t s_dst[kMaxTopk];
+  __shared__ float s_red[4];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    const int i = t * k + tid;
+    const int e = ids[i];
+    int d = -1;
+    if (e >= 0 && e < E) {
+      d = blk_base[static_cast<size_t>(i / kPermChunk) * E + e] + local_rank[i];
+      src_tok[d] = t;
+    }
+    dst_row[i] = d;
+    s_dst[tid] = d;
+  }
+  if (PREC != MOE_PREC_FP8) {
+    __syncthreads();
+    const int esz = (PREC == MOE_PREC_F32) ? 4 : 2;
+    const int nvec = h * esz / 16;
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(X) +
+                                                      static_cast<size_t>(t) * h * esz);
+    for (int v = tid; v < nvec; v += 256) {
+      uint4 val = src[v];
+      for (int j = 0; j < k; ++j) {
+        int d = s_dst[j];
+        if (d >= 0)
+          reinterpret_cast<uint4*>(static_cast<char*>(Xp) + static_cast<size_t>(d) * h * esz)[v] =
+              val;
+      }
+    }
+  } else {
+    // A8W8: scale = max|x| / 448 (1 for a zero row), codes = RNE_sat(x / scale)
+    const uint16_t* xr = static_cast<const uint16_t*>(X) + static_cast<size_t>(t) * h;
+    float amax = 0.0f;
+    for (int c = tid * 8; c < h; c += 256 * 8) {
+      uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[q] << 16)));
+        amax = fmaxf(amax, fabsf(__uint_as_float(w[q] & 0xffff0000u)));
+      }
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) s_red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    if (tid == 0) x_scale[t] = s;
+    if (tid < k && s_dst[tid] >= 0) xp_scale[s_dst[tid]] = s;
+    uint8_t* xq = static_cast<uint8_t*>(Xq) + static_cast<size_t>(t) * h;
+    for (int c = tid * 8; c < h; c += 256 * 8) {
+      uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t lo = f32x4_to_e4m3x4(__uint_as_float(w[0] << 16) / s,
+                                    __uint_as_float(w[0] & 0xffff0000u) / s,
+                                    __uint_as_float(w[1] << 16) / s,
+                                    __uint_as_float(w[1] & 0xffff0000u) / s);
+      uint32_t hi = f32x4_to_e4m3x4(__uint_as_float(w[2] << 16) / s,
+                                    __uint_as_float(w[2] & 0xffff0000u) / s,
+                                    __uint_as_float(w[3] << 16) / s,
+                                    __uint_as_float(w[3] & 0xffff0000u) / s);
+      uint2 q = make_uint2(lo, hi);
+      *reinterpret_cast<uint2*>(xq + c) = q;
+      for (int j = 0; j < k; ++j) {
+        int d = s_dst[j];
+        if (d >= 0)
+          *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Xp) + static_cast<size_t>(d) * h + c) =
+              q;
+      }
+    }
+  }
+}
+
+__global__ void clear_flag_kernel(int32_t* flag) { flag[0] = 0; }
+
+}  // namespace
+
+hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, stream, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
+  const int n = a.T * a.k;
+  hipLaunchKernelGGL(count_rank_kernel, dim3(a.nblk), dim3(kPermChunk), 0, stream, a.ids, n, a.E,
+                     a.blk_cnt, a.local_rank, a.flag);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.nblk, a.E, a.blk_cnt,
+                     a.counts, a.offsets);
+  switch (a.precision) {
+    case MOE_PREC_F32:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_F32>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
+                         a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
+                         a.xp_scale, a.Xq, a.x_scale);
+      break;
+    case MOE_PREC_BF16:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_BF16>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
+                         a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
+                         a.xp_scale, a.Xq, a.x_scale);
+      break;
+    default:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_FP8>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
+                         a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
+                         a.xp_scale, a.Xq, a.x_scale);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe
