@@ -1,0 +1,254 @@
+"""Benchmark of the routed MoE layer forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one whole layer forward (route -> permute -> expert FFN -> combine,
+the four C-ABI calls that moe_forward makes) over one batch of seeded
+synthetic tokens already resident in HBM.  The default workload is the
+V4-Pro-shaped bf16 layer (T=8192, h=7168, 384 experts, top-6, f=3072, one
+shared expert, Zipf(0.8) expert load).  HIP events recorded on the launch
+stream between the four calls give per-stage times inside the timed region;
+the grouped GEMM stage (moe_expert_ffn: Linear1+SwiGLU and Linear2) is the
+dominant one and carries the roofline figures.
+
+Prints one JSON line.  Runs on one GPU only: --gpus N with N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak) at 1 GPU"
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp32": 157.3}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(wl, counts):
+    """FLOPs and HBM bytes the grouped GEMM stage must do for these counts:
+    every routed and shared row through Linear1 (h -> 2f) and Linear2 (f -> h);
+    the weights of every expert that received a row, read once; the input rows
+    read once and the output rows written once."""
+    h, f, k, T = wl.hidden, wl.inter, wl.topk, wl.T
+    rows = T * k + (T if wl.shared else 0)
+    flops = 2.0 * rows * (h * 2 * f + f * h)
+    wbytes = 1 if wl.precision == "fp8" else (4 if wl.precision == "fp32" else 2)
+    xbytes = wbytes
+    obytes = 4 if wl.precision == "fp32" else 2
+    active = int((counts > 0).sum()) + (1 if wl.shared else 0)
+    weight_bytes = active * 3.0 * h * f * wbytes
+    act_bytes = rows * h * (xbytes + obytes)
+    return flops, weight_bytes + act_bytes, active
+
+
+def cpu_baseline(inp, gpu_ids, n_tok, log_fn=log):
+    """Time the CPU oracle (as it stands) on the first n_tok tokens: routing
+    of those tokens plus the per-token expert loop."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tests.helpers import bits, f64
+
+    wl = inp["workload"]
+    sel = np.arange(n_tok)
+    ids_g = gpu_ids[:n_tok]
+    experts = sorted(set(int(e) for e in ids_g.ravel() if e >= 0))
+    remap = {e: i for i, e in enumerate(experts)}
+    sub = {}
+    idx = torch.tensor(experts, dtype=torch.long, device=inp["W1"].device)
+    sub["W1"] = bits(inp["W1"].index_select(0, idx))
+    sub["W2"] = bits(inp["W2"].index_select(0, idx))
+    sub["w1_scale"] = bits(inp["w1_scale"].index_select(0, idx)) if inp["w1_scale"] is not None else None
+    sub["w2_scale"] = bits(inp["w2_scale"].index_select(0, idx)) if inp["w2_scale"] is not None else None
+    X = bits(inp["X"][:n_tok])
+    Wg = bits(inp["Wg"])
+    t0 = time.perf_counter()
+    r = oracle.route(X, Wg, wl.topk, gate_bias=f64(inp["gate_bias"]), beta=f64(inp["beta"]),
+                     score=wl.score, renorm=wl.renorm, alpha=wl.alpha,
+                     token_ids=bits(inp["token_ids"][:n_tok]) if inp["token_ids"] is not None else None,
+                     tid2eid=bits(inp["tid2eid"]))
+    t_route = time.perf_counter() - t0
+    # the expert loop runs on the GPU's selection (equal to the oracle's at
+    # every clear margin) so that only the copied experts are needed
+    ids_local = np.vectorize(remap.get)(ids_g).astype(np.int32)
+    L = oracle.Layer(wl.precision, X, sub["W1"], sub["W2"], w1_scale=sub["w1_scale"],
+                     w2_scale=sub["w2_scale"], Ws1=bits(inp["Ws1"]), Ws2=bits(inp["Ws2"]),
+                     ws1_scale=bits(inp["ws1_scale"]), ws2_scale=bits(inp["ws2_scale"]),
+                     k=wl.topk)
+    t1 = time.perf_counter()
+    L.tokens(ids_local, r["G"])
+    t_ffn = time.perf_counter() - t1
+    total = t_route + t_ffn
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    cores = min(cores, len(os.sched_getaffinity(0)))
+    log_fn(f"[bench] cpu oracle: {n_tok} tokens in {total:.2f} s (route {t_route:.2f} s)")
+    return {"value": n_tok / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tok} of {wl.T} tokens of the same workload: fp64 routing of "
+                      f"those tokens + per-token loop over their {wl.topk} routed experts"
+                      + (" and the shared expert" if wl.shared else ""),
+            "seconds": round(total, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="v4pro_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0: auto)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "part of it (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_09_amd as moe
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {wl.name} on cuda:0")
+    t = time.perf_counter()
+    inp = synth.make_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.perf_counter() - t:.1f} s")
+
+    shape = moe.make_shape(wl.T, wl.hidden, wl.experts, wl.topk, wl.inter, wl.shared, wl.precision)
+    ws = moe.alloc_workspace(shape)
+    opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, inp["beta"], inp["gate_bias"],
+                               inp["token_ids"], inp["tid2eid"])
+    weights = moe.make_weights(inp["W1"], inp["W2"], inp["w1_scale"], inp["w2_scale"], inp["Ws1"],
+                               inp["Ws2"], inp["ws1_scale"], inp["ws2_scale"])
+    dev = "cuda"
+    fp8 = wl.precision == "fp8"
+    odt = torch.float32 if wl.precision == "fp32" else torch.bfloat16
+    xdt = torch.float8_e4m3fn if fp8 else odt
+    T, k, h, E = wl.T, wl.topk, wl.hidden, wl.experts
+    n = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    G = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    dst = torch.empty(n, dtype=torch.int32, device=dev)
+    src = torch.empty(n, dtype=torch.int32, device=dev)
+    Xp = torch.empty((n, h), dtype=xdt, device=dev)
+    xps = torch.empty(n, dtype=torch.float32, device=dev) if fp8 else None
+    Xq = torch.empty((T, h), dtype=torch.float8_e4m3fn, device=dev) if fp8 else None
+    xs = torch.empty(T, dtype=torch.float32, device=dev) if fp8 else None
+    Yp = torch.empty((n, h), dtype=odt, device=dev)
+    Ys = torch.empty((T, h), dtype=odt, device=dev) if wl.shared else None
+    Y = torch.empty((T, h), dtype=odt, device=dev)
+    X = inp["X"]
+    Xs_in = (Xq if fp8 else X) if wl.shared else None
+    xs_in = xs if (fp8 and wl.shared) else None
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        moe.moe_route(shape, opts, X, inp["Wg"], ids, G, None, ws)
+        if ev:
+            ev[1].record(stream)
+        moe.moe_permute(shape, ids, X, counts, offsets, dst, src, Xp, xps, Xq, xs, ws)
+        if ev:
+            ev[2].record(stream)
+        moe.moe_expert_ffn(shape, Xp, xps, offsets, Xs_in, xs_in, weights, Yp, Ys, ws)
+        if ev:
+            ev[3].record(stream)
+        moe.moe_combine(shape, Yp, dst, G, Ys, Y)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(ws) == 0
+    log(f"[bench] warmup done; timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs]).mean(0)
+    log(f"[bench] {ms_per_step:.3f} ms/step; stages (route, permute, ffn, combine) ms: "
+        f"{np.round(stage_ms, 4).tolist()}")
+
+    # moe_forward (one call for all four stages) over the same inputs
+    for _ in range(2):
+        moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - tf0) * 1000.0 / args.steps
+
+    cnt = counts.cpu().numpy()
+    flops, nbytes, active = algorithmic_work(wl, cnt)
+    ffn_s = stage_ms[2] / 1000.0
+    tflops = flops / ffn_s / 1e12
+    gbs = nbytes / ffn_s / 1e9
+    prec = wl.precision
+    t_mfma = flops / (PEAK_MFMA_TFLOPS[prec] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS[prec],
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
+                "traffic": None}
+    roof.update({"kernel": "moe_expert_ffn (grouped Linear1+SwiGLU, Linear2)",
+                 "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                 "ms": round(stage_ms[2], 4),
+                 "frac_of_roofline": round(max(t_mfma, t_hbm) / ffn_s, 4)})
+    value = T / (ms_per_step / 1000.0)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 activations/output)",
+                  "fp32": "f32"}[prec],
+        "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": wl.name, "tokens": T, "hidden": h, "experts": E, "topk": k,
+                   "inter": wl.inter, "shared_experts": wl.shared, "score": wl.score,
+                   "renorm": wl.renorm, "alpha": wl.alpha, "routing": "hash" if wl.hash else "score",
+                   "expert_load": "zipf(0.8)" if wl.zipf else "random gate",
+                   "active_experts": active},
+        "grouped_gemm": {"tflops": round(tflops, 1),
+                         "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
+                         "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)},
+        "stages_ms": {"route": round(stage_ms[0], 4), "permute": round(stage_ms[1], 4),
+                      "expert_ffn": round(stage_ms[2], 4), "combine": round(stage_ms[3], 4)},
+        "moe_forward_ms": round(fwd_ms, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or (16 if wl.T > 1024 else min(wl.T, 32))
+        out["cpu_baseline"] = cpu_baseline(inp, ids.cpu().numpy(), n_tok)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -11,18 +11,22 @@
 //
 // Tile schedule (device side, no host sync): tile_off[e] is the prefix sum of
 // ceil(rows_e / BM) over segments 0..E (E = shared).  The grid is an upper
-// bound of m-tiles times the n-tiles; a block maps its id to (m-tile, n-tile),
-// finds its segment by binary search over tile_off, and exits if past the
-// end.  Padding rows are never computed into outputs and are not counted as
-// work.
+// bound of m-tiles times the n-tiles; blocks past the real count exit at
+// once.  A block renumbers itself so that each of the 8 XCDs (blocks are dealt
+// to them round-robin) runs one contiguous range of work items, and inside a
+// segment items go in groups of 4 m-tiles, n-tile major: the blocks an XCD
+// runs together share weight columns and token rows in its L2.  16-row MFMA
+// tiles past a segment's last row are skipped, so a cold expert's tile costs
+// only the rows it has, and padding rows are never stored.
 //
-// A block is 256 threads (4 waves) computing a BM x BN tile with K-tiles of
-// 128 bytes: 64 bf16 or 128 e4m3 elements.  Rows of X are K-contiguous and
-// go to LDS as they are; weights are [K, N] row-major, so each thread loads
-// a 4 x 16-byte block and writes it transposed (v_perm byte shuffles) so that
-// LDS holds both operands K-contiguous, which is what each MFMA lane reads.
-// LDS is double buffered and the next K-tile is prefetched into registers
-// while the current one is multiplied.
+// Prefill tiles are 256 x 256 on 8 waves (each wave 128 x 64); decode tiles
+// are 16 x 256 on 4 waves with one LDS stage, which fits more blocks per CU
+// and so keeps more weight bytes in flight.  K-tiles are 128 bytes: 64 bf16
+// or 128 e4m3 elements.  Token rows are K-contiguous and go to LDS as they
+// are; weights are [K, N] row-major, so each thread loads a 4 x 16-byte block
+// and writes it transposed (v_perm byte shuffles), and LDS holds both
+// operands K-contiguous, which is what each MFMA lane reads.  The next K-tile
+// is prefetched into registers while the current one is multiplied.
 //   bf16: v_mfma_f32_16x16x32_bf16 (a lane holds 8 K-consecutive elements)
 //   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (32 per lane)
 // For SwiGLU an N-tile of BN columns holds BN/2 gate columns and the
@@ -37,7 +41,6 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBKBytes = 128;
 constexpr int kRowBytes = kBKBytes + 16;  // padded LDS row
 
@@ -111,24 +114,25 @@ __device__ __forceinline__ void store_bt(char* Bs, int nl, int kbyte, const uint
   }
 }
 
-template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU>
-__global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(GemmArgs g) {
   using M = Mfma<PREC>;
+  constexpr int NTHR = 64 * WAVES_M * WAVES_N;
   constexpr int ESZ = M::kEsz;
   constexpr int kColsPer16B = 16 / ESZ;           // elements per 16-byte load
   constexpr int WM = BM / WAVES_M;
   constexpr int MT = WM / 16;
   constexpr int NTW = BN / WAVES_N / 16;          // n-tiles per wave
   constexpr int kAChunks = BM * kBKBytes / 16;
-  constexpr int kAPer = (kAChunks + kThreads - 1) / kThreads;
+  constexpr int kAPer = (kAChunks + NTHR - 1) / NTHR;
   constexpr int kBBlocks = (kBKBytes / ESZ / 4) * (BN / kColsPer16B);
-  constexpr int kBPer = (kBBlocks + kThreads - 1) / kThreads;
+  constexpr int kBPer = (kBBlocks + NTHR - 1) / NTHR;
   constexpr int kBColBlocks = BN / kColsPer16B;
   static_assert(MT >= 1 && NTW >= 1, "tile shape");
   static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
 
-  __shared__ __attribute__((aligned(16))) char As[2][BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char Bs[2][BN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char As[STAGES][BM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char Bs[STAGES][BN * kRowBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -137,19 +141,40 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   const int wn = wave % WAVES_N;
 
   // ------------------------------------------------ tile -> segment
-  const int m = blockIdx.x / g.n_tiles;
-  const int nt = blockIdx.x % g.n_tiles;
+  // Work items: (m-tile, n-tile) pairs, m-tiles ordered by segment.  Blocks
+  // are dealt round-robin to the 8 XCDs, so block b is renumbered such that
+  // each XCD runs one contiguous range of work items; inside a segment, items
+  // go in groups of GROUP_M m-tiles, n-tile major, so the blocks an XCD runs
+  // at the same time share both their weight columns and their rows in L2.
+  constexpr int GROUP_M = 4;
   const int E = g.E;
-  if (m >= g.tile_off[E + 1]) return;
+  const int NT = g.n_tiles;
+  const int total = g.tile_off[E + 1] * NT;
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  int item;
+  {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    item = x * per + min(x, rem) + slot;
+  }
+  const int mq = item / NT;  // segment search key: m-tile index of the item's group row
   int lo = 0, hi = E;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (g.tile_off[mid] <= m)
+    if (g.tile_off[mid] <= mq)
       lo = mid;
     else
       hi = mid - 1;
   }
   const int seg = lo;
+  const int mt_seg = g.tile_off[seg + 1] - g.tile_off[seg];
+  const int local = item - g.tile_off[seg] * NT;
+  const int grp = local / (GROUP_M * NT);
+  const int gsz = min(GROUP_M, mt_seg - grp * GROUP_M);
+  const int rin = local - grp * GROUP_M * NT;
+  const int nt = rin / gsz;
+  const int mtile = grp * GROUP_M + rin % gsz;
+
   const bool shared = (seg == E);
   int row0, row_end;
   const char* Abase;
@@ -158,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
   const float* asc;
   char* obase;
   if (!shared) {
-    row0 = g.offsets[seg] + (m - g.tile_off[seg]) * BM;
+    row0 = g.offsets[seg] + mtile * BM;
     row_end = g.offsets[seg + 1];
     Abase = static_cast<const char*>(g.A);
     Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * ESZ;
@@ -166,7 +191,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     asc = g.a_scale;
     obase = static_cast<char*>(g.out);
   } else {
-    row0 = (m - g.tile_off[E]) * BM;
+    row0 = mtile * BM;
     row_end = g.T;
     Abase = static_cast<const char*>(g.A_sh);
     Wbase = static_cast<const char*>(g.W_sh);
@@ -174,6 +199,9 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     asc = g.a_scale_sh;
     obase = static_cast<char*>(g.out_sh);
   }
+  const int rows_valid = min(BM, row_end - row0);
+  // number of this wave's 16-row tiles that hold at least one valid row
+  const int mt_live = max(0, min(MT, (rows_valid - wm * WM + 15) / 16));
   const int K = g.K;
   const size_t a_ld = static_cast<size_t>(K) * ESZ;    // bytes per A row
   const size_t w_ld = static_cast<size_t>(g.Nw) * ESZ;  // bytes per W row
@@ -187,53 +215,48 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     return nt * BN + nl;
   };
 
-  uint4 ra[kAPer];
+  // Loads are unconditional (rows clamped into the segment, surplus threads
+  // repeat a chunk and store the same bytes) so that no branch separates a
+  // load from its use and all of a tile's loads are in flight together.
+  i32x4_t ra[kAPer];
   uint32_t rb[kBPer][4][4];
   auto gload = [&](int kt) {
     const size_t kb0 = static_cast<size_t>(kt) * kBKBytes;
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
-      int c = tid + q * kThreads;
-      if (kAChunks % kThreads == 0 || c < kAChunks) {
-        int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
-        int row = min(row0 + r, row_end - 1);
-        ra[q] = *reinterpret_cast<const uint4*>(Abase + row * a_ld + kb0 + c16 * 16);
-      }
+      const int c = (tid + q * NTHR) % kAChunks;
+      const int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
+      const int row = min(row0 + r, row_end - 1);
+      ra[q] = *reinterpret_cast<const i32x4_t*>(Abase + row * a_ld + kb0 + c16 * 16);
     }
 #pragma unroll
     for (int q = 0; q < kBPer; ++q) {
-      int b = tid + q * kThreads;
-      if (kBBlocks % kThreads == 0 || b < kBBlocks) {
-        int nb = b % kBColBlocks, kb = b / kBColBlocks;
-        const char* p = Wbase + (static_cast<size_t>(kt) * (kBKBytes / ESZ) + kb * 4) * w_ld +
-                        static_cast<size_t>(wcol(nb * kColsPer16B)) * ESZ;
+      const int b = (tid + q * NTHR) % kBBlocks;
+      const int nb = b % kBColBlocks, kb = b / kBColBlocks;
+      const char* p = Wbase + (static_cast<size_t>(kt) * (kBKBytes / ESZ) + kb * 4) * w_ld +
+                      static_cast<size_t>(wcol(nb * kColsPer16B)) * ESZ;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint4 v = *reinterpret_cast<const uint4*>(p + r * w_ld);
-          rb[q][r][0] = v.x;
-          rb[q][r][1] = v.y;
-          rb[q][r][2] = v.z;
-          rb[q][r][3] = v.w;
-        }
+      for (int r = 0; r < 4; ++r) {
+        i32x4_t v = *reinterpret_cast<const i32x4_t*>(p + r * w_ld);
+        rb[q][r][0] = v[0];
+        rb[q][r][1] = v[1];
+        rb[q][r][2] = v[2];
+        rb[q][r][3] = v[3];
       }
     }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < kAPer; ++q) {
-      int c = tid + q * kThreads;
-      if (kAChunks % kThreads == 0 || c < kAChunks) {
-        int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
-        *reinterpret_cast<uint4*>(&As[buf][r * kRowBytes + c16 * 16]) = ra[q];
-      }
+      const int c = (tid + q * NTHR) % kAChunks;
+      const int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
+      *reinterpret_cast<i32x4_t*>(&As[buf][r * kRowBytes + c16 * 16]) = ra[q];
     }
 #pragma unroll
     for (int q = 0; q < kBPer; ++q) {
-      int b = tid + q * kThreads;
-      if (kBBlocks % kThreads == 0 || b < kBBlocks) {
-        int nb = b % kBColBlocks, kb = b / kBColBlocks;
-        store_bt<ESZ>(Bs[buf], nb * kColsPer16B, kb * 4 * ESZ, rb[q]);
-      }
+      const int b = (tid + q * NTHR) % kBBlocks;
+      const int nb = b % kBColBlocks, kb = b / kBColBlocks;
+      store_bt<ESZ>(Bs[buf], nb * kColsPer16B, kb * 4 * ESZ, rb[q]);
     }
   };
 
@@ -252,36 +275,47 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_kernel(GemmArgs g) {
     return wn * (BN / WAVES_N) + j * 16;
   };
 
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < kBKBytes; ks += M::kStepBytes) {
+      const int koff = ks + (lane >> 4) * (M::kStepBytes / 4);
+      typename M::frag bfr[NTW];
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        bfr[j] = M::load(&Bs[buf][(brow(j) + (lane & 15)) * kRowBytes + koff]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        if (i < mt_live) {
+          typename M::frag af =
+              M::load(&As[buf][(wm * WM + i * 16 + (lane & 15)) * kRowBytes + koff]);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) acc[i][j] = M::mma(af, bfr[j], acc[i][j]);
+        }
+      }
+    }
+  };
+
   const int KT = K * ESZ / kBKBytes;
   gload(0);
   sstore(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < kBKBytes; ks += M::kStepBytes) {
-      const int koff = ks + (lane >> 4) * (M::kStepBytes / 4);
-      typename M::frag af[MT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-        af[i] = M::load(&As[buf][(wm * WM + i * 16 + (lane & 15)) * kRowBytes + koff]);
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        typename M::frag bfr = M::load(&Bs[buf][(brow(j) + (lane & 15)) * kRowBytes + koff]);
-#pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i][j] = M::mma(af[i], bfr, acc[i][j]);
-      }
-    }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+  // steady state without conditionals (the last K-tile is peeled off)
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    const int buf = (STAGES == 2) ? (kt & 1) : 0;
+    gload(kt + 1);
+    compute(buf);
+    if (STAGES == 1) __syncthreads();  // the single buffer is about to be overwritten
+    sstore(STAGES == 2 ? (buf ^ 1) : 0);
     __syncthreads();
   }
+  compute(STAGES == 2 ? ((KT - 1) & 1) : 0);
 
   // ------------------------------------------------ epilogue
   // lane holds column (lane & 15) and rows 4*(lane >> 4) + v of each 16x16 tile
   const int col_in = lane & 15;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
+    if (i >= mt_live) continue;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
@@ -421,18 +455,16 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
   out[o] = y;
 }
 
-template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU>
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
   dim3 grid(ub_m * g.n_tiles);
-  hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU>), grid,
-                     dim3(kThreads), 0, stream, g);
+  hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
+                     dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
   return hipGetLastError();
 }
 
-template <int PREC, int BM, int WAVES_M, int WAVES_N>
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
-  constexpr int BN = 128;
-  constexpr int ESZ = (PREC == MOE_PREC_FP8) ? 1 : 2;
   const int rows = a.T * a.k;
   const int T_sh = a.has_shared ? a.T : 0;
   hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.offsets, a.E,
@@ -463,7 +495,7 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   g1.f = a.f;
   g1.T = a.T;
   g1.n_tiles = 2 * a.f / BN;
-  err = launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, true>(g1, ub_m, stream);
+  err = launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, true, STAGES>(g1, ub_m, stream);
   if (err != hipSuccess) return err;
 
   const void* A2 = a.A;
@@ -497,8 +529,28 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   g2.f = a.f;
   g2.T = a.T;
   g2.n_tiles = a.h / BN;
-  (void)ESZ;
-  return launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, false>(g2, ub_m, stream);
+  return launch_gemm<PREC, BM, BN, WAVES_M, WAVES_N, false, STAGES>(g2, ub_m, stream);
+}
+
+template <int PREC>
+hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
+  const int rows = a.T * a.k;
+  // Decode-sized batches (a few rows per expert) stream weights with 16-row
+  // tiles and one LDS stage, so more blocks fit on a CU; prefill batches use
+  // 256x256 tiles on 8 waves.  N tiles of 256 need hidden and 2*inter to be
+  // multiples of 256, else 128.
+  const bool small = static_cast<long>(rows) < 16L * a.E;
+  const bool wide = (a.h % 256 == 0) && ((2 * a.f) % 256 == 0);
+  if (small)
+    return wide ? run_ffn<PREC, 16, 256, 1, 4, 1>(a, stream)
+                : run_ffn<PREC, 16, 128, 1, 4, 1>(a, stream);
+  // e4m3 operands are 32 bytes per lane: 256x256 tiles would spill
+  if constexpr (PREC == MOE_PREC_FP8) {
+    return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+  } else {
+    return wide ? run_ffn<PREC, 256, 256, 2, 4, 2>(a, stream)
+                : run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+  }
 }
 
 }  // namespace
@@ -515,14 +567,8 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(l2_f32_kernel, dim3((n2 + 255) / 256), dim3(256), 0, stream, a, rows);
     return hipGetLastError();
   }
-  // Rows per expert decide the M tile: a decode-sized batch (a few rows per
-  // expert) streams weights with 16-row tiles, a prefill batch uses 128.
-  const bool small = static_cast<long>(rows) < 16L * a.E;
-  if (a.precision == MOE_PREC_BF16)
-    return small ? run_ffn<MOE_PREC_BF16, 16, 1, 4>(a, stream)
-                 : run_ffn<MOE_PREC_BF16, 128, 2, 2>(a, stream);
-  return small ? run_ffn<MOE_PREC_FP8, 16, 1, 4>(a, stream)
-               : run_ffn<MOE_PREC_FP8, 128, 2, 2>(a, stream);
+  if (a.precision == MOE_PREC_BF16) return dispatch_ffn<MOE_PREC_BF16>(a, stream);
+  return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 
 }  // namespace moe

@@ -214,10 +214,12 @@ def test_edge_cases(kind):
     _need_gpu()
     spec = {
         "one_token": ("v4pro_bf16", dict(T=1, hidden=256, experts=64, inter=128)),
-        "all_to_one_expert": ("v4pro_bf16", dict(T=300, hidden=256, experts=64, inter=128, topk=1)),
+        "all_to_one_expert": ("v4pro_bf16", dict(T=300, hidden=256, experts=64, inter=128, topk=1,
+                                                  zipf=False)),
         "k_equals_E": ("tiny_fp32", dict(T=40, experts=4, topk=4)),
         "single_expert": ("llama_bf16", dict(T=200, hidden=128, experts=1, topk=1, inter=64)),
-        "fp8_all_to_one": ("v4pro_fp8", dict(T=300, hidden=256, experts=64, inter=128, topk=1)),
+        "fp8_all_to_one": ("v4pro_fp8", dict(T=300, hidden=256, experts=64, inter=128, topk=1,
+                                              zipf=False)),
         "decode_one_token": ("decode_hash_bf16", dict(T=1, hidden=256, experts=64, inter=128)),
     }[kind]
     cpu, L = _edge(spec[0], **spec[1])
