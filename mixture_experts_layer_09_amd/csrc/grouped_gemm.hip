@@ -42,7 +42,19 @@ namespace moe {
 namespace {
 
 constexpr int kBKBytes = 128;
-constexpr int kRowBytes = kBKBytes + 16;  // padded LDS row
+constexpr int kRowBytes = kBKBytes;  // LDS row: one K-tile of one row, no padding
+
+// LDS byte offset of 16-byte chunk `chunk` (0..7) of row `row`.  Chunks are
+// XOR-swizzled by f(row) = ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2), which
+// is constant on no two rows of equal parity within an aligned group of 16:
+//   - an MFMA operand read (16 consecutive rows, one logical chunk) hits 16
+//     distinct 4-bank groups;
+//   - 16-byte row writes (8 lanes per row) fill all 64 banks;
+//   - the transposed weight writes below (see store_bt) are conflict-free.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  const int f = ((row >> 1) & 7) ^ (((row >> 5) & 1) << 2);
+  return row * kRowBytes + ((chunk ^ f) << 4);
+}
 
 struct GemmArgs {
   const void* A;         // routed input rows [M, K]
@@ -68,7 +80,10 @@ struct Mfma<MOE_PREC_BF16> {
   static constexpr int kEsz = 2;
   static constexpr int kStepBytes = 64;  // K bytes per MFMA (32 bf16)
   typedef bf16x8_t frag;
-  __device__ static frag load(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+  // lane's 8 K-consecutive elements: chunk (kstep * 4 + lane / 16) of the row
+  __device__ static frag load(const char* base, int row, int kstep, int lane) {
+    return *reinterpret_cast<const bf16x8_t*>(base + lds_off(row, kstep * 4 + (lane >> 4)));
+  }
   __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -79,9 +94,12 @@ struct Mfma<MOE_PREC_FP8> {
   static constexpr int kEsz = 1;
   static constexpr int kStepBytes = 128;  // K bytes per MFMA (128 e4m3)
   typedef i32x8_t frag;
-  __device__ static frag load(const char* p) {
-    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p);
-    i32x4_t hi = *reinterpret_cast<const i32x4_t*>(p + 16);
+  // lane's 32 K-consecutive elements: chunks 2 * (lane / 16) and the next
+  __device__ static frag load(const char* base, int row, int kstep, int lane) {
+    const int c = (lane >> 4) * 2;
+    i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + lds_off(row, c));
+    i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + lds_off(row, c + 1));
+    (void)kstep;
     return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
@@ -90,25 +108,35 @@ struct Mfma<MOE_PREC_FP8> {
   }
 };
 
-// Transposed store of a 4(k) x 16-byte block: r[q] holds row k0+q.
+// Transposed store of a 4(k) x 16-byte block of weights: r[q] holds K-row
+// kb*4+q, columns nl.. of the tile.  Writes each column's 4 K-values (8 bytes
+// of bf16, 4 of e4m3) into its LDS row.  A wave's lanes hold 16 K-groups x 4
+// column chunks; lanes of odd chunks write their columns in the order c ^ 1
+// (`rot`), so at every write half the wave is on even rows and half on odd
+// rows, which with the swizzle spreads one write instruction over all banks.
 template <int ESZ>
-__device__ __forceinline__ void store_bt(char* Bs, int nl, int kbyte, const uint32_t (&r)[4][4]) {
+__device__ __forceinline__ void store_bt(char* Bs, int nl, int kb, int rot,
+                                         const uint32_t (&r)[4][4]) {
+  const int kbyte = kb * 4 * ESZ;
+  const int chunk = kbyte >> 4, within = kbyte & 15;
   if (ESZ == 2) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      const int cc = c ^ rot;
+      const uint32_t sel = (cc & 1) ? 0x07060302u : 0x05040100u;
       uint32_t d0 = __builtin_amdgcn_perm(r[1][c >> 1], r[0][c >> 1], sel);
       uint32_t d1 = __builtin_amdgcn_perm(r[3][c >> 1], r[2][c >> 1], sel);
-      *reinterpret_cast<uint2*>(Bs + (nl + c) * kRowBytes + kbyte) = make_uint2(d0, d1);
+      *reinterpret_cast<uint2*>(Bs + lds_off(nl + cc, chunk) + within) = make_uint2(d0, d1);
     }
   } else {
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const uint32_t b = c & 3;
+      const int cc = c ^ rot;
+      const uint32_t b = cc & 3;
       const uint32_t sel = b | ((4u + b) << 8) | (b << 16) | ((4u + b) << 24);
       uint32_t t01 = __builtin_amdgcn_perm(r[1][c >> 2], r[0][c >> 2], sel);
       uint32_t t23 = __builtin_amdgcn_perm(r[3][c >> 2], r[2][c >> 2], sel);
-      *reinterpret_cast<uint32_t*>(Bs + (nl + c) * kRowBytes + kbyte) =
+      *reinterpret_cast<uint32_t*>(Bs + lds_off(nl + cc, chunk) + within) =
           __builtin_amdgcn_perm(t23, t01, 0x05040100u);
     }
   }
@@ -127,7 +155,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
   constexpr int kAPer = (kAChunks + NTHR - 1) / NTHR;
   constexpr int kBBlocks = (kBKBytes / ESZ / 4) * (BN / kColsPer16B);
   constexpr int kBPer = (kBBlocks + NTHR - 1) / NTHR;
-  constexpr int kBColBlocks = BN / kColsPer16B;
+  constexpr int kBKRows = kBKBytes / ESZ / 4;  // 4-row K groups per tile (16 or 32)
+  constexpr int kKGroups = kBKRows / 16;        // 16-lane K spans per tile
+  static_assert((BN / kColsPer16B) % 4 == 0, "B mapping needs 4 column chunks per wave");
   static_assert(MT >= 1 && NTW >= 1, "tile shape");
   static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
 
@@ -232,7 +262,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 #pragma unroll
     for (int q = 0; q < kBPer; ++q) {
       const int b = (tid + q * NTHR) % kBBlocks;
-      const int nb = b % kBColBlocks, kb = b / kBColBlocks;
+      const int kb = ((b >> 6) % kKGroups) * 16 + (b & 15);
+      const int nb = ((b >> 6) / kKGroups) * 4 + ((b >> 4) & 3);
       const char* p = Wbase + (static_cast<size_t>(kt) * (kBKBytes / ESZ) + kb * 4) * w_ld +
                       static_cast<size_t>(wcol(nb * kColsPer16B)) * ESZ;
 #pragma unroll
@@ -250,13 +281,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     for (int q = 0; q < kAPer; ++q) {
       const int c = (tid + q * NTHR) % kAChunks;
       const int r = c / (kBKBytes / 16), c16 = c % (kBKBytes / 16);
-      *reinterpret_cast<i32x4_t*>(&As[buf][r * kRowBytes + c16 * 16]) = ra[q];
+      *reinterpret_cast<i32x4_t*>(&As[buf][lds_off(r, c16)]) = ra[q];
     }
 #pragma unroll
     for (int q = 0; q < kBPer; ++q) {
       const int b = (tid + q * NTHR) % kBBlocks;
-      const int nb = b % kBColBlocks, kb = b / kBColBlocks;
-      store_bt<ESZ>(Bs[buf], nb * kColsPer16B, kb * 4 * ESZ, rb[q]);
+      const int kb = ((b >> 6) % kKGroups) * 16 + (b & 15);
+      const int nb = ((b >> 6) / kKGroups) * 4 + ((b >> 4) & 3);
+      store_bt<ESZ>(Bs[buf], nb * kColsPer16B, kb, nb & 1, rb[q]);
     }
   };
 
@@ -277,17 +309,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int ks = 0; ks < kBKBytes; ks += M::kStepBytes) {
-      const int koff = ks + (lane >> 4) * (M::kStepBytes / 4);
+    for (int ks = 0; ks < kBKBytes / M::kStepBytes; ++ks) {
       typename M::frag bfr[NTW];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        bfr[j] = M::load(&Bs[buf][(brow(j) + (lane & 15)) * kRowBytes + koff]);
+      for (int j = 0; j < NTW; ++j) bfr[j] = M::load(Bs[buf], brow(j) + (lane & 15), ks, lane);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         if (i < mt_live) {
-          typename M::frag af =
-              M::load(&As[buf][(wm * WM + i * 16 + (lane & 15)) * kRowBytes + koff]);
+          typename M::frag af = M::load(As[buf], wm * WM + i * 16 + (lane & 15), ks, lane);
 #pragma unroll
           for (int j = 0; j < NTW; ++j) acc[i][j] = M::mma(af, bfr[j], acc[i][j]);
         }
@@ -346,6 +375,303 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
           if (PREC == MOE_PREC_FP8) y *= wsc[ncol] * rs;
           reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
               f32_to_bf16(y);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16 DMA path
+// The bf16 grouped GEMM with both operands brought into LDS by asynchronous
+// global->LDS DMA (global_load_lds_dwordx4: each lane's 16 bytes land at
+// base + 16 * lane) into a ring of STAGES K-slices of 32 elements, so that
+// STAGES-1 slices are in flight while one is multiplied.  Weights stay in
+// their [K, N] layout in LDS; the MFMA B fragments are read with gfx950's
+// transposing LDS load ds_read_b64_tr_b16: in each 16-lane group, output
+// lane i, element q, is element i % 4 of the 8-byte piece addressed by lane
+// 4q + i / 4, so lane p addresses row k0 + p / 4, columns n0 + 4 (p % 4) and
+// receives column n0 + i of rows k0..k0+3.  Two such loads give the 8
+// K-consecutive values of one lane's B fragment.
+//
+// LDS layout of one stage:
+//   A: BM rows x 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
+//      (an MFMA read of 16 consecutive rows then covers all 64 banks);
+//   B: 32 rows (k) x BN*2 bytes; chunk c of row r at c ^ 2 s(r),
+//      s(r) = (r & 3) + 4 ((r >> 3) & 1), which makes each transposing load
+//      touch every bank exactly twice.
+// The swizzles are applied on the global side: lane i of a DMA instruction
+// fetches the chunk that belongs at LDS position i.
+//
+// The DMA writes LDS outside the compiler's view, so every wait is explicit:
+// s_waitcnt vmcnt(n) leaves exactly the later stages in flight, then a plain
+// s_barrier (no fence, which would drain all of them) publishes the stage.
+
+// One DMA instruction: 16 bytes per lane from `src` to LDS lds_dst + 16 * lane
+// (lds_dst is wave-uniform and goes through M0).  Written as inline asm so
+// that the compiler, which would otherwise make every later LDS read wait
+// for all DMA in flight, leaves the waiting to wait_vmcnt; the memory clobber
+// keeps LDS reads and other memory operations on their side of it.
+__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+__device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)(p));
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_kernel(
+    GemmArgs g) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int BK = 32;                  // K elements per stage
+  constexpr int A_ROW = BK * 2;           // bytes
+  constexpr int B_ROW = BN * 2;           // bytes
+  constexpr int A_BYTES = BM * A_ROW;
+  constexpr int B_BYTES = BK * B_ROW;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INSTS = (A_BYTES + 1023) / 1024;
+  constexpr int B_INSTS = B_BYTES / 1024;
+  constexpr int A_OPS = (A_INSTS + NW - 1) / NW;  // DMA instructions per wave per stage
+  constexpr int B_OPS = B_INSTS / NW;
+  constexpr int OPS = A_OPS + B_OPS;
+  constexpr int B_CHUNKS = B_ROW / 16;    // 16-byte chunks per B row
+  constexpr int B_RPI = 1024 / B_ROW;     // B rows per DMA instruction
+  constexpr int WM = BM / WAVES_M;
+  constexpr int MT = WM / 16;
+  constexpr int NTW = BN / WAVES_N / 16;
+  static_assert(B_INSTS % NW == 0, "B stage must split evenly over the waves");
+  static_assert(A_BYTES % 1024 == 0 || A_INSTS == 1, "A stage granularity");
+  static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
+
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+
+  // ------------------------------------------------ tile -> segment (as above)
+  constexpr int GROUP_M = 4;
+  const int E = g.E;
+  const int NT = g.n_tiles;
+  const int total = g.tile_off[E + 1] * NT;
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  int item;
+  {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    item = x * per + min(x, rem) + slot;
+  }
+  const int mq = item / NT;
+  int lo = 0, hi = E;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (g.tile_off[mid] <= mq)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int seg = lo;
+  const int mt_seg = g.tile_off[seg + 1] - g.tile_off[seg];
+  const int local = item - g.tile_off[seg] * NT;
+  const int grp = local / (GROUP_M * NT);
+  const int gsz = min(GROUP_M, mt_seg - grp * GROUP_M);
+  const int rin = local - grp * GROUP_M * NT;
+  const int nt = rin / gsz;
+  const int mtile = grp * GROUP_M + rin % gsz;
+
+  const bool shared = (seg == E);
+  int row0, row_end;
+  const char* Abase;
+  const char* Wbase;
+  char* obase;
+  if (!shared) {
+    row0 = g.offsets[seg] + mtile * BM;
+    row_end = g.offsets[seg + 1];
+    Abase = static_cast<const char*>(g.A);
+    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * 2;
+    obase = static_cast<char*>(g.out);
+  } else {
+    row0 = mtile * BM;
+    row_end = g.T;
+    Abase = static_cast<const char*>(g.A_sh);
+    Wbase = static_cast<const char*>(g.W_sh);
+    obase = static_cast<char*>(g.out_sh);
+  }
+  const int rows_valid = min(BM, row_end - row0);
+  // wave-uniform: keep it scalar so the skip below is a scalar branch
+  const int mt_live =
+      __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
+  const size_t a_ld = static_cast<size_t>(g.K) * 2;
+  const size_t w_ld = static_cast<size_t>(g.Nw) * 2;
+
+  // Per-lane global sources of this wave's DMA instructions (K offset added
+  // per stage).  A: instruction blk covers rows 16 blk .. 16 blk + 15.
+  const char* a_src[A_OPS];
+#pragma unroll
+  for (int q = 0; q < A_OPS; ++q) {
+    const int blk = (wave * A_OPS + q) % A_INSTS;
+    const int r = blk * 16 + lane / 4;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int row = min(row0 + r, row_end - 1);
+    a_src[q] = Abase + static_cast<size_t>(row) * a_ld + c * 16;
+  }
+  const char* b_src[B_OPS];
+#pragma unroll
+  for (int q = 0; q < B_OPS; ++q) {
+    const int blk = wave * B_OPS + q;
+    const int r = blk * B_RPI + lane / B_CHUNKS;
+    const int sr = (r & 3) + 4 * ((r >> 3) & 1);
+    const int c = (lane % B_CHUNKS) ^ (2 * sr);
+    const int nl = c * 8;  // LDS column (element) of the chunk
+    int col;
+    if (SWIGLU) {
+      const int half = BN / 2;
+      col = nl < half ? nt * half + nl : g.f + nt * half + (nl - half);
+    } else {
+      col = nt * BN + nl;
+    }
+    b_src[q] = Wbase + static_cast<size_t>(r) * w_ld + static_cast<size_t>(col) * 2;
+  }
+  auto issue = [&](int kt, int slot) {
+    char* st = smem + slot * STAGE;
+#pragma unroll
+    for (int q = 0; q < A_OPS; ++q) {
+      const int blk = (wave * A_OPS + q) % A_INSTS;
+      dma16(a_src[q] + static_cast<size_t>(kt) * A_ROW, st + blk * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < B_OPS; ++q) {
+      const int blk = wave * B_OPS + q;
+      dma16(b_src[q] + static_cast<size_t>(kt) * BK * w_ld, st + A_BYTES + blk * 1024);
+    }
+  };
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto bcol = [&](int j) -> int {  // first LDS column of this wave's n-tile j
+    if (SWIGLU) {
+      const int half = BN / 2, per = BN / 2 / WAVES_N;
+      return j < NTW / 2 ? wn * per + j * 16 : half + wn * per + (j - NTW / 2) * 16;
+    }
+    return wn * (BN / WAVES_N) + j * 16;
+  };
+
+  // lane's transposing-load addresses inside a stage's B region (two halves)
+  const int grp4 = lane >> 4, p = lane & 15;
+  int b_off[NTW][2];
+#pragma unroll
+  for (int j = 0; j < NTW; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * grp4 + 4 * h + (p >> 2);
+      const int col = bcol(j) + (p & 3) * 4;
+      const int sr = (r & 3) + 4 * ((r >> 3) & 1);
+      const int c = (col >> 3) ^ (2 * sr);
+      b_off[j][h] = A_BYTES + r * B_ROW + c * 16 + (col & 7) * 2;
+    }
+  int a_off[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = wm * WM + i * 16 + (lane & 15);
+    a_off[i] = r * A_ROW + ((grp4 ^ ((r >> 2) & 3)) << 4);
+  }
+
+  auto compute = [&](int slot) {
+    const char* st = smem + slot * STAGE;
+    bf16x8_t bfr[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      i16x4_t lo4 = ds_read_tr16(st + b_off[j][0]);
+      i16x4_t hi4 = ds_read_tr16(st + b_off[j][1]);
+      typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+      i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      bfr[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    // all A fragments are read (rows past the segment are in-bounds LDS and
+    // only feed accumulators that are never stored); MFMAs run for live tiles
+    bf16x8_t af[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      if (i < mt_live)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  // The K loop is unrolled by STAGES so that every stage slot is a constant
+  // LDS range: the compiler then sees DMA targets and operand reads as
+  // disjoint and leaves the waiting to the explicit vmcnt below.
+  const int KT = g.K / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s);
+  for (int k0 = 0; k0 < KT; k0 += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      const int kt = k0 + s;
+      if (kt < KT) {
+        // stage kt is in LDS once at most the stages issued after it are in flight
+        const int after = min(STAGES - 2, KT - 1 - kt);
+        if (after >= STAGES - 2)
+          wait_vmcnt<(STAGES - 2) * OPS>();
+        else if (STAGES >= 4 && after == 1)
+          wait_vmcnt<OPS>();
+        else if (STAGES >= 5 && after == 2)
+          wait_vmcnt<2 * OPS>();
+        else
+          wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+        compute(s);
+      }
+    }
+  }
+
+  // ------------------------------------------------ epilogue
+  const int col_in = lane & 15;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i >= mt_live) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+      if (row >= row_end) continue;
+      if (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < NTW / 2; ++j) {
+          const int ncol = nt * (BN / 2) + bcol(j) + col_in;
+          reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+              f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + NTW / 2][v]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const int ncol = nt * BN + bcol(j) + col_in;
+          reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+              f32_to_bf16(acc[i][j][v]);
         }
       }
     }
@@ -458,8 +784,14 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
   dim3 grid(ub_m * g.n_tiles);
-  hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
-                     dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+  if constexpr (STAGES >= 3) {
+    static_assert(PREC == MOE_PREC_BF16, "the DMA pipeline is bf16");
+    hipLaunchKernelGGL((grouped_gemm_bf16_dma_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
+                       grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+  } else {
+    hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
+                       dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+  }
   return hipGetLastError();
 }
 
@@ -548,7 +880,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
   if constexpr (PREC == MOE_PREC_FP8) {
     return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
   } else {
-    return wide ? run_ffn<PREC, 256, 256, 2, 4, 2>(a, stream)
+    return wide ? run_ffn<PREC, 256, 256, 2, 4, 4>(a, stream)
                 : run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
   }
 }
