@@ -1,0 +1,129 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (moe_forward and the four entry points it chains).
+
+Checked on every token: the router's selection (exact at every clear margin,
+and equal to the top-k of the kernel's own keys everywhere), the dispatch
+(counts, offsets, row maps bit-exact against the oracle on the same ids) and
+the copies into Xp (bit-exact on sampled rows).  Checked on sampled tokens:
+the layer output against the oracle, with samples chosen to cover the
+hottest expert's last (ragged) tile, the coldest active experts and the
+shared expert.  The oracle receives host copies of only the experts the
+sampled tokens use.
+"""
+from __future__ import annotations
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import bits, f64, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+DELTA = 1e-5
+FULL = ["v4pro_bf16", "v4pro_fp8", "llama_bf16", "decode_hash_bf16", "decode_score_bf16",
+        "ep_share_bf16"]
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _sample_tokens(ids: np.ndarray, counts: np.ndarray, n_each: int = 4) -> np.ndarray:
+    """Tokens that hit the hottest expert last (its ragged tail), tokens of the
+    coldest active experts, and the first and last tokens."""
+    T = ids.shape[0]
+    hot = int(np.argmax(counts))
+    hot_tok = np.nonzero((ids == hot).any(axis=1))[0][-n_each:]
+    active = np.nonzero(counts > 0)[0]
+    cold = active[np.argsort(counts[active], kind="stable")[:n_each]]
+    cold_tok = [int(np.nonzero((ids == e).any(axis=1))[0][0]) for e in cold]
+    toks = np.unique(np.concatenate([hot_tok, cold_tok, [0, T - 1]])).astype(np.int32)
+    return toks
+
+
+def _oracle_on_tokens(inp, ids, G, toks):
+    """oracle.Layer on the sampled tokens, with only their experts copied."""
+    wl = inp["workload"]
+    sub_ids = ids[toks]
+    experts = sorted(set(int(e) for e in sub_ids.ravel() if e >= 0))
+    remap = np.full(wl.experts, -1, np.int32)
+    remap[experts] = np.arange(len(experts), dtype=np.int32)
+    idx = torch.tensor(experts, dtype=torch.long, device=inp["W1"].device)
+    sel = lambda t: None if t is None else bits(t.index_select(0, idx))  # noqa: E731
+    L = oracle.Layer(wl.precision, bits(inp["X"][torch.from_numpy(toks).long().cuda()]),
+                     sel(inp["W1"]), sel(inp["W2"]), w1_scale=sel(inp["w1_scale"]),
+                     w2_scale=sel(inp["w2_scale"]), Ws1=bits(inp["Ws1"]), Ws2=bits(inp["Ws2"]),
+                     ws1_scale=bits(inp["ws1_scale"]), ws2_scale=bits(inp["ws2_scale"]),
+                     k=wl.topk)
+    return L.tokens(remap[sub_ids], G[toks])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_forward(name):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests.gpu_layer import GpuLayer
+    wl = synth.WORKLOADS[name]
+    _log(f"[full] {name}: generating on cuda:0")
+    inp = synth.make_inputs(wl, device="cuda")
+    L = GpuLayer(inp)
+    _log(f"[full] {name}: moe_route + moe_permute")
+    ids_g, G_g, keys_g = L.route()
+    p = L.permute(ids_g)
+    torch.cuda.synchronize()
+    assert L.device_error() == 0
+    ids = ids_g.cpu().numpy()
+    keys = keys_g.cpu().numpy()
+
+    # routing on every token
+    _log(f"[full] {name}: oracle routing of {wl.T} tokens")
+    r = oracle.route(bits(inp["X"]), bits(inp["Wg"]), wl.topk, gate_bias=f64(inp["gate_bias"]),
+                     beta=f64(inp["beta"]), score=wl.score, renorm=wl.renorm, alpha=wl.alpha,
+                     token_ids=bits(inp["token_ids"]), tid2eid=bits(inp["tid2eid"]))
+    sure = r["margin"] >= DELTA
+    assert np.array_equal(ids[sure], r["ids"][sure])
+    if not wl.hash:
+        ids_k, _ = oracle.topk(keys.astype(np.float64), wl.topk)
+        assert np.array_equal(ids, ids_k)
+    np.testing.assert_allclose(keys, r["keys"], atol=1e-5, rtol=0)
+    same = (ids == r["ids"]).all(axis=1)
+    np.testing.assert_allclose(G_g.cpu().numpy()[same], r["G"][same],
+                               atol=1e-5 * max(1.0, wl.alpha), rtol=1e-5)
+    _log(f"[full] {name}: near-tie tokens {int((~sure).sum())}")
+
+    # dispatch on every assignment, copies on sampled rows
+    d = oracle.dispatch(ids, wl.experts)
+    for k in ("counts", "offsets", "dst_row", "src_tok"):
+        assert np.array_equal(p[k].cpu().numpy(), d[k]), k
+    rows = np.linspace(0, wl.T * wl.topk - 1, 64).astype(np.int64)
+    Xp_rows = bits(p["Xp"][torch.from_numpy(rows).cuda()])
+    src = d["src_tok"][rows]
+    if wl.precision == "fp8":
+        q, s = oracle.quantize_rows_f32(inp["X"][torch.from_numpy(src).long().cuda()].float()
+                                        .cpu().numpy())
+        assert np.array_equal(Xp_rows, q)
+        assert np.array_equal(bits(p["xp_scale"])[rows], s)
+    else:
+        assert np.array_equal(Xp_rows, bits(inp["X"][torch.from_numpy(src).long().cuda()]))
+
+    # the whole layer as the benchmark runs it
+    _log(f"[full] {name}: moe_forward")
+    Y, ids_f, G_f = L.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(ids_f, ids_g) and torch.equal(G_f, G_g)
+    counts = d["counts"]
+    toks = _sample_tokens(ids, counts)
+    _log(f"[full] {name}: oracle on {len(toks)} sampled tokens")
+    ref = _oracle_on_tokens(inp, ids, G_g.cpu().numpy().astype(np.float64), toks)
+    err = row_rel_err(f64(Y)[toks], ref)
+    _log(f"[full] {name}: max row-relative error {err:.3e}")
+    assert err <= TOL[wl.precision]
+    del inp, L, p, Y
+    gc.collect()
+    torch.cuda.empty_cache()
