@@ -427,6 +427,29 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 16].
+__device__ __forceinline__ void wait_vmcnt_rt(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<1>(); break;
+    case 2: wait_vmcnt<2>(); break;
+    case 3: wait_vmcnt<3>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 9: wait_vmcnt<9>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 11: wait_vmcnt<11>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 13: wait_vmcnt<13>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    case 15: wait_vmcnt<15>(); break;
+    default: wait_vmcnt<16>(); break;
+  }
+}
+
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 __device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
@@ -434,9 +457,11 @@ __device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
+// Two waves per SIMD: an 8-wave block alone, or two 4-wave blocks that cover
+// each other's stage barriers.
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_kernel(
-    GemmArgs g) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int BK = 32;                  // K elements per stage
   constexpr int A_ROW = BK * 2;           // bytes
@@ -549,12 +574,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_
     }
     b_src[q] = Wbase + static_cast<size_t>(r) * w_ld + static_cast<size_t>(col) * 2;
   }
+  // Only A blocks (16 rows each) that hold a valid row are fetched; rows
+  // past them are never read by a live MFMA.  The count is wave-uniform and
+  // so is this wave's number of DMA instructions per stage.
+  const int a_live = (A_INSTS == 1) ? A_OPS
+                                    : __builtin_amdgcn_readfirstlane(max(
+                                          0, min(A_OPS, ((rows_valid + 15) / 16) - wave * A_OPS)));
+  const int ops_w = a_live + B_OPS;
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
 #pragma unroll
     for (int q = 0; q < A_OPS; ++q) {
       const int blk = (wave * A_OPS + q) % A_INSTS;
-      dma16(a_src[q] + static_cast<size_t>(kt) * A_ROW, st + blk * 1024);
+      if (q < a_live) dma16(a_src[q] + static_cast<size_t>(kt) * A_ROW, st + blk * 1024);
     }
 #pragma unroll
     for (int q = 0; q < B_OPS; ++q) {
@@ -597,7 +629,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_
     a_off[i] = r * A_ROW + ((grp4 ^ ((r >> 2) & 3)) << 4);
   }
 
+  // A wave with any live row multiplies all of its MT row tiles (rows past the
+  // segment only feed accumulators that are never stored); a wave with none
+  // skips the stage's reads and MFMAs.  A single branch lets every fragment
+  // read of the stage issue before the first MFMA.
   auto compute = [&](int slot) {
+    if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
     bf16x8_t bfr[NTW];
 #pragma unroll
@@ -608,17 +645,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_
       i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       bfr[j] = __builtin_bit_cast(bf16x8_t, v);
     }
-    // all A fragments are read (rows past the segment are in-bounds LDS and
-    // only feed accumulators that are never stored); MFMAs run for live tiles
     bf16x8_t af[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i]);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
-      if (i < mt_live)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NTW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
 
   // The K loop is unrolled by STAGES so that every stage slot is a constant
@@ -635,14 +669,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_bf16_dma_
       if (kt < KT) {
         // stage kt is in LDS once at most the stages issued after it are in flight
         const int after = min(STAGES - 2, KT - 1 - kt);
-        if (after >= STAGES - 2)
-          wait_vmcnt<(STAGES - 2) * OPS>();
-        else if (STAGES >= 4 && after == 1)
-          wait_vmcnt<OPS>();
-        else if (STAGES >= 5 && after == 2)
-          wait_vmcnt<2 * OPS>();
-        else
-          wait_vmcnt<0>();
+        wait_vmcnt_rt(after * ops_w);
         __builtin_amdgcn_s_barrier();
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
         compute(s);
@@ -880,7 +907,7 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
   if constexpr (PREC == MOE_PREC_FP8) {
     return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
   } else {
-    return wide ? run_ffn<PREC, 256, 256, 2, 4, 4>(a, stream)
+    return wide ? run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream)
                 : run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
   }
 }
