@@ -907,8 +907,8 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
   if constexpr (PREC == MOE_PREC_FP8) {
     return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
   } else {
-    return wide ? run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream)
-                : run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+    if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+    return run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream);
   }
 }
 

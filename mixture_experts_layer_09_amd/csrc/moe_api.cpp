@@ -83,7 +83,9 @@ RouteArgs route_args(const moe_shape* s, const moe_route_opts* o, const void* X,
   a.ids = ids;
   a.G = G;
   a.keys = keys;
-  a.flag = at<int32_t>(ws, make_layout(*s).flag);
+  const Layout L = make_layout(*s);
+  a.flag = at<int32_t>(ws, L.flag);
+  a.part = at<float>(ws, L.part);
   return a;
 }
 

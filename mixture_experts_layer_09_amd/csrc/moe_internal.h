@@ -76,9 +76,13 @@ inline size_t xp_bytes(int precision) {
   return precision == MOE_PREC_F32 ? 4 : (precision == MOE_PREC_BF16 ? 2 : 1);
 }
 
+// Bytes of split-K partial gate logits the router may use (0 if none).
+size_t route_partial_bytes(int T, int h, int E);
+
 // Byte offsets of every region inside the caller's workspace.
 struct Layout {
   size_t flag;        // int32 error flag (+ padding to 256 B)
+  size_t part;        // router: fp32 partial logits [splits, T, E]
   size_t blk_cnt;     // [nblk, E] int32 per-block expert counts
   size_t local_rank;  // [T*k] int32 rank of an assignment inside its block
   size_t tile_off;    // [E+2] int32 m-tile prefix of the grouped GEMM
@@ -103,6 +107,7 @@ inline Layout make_layout(const moe_shape& s) {
     return at;
   };
   L.flag = take(kAlign);
+  L.part = take(route_partial_bytes(s.tokens, s.hidden, s.experts));
   L.blk_cnt = take(static_cast<size_t>(L.nblk) * E * 4);
   L.local_rank = take(rows * 4);
   L.tile_off = take((E + 2) * 4);
@@ -140,6 +145,7 @@ struct RouteArgs {
   float* G;
   float* keys;
   int32_t* flag;
+  float* part;  // workspace for split-K partial logits
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
