@@ -134,6 +134,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v4pro_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
+                    help="override a workload field (exploration; e.g. --set zipf=False)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args(argv)
@@ -151,7 +153,10 @@ def main(argv=None):
     import mixture_experts_layer_09_amd as moe
     import synth
 
+    import ast
     wl = synth.WORKLOADS[args.workload]
+    if args.set:
+        wl = wl.replace(**{k: ast.literal_eval(v) for k, v in (x.split("=", 1) for x in args.set)})
     torch.cuda.set_device(0)
     log(f"[bench] generating {wl.name} on cuda:0")
     t = time.perf_counter()
@@ -264,7 +269,8 @@ def main(argv=None):
                    "inter": wl.inter, "shared_experts": wl.shared, "score": wl.score,
                    "renorm": wl.renorm, "alpha": wl.alpha, "routing": "hash" if wl.hash else "score",
                    "expert_load": "zipf(0.8)" if wl.zipf else "random gate",
-                   "active_experts": active},
+                   "active_experts": active,
+                   **({"overrides": args.set} if args.set else {})},
         "grouped_gemm": {"tflops": round(tflops, 1),
                          "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
                          "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)},

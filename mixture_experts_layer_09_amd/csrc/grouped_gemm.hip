@@ -457,15 +457,116 @@ __device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
       (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
-// Two waves per SIMD: an 8-wave block alone, or two 4-wave blocks that cover
-// each other's stage barriers.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
-void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
+typedef __attribute__((ext_vector_type(2))) int i32x2v_t;
+
+__device__ __forceinline__ i32x2v_t ds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2v_t*)(p));
+}
+
+// Operand layout of one precision in the DMA pipeline (see above).
+//   bf16: K-stage 32 elements; A rows 64 B (4 chunks, swizzle (r>>2)&3); B
+//         fragments from 2 transposing 16-bit reads of 4 K-rows each.
+//   e4m3: K-stage 128 elements; A rows 128 B (8 chunks, swizzle (r>>1)&7); B
+//         fragments from 4 transposing 8-bit reads of 8 K-rows each; in a
+//         16-lane group, output lane i byte q is byte i % 8 of the piece
+//         addressed by lane 2q + i / 8, so lane p addresses row k0 + p / 2,
+//         columns n0 + 8 (p % 2), and receives column n0 + i of 8 rows.
+// B chunk swizzles spread each transposing read over all banks (twice).
+template <int PREC, int BN>
+struct DmaOps;
+
+template <int BN>
+struct DmaOps<MOE_PREC_BF16, BN> {
+  static constexpr int ESZ = 2, BK = 32, A_CHUNKS = 4;
+  typedef bf16x8_t frag;
+  __device__ static int swz_a(int r) { return (r >> 2) & 3; }
+  __device__ static int swz_b(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
+  // byte offsets (inside a stage's B region) of this lane's transposing reads
+  template <int B_ROW>
+  __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * g + 4 * h + (p >> 2);
+      const int col = col0 + (p & 3) * 4;  // element
+      o[h] = r * B_ROW + (((col >> 3) ^ swz_b(r)) << 4) + (col & 7) * 2;
+    }
+    o[2] = o[3] = 0;
+  }
+  __device__ static frag load_b(const char* st, const int (&o)[4]) {
+    const i16x4_t lo4 = ds_read_tr16(st + o[0]);
+    const i16x4_t hi4 = ds_read_tr16(st + o[1]);
+    typedef __attribute__((ext_vector_type(8))) short i16x8_t;
+    const i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+  template <int A_ROW>
+  __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
+    o[0] = r * A_ROW + (((lane >> 4) ^ swz_a(r)) << 4);
+    o[1] = 0;
+  }
+  __device__ static frag load_a(const char* st, const int (&o)[2]) {
+    return *reinterpret_cast<const bf16x8_t*>(st + o[0]);
+  }
+  __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int BN>
+struct DmaOps<MOE_PREC_FP8, BN> {
+  static constexpr int ESZ = 1, BK = 128, A_CHUNKS = 8;
+  typedef i32x8_t frag;
+  __device__ static int swz_a(int r) { return (r >> 1) & 7; }
+  __device__ static int swz_b(int r) {
+    return BN >= 256 ? (r & 7) + 8 * ((r >> 5) & 1) : ((r & 7) >> 1) + 4 * ((r >> 5) & 1);
+  }
+  template <int B_ROW>
+  __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int r = 32 * g + 8 * h + (p >> 1);
+      const int col = col0 + (p & 1) * 8;  // byte
+      o[h] = r * B_ROW + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+    }
+  }
+  __device__ static frag load_b(const char* st, const int (&o)[4]) {
+    const i32x2v_t a = ds_read_tr8(st + o[0]);
+    const i32x2v_t b = ds_read_tr8(st + o[1]);
+    const i32x2v_t c = ds_read_tr8(st + o[2]);
+    const i32x2v_t d = ds_read_tr8(st + o[3]);
+    return i32x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+  template <int A_ROW>
+  __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
+    const int c = (lane >> 4) * 2;
+    o[0] = r * A_ROW + ((c ^ swz_a(r)) << 4);
+    o[1] = r * A_ROW + (((c + 1) ^ swz_a(r)) << 4);
+  }
+  __device__ static frag load_a(const char* st, const int (&o)[2]) {
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + o[0]);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + o[1]);
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// Two waves per SIMD for bf16 (two 4-wave blocks that cover each other's
+// stage barriers); e4m3 keeps one block of deeper stages per CU.
+template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
+__attribute__((amdgpu_waves_per_eu((PREC == MOE_PREC_BF16 || STAGES * (BM + BN) * 128 <= 81920) ? 2 : 1)))
+void grouped_gemm_dma_kernel(GemmArgs g) {
+  using O = DmaOps<PREC, BN>;
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int BK = 32;                  // K elements per stage
-  constexpr int A_ROW = BK * 2;           // bytes
-  constexpr int B_ROW = BN * 2;           // bytes
+  constexpr int ESZ = O::ESZ;
+  constexpr int BK = O::BK;               // K elements per stage (one MFMA step)
+  constexpr int A_ROW = BK * ESZ;         // bytes
+  constexpr int B_ROW = BN * ESZ;         // bytes
   constexpr int A_BYTES = BM * A_ROW;
   constexpr int B_BYTES = BK * B_ROW;
   constexpr int STAGE = A_BYTES + B_BYTES;
@@ -473,7 +574,7 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
   constexpr int B_INSTS = B_BYTES / 1024;
   constexpr int A_OPS = (A_INSTS + NW - 1) / NW;  // DMA instructions per wave per stage
   constexpr int B_OPS = B_INSTS / NW;
-  constexpr int OPS = A_OPS + B_OPS;
+  constexpr int A_RPI = 1024 / A_ROW;     // A rows per DMA instruction
   constexpr int B_CHUNKS = B_ROW / 16;    // 16-byte chunks per B row
   constexpr int B_RPI = 1024 / B_ROW;     // B rows per DMA instruction
   constexpr int WM = BM / WAVES_M;
@@ -525,35 +626,41 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
   int row0, row_end;
   const char* Abase;
   const char* Wbase;
+  const float* wsc;
+  const float* asc;
   char* obase;
   if (!shared) {
     row0 = g.offsets[seg] + mtile * BM;
     row_end = g.offsets[seg + 1];
     Abase = static_cast<const char*>(g.A);
-    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * 2;
+    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * ESZ;
+    wsc = g.w_scale ? g.w_scale + static_cast<size_t>(seg) * g.Nw : nullptr;
+    asc = g.a_scale;
     obase = static_cast<char*>(g.out);
   } else {
     row0 = mtile * BM;
     row_end = g.T;
     Abase = static_cast<const char*>(g.A_sh);
     Wbase = static_cast<const char*>(g.W_sh);
+    wsc = g.w_scale_sh;
+    asc = g.a_scale_sh;
     obase = static_cast<char*>(g.out_sh);
   }
   const int rows_valid = min(BM, row_end - row0);
   // wave-uniform: keep it scalar so the skip below is a scalar branch
   const int mt_live =
       __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
-  const size_t a_ld = static_cast<size_t>(g.K) * 2;
-  const size_t w_ld = static_cast<size_t>(g.Nw) * 2;
+  const size_t a_ld = static_cast<size_t>(g.K) * ESZ;
+  const size_t w_ld = static_cast<size_t>(g.Nw) * ESZ;
 
   // Per-lane global sources of this wave's DMA instructions (K offset added
-  // per stage).  A: instruction blk covers rows 16 blk .. 16 blk + 15.
+  // per stage).  A: instruction blk covers rows A_RPI blk .. + A_RPI - 1.
   const char* a_src[A_OPS];
 #pragma unroll
   for (int q = 0; q < A_OPS; ++q) {
     const int blk = (wave * A_OPS + q) % A_INSTS;
-    const int r = blk * 16 + lane / 4;
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = blk * A_RPI + lane / O::A_CHUNKS;
+    const int c = (lane % O::A_CHUNKS) ^ O::swz_a(r);
     const int row = min(row0 + r, row_end - 1);
     a_src[q] = Abase + static_cast<size_t>(row) * a_ld + c * 16;
   }
@@ -562,9 +669,8 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
   for (int q = 0; q < B_OPS; ++q) {
     const int blk = wave * B_OPS + q;
     const int r = blk * B_RPI + lane / B_CHUNKS;
-    const int sr = (r & 3) + 4 * ((r >> 3) & 1);
-    const int c = (lane % B_CHUNKS) ^ (2 * sr);
-    const int nl = c * 8;  // LDS column (element) of the chunk
+    const int c = (lane % B_CHUNKS) ^ O::swz_b(r);
+    const int nl = c * (16 / ESZ);  // LDS column (element) of the chunk
     int col;
     if (SWIGLU) {
       const int half = BN / 2;
@@ -572,14 +678,16 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
     } else {
       col = nt * BN + nl;
     }
-    b_src[q] = Wbase + static_cast<size_t>(r) * w_ld + static_cast<size_t>(col) * 2;
+    b_src[q] = Wbase + static_cast<size_t>(r) * w_ld + static_cast<size_t>(col) * ESZ;
   }
-  // Only A blocks (16 rows each) that hold a valid row are fetched; rows
-  // past them are never read by a live MFMA.  The count is wave-uniform and
-  // so is this wave's number of DMA instructions per stage.
-  const int a_live = (A_INSTS == 1) ? A_OPS
-                                    : __builtin_amdgcn_readfirstlane(max(
-                                          0, min(A_OPS, ((rows_valid + 15) / 16) - wave * A_OPS)));
+  // Only A blocks that hold a valid row are fetched; rows past them are never
+  // read by a live MFMA.  The count is wave-uniform and so is this wave's
+  // number of DMA instructions per stage.
+  const int a_live =
+      (A_INSTS == 1)
+          ? A_OPS
+          : __builtin_amdgcn_readfirstlane(
+                max(0, min(A_OPS, ((rows_valid + A_RPI - 1) / A_RPI) - wave * A_OPS)));
   const int ops_w = a_live + B_OPS;
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
@@ -609,25 +717,16 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
     return wn * (BN / WAVES_N) + j * 16;
   };
 
-  // lane's transposing-load addresses inside a stage's B region (two halves)
-  const int grp4 = lane >> 4, p = lane & 15;
-  int b_off[NTW][2];
+  int b_off[NTW][4];
 #pragma unroll
-  for (int j = 0; j < NTW; ++j)
+  for (int j = 0; j < NTW; ++j) {
+    O::template b_offsets<B_ROW>(lane, bcol(j), b_off[j]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 8 * grp4 + 4 * h + (p >> 2);
-      const int col = bcol(j) + (p & 3) * 4;
-      const int sr = (r & 3) + 4 * ((r >> 3) & 1);
-      const int c = (col >> 3) ^ (2 * sr);
-      b_off[j][h] = A_BYTES + r * B_ROW + c * 16 + (col & 7) * 2;
-    }
-  int a_off[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int r = wm * WM + i * 16 + (lane & 15);
-    a_off[i] = r * A_ROW + ((grp4 ^ ((r >> 2) & 3)) << 4);
+    for (int h = 0; h < 4; ++h) b_off[j][h] += A_BYTES;
   }
+  int a_off[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) O::template a_offsets<A_ROW>(wm * WM + i * 16 + (lane & 15), lane, a_off[i]);
 
   // A wave with any live row multiplies all of its MT row tiles (rows past the
   // segment only feed accumulators that are never stored); a wave with none
@@ -636,23 +735,16 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
   auto compute = [&](int slot) {
     if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
-    bf16x8_t bfr[NTW];
+    typename O::frag bfr[NTW];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      i16x4_t lo4 = ds_read_tr16(st + b_off[j][0]);
-      i16x4_t hi4 = ds_read_tr16(st + b_off[j][1]);
-      typedef __attribute__((ext_vector_type(8))) short i16x8_t;
-      i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      bfr[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-    bf16x8_t af[MT];
+    for (int j = 0; j < NTW; ++j) bfr[j] = O::load_b(st, b_off[j]);
+    typename O::frag af[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i]);
+    for (int i = 0; i < MT; ++i) af[i] = O::load_a(st, a_off[i]);
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(af[i], bfr[j], acc[i][j]);
   };
 
   // The K loop is unrolled by STAGES so that every stage slot is a constant
@@ -686,19 +778,31 @@ void grouped_gemm_bf16_dma_kernel(GemmArgs g) {
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
       if (row >= row_end) continue;
+      const float rs = (PREC == MOE_PREC_FP8) ? asc[row] : 1.0f;
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NTW / 2; ++j) {
           const int ncol = nt * (BN / 2) + bcol(j) + col_in;
-          reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
-              f32_to_bf16(silu(acc[i][j][v]) * acc[i][j + NTW / 2][v]);
+          float hg = acc[i][j][v];
+          float hu = acc[i][j + NTW / 2][v];
+          if (PREC == MOE_PREC_FP8) {
+            hg *= wsc[ncol] * rs;
+            hu *= wsc[g.f + ncol] * rs;
+            reinterpret_cast<float*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+                silu(hg) * hu;
+          } else {
+            reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+                f32_to_bf16(silu(hg) * hu);
+          }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const int ncol = nt * BN + bcol(j) + col_in;
+          float y = acc[i][j][v];
+          if (PREC == MOE_PREC_FP8) y *= wsc[ncol] * rs;
           reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
-              f32_to_bf16(acc[i][j][v]);
+              f32_to_bf16(y);
         }
       }
     }
@@ -812,8 +916,7 @@ template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int S
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
   dim3 grid(ub_m * g.n_tiles);
   if constexpr (STAGES >= 3) {
-    static_assert(PREC == MOE_PREC_BF16, "the DMA pipeline is bf16");
-    hipLaunchKernelGGL((grouped_gemm_bf16_dma_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
                        grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
   } else {
     hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
@@ -905,7 +1008,9 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
                 : run_ffn<PREC, 16, 128, 1, 4, 1>(a, stream);
   // e4m3 operands are 32 bytes per lane: 256x256 tiles would spill
   if constexpr (PREC == MOE_PREC_FP8) {
-    return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+    // e4m3: the MFMA is twice as fast per operand byte, so LDS bandwidth
+    // binds first: 64 x 256 tiles with 64 x 64 wave tiles, one block per CU
+    return run_ffn<PREC, 64, 256, 1, 4, 3>(a, stream);
   } else {
     if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
     return run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream);
