@@ -112,6 +112,40 @@ def cpu_baseline(inp, gpu_ids, counts, target_s=12.0, max_s=30.0, log_fn=log):
             "seconds": round(el, 2)}
 
 
+TRAFFIC_SOURCES = ("mixture_experts_layer_09_amd/csrc/grouped_gemm.hip",
+                   "mixture_experts_layer_09_amd/csrc/moe_internal.h")
+
+
+def grouped_gemm_source_hash() -> str:
+    """sha256 over the sources the grouped GEMM kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes of one moe_expert_ffn call on this workload, from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE of the two
+    GEMM dispatches, scaled by the copy-probe calibration), or None when there
+    is none or it was taken on other grouped GEMM sources than these."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_hbm_bytes.md")
+    try:
+        with open(path) as fh:
+            text = fh.read()
+        sha = grouped_gemm_source_hash()
+    except OSError:
+        return None
+    m = re.search(r"^bench-traffic: bytes_per_call=(\d+) sources_sha256=([0-9a-f]{64})\s*$",
+                  text, re.M)
+    if not m or m.group(2) != sha:
+        return None
+    return int(m.group(1))
+
+
 def copy_probe(nbytes: int, reps: int = 5):
     """A plain device-to-device copy of nbytes, for calibrating the HBM byte
     counters (FETCH_SIZE / WRITE_SIZE) against a known amount of traffic."""
@@ -142,8 +176,8 @@ def main(argv=None):
     if args.copy_probe:
         return copy_probe(args.copy_probe)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "part of it (see the sharding notes in DESIGN.md)",
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; "
+                                   "runs on more than one GPU are not supported",
                           "n_gpus": args.gpus}))
         return 2
 
@@ -253,7 +287,10 @@ def main(argv=None):
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS[prec],
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
                 "traffic": None}
+    traffic = measured_traffic(wl.name) if not args.set else None
+    roof["traffic"] = traffic
     roof.update({"kernel": "moe_expert_ffn (grouped Linear1+SwiGLU, Linear2)",
+                 "traffic_over_algorithmic": (round(traffic / nbytes, 3) if traffic else None),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                  "ms": round(stage_ms[2], 4),
                  "frac_of_roofline": round(max(t_mfma, t_hbm) / ffn_s, 4)})

@@ -55,17 +55,29 @@ __global__ __launch_bounds__(256) void combine_kernel(int h, int k,
     const int nv = h / 8;
     for (int v = threadIdx.x; v < nv; v += 256) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int r = s_row[j];
-        if (r < 0) continue;
-        const float g = s_g[j];
-        uint4 y = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Yp) +
-                                                 static_cast<size_t>(r) * h)[v];
-        uint32_t w[4] = {y.x, y.y, y.z, y.w};
+      // groups of 8 rows: all loads of a group are issued before any is used
+      for (int j0 = 0; j0 < k; j0 += 8) {
+        uint4 yr[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(g, __uint_as_float(w[q] << 16), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(g, __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
+        for (int q = 0; q < 8; ++q) {
+          const int j = j0 + q;
+          const int r = (j < k) ? s_row[j] : -1;
+          yr[q] = make_uint4(0u, 0u, 0u, 0u);
+          if (r >= 0)
+            yr[q] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Yp) +
+                                                   static_cast<size_t>(r) * h)[v];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = j0 + q;
+          if (j >= k || s_row[j] < 0) continue;
+          const float g = s_g[j];
+          uint32_t w[4] = {yr[q].x, yr[q].y, yr[q].z, yr[q].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[2 * c] = fmaf(g, __uint_as_float(w[c] << 16), acc[2 * c]);
+            acc[2 * c + 1] = fmaf(g, __uint_as_float(w[c] & 0xffff0000u), acc[2 * c + 1]);
+          }
         }
       }
       if (Ys) {

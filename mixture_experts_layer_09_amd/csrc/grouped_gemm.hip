@@ -14,19 +14,23 @@
 // bound of m-tiles times the n-tiles; blocks past the real count exit at
 // once.  A block renumbers itself so that each of the 8 XCDs (blocks are dealt
 // to them round-robin) runs one contiguous range of work items, and inside a
-// segment items go in groups of 4 m-tiles, n-tile major: the blocks an XCD
-// runs together share weight columns and token rows in its L2.  16-row MFMA
-// tiles past a segment's last row are skipped, so a cold expert's tile costs
-// only the rows it has, and padding rows are never stored.
+// segment items go in groups of m-tiles (1024 rows), n-tile major: the blocks
+// an XCD runs together share weight columns and token rows in its L2.  16-row
+// MFMA tiles past a segment's last row are skipped, so a cold expert's tile
+// costs only the rows it has, and padding rows are never stored.
 //
-// Prefill tiles are 256 x 256 on 8 waves (each wave 128 x 64); decode tiles
-// are 16 x 256 on 4 waves with one LDS stage, which fits more blocks per CU
-// and so keeps more weight bytes in flight.  K-tiles are 128 bytes: 64 bf16
-// or 128 e4m3 elements.  Token rows are K-contiguous and go to LDS as they
-// are; weights are [K, N] row-major, so each thread loads a 4 x 16-byte block
-// and writes it transposed (v_perm byte shuffles), and LDS holds both
-// operands K-contiguous, which is what each MFMA lane reads.  The next K-tile
-// is prefetched into registers while the current one is multiplied.
+// Prefill (grouped_gemm_dma_kernel): operands go global -> LDS by DMA
+// (global_load_lds_dwordx4) into a 3-stage ring, with waits written out as
+// s_waitcnt vmcnt + s_barrier.  Weights are [K, N] row-major and stay so in
+// LDS; the MFMA's K-consecutive B fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16 / _tr_b8).  Tiles: bf16 128 x 256 on 4 waves, two
+// blocks per CU, or 128 x 512 on 8 waves when experts hold about one m-tile
+// of rows; e4m3 64 x 256 on 4 waves.
+// Decode (grouped_gemm_kernel, a few rows per expert): 16 x 256 tiles on 4
+// waves with one LDS stage, which fits more blocks per CU and so keeps more
+// weight bytes in flight; each thread loads a 4 x 16-byte weight block into
+// registers and writes it transposed (v_perm byte shuffles), and the next
+// K-tile is prefetched into registers while the current one is multiplied.
 //   bf16: v_mfma_f32_16x16x32_bf16 (a lane holds 8 K-consecutive elements)
 //   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (32 per lane)
 // For SwiGLU an N-tile of BN columns holds BN/2 gate columns and the
@@ -406,18 +410,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 // s_waitcnt vmcnt(n) leaves exactly the later stages in flight, then a plain
 // s_barrier (no fence, which would drain all of them) publishes the stage.
 
-// One DMA instruction: 16 bytes per lane from `src` to LDS lds_dst + 16 * lane
-// (lds_dst is wave-uniform and goes through M0).  Written as inline asm so
-// that the compiler, which would otherwise make every later LDS read wait
-// for all DMA in flight, leaves the waiting to wait_vmcnt; the memory clobber
-// keeps LDS reads and other memory operations on their side of it.
-__device__ __forceinline__ void dma16(const void* src, char* lds_dst) {
+// One DMA instruction: 16 bytes per lane from sbase + voff to LDS lds_dst +
+// 16 * lane (sbase and lds_dst are wave-uniform; lds_dst goes through M0).
+// Written as inline asm so that the compiler, which would otherwise make
+// every later LDS read wait for all DMA in flight, leaves the waiting to
+// wait_vmcnt; the memory clobber keeps LDS reads and other memory operations
+// on their side of it.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "s"(lds)
+               : "v"(voff), "s"(sbase), "s"(lds)
                : "memory");
+}
+
+// A pointer the compiler may not prove wave-uniform, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).
@@ -593,7 +606,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   const int wn = wave % WAVES_N;
 
   // ------------------------------------------------ tile -> segment (as above)
-  constexpr int GROUP_M = 4;
+  constexpr int GROUP_M = 1024 / BM;  // m-tiles of one group: 1024 rows
   const int E = g.E;
   const int NT = g.n_tiles;
   const int total = g.tile_off[E + 1] * NT;
@@ -653,32 +666,32 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   const size_t a_ld = static_cast<size_t>(g.K) * ESZ;
   const size_t w_ld = static_cast<size_t>(g.Nw) * ESZ;
 
-  // Per-lane global sources of this wave's DMA instructions (K offset added
-  // per stage).  A: instruction blk covers rows A_RPI blk .. + A_RPI - 1.
-  const char* a_src[A_OPS];
+  // DMA sources: a wave-uniform base (the tile's first row and column, K
+  // offset added per stage) plus a 32-bit per-lane offset.  A: instruction
+  // blk covers rows A_RPI blk .. + A_RPI - 1 of the tile (clamped to the
+  // segment's last row).
+  const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * a_ld);
+  uint32_t a_voff[A_OPS];
 #pragma unroll
   for (int q = 0; q < A_OPS; ++q) {
     const int blk = (wave * A_OPS + q) % A_INSTS;
     const int r = blk * A_RPI + lane / O::A_CHUNKS;
     const int c = (lane % O::A_CHUNKS) ^ O::swz_a(r);
-    const int row = min(row0 + r, row_end - 1);
-    a_src[q] = Abase + static_cast<size_t>(row) * a_ld + c * 16;
+    a_voff[q] = static_cast<uint32_t>(min(r, row_end - 1 - row0)) * static_cast<uint32_t>(a_ld) +
+                c * 16;
   }
-  const char* b_src[B_OPS];
+  const char* b_base = uniform_ptr(
+      Wbase + static_cast<size_t>(nt) * (SWIGLU ? BN / 2 : BN) * ESZ);
+  uint32_t b_voff[B_OPS];
 #pragma unroll
   for (int q = 0; q < B_OPS; ++q) {
     const int blk = wave * B_OPS + q;
     const int r = blk * B_RPI + lane / B_CHUNKS;
     const int c = (lane % B_CHUNKS) ^ O::swz_b(r);
     const int nl = c * (16 / ESZ);  // LDS column (element) of the chunk
-    int col;
-    if (SWIGLU) {
-      const int half = BN / 2;
-      col = nl < half ? nt * half + nl : g.f + nt * half + (nl - half);
-    } else {
-      col = nt * BN + nl;
-    }
-    b_src[q] = Wbase + static_cast<size_t>(r) * w_ld + static_cast<size_t>(col) * ESZ;
+    int col = nl;  // column relative to the tile's first gate (or plain) column
+    if (SWIGLU && nl >= BN / 2) col = g.f + (nl - BN / 2);
+    b_voff[q] = static_cast<uint32_t>(r) * static_cast<uint32_t>(w_ld) + col * ESZ;
   }
   // Only A blocks that hold a valid row are fetched; rows past them are never
   // read by a live MFMA.  The count is wave-uniform and so is this wave's
@@ -694,12 +707,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < A_OPS; ++q) {
       const int blk = (wave * A_OPS + q) % A_INSTS;
-      if (q < a_live) dma16(a_src[q] + static_cast<size_t>(kt) * A_ROW, st + blk * 1024);
+      if (q < a_live) dma16(a_base + static_cast<size_t>(kt) * A_ROW, a_voff[q], st + blk * 1024);
     }
 #pragma unroll
     for (int q = 0; q < B_OPS; ++q) {
       const int blk = wave * B_OPS + q;
-      dma16(b_src[q] + static_cast<size_t>(kt) * BK * w_ld, st + A_BYTES + blk * 1024);
+      dma16(b_base + static_cast<size_t>(kt) * BK * w_ld, b_voff[q], st + A_BYTES + blk * 1024);
     }
   };
 
@@ -914,11 +927,11 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
 
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
-  dim3 grid(ub_m * g.n_tiles);
   if constexpr (STAGES >= 3) {
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
-                       grid, dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+                       dim3(ub_m * g.n_tiles), dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
   } else {
+    dim3 grid(ub_m * g.n_tiles);
     hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
                        dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
   }
@@ -999,20 +1012,26 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
   const int rows = a.T * a.k;
   // Decode-sized batches (a few rows per expert) stream weights with 16-row
   // tiles and one LDS stage, so more blocks fit on a CU; prefill batches use
-  // 256x256 tiles on 8 waves.  N tiles of 256 need hidden and 2*inter to be
+  // the 3-stage DMA pipeline.  N tiles of 256 need hidden and 2*inter to be
   // multiples of 256, else 128.
   const bool small = static_cast<long>(rows) < 16L * a.E;
   const bool wide = (a.h % 256 == 0) && ((2 * a.f) % 256 == 0);
   if (small)
     return wide ? run_ffn<PREC, 16, 256, 1, 4, 1>(a, stream)
                 : run_ffn<PREC, 16, 128, 1, 4, 1>(a, stream);
-  // e4m3 operands are 32 bytes per lane: 256x256 tiles would spill
   if constexpr (PREC == MOE_PREC_FP8) {
     // e4m3: the MFMA is twice as fast per operand byte, so LDS bandwidth
     // binds first: 64 x 256 tiles with 64 x 64 wave tiles, one block per CU
     return run_ffn<PREC, 64, 256, 1, 4, 3>(a, stream);
   } else {
     if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
+    // About one m-tile of rows per expert: every m-tile's token rows are read
+    // once per n-tile, so 512-wide n-tiles on 8 waves halve that traffic.
+    // With more rows per expert the weight tiles dominate and two 4-wave
+    // blocks of 128 x 256 per CU are faster.
+    const bool w512 = (a.h % 512 == 0) && ((2 * a.f) % 512 == 0);
+    if (w512 && static_cast<long>(rows) < 256L * a.E)
+      return run_ffn<PREC, 128, 512, 2, 4, 3>(a, stream);
     return run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream);
   }
 }

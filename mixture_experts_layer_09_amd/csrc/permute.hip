@@ -56,16 +56,27 @@ __global__ __launch_bounds__(kPermChunk) void count_rank_kernel(const int32_t* _
     blk_cnt[static_cast<size_t>(blockIdx.x) * E + x] = s_cnt[x];
 }
 
-// One block of 512 threads; E <= 512, one thread per expert.
+// One block of 512 threads; E <= 512, one thread per expert.  The loops over
+// the per-block counts load 8 blocks at a time so that the loads overlap.
 __global__ __launch_bounds__(kMaxExperts) void scan_kernel(int nblk, int E,
                                                            int32_t* __restrict__ blk_cnt,
                                                            int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets) {
   __shared__ int32_t s[kMaxExperts];
+  constexpr int U = 8;
   const int e = threadIdx.x;
   int total = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) total += blk_cnt[static_cast<size_t>(b) * E + e];
+  if (e < E) {
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = blk_cnt[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) total += v[u];
+    }
+    for (; b < nblk; ++b) total += blk_cnt[static_cast<size_t>(b) * E + e];
+  }
   s[e] = (e < E) ? total : 0;
   __syncthreads();
   // inclusive Hillis-Steele scan over the experts
@@ -81,9 +92,20 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(int nblk, int E,
     offsets[e] = off;
     if (e == E - 1) offsets[E] = s[e];
     int run = off;
-    for (int b = 0; b < nblk; ++b) {
-      size_t at = static_cast<size_t>(b) * E + e;
-      int c = blk_cnt[at];
+    int b = 0;
+    for (; b + U <= nblk; b += U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = blk_cnt[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        blk_cnt[static_cast<size_t>(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; b < nblk; ++b) {
+      const size_t at = static_cast<size_t>(b) * E + e;
+      const int c = blk_cnt[at];
       blk_cnt[at] = run;
       run += c;
     }
