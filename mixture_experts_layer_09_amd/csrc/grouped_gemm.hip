@@ -13,9 +13,11 @@
 // ceil(rows_e / BM) over segments 0..E (E = shared).  The grid is an upper
 // bound of m-tiles times the n-tiles; blocks past the real count exit at
 // once.  A block renumbers itself so that each of the 8 XCDs (blocks are dealt
-// to them round-robin) runs one contiguous range of work items, and inside a
-// segment items go in groups of m-tiles (1024 rows), n-tile major: the blocks
-// an XCD runs together share weight columns and token rows in its L2.  16-row
+// to them round-robin) runs runs of consecutive work items (one contiguous
+// range, or chunks of two m-tiles' items dealt to the XCDs in turn), and
+// inside a segment items go in groups of m-tiles (1024 rows), n-tile major:
+// the blocks an XCD runs together share weight columns and token rows in its
+// L2.  16-row
 // MFMA tiles past a segment's last row are skipped, so a cold expert's tile
 // costs only the rows it has, and padding rows are never stored.
 //
@@ -25,7 +27,7 @@
 // LDS; the MFMA's K-consecutive B fragments come from transposing LDS reads
 // (ds_read_b64_tr_b16 / _tr_b8).  Tiles: bf16 128 x 256 on 4 waves, two
 // blocks per CU, or 128 x 512 on 8 waves when experts hold about one m-tile
-// of rows; e4m3 64 x 256 on 4 waves.
+// of rows; e4m3 128 x 256 on 8 waves.
 // Decode (grouped_gemm_kernel, a few rows per expert): 16 x 256 tiles on 4
 // waves with one LDS stage, which fits more blocks per CU and so keeps more
 // weight bytes in flight; each thread loads a 4 x 16-byte weight block into
@@ -74,6 +76,7 @@ struct GemmArgs {
   const int32_t* offsets;
   const int32_t* tile_off;
   int E, K, Nw, Nout, f, T, n_tiles;
+  int chunk;  // DMA kernel: items per XCD chunk (0: one contiguous range per XCD)
 };
 
 template <int PREC>
@@ -572,7 +575,7 @@ struct DmaOps<MOE_PREC_FP8, BN> {
 // stage barriers); e4m3 keeps one block of deeper stages per CU.
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N)
-__attribute__((amdgpu_waves_per_eu((PREC == MOE_PREC_BF16 || STAGES * (BM + BN) * 128 <= 81920) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu((PREC == MOE_PREC_BF16 || WAVES_M * WAVES_N >= 8 || STAGES * (BM + BN) * 128 <= 81920) ? 2 : 1)))
 void grouped_gemm_dma_kernel(GemmArgs g) {
   using O = DmaOps<PREC, BN>;
   constexpr int NW = WAVES_M * WAVES_N;
@@ -610,9 +613,13 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   const int E = g.E;
   const int NT = g.n_tiles;
   const int total = g.tile_off[E + 1] * NT;
-  if (static_cast<int>(blockIdx.x) >= total) return;
   int item;
-  {
+  if (g.chunk > 0) {  // chunks of C items dealt to the XCDs in turn
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, C = g.chunk;
+    item = (slot / C) * (8 * C) + x * C + slot % C;
+    if (item >= total) return;
+  } else {
+    if (static_cast<int>(blockIdx.x) >= total) return;
     const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
     const int per = total >> 3, rem = total & 7;
     item = x * per + min(x, rem) + slot;
@@ -928,8 +935,15 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
   if constexpr (STAGES >= 3) {
+    // bf16: chunks of two m-tiles' worth of items are dealt to the XCDs in
+    // turn, which evens out the XCDs' loads when a few segments (the shared
+    // expert, hot experts) hold many m-tiles; e4m3 keeps contiguous ranges.
+    GemmArgs gg = g;
+    gg.chunk = (PREC == MOE_PREC_BF16) ? 2 * g.n_tiles : 0;
+    long grid = static_cast<long>(ub_m) * g.n_tiles;
+    if (gg.chunk > 0) grid = (grid + 8L * gg.chunk - 1) / (8L * gg.chunk) * (8L * gg.chunk);
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
-                       dim3(ub_m * g.n_tiles), dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+                       dim3(grid), dim3(64 * WAVES_M * WAVES_N), 0, stream, gg);
   } else {
     dim3 grid(ub_m * g.n_tiles);
     hipLaunchKernelGGL((grouped_gemm_kernel<PREC, BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>), grid,
@@ -1020,9 +1034,10 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
     return wide ? run_ffn<PREC, 16, 256, 1, 4, 1>(a, stream)
                 : run_ffn<PREC, 16, 128, 1, 4, 1>(a, stream);
   if constexpr (PREC == MOE_PREC_FP8) {
-    // e4m3: the MFMA is twice as fast per operand byte, so LDS bandwidth
-    // binds first: 64 x 256 tiles with 64 x 64 wave tiles, one block per CU
-    return run_ffn<PREC, 64, 256, 1, 4, 3>(a, stream);
+    // e4m3: 128 x 256 tiles on 8 waves (64 x 64 per wave): the 3-stage ring
+    // (144 KB) allows one block per CU, and 8 waves give two per SIMD to
+    // cover each other's LDS and DMA waits
+    return run_ffn<PREC, 128, 256, 2, 4, 3>(a, stream);
   } else {
     if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
     // About one m-tile of rows per expert: every m-tile's token rows are read
