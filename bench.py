@@ -35,6 +35,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def stage_bytes(wl):
+    """Algorithmic HBM bytes of the stages around the grouped GEMM (each
+    tensor read or written once): route reads X and Wg and writes the ids and
+    gate weights; permute reads the ids and X and writes the row maps and the
+    k copies (e4m3: plus the quantised X and scales); combine reads the k
+    expert rows, the gate weights and row map (and the shared row) and writes
+    Y."""
+    T, h, E, k = wl.T, wl.hidden, wl.experts, wl.topk
+    ab = 4 if wl.precision == "fp32" else 2             # activation / output bytes
+    xb = 1 if wl.precision == "fp8" else ab             # dispatched row bytes
+    route = T * h * ab + h * E * ab + T * k * 8 + (T * 4 if wl.hash else 0)
+    permute = 2 * T * k * 4 + T * h * ab + T * k * h * xb + 2 * T * k * 4
+    if wl.precision == "fp8":
+        permute += T * h + T * 4 + T * k * 4
+    combine = T * k * h * ab + T * k * 8 + (T * h * ab if wl.shared else 0) + T * h * ab
+    return {"route": route, "permute": permute, "combine": combine}
+
+
 def algorithmic_work(wl, counts):
     """FLOPs and HBM bytes the grouped GEMM stage must do for these counts:
     every routed and shared row through Linear1 (h -> 2f) and Linear2 (f -> h);
@@ -102,14 +120,49 @@ def cpu_baseline(inp, gpu_ids, counts, target_s=12.0, max_s=30.0, log_fn=log):
         if el >= target_s or el * (reps + 1) / reps > max_s:
             break
     n = reps * len(toks)
-    cores = min(int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0)),
-                len(os.sched_getaffinity(0)))
-    log_fn(f"[bench] cpu oracle: {n} tokens ({reps} x {len(toks)}) in {el:.2f} s")
+    cores = oracle.set_threads(0)
+    log_fn(f"[bench] cpu oracle: {n} tokens ({reps} x {len(toks)}) in {el:.2f} s on {cores} threads")
+    # the same per-token work on one thread, over the first tokens of the sample
+    one = min(len(toks), 32)
+    oracle.set_threads(1)
+    n1, t1 = 0, time.perf_counter()
+    try:
+        while True:
+            r1 = oracle.route(X[:one], Wg, wl.topk, gate_bias=f64(inp["gate_bias"]),
+                              beta=f64(inp["beta"]), score=wl.score, renorm=wl.renorm,
+                              alpha=wl.alpha,
+                              token_ids=None if tok_ids is None else tok_ids[:one],
+                              tid2eid=bits(inp["tid2eid"]))
+            G1 = r["G"].copy()
+            G1[:one] = r1["G"]
+            L.tokens(ids_local, G1, tokens=np.arange(one))
+            n1 += one
+            el1 = time.perf_counter() - t1
+            if el1 >= 3.0:
+                break
+    finally:
+        oracle.set_threads(0)
+    log_fn(f"[bench] cpu oracle, one thread: {n1} tokens in {el1:.2f} s")
     return {"value": round(n / el, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(toks)} of the {wl.T} tokens ({how}), repeated {reps} times: fp64 "
                       f"routing of those tokens + the per-token loop over their {wl.topk} routed "
                       "experts" + (" and the shared expert" if wl.shared else ""),
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2),
+            "value_1core": round(n1 / el1, 2),
+            "sample_1core": f"the first {one} tokens of that sample, on one thread, "
+                            f"repeated for {el1:.1f} s",
+            "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 TRAFFIC_SOURCES = ("mixture_experts_layer_09_amd/csrc/grouped_gemm.hip",
@@ -144,6 +197,24 @@ def measured_traffic(workload: str):
     if not m or m.group(2) != sha:
         return None
     return int(m.group(1))
+
+
+def device_copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Context figure: read + write GB/s of a plain device-to-device copy."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    s1.record()
+    s1.synchronize()
+    ms = s0.elapsed_time(s1) / reps
+    del a, b
+    return round(2 * nbytes / (ms / 1000.0) / 1e9, 1)
 
 
 def copy_probe(nbytes: int, reps: int = 5):
@@ -294,6 +365,9 @@ def main(argv=None):
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                  "ms": round(stage_ms[2], 4),
                  "frac_of_roofline": round(max(t_mfma, t_hbm) / ffn_s, 4)})
+    sbytes = stage_bytes(wl)
+    layer_bytes = nbytes + sum(sbytes.values())
+    copy_gbs = device_copy_gbs()
     value = T / (ms_per_step / 1000.0)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -314,6 +388,16 @@ def main(argv=None):
         "stages_ms": {"route": round(stage_ms[0], 4), "permute": round(stage_ms[1], 4),
                       "expert_ffn": round(stage_ms[2], 4), "combine": round(stage_ms[3], 4)},
         "moe_forward_ms": round(fwd_ms, 4),
+        "stages_hbm": {name: {"gbs": round(b / (stage_ms[i] / 1000.0) / 1e9, 1),
+                              "frac_hbm_peak": round(b / (stage_ms[i] / 1000.0) / 1e9
+                                                     / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes": b}
+                       for i, (name, b) in zip((0, 1, 3), sbytes.items())},
+        "layer_hbm": {"gbs": round(layer_bytes / (ms_per_step / 1000.0) / 1e9, 1),
+                      "frac_hbm_peak": round(layer_bytes / (ms_per_step / 1000.0) / 1e9
+                                             / PEAK_HBM_GBS, 4),
+                      "algorithmic_bytes": layer_bytes},
+        "hbm_copy_probe_gbs": copy_gbs,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -61,6 +61,8 @@ def lib():
             build(force=False)
         L = C.CDLL(_LIB_PATH)
         vp, i32, dbl = C.c_void_p, C.c_int, C.c_double
+        L.oracle_set_threads.restype = i32
+        L.oracle_set_threads.argtypes = [i32]
         L.oracle_e4m3_decode.restype = dbl
         L.oracle_e4m3_decode.argtypes = [C.c_uint8]
         L.oracle_e4m3_encode.restype = C.c_uint8
@@ -170,6 +172,12 @@ def route(X, Wg, k, *, gate_bias=None, beta=None, score="sigmoid", renorm=True, 
                        _p(_c(token_ids, np.int32)), _p(_c(tid2eid, np.int32)), _p(ids), _p(G),
                        _p(logits), _p(keys), _p(margin))
     return {"ids": ids, "G": G, "logits": logits, "keys": keys, "margin": margin}
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads of the oracle's parallel loops (n < 1: default); returns
+    the count now in effect.  No effect on results."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 # ---------------------------------------------------------------- dispatch
