@@ -30,7 +30,8 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-PRECISIONS = {"fp32": 0, "bf16": 1, "fp8": 2}
+PRECISIONS = {"fp32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3, "mxfp4": 4}
+MX_FORMATS = {"e4m3": 0, "e2m1": 1}
 SCORES = {"sigmoid": 0, "softmax": 1, "sqrt_softplus": 2}
 
 
@@ -63,6 +64,15 @@ def lib():
         vp, i32, dbl = C.c_void_p, C.c_int, C.c_double
         L.oracle_set_threads.restype = i32
         L.oracle_set_threads.argtypes = [i32]
+        L.oracle_e2m1_decode.restype = dbl
+        L.oracle_e2m1_decode.argtypes = [C.c_uint8]
+        L.oracle_e2m1_encode.restype = C.c_uint8
+        L.oracle_e2m1_encode.argtypes = [dbl]
+        L.oracle_mx_scale_code.restype = C.c_uint8
+        L.oracle_mx_scale_code.argtypes = [dbl, i32]
+        L.oracle_mx_quantize.argtypes = [i32, vp, i32, vp, vp]
+        L.oracle_mx_value.restype = dbl
+        L.oracle_mx_value.argtypes = [C.c_uint8, C.c_uint8, i32]
         L.oracle_e4m3_decode.restype = dbl
         L.oracle_e4m3_decode.argtypes = [C.c_uint8]
         L.oracle_e4m3_encode.restype = C.c_uint8
@@ -174,6 +184,37 @@ def route(X, Wg, k, *, gate_bias=None, beta=None, score="sigmoid", renorm=True, 
     return {"ids": ids, "G": G, "logits": logits, "keys": keys, "margin": margin}
 
 
+def e2m1_decode(code: int) -> float:
+    return float(lib().oracle_e2m1_decode(int(code) & 0xF))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(lib().oracle_e2m1_encode(float(v)))
+
+
+def mx_scale_code(amax: float, fmt: str) -> int:
+    """E8M0 code of a group's shared scale (OCP MX rule; see moe_oracle.c)."""
+    return int(lib().oracle_mx_scale_code(float(amax), MX_FORMATS[fmt]))
+
+
+def mx_quantize(x, fmt: str):
+    """MX quantisation along the last axis (a multiple of 32) in groups of 32:
+    returns (element codes, one per value, uint8; E8M0 scale codes, uint8)."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % 32 == 0
+    flat = np.ascontiguousarray(x.reshape(-1, n))
+    q = np.empty(flat.shape, np.uint8)
+    sc = np.empty((flat.shape[0], n // 32), np.uint8)
+    for r in range(flat.shape[0]):
+        lib().oracle_mx_quantize(n, _p(flat[r]), MX_FORMATS[fmt], _p(q[r]), _p(sc[r]))
+    return q.reshape(x.shape), sc.reshape(x.shape[:-1] + (n // 32,))
+
+
+def mx_value(code: int, scale: int, fmt: str) -> float:
+    return float(lib().oracle_mx_value(int(code), int(scale), MX_FORMATS[fmt]))
+
+
 def set_threads(n: int) -> int:
     """OpenMP threads of the oracle's parallel loops (n < 1: default); returns
     the count now in effect.  No effect on results."""
@@ -209,28 +250,39 @@ class Layer:
 
     precision 'fp32': X, W float32.  'bf16': X, W uint16 bits.  'fp8': X uint16
     (bf16 bits, quantised per token inside the layer), W uint8 e4m3 codes with
-    float32 per-output-channel scales.
+    float32 per-output-channel scales.  'mxfp8' / 'mxfp4': X uint16 (bf16
+    bits, MX-quantised inside the layer), W uint8 e4m3 codes [E,K,N] / e2m1
+    code pairs [E,K,N/2] (element 2i in the low nibble), scales uint8 E8M0
+    [E,K/32,N].
     """
 
     def __init__(self, precision, X, W1, W2, *, w1_scale=None, w2_scale=None, Ws1=None, Ws2=None,
                  ws1_scale=None, ws2_scale=None, k=1):
         self.precision = precision
-        wdt = {"fp32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[precision]
+        mx = precision.startswith("mx")
+        wdt = {"fp32": np.float32, "bf16": np.uint16}.get(precision, np.uint8)
+        sdt = np.uint8 if mx else np.float32
         xdt = np.float32 if precision == "fp32" else np.uint16
         self.X = _c(X, xdt)
         self.W1 = _c(W1, wdt)
         self.W2 = _c(W2, wdt)
-        self.w1_scale = _c(w1_scale, np.float32)
-        self.w2_scale = _c(w2_scale, np.float32)
+        self.w1_scale = _c(w1_scale, sdt)
+        self.w2_scale = _c(w2_scale, sdt)
         self.Ws1 = _c(Ws1, wdt)
         self.Ws2 = _c(Ws2, wdt)
-        self.ws1_scale = _c(ws1_scale, np.float32)
-        self.ws2_scale = _c(ws2_scale, np.float32)
+        self.ws1_scale = _c(ws1_scale, sdt)
+        self.ws2_scale = _c(ws2_scale, sdt)
         T, h = self.X.shape
         E, h2, f2 = self.W1.shape
+        if precision == "mxfp4":
+            f2 *= 2  # two e2m1 codes per byte
         assert h2 == h and f2 % 2 == 0
         self.T, self.hidden, self.E, self.inter, self.k = T, h, E, f2 // 2, int(k)
-        if precision == "fp8":
+        if mx:
+            assert h % 32 == 0 and self.inter % 32 == 0
+            assert self.w1_scale.shape == (E, h // 32, f2)
+            assert self.w2_scale.shape == (E, self.inter // 32, h)
+        if precision in ("fp8", "mxfp8", "mxfp4"):
             assert self.w1_scale is not None and self.w2_scale is not None
         self._s = _Layer(T, h, E, self.k, self.inter, int(self.Ws1 is not None),
                          PRECISIONS[precision], _p(self.X), _p(self.W1), _p(self.W2),

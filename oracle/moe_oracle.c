@@ -37,10 +37,21 @@
  *     scale 1 and code 0;
  *   - the per-token activation quantisation of X is an integer decision
  *     taken from an input, so it is done in fp32 (the kernel's precision),
- *     everything else is fp64.
+ *     everything else is fp64;
+ *   - MX block quantisation ([MM] MXFP block: groups of 32 elements along the
+ *     contraction dimension share one E8M0 scale, elements FP8 e4m3fn or
+ *     FP4 e2m1): the pages name the group size, the element and scale types
+ *     and that a shared exponent is extracted per group, but not the rule;
+ *     the OCP MX v1.0 rule is taken: shared exponent = floor(log2(max|v|))
+ *     - emax(element) (emax 8 for e4m3, 2 for e2m1), clamped to the E8M0
+ *     range [-127, 127] (code = exponent + 127; an all-zero group gets code
+ *     0), and each element is v / 2^exponent rounded to nearest even and
+ *     saturated to the element's largest magnitude (448, 6).
  *
  * Element codes for tensors handed in: 0 = fp32, 1 = bf16 (raw 16-bit words),
- * 2 = fp8 e4m3fn (raw bytes).  All arrays are host memory, row major.
+ * 2 = fp8 e4m3fn (raw bytes).  MX tensors: e4m3 codes one per byte, e2m1
+ * codes two per byte (element 2i in the low nibble), E8M0 scale codes one per
+ * byte.  All arrays are host memory, row major.
  */
 #include <math.h>
 #include <stdint.h>
@@ -127,6 +138,77 @@ uint8_t oracle_e4m3_encode(double v) {
   else
     pick = (lo & 1) ? hi : lo; /* tie: even mantissa */
   return (uint8_t)(sign | pick);
+}
+
+/* OCP e2m1 (FP4): sign, 2 exponent bits (bias 1), 1 mantissa bit; no
+ * infinities or NaN.  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double oracle_e2m1_decode(uint8_t code) {
+  int sign = (code >> 3) & 1;
+  int ex = (code >> 1) & 3;
+  int man = code & 1;
+  double v = (ex == 0) ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+  return sign ? -v : v;
+}
+
+/* Nearest e2m1 value, ties to the even mantissa, saturating at 6. */
+uint8_t oracle_e2m1_encode(double v) {
+  uint8_t sign = (v < 0.0 || (v == 0.0 && signbit(v))) ? 0x8 : 0x0;
+  double a = fabs(v);
+  if (isnan(v) || a >= 6.0) return (uint8_t)(sign | 0x7);
+  int lo = 0, hi = 7; /* value(lo) <= a < value(hi) */
+  while (hi - lo > 1) {
+    int mid = (lo + hi) / 2;
+    if (oracle_e2m1_decode((uint8_t)mid) <= a)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  double dlo = a - oracle_e2m1_decode((uint8_t)lo);
+  double dhi = oracle_e2m1_decode((uint8_t)hi) - a;
+  int pick = dlo < dhi ? lo : (dhi < dlo ? hi : ((lo & 1) ? hi : lo));
+  return (uint8_t)(sign | pick);
+}
+
+#define ORC_FMT_E4M3 0
+#define ORC_FMT_E2M1 1
+
+/* E8M0 code of the shared scale of a group whose largest magnitude is amax
+ * (see the MX reading in the header). */
+uint8_t oracle_mx_scale_code(double amax, int fmt) {
+  if (!(amax > 0.0)) return 0;
+  int e2;
+  frexp(amax, &e2); /* amax = m * 2^e2, m in [0.5, 1): floor(log2 amax) = e2 - 1 */
+  int x = (e2 - 1) - (fmt == ORC_FMT_E4M3 ? 8 : 2);
+  if (x < -127) x = -127;
+  if (x > 127) x = 127;
+  return (uint8_t)(x + 127);
+}
+
+static double element_decode(uint8_t code, int fmt) {
+  return fmt == ORC_FMT_E4M3 ? oracle_e4m3_decode(code) : oracle_e2m1_decode(code);
+}
+static uint8_t element_encode(double v, int fmt) {
+  return fmt == ORC_FMT_E4M3 ? oracle_e4m3_encode(v) : oracle_e2m1_encode(v);
+}
+
+/* MX quantisation of n values (n a multiple of 32): one element code per
+ * value in q (unpacked, one per byte) and one E8M0 code per group in scale. */
+void oracle_mx_quantize(int n, const double* x, int fmt, uint8_t* q, uint8_t* scale) {
+  for (int g = 0; g < n / 32; ++g) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+      double a = fabs(x[g * 32 + i]);
+      amax = a > amax ? a : amax;
+    }
+    uint8_t sc = oracle_mx_scale_code(amax, fmt);
+    scale[g] = sc;
+    for (int i = 0; i < 32; ++i) q[g * 32 + i] = element_encode(ldexp(x[g * 32 + i], 127 - sc), fmt);
+  }
+}
+
+/* Value of an MX element: decode(code) * 2^(scale - 127). */
+double oracle_mx_value(uint8_t code, uint8_t scale, int fmt) {
+  return ldexp(element_decode(code, fmt), (int)scale - 127);
 }
 
 /* Values of all 256 e4m3 codes, filled from oracle_e4m3_decode on first use
@@ -359,19 +441,52 @@ static void swiglu_row_fp8(int hidden, int f, const uint8_t* qx, double sx, cons
   for (int o = 0; o < hidden; ++o) out[o] = out[o] * (double)s_w2[o] * sa;
 }
 
+/* Element (c, n) of an MX weight matrix with N columns: codes [K, N] (e2m1:
+ * two per byte along N), scales [K/32, N]. */
+static double mx_weight(const uint8_t* W, const uint8_t* S, int N, int c, int n, int fmt) {
+  size_t i = (size_t)c * N + n;
+  uint8_t code = fmt == ORC_FMT_E4M3 ? W[i] : (uint8_t)((W[i / 2] >> (4 * (i & 1))) & 0xF);
+  return oracle_mx_value(code, S[(size_t)(c / 32) * N + n], fmt);
+}
+
+/* The MX expert of [MM]'s MXFP block: x is quantised per group of 32 along
+ * hidden (Q_MX), Linear1 multiplies the dequantised operands (DQ_MX(X^) .
+ * DQ_MX(W1)), SwiGLU in fp64, the SwiGLU output is quantised per group of 32
+ * along inter and dequantised for Linear2 against DQ_MX(W2). */
+static void swiglu_row_mx(int hidden, int f, const double* x, int fmt, const uint8_t* W1,
+                          const uint8_t* S1, const uint8_t* W2, const uint8_t* S2, double* xd,
+                          uint8_t* qbuf, uint8_t* sbuf, double* h1, double* out) {
+  oracle_mx_quantize(hidden, x, fmt, qbuf, sbuf);
+  for (int c = 0; c < hidden; ++c) xd[c] = oracle_mx_value(qbuf[c], sbuf[c / 32], fmt);
+  for (int n = 0; n < 2 * f; ++n) h1[n] = 0.0;
+  for (int c = 0; c < hidden; ++c) {
+    double xc = xd[c];
+    if (xc == 0.0) continue;
+    for (int n = 0; n < 2 * f; ++n) h1[n] += xc * mx_weight(W1, S1, 2 * f, c, n, fmt);
+  }
+  for (int n = 0; n < f; ++n) h1[n] = silu(h1[n]) * h1[f + n];
+  oracle_mx_quantize(f, h1, fmt, qbuf, sbuf);
+  for (int o = 0; o < hidden; ++o) out[o] = 0.0;
+  for (int n = 0; n < f; ++n) {
+    double u = oracle_mx_value(qbuf[n], sbuf[n / 32], fmt);
+    if (u == 0.0) continue;
+    for (int o = 0; o < hidden; ++o) out[o] += u * mx_weight(W2, S2, hidden, n, o, fmt);
+  }
+}
+
 /* Everything that describes one layer.  Pointers are host memory. */
 typedef struct {
   int T, hidden, E, k, inter, has_shared;
-  int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3 */
+  int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3, 3 = MXFP8, 4 = MXFP4 */
   const void* X;        /* [T,hidden]: fp32 (precision 0) or bf16 */
-  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes */
+  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes / e2m1 pairs */
   const void* W2;       /* [E,f,hidden] */
-  const float* w1_scale; /* [E,2f], e4m3 only */
-  const float* w2_scale; /* [E,hidden], e4m3 only */
+  const void* w1_scale; /* A8W8: fp32 [E,2f]; MX: E8M0 [E,hidden/32,2f] */
+  const void* w2_scale; /* A8W8: fp32 [E,hidden]; MX: E8M0 [E,f/32,hidden] */
   const void* Ws1;      /* shared [hidden,2f] or NULL */
   const void* Ws2;      /* shared [f,hidden] */
-  const float* ws1_scale;
-  const float* ws2_scale;
+  const void* ws1_scale;
+  const void* ws2_scale;
 } oracle_layer;
 
 static int w_dt(int precision) {
@@ -385,18 +500,34 @@ static void expert_of_token(const oracle_layer* L, int t, int e, double* xbuf, u
   int shared = (e == L->E);
   const char* W1 = shared ? (const char*)L->Ws1 : (const char*)L->W1;
   const char* W2 = shared ? (const char*)L->Ws2 : (const char*)L->W2;
+  int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16;
+  if (L->precision >= 3) {
+    int fmt = L->precision == 3 ? ORC_FMT_E4M3 : ORC_FMT_E2M1;
+    size_t d1 = (size_t)h * 2 * f, d2 = (size_t)f * h; /* elements per expert */
+    const uint8_t* S1 = shared ? (const uint8_t*)L->ws1_scale
+                               : (const uint8_t*)L->w1_scale + (size_t)e * (h / 32) * 2 * f;
+    const uint8_t* S2 = shared ? (const uint8_t*)L->ws2_scale
+                               : (const uint8_t*)L->w2_scale + (size_t)e * (f / 32) * h;
+    if (!shared) {
+      W1 += fmt == ORC_FMT_E4M3 ? (size_t)e * d1 : (size_t)e * d1 / 2;
+      W2 += fmt == ORC_FMT_E4M3 ? (size_t)e * d2 : (size_t)e * d2 / 2;
+    }
+    for (int c = 0; c < h; ++c) xbuf[c] = elem(L->X, xdt, (size_t)t * h + c);
+    swiglu_row_mx(h, f, xbuf, fmt, (const uint8_t*)W1, S1, (const uint8_t*)W2, S2,
+                  xbuf + h, qbuf, qbuf + (h > f ? h : f), h1, out);
+    return;
+  }
   size_t wb = (L->precision == 0) ? 4 : (L->precision == 1 ? 2 : 1);
   if (!shared) {
     W1 += (size_t)e * h * 2 * f * wb;
     W2 += (size_t)e * f * h * wb;
   }
-  int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16;
   if (L->precision == 2) {
     for (int c = 0; c < h; ++c) fbuf[c] = (float)elem(L->X, xdt, (size_t)t * h + c);
     float sx;
     oracle_quantize_row_f32(h, fbuf, qbuf, &sx);
-    const float* s1 = shared ? L->ws1_scale : L->w1_scale + (size_t)e * 2 * f;
-    const float* s2 = shared ? L->ws2_scale : L->w2_scale + (size_t)e * h;
+    const float* s1 = shared ? (const float*)L->ws1_scale : (const float*)L->w1_scale + (size_t)e * 2 * f;
+    const float* s2 = shared ? (const float*)L->ws2_scale : (const float*)L->w2_scale + (size_t)e * h;
     swiglu_row_fp8(h, f, qbuf, (double)sx, (const uint8_t*)W1, s1, (const uint8_t*)W2, s2, h1,
                    out);
   } else {
@@ -415,8 +546,8 @@ void oracle_layer_tokens(const oracle_layer* L, const int32_t* ids, const double
   e4m3_table_init();
 #pragma omp parallel
   {
-    double* xbuf = (double*)malloc(sizeof(double) * h);
-    uint8_t* qbuf = (uint8_t*)malloc((size_t)h);
+    double* xbuf = (double*)malloc(sizeof(double) * 2 * h);
+    uint8_t* qbuf = (uint8_t*)malloc((size_t)2 * (h > f ? h : f));
     float* fbuf = (float*)malloc(sizeof(float) * h);
     double* h1 = (double*)malloc(sizeof(double) * 2 * f);
     double* fe = (double*)malloc(sizeof(double) * h);
@@ -457,8 +588,8 @@ void oracle_expert_rows(const oracle_layer* L, const int32_t* offsets, const int
   e4m3_table_init();
 #pragma omp parallel
   {
-    double* xbuf = (double*)malloc(sizeof(double) * h);
-    uint8_t* qbuf = (uint8_t*)malloc((size_t)h);
+    double* xbuf = (double*)malloc(sizeof(double) * 2 * h);
+    uint8_t* qbuf = (uint8_t*)malloc((size_t)2 * (h > f ? h : f));
     float* fbuf = (float*)malloc(sizeof(float) * h);
     double* h1 = (double*)malloc(sizeof(double) * 2 * f);
 #pragma omp for schedule(dynamic, 1)

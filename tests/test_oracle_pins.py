@@ -363,6 +363,148 @@ def test_fp8_layer_within_quantisation_error_of_exact_layer():
     assert rel.max() < 0.1 and rel.max() > 1e-4   # lossy, but only by the fp8 rounding
 
 
+# ------------------------------------------------------------------ MX (group-32, E8M0)
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # OCP FP4 e2m1, codes 0..7
+EMAX = {"e4m3": 8, "e2m1": 2}                                # exponent of the largest normal
+
+
+def _e2m1_nearest_even(v):
+    """Brute force: the e2m1 code nearest to v, ties to the even code, |v| >= 6 -> 6."""
+    out = []
+    for x in np.asarray(v, np.float64).ravel():
+        a = min(abs(x), 6.0)
+        d = [abs(a - m) for m in E2M1_MAGNITUDES]
+        best = min(d)
+        cands = [c for c in range(8) if d[c] == best]
+        c = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        out.append(c | (8 if (x < 0 or (x == 0 and math.copysign(1, x) < 0)) else 0))
+    return np.array(out, np.uint8).reshape(np.shape(v))
+
+
+def _mx_dequant(codes, scales, fmt):
+    """Independent MX dequantisation: element values from torch (e4m3) or the
+    OCP table (e2m1), times 2^(scale - 127) per group of 32 along the last axis."""
+    codes = np.asarray(codes, np.uint8)
+    if fmt == "e4m3":
+        v = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    else:
+        mag = np.array(E2M1_MAGNITUDES)[codes & 7]
+        v = np.where(codes & 8, -mag, mag)
+    sc = np.repeat(np.asarray(scales, np.int64), 32, axis=-1)
+    return np.ldexp(v, sc - 127)
+
+
+def test_e2m1_codes_are_the_ocp_table():
+    vals = [oracle.e2m1_decode(c) for c in range(16)]
+    assert vals[:8] == E2M1_MAGNITUDES
+    assert vals[8:] == [-m for m in E2M1_MAGNITUDES]
+    assert all(oracle.e2m1_encode(vals[c]) == c for c in range(16))
+    # ties go to the even code; beyond 6 saturates
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0, 7.0, 1e9]
+    assert [oracle.e2m1_encode(v) for v in ties] == [0, 2, 2, 4, 4, 6, 6, 14, 7, 7]
+
+
+def test_e2m1_encode_matches_brute_force():
+    rng = np.random.default_rng(21)
+    v = np.concatenate([rng.standard_normal(3000) * 3, rng.uniform(-8, 8, 3000),
+                        np.arange(-28, 29) / 4.0])
+    ours = np.array([oracle.e2m1_encode(x) for x in v], np.uint8)
+    assert np.array_equal(ours, _e2m1_nearest_even(v))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_mx_scale_code_is_floor_log2_minus_emax(fmt):
+    rng = np.random.default_rng(22)
+    amax = np.concatenate([np.exp(rng.uniform(-60, 60, 2000)), 2.0 ** np.arange(-20, 21)])
+    ref = np.clip(np.floor(np.log2(amax)).astype(np.int64) - EMAX[fmt] + 127, 0, 254)
+    assert [oracle.mx_scale_code(a, fmt) for a in amax] == ref.tolist()
+    assert oracle.mx_scale_code(0.0, fmt) == 0
+    assert oracle.mx_scale_code(1.0, fmt) == 127 - EMAX[fmt]
+
+
+def test_mx_quantize_e4m3_matches_torch_cast_and_error_bound():
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((40, 256)) * np.exp(rng.uniform(-8, 8, (40, 1)))
+    x[3] = 0.0
+    x[5, :32] = 1.0          # one value, scale 2^-8, element 256
+    x[6, :32] = 500.0        # scale 2^0: 500 saturates to 448
+    q, sc = oracle.mx_quantize(x, "e4m3")
+    assert sc.shape == (40, 8) and np.all(sc[3] == 0) and np.all(q[3] == 0)
+    assert sc[5, 0] == 119 and np.all(q[5, :32] == 0x78)
+    assert sc[6, 0] == 127 and np.all(q[6, :32] == 0x7E)
+    # element codes: the torch e4m3fn cast of the scaled, clamped values
+    scaled = np.ldexp(x, 127 - np.repeat(sc.astype(np.int64), 32, axis=1))
+    ref = torch.from_numpy(np.clip(scaled, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    # round trip: relative error at most 2^-4 where the scaled value is a normal e4m3
+    dq = _mx_dequant(q, sc, "e4m3")
+    normal = (np.abs(scaled) >= 2.0 ** -6) & (np.abs(scaled) <= 448)
+    assert np.all(np.abs(dq - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
+
+
+def test_mx_quantize_e2m1_matches_brute_force():
+    rng = np.random.default_rng(24)
+    x = rng.standard_normal((12, 128)) * np.exp(rng.uniform(-4, 4, (12, 1)))
+    x[2] = 0.0
+    q, sc = oracle.mx_quantize(x, "e2m1")
+    amax = np.abs(x.reshape(12, 4, 32)).max(-1)
+    ref_sc = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1))) - 2 + 127, 0)
+    assert np.array_equal(sc, ref_sc.astype(np.uint8))
+    scaled = np.ldexp(x, 127 - np.repeat(sc.astype(np.int64), 32, axis=1))
+    assert np.array_equal(q, _e2m1_nearest_even(scaled))
+
+
+def _mx_weights(rng, E, K, N, fmt):
+    """Random MX weight codes [E,K,N] (e2m1: packed [E,K,N/2], element 2i low
+    nibble) and E8M0 scales [E,K/32,N]."""
+    if fmt == "e4m3":
+        codes = rng.integers(0, 0x7E, size=(E, K, N)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(E, K, N)).astype(np.uint8) << 7)
+        packed = codes
+    else:
+        codes = rng.integers(0, 16, size=(E, K, N)).astype(np.uint8)
+        packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(112, 124, size=(E, K // 32, N)).astype(np.uint8)
+    # dequantised: scale of W[e, k, n] is scales[e, k // 32, n]
+    deq = _mx_dequant(np.swapaxes(codes, 1, 2), np.swapaxes(scales, 1, 2), fmt)
+    return packed, scales, np.swapaxes(deq, 1, 2)
+
+
+@pytest.mark.parametrize("prec,fmt", [("mxfp8", "e4m3"), ("mxfp4", "e2m1")])
+def test_mx_layer_is_the_dense_swiglu_of_dequantised_operands(prec, fmt):
+    """Each routed and the shared expert: Q_MX(x) -> DQ . DQ(W1) -> SwiGLU ->
+    Q_MX -> DQ . DQ(W2), rebuilt here with numpy matmuls and the independent
+    dequantisation above (the quantisation steps themselves are pinned by
+    the tests before)."""
+    rng = np.random.default_rng(25)
+    T, h, f, E, k = 5, 64, 64, 3, 2
+    X = rng.standard_normal((T, h))
+    Xb = _bf16(X)
+    W1, s1, dq1 = _mx_weights(rng, E, h, 2 * f, fmt)
+    W2, s2, dq2 = _mx_weights(rng, E, f, h, fmt)
+    Ws1, ss1, dqs1 = _mx_weights(rng, 1, h, 2 * f, fmt)
+    Ws2, ss2, dqs2 = _mx_weights(rng, 1, f, h, fmt)
+    ids = np.array([[t % E, (t + 1) % E] for t in range(T)], np.int32)
+    G = rng.uniform(0.1, 1.0, (T, k))
+    L = oracle.Layer(prec, bits(Xb), W1, W2, w1_scale=s1, w2_scale=s2, Ws1=Ws1[0], Ws2=Ws2[0],
+                     ws1_scale=ss1[0], ws2_scale=ss2[0], k=k)
+    y = L.tokens(ids, G)
+    xq, xs = oracle.mx_quantize(Xb.double().numpy(), fmt)
+    xd = _mx_dequant(xq, xs, fmt)
+
+    def expert(x, d1, d2):
+        hh = x @ d1
+        u = hh[:, :f] / (1.0 + np.exp(-hh[:, :f])) * hh[:, f:]
+        uq, us = oracle.mx_quantize(u, fmt)
+        return _mx_dequant(uq, us, fmt) @ d2
+
+    for t in range(T):
+        ref = expert(xd[t:t + 1], dqs1[0], dqs2[0])
+        for j in range(k):
+            ref = ref + G[t, j] * expert(xd[t:t + 1], dq1[ids[t, j]], dq2[ids[t, j]])
+        np.testing.assert_allclose(y[t:t + 1], ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+
 # ------------------------------------------------------------------ shapes
 def test_workload_shapes_match_the_pages_arithmetic():
     v4 = synth.WORKLOADS["v4pro_bf16"]
@@ -381,13 +523,28 @@ def test_zipf_fixture_gives_skewed_load():
 
 
 # ------------------------------------------------------------------ planted mistake
-def test_pins_catch_a_planted_mistake(tmp_path):
-    """Build a copy of the oracle with the SwiGLU halves swapped (a plausible
-    slip) and check that the dense-SwiGLU pin rejects it."""
+PLANTED = {
+    # SwiGLU halves swapped in the bf16/fp32 expert
+    "swiglu": ("h1[n] = silu(h1[n]) * h1[f + n];", "h1[n] = silu(h1[f + n]) * h1[n];",
+               lambda: test_single_expert_top1_is_dense_swiglu_plus_shared()),
+    # e2m1 weight pairs read high nibble first
+    "nibble": ("(W[i / 2] >> (4 * (i & 1)))", "(W[i / 2] >> (4 * (1 - (i & 1))))",
+               lambda: test_mx_layer_is_the_dense_swiglu_of_dequantised_operands("mxfp4", "e2m1")),
+    # MX weight scale taken from the next group
+    "mxscale": ("S[(size_t)(c / 32) * N + n]", "S[(size_t)((c + 32) / 32 % (c / 32 + 1)) * N + n]",
+                lambda: test_mx_layer_is_the_dense_swiglu_of_dequantised_operands("mxfp8", "e4m3")),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PLANTED))
+def test_pins_catch_a_planted_mistake(tmp_path, name):
+    """Build a copy of the oracle with a plausible slip planted and check that
+    the pin for that part rejects it."""
     import ctypes
     import subprocess
     src = open(os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")).read()
-    bad = src.replace("h1[n] = silu(h1[n]) * h1[f + n];", "h1[n] = silu(h1[f + n]) * h1[n];", 1)
+    good, slip, pin = PLANTED[name]
+    bad = src.replace(good, slip, 1)
     assert bad != src
     c = tmp_path / "bad.c"
     c.write_text(bad)
@@ -399,7 +556,7 @@ def test_pins_catch_a_planted_mistake(tmp_path):
         real = oracle._LIB_PATH
         oracle._LIB_PATH = str(so)
         with pytest.raises(AssertionError):
-            test_single_expert_top1_is_dense_swiglu_plus_shared()
+            pin()
     finally:
         oracle._LIB_PATH = real
         oracle._lib = saved
