@@ -46,9 +46,20 @@
  *       MOE_PREC_FP8:  X, Wg, Yp, Ys, Y bf16; W1/W2/Ws1/Ws2 OCP e4m3fn codes
  *                      with fp32 per-output-channel scales; Xp, Xq e4m3fn
  *                      codes with fp32 per-row scales.
+ *       MOE_PREC_MXFP8: the mega_moe page's MXFP mode (MX block quantisation,
+ *                      groups of 32 along the contraction dimension, one
+ *                      E8M0 scale byte per group, value = e4m3fn(code) *
+ *                      2^(scale - 127)).  X, Wg, Yp, Ys, Y bf16; W* e4m3fn
+ *                      codes with E8M0 scales [.., K/32, N]; Xp, Xq e4m3fn
+ *                      codes with E8M0 scales [rows, hidden/32].  A group's
+ *                      scale exponent is floor(log2(max|v|)) - 8 (0 for an
+ *                      all-zero group) and its elements v / 2^exponent
+ *                      rounded to nearest even, saturating at 448 (the OCP
+ *                      MX rule; the page names the group size and types).
  *   - Shape limits: 1 <= T; 1 <= topk <= min(16, experts) (the mega_moe
  *     constraint on top-k); experts <= 512; hidden a multiple of 128 and
- *     inter a multiple of 64 (the kernels' tile granularity).
+ *     inter a multiple of 64 (the kernels' tile granularity); for FP8 and
+ *     MXFP8 hidden a multiple of 256 and inter a multiple of 128.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -71,7 +82,12 @@ typedef enum {
   MOE_ERR_DEVICE_DATA = -5  /* device data broke the contract (bad expert id) */
 } moe_status;
 
-typedef enum { MOE_PREC_F32 = 0, MOE_PREC_BF16 = 1, MOE_PREC_FP8 = 2 } moe_precision;
+typedef enum {
+  MOE_PREC_F32 = 0,
+  MOE_PREC_BF16 = 1,
+  MOE_PREC_FP8 = 2,
+  MOE_PREC_MXFP8 = 3
+} moe_precision;
 
 typedef enum {
   MOE_SCORE_SIGMOID = 0,      /* a = 1 / (1 + exp(-l)) */
@@ -108,17 +124,22 @@ typedef struct {
 
 /* Expert weights.  W1 [E, hidden, 2*inter], W2 [E, inter, hidden]; shared
  * Ws1 [hidden, 2*inter], Ws2 [inter, hidden] (NULL without a shared expert).
- * Scales (MOE_PREC_FP8 only, else ignored): w1_scale [E, 2*inter], w2_scale
- * [E, hidden], ws1_scale [2*inter], ws2_scale [hidden]. */
+ * Scales, ignored for F32 and BF16:
+ *   MOE_PREC_FP8: fp32 per output channel: w1_scale [E, 2*inter], w2_scale
+ *     [E, hidden], ws1_scale [2*inter], ws2_scale [hidden].
+ *   MOE_PREC_MXFP8: E8M0 bytes per group of 32 rows (K) and column:
+ *     w1_scale [E, hidden/32, 2*inter], w2_scale [E, inter/32, hidden],
+ *     ws1_scale [hidden/32, 2*inter], ws2_scale [inter/32, hidden]; the
+ *     scale of W1[e, k, n] is w1_scale[e, k/32, n]. */
 typedef struct {
   const void* W1;
-  const float* w1_scale;
+  const void* w1_scale;
   const void* W2;
-  const float* w2_scale;
+  const void* w2_scale;
   const void* Ws1;
-  const float* ws1_scale;
+  const void* ws1_scale;
   const void* Ws2;
-  const float* ws2_scale;
+  const void* ws2_scale;
 } moe_expert_weights;
 
 /* Bytes of device workspace that moe_forward needs for this shape (every
@@ -146,24 +167,30 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
  *   out: Xp[dst_row[i]] = X[i / topk].
  *   MOE_PREC_FP8: X is bf16 and is quantised per token first (scale =
  *   max|x| / 448, codes = round-to-nearest-even of x / scale, saturating);
- *   Xq [T, hidden] e4m3 and x_scale [T] receive that, Xp holds codes and
- *   xp_scale [T*topk] the scale of each row.  Otherwise xp_scale, Xq and
- *   x_scale are ignored.
+ *   Xq [T, hidden] e4m3 and x_scale [T] fp32 receive that, Xp holds codes
+ *   and xp_scale [T*topk] fp32 the scale of each row.
+ *   MOE_PREC_MXFP8: X is bf16 and is MX-quantised per token (groups of 32
+ *   along hidden); Xq [T, hidden] e4m3 and x_scale [T, hidden/32] E8M0 bytes
+ *   receive that, Xp holds codes and xp_scale [T*topk, hidden/32] the scales
+ *   of each row.
+ *   Otherwise xp_scale, Xq and x_scale are ignored.
  * Expert ids outside [0, E) are skipped (dst_row = -1) and flagged. */
 int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,
                 int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
-                float* xp_scale, void* Xq, float* x_scale, void* workspace,
+                void* xp_scale, void* Xq, void* x_scale, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
 /* Step 4: grouped Linear1 -> SwiGLU -> Linear2 over the expert blocks given
  * by offsets [E+1] (rows offsets[e] .. offsets[e+1]-1 of Xp belong to expert
  * e), fp32 accumulation.  Yp [T*topk, hidden] out (fp32 for F32, else bf16).
  * With a shared expert: Xs [T, hidden] is its input (X, or Xq with
- * xs_scale for FP8) and Ys [T, hidden] its output; else both may be NULL.
- * The SwiGLU output is held in the workspace in the compute type (fp32 for
- * FP8, before its per-row e4m3 requantisation). */
-int moe_expert_ffn(const moe_shape* shape, const void* Xp, const float* xp_scale,
-                   const int32_t* offsets, const void* Xs, const float* xs_scale,
+ * xs_scale for FP8 and MXFP8) and Ys [T, hidden] its output; else both may
+ * be NULL.  Scales have the types moe_permute gives them.  The SwiGLU output
+ * is held in the workspace: bf16 (BF16), fp32 before its per-row e4m3
+ * requantisation (FP8), or MX-quantised in groups of 32 along inter as it
+ * is produced (MXFP8). */
+int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
+                   const int32_t* offsets, const void* Xs, const void* xs_scale,
                    const moe_expert_weights* weights, void* Yp, void* Ys, void* workspace,
                    size_t workspace_bytes, hipStream_t stream);
 

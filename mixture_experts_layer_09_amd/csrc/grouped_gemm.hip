@@ -65,12 +65,14 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 struct GemmArgs {
   const void* A;         // routed input rows [M, K]
   const void* A_sh;      // shared-expert input rows [T, K] (or null)
-  const float* a_scale;  // FP8: per routed row
-  const float* a_scale_sh;
+  const void* a_scale;  // FP8: fp32 per routed row; MX: E8M0 [rows, K/32]
+  const void* a_scale_sh;
   const void* W;         // [E, K, Nw]
   const void* W_sh;      // [K, Nw]
-  const float* w_scale;  // FP8: [E, Nw]
-  const float* w_scale_sh;
+  const void* w_scale;  // FP8: fp32 [E, Nw]; MX: E8M0 [E, K/32, Nw]
+  const void* w_scale_sh;
+  void* out_scale;      // MX SwiGLU: E8M0 scales [rows, Nout/32] of the output codes
+  void* out_scale_sh;
   void* out;             // routed rows [M, Nout]
   void* out_sh;          // shared rows [T, Nout]
   const int32_t* offsets;
@@ -224,16 +226,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
     row_end = g.offsets[seg + 1];
     Abase = static_cast<const char*>(g.A);
     Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * ESZ;
-    wsc = g.w_scale ? g.w_scale + static_cast<size_t>(seg) * g.Nw : nullptr;
-    asc = g.a_scale;
+    wsc = g.w_scale ? static_cast<const float*>(g.w_scale) + static_cast<size_t>(seg) * g.Nw
+                    : nullptr;
+    asc = static_cast<const float*>(g.a_scale);
     obase = static_cast<char*>(g.out);
   } else {
     row0 = mtile * BM;
     row_end = g.T;
     Abase = static_cast<const char*>(g.A_sh);
     Wbase = static_cast<const char*>(g.W_sh);
-    wsc = g.w_scale_sh;
-    asc = g.a_scale_sh;
+    wsc = static_cast<const float*>(g.w_scale_sh);
+    asc = static_cast<const float*>(g.a_scale_sh);
     obase = static_cast<char*>(g.out_sh);
   }
   const int rows_valid = min(BM, row_end - row0);
@@ -428,6 +431,16 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* ld
                : "memory");
 }
 
+// As dma16 with 4 bytes per lane (LDS lds_dst + 4 * lane).
+__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, char* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
 // A pointer the compiler may not prove wave-uniform, moved to scalar registers.
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint64_t v = reinterpret_cast<uintptr_t>(p);
@@ -538,12 +551,18 @@ struct DmaOps<MOE_PREC_FP8, BN> {
   __device__ static int swz_b(int r) {
     return BN >= 256 ? (r & 7) + 8 * ((r >> 5) & 1) : ((r & 7) >> 1) + 4 * ((r >> 5) & 1);
   }
+  // K placement of the 16x16x128 8-bit MFMA: byte j of lane group g is K
+  // index (j < 16 ? 0 : 64) + 16 g + j % 16, and the E8M0 scale of lane group
+  // s covers K 32 s .. 32 s + 31 (read off the instruction on the GPU with
+  // one-hot operands).  Both fragments follow it, so a lane group's scale is
+  // the scale of the K-group it holds.
+  __device__ static int k_of(int g, int half) { return (half ? 64 : 0) + 16 * g; }
   template <int B_ROW>
   __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
     const int g = lane >> 4, p = lane & 15;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const int r = 32 * g + 8 * h + (p >> 1);
+      const int r = k_of(g, h >> 1) + 8 * (h & 1) + (p >> 1);
       const int col = col0 + (p & 1) * 8;  // byte
       o[h] = r * B_ROW + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
     }
@@ -557,9 +576,9 @@ struct DmaOps<MOE_PREC_FP8, BN> {
   }
   template <int A_ROW>
   __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
-    const int c = (lane >> 4) * 2;
-    o[0] = r * A_ROW + ((c ^ swz_a(r)) << 4);
-    o[1] = r * A_ROW + (((c + 1) ^ swz_a(r)) << 4);
+    const int g = lane >> 4;  // 16-byte chunks k_of(g, 0) / 16 and k_of(g, 1) / 16
+    o[0] = r * A_ROW + (((k_of(g, 0) >> 4) ^ swz_a(r)) << 4);
+    o[1] = r * A_ROW + (((k_of(g, 1) >> 4) ^ swz_a(r)) << 4);
   }
   __device__ static frag load_a(const char* st, const int (&o)[2]) {
     const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + o[0]);
@@ -570,6 +589,26 @@ struct DmaOps<MOE_PREC_FP8, BN> {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
 };
+
+// MXFP8 shares the e4m3 operand layout; its MFMA takes each lane's E8M0
+// scale byte (the lane's 32 K-values are one MX group) for A and for B.
+template <int BN>
+struct DmaOps<MOE_PREC_MXFP8, BN> : DmaOps<MOE_PREC_FP8, BN> {};
+
+__device__ __forceinline__ f32x4_t mma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// E8M0 code of the MX group scale for an e4m3 group whose largest magnitude
+// is amax (fp32): floor(log2 amax) - 8, i.e. the biased exponent minus 8,
+// clamped at 0 (all-zero and tiny groups); and 2^(127 - code) as a float.
+__device__ __forceinline__ uint32_t mx_e4m3_code(float amax) {
+  const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
+  return static_cast<uint32_t>(e > 8 ? e - 8 : 0);
+}
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
 
 // Two waves per SIMD for bf16 (two 4-wave blocks that cover each other's
 // stage barriers); e4m3 keeps one block of deeper stages per CU.
@@ -585,7 +624,13 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int B_ROW = BN * ESZ;         // bytes
   constexpr int A_BYTES = BM * A_ROW;
   constexpr int B_BYTES = BK * B_ROW;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr bool MX = PREC == MOE_PREC_MXFP8;
+  // MX: each stage also holds the E8M0 scales of its 4 K-groups: A [BM][4]
+  // (one dword per row) and B [4][BN] (one byte per group row and column)
+  constexpr int AS_OFF = A_BYTES + B_BYTES;
+  constexpr int BS_OFF = AS_OFF + (MX ? BM * 4 : 0);
+  constexpr int STAGE = BS_OFF + (MX ? 4 * BN : 0);
+  constexpr int AS_INSTS = MX ? BM / 64 : 0;  // dword DMA: 64 rows per instruction
   constexpr int A_INSTS = (A_BYTES + 1023) / 1024;
   constexpr int B_INSTS = B_BYTES / 1024;
   constexpr int A_OPS = (A_INSTS + NW - 1) / NW;  // DMA instructions per wave per stage
@@ -599,6 +644,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   static_assert(B_INSTS % NW == 0, "B stage must split evenly over the waves");
   static_assert(A_BYTES % 1024 == 0 || A_INSTS == 1, "A stage granularity");
   static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
+  static_assert(!MX || (BN == 256 && BM % 64 == 0 && NW > AS_INSTS),
+                "MX scale DMA: one 1 KB instruction for B, 64-row ones for A");
+  static_assert(!MX || !SWIGLU || (NTW / 2) % 2 == 0,
+                "MX SwiGLU epilogue: whole 32-column groups per wave");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
@@ -654,17 +703,28 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     row_end = g.offsets[seg + 1];
     Abase = static_cast<const char*>(g.A);
     Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.K * g.Nw * ESZ;
-    wsc = g.w_scale ? g.w_scale + static_cast<size_t>(seg) * g.Nw : nullptr;
-    asc = g.a_scale;
+    wsc = g.w_scale ? static_cast<const float*>(g.w_scale) + static_cast<size_t>(seg) * g.Nw
+                    : nullptr;
+    asc = static_cast<const float*>(g.a_scale);
     obase = static_cast<char*>(g.out);
   } else {
     row0 = mtile * BM;
     row_end = g.T;
     Abase = static_cast<const char*>(g.A_sh);
     Wbase = static_cast<const char*>(g.W_sh);
-    wsc = g.w_scale_sh;
-    asc = g.a_scale_sh;
+    wsc = static_cast<const float*>(g.w_scale_sh);
+    asc = static_cast<const float*>(g.a_scale_sh);
     obase = static_cast<char*>(g.out_sh);
+  }
+  // MX scale arrays of this segment (E8M0 bytes)
+  const uint8_t* asc8 = nullptr;
+  const uint8_t* wsc8 = nullptr;
+  uint8_t* osc8 = nullptr;
+  if constexpr (MX) {
+    asc8 = static_cast<const uint8_t*>(shared ? g.a_scale_sh : g.a_scale);
+    wsc8 = static_cast<const uint8_t*>(shared ? g.w_scale_sh : g.w_scale) +
+           (shared ? 0 : static_cast<size_t>(seg) * (g.K / 32) * g.Nw);
+    osc8 = static_cast<uint8_t*>(shared ? g.out_scale_sh : g.out_scale);
   }
   const int rows_valid = min(BM, row_end - row0);
   // wave-uniform: keep it scalar so the skip below is a scalar branch
@@ -708,7 +768,25 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
           ? A_OPS
           : __builtin_amdgcn_readfirstlane(
                 max(0, min(A_OPS, ((rows_valid + A_RPI - 1) / A_RPI) - wave * A_OPS)));
-  const int ops_w = a_live + B_OPS;
+  // MX scale DMA: waves 0 .. AS_INSTS-1 fetch 64 rows' A scale dwords each,
+  // wave AS_INSTS the B scales (4 group rows of the tile's BN columns)
+  const size_t sc_ld = static_cast<size_t>(g.K / 32);  // scale bytes per A row
+  const char* as_base = nullptr;
+  const char* bs_base = nullptr;
+  uint32_t as_voff = 0, bs_voff = 0;
+  int ops_sc = 0;
+  if constexpr (MX) {
+    as_base = uniform_ptr(reinterpret_cast<const char*>(asc8) + static_cast<size_t>(row0) * sc_ld);
+    as_voff = static_cast<uint32_t>(min(wave * 64 + lane, row_end - 1 - row0)) *
+              static_cast<uint32_t>(sc_ld);
+    bs_base = uniform_ptr(reinterpret_cast<const char*>(wsc8) +
+                          static_cast<size_t>(nt) * (SWIGLU ? BN / 2 : BN));
+    const int nl = (lane % 16) * 16;
+    const int col = (SWIGLU && nl >= BN / 2) ? g.f + (nl - BN / 2) : nl;
+    bs_voff = static_cast<uint32_t>(lane / 16) * static_cast<uint32_t>(g.Nw) + col;
+    ops_sc = (wave <= AS_INSTS) ? 1 : 0;
+  }
+  const int ops_w = a_live + B_OPS + ops_sc;
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
 #pragma unroll
@@ -720,6 +798,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     for (int q = 0; q < B_OPS; ++q) {
       const int blk = wave * B_OPS + q;
       dma16(b_base + static_cast<size_t>(kt) * BK * w_ld, b_voff[q], st + A_BYTES + blk * 1024);
+    }
+    if constexpr (MX) {
+      if (wave < AS_INSTS)
+        dma4(as_base + static_cast<size_t>(kt) * 4, as_voff, st + AS_OFF + wave * 256);
+      else if (wave == AS_INSTS)
+        dma16(bs_base + static_cast<size_t>(kt) * 4 * g.Nw, bs_voff, st + BS_OFF);
     }
   };
 
@@ -747,6 +831,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   int a_off[MT][2];
 #pragma unroll
   for (int i = 0; i < MT; ++i) O::template a_offsets<A_ROW>(wm * WM + i * 16 + (lane & 15), lane, a_off[i]);
+  // MX: LDS byte of this lane's scale for A row tile i / B column tile j
+  int as_off[MT], bs_off[NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) as_off[i] = AS_OFF + (wm * WM + i * 16 + (lane & 15)) * 4 + (lane >> 4);
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) bs_off[j] = BS_OFF + (lane >> 4) * BN + bcol(j) + (lane & 15);
 
   // A wave with any live row multiplies all of its MT row tiles (rows past the
   // segment only feed accumulators that are never stored); a wave with none
@@ -761,10 +851,22 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     typename O::frag af[MT];
 #pragma unroll
     for (int i = 0; i < MT; ++i) af[i] = O::load_a(st, a_off[i]);
+    if constexpr (MX) {
+      int sa[MT], sb[NTW];
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) sa[i] = *reinterpret_cast<const uint8_t*>(st + as_off[i]);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < NTW; ++j) sb[j] = *reinterpret_cast<const uint8_t*>(st + bs_off[j]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = mma_mx(af[i], bfr[j], acc[i][j], sa[i], sb[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(af[i], bfr[j], acc[i][j]);
+    }
   };
 
   // The K loop is unrolled by STAGES so that every stage slot is a constant
@@ -791,6 +893,38 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 
   // ------------------------------------------------ epilogue
   const int col_in = lane & 15;
+  if constexpr (MX && SWIGLU) {
+    // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
+    // gate tiles (j, j+1) of one row, i.e. 2 values in each of the 16 lanes
+    // that hold the row; their amax goes round those lanes by xor shuffles.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) continue;  // wave-uniform
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+#pragma unroll
+        for (int j = 0; j < NTW / 2; j += 2) {
+          const float u0 = silu(acc[i][j][v]) * acc[i][j + NTW / 2][v];
+          const float u1 = silu(acc[i][j + 1][v]) * acc[i][j + 1 + NTW / 2][v];
+          float amax = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          const uint32_t code = mx_e4m3_code(amax);
+          const float inv = mx_inv_scale(code);
+          if (row < row_end) {
+            const int c0 = nt * (BN / 2) + bcol(j);  // first column of the group
+            uint8_t* orow = reinterpret_cast<uint8_t*>(obase) + static_cast<size_t>(row) * g.Nout;
+            orow[c0 + col_in] = static_cast<uint8_t>(f32_to_e4m3(u0 * inv));
+            orow[c0 + 16 + col_in] = static_cast<uint8_t>(f32_to_e4m3(u1 * inv));
+            if (col_in == 0)
+              osc8[static_cast<size_t>(row) * (g.Nout / 32) + c0 / 32] = static_cast<uint8_t>(code);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     if (i >= mt_live) continue;
@@ -798,7 +932,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
       if (row >= row_end) continue;
-      const float rs = (PREC == MOE_PREC_FP8) ? asc[row] : 1.0f;
+      const float rs = (PREC == MOE_PREC_FP8) ? asc[row] : 1.0f;  // MX: scales are in the MFMA
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NTW / 2; ++j) {
@@ -961,7 +1095,9 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ub_m = (rows + BM - 1) / BM + (a.E < rows ? a.E : rows) + (T_sh + BM - 1) / BM;
-  const size_t arow_bytes = static_cast<size_t>(a.f) * (PREC == MOE_PREC_FP8 ? 1 : 2);
+  constexpr bool MX = PREC == MOE_PREC_MXFP8;
+  constexpr bool Q8 = PREC == MOE_PREC_FP8 || MX;  // e4m3 activation codes into Linear2
+  const size_t arow_bytes = static_cast<size_t>(a.f) * (Q8 ? 1 : 2);
 
   GemmArgs g1{};
   g1.A = a.Xp;
@@ -972,9 +1108,16 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   g1.W_sh = a.w.Ws1;
   g1.w_scale = a.w.w1_scale;
   g1.w_scale_sh = a.w.ws1_scale;
-  g1.out = a.A;
-  g1.out_sh = static_cast<char*>(a.A) +
-              static_cast<size_t>(rows) * a.f * (PREC == MOE_PREC_FP8 ? 4 : 2);
+  if (MX) {  // the SwiGLU output is MX-quantised by the Linear1 epilogue
+    g1.out = a.Aq;
+    g1.out_sh = static_cast<char*>(a.Aq) + static_cast<size_t>(rows) * a.f;
+    g1.out_scale = a.a_scale;
+    g1.out_scale_sh = static_cast<char*>(a.a_scale) + static_cast<size_t>(rows) * (a.f / 32);
+  } else {
+    g1.out = a.A;
+    g1.out_sh = static_cast<char*>(a.A) +
+                static_cast<size_t>(rows) * a.f * (PREC == MOE_PREC_FP8 ? 4 : 2);
+  }
   g1.offsets = a.offsets;
   g1.tile_off = a.tile_off;
   g1.E = a.E;
@@ -988,21 +1131,24 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
 
   const void* A2 = a.A;
-  const float* as2 = nullptr;
+  const char* as2 = nullptr;
   if (PREC == MOE_PREC_FP8) {
     const int arows = rows + T_sh;
     hipLaunchKernelGGL(requant_kernel, dim3(arows), dim3(256), 0, stream,
-                       static_cast<const float*>(a.A), a.f, static_cast<uint8_t*>(a.Aq), a.a_scale);
+                       static_cast<const float*>(a.A), a.f, static_cast<uint8_t*>(a.Aq),
+                       static_cast<float*>(a.a_scale));
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+  }
+  if (Q8) {
     A2 = a.Aq;
-    as2 = a.a_scale;
+    as2 = static_cast<const char*>(a.a_scale);
   }
   GemmArgs g2{};
   g2.A = A2;
   g2.A_sh = static_cast<const char*>(A2) + static_cast<size_t>(rows) * arow_bytes;
   g2.a_scale = as2;
-  g2.a_scale_sh = as2 ? as2 + rows : nullptr;
+  g2.a_scale_sh = as2 ? as2 + static_cast<size_t>(rows) * (MX ? a.f / 32 : 4) : nullptr;
   g2.W = a.w.W2;
   g2.W_sh = a.w.Ws2;
   g2.w_scale = a.w.w2_scale;
@@ -1066,6 +1212,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   if (a.precision == MOE_PREC_BF16) return dispatch_ffn<MOE_PREC_BF16>(a, stream);
+  // MX: the 3-stage DMA pipeline at every batch size (the 16-row decode
+  // kernel has no per-group scales)
+  if (a.precision == MOE_PREC_MXFP8) return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 

@@ -17,10 +17,12 @@ int check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->topk > s->experts || s->topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
-  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_FP8) return MOE_ERR_INVALID_ARG;
+  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
   if (s->experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if (s->inter % (s->precision == MOE_PREC_FP8 ? 128 : 64) != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->inter % (s->precision >= MOE_PREC_FP8 ? 128 : 64) != 0) return MOE_ERR_UNSUPPORTED;
+  // e4m3 grouped GEMMs use 256-column n-tiles for Linear2
+  if (s->precision >= MOE_PREC_FP8 && s->hidden % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // row and element counts must fit the kernels' 32-bit row indices
   const long long rows = static_cast<long long>(s->tokens) * (s->topk + 1);
   if (rows > (1LL << 30)) return MOE_ERR_UNSUPPORTED;
@@ -43,10 +45,11 @@ T* at(void* ws, size_t off) {
 
 int check_weights(const moe_shape* s, const moe_expert_weights* w) {
   if (!w || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
-  if (s->precision == MOE_PREC_FP8 && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  const bool scaled = s->precision == MOE_PREC_FP8 || s->precision == MOE_PREC_MXFP8;
+  if (scaled && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
   if (s->has_shared) {
     if (!w->Ws1 || !w->Ws2) return MOE_ERR_INVALID_ARG;
-    if (s->precision == MOE_PREC_FP8 && (!w->ws1_scale || !w->ws2_scale))
+    if (scaled && (!w->ws1_scale || !w->ws2_scale))
       return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
@@ -91,7 +94,7 @@ RouteArgs route_args(const moe_shape* s, const moe_route_opts* o, const void* X,
 
 PermuteArgs permute_args(const moe_shape* s, const int32_t* ids, const void* X, int32_t* counts,
                          int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
-                         float* xp_scale, void* Xq, float* x_scale, void* ws) {
+                         void* xp_scale, void* Xq, void* x_scale, void* ws) {
   Layout L = make_layout(*s);
   PermuteArgs a{};
   a.T = s->tokens;
@@ -116,8 +119,8 @@ PermuteArgs permute_args(const moe_shape* s, const int32_t* ids, const void* X, 
   return a;
 }
 
-FfnArgs ffn_args(const moe_shape* s, const void* Xp, const float* xp_scale, const int32_t* offsets,
-                 const void* Xs, const float* xs_scale, const moe_expert_weights* w, void* Yp,
+FfnArgs ffn_args(const moe_shape* s, const void* Xp, const void* xp_scale, const int32_t* offsets,
+                 const void* Xs, const void* xs_scale, const moe_expert_weights* w, void* Yp,
                  void* Ys, void* ws) {
   Layout L = make_layout(*s);
   FfnArgs a{};
@@ -138,7 +141,7 @@ FfnArgs ffn_args(const moe_shape* s, const void* Xp, const float* xp_scale, cons
   a.Ys = Ys;
   a.A = at<void>(ws, L.A);
   a.Aq = at<void>(ws, L.Aq);
-  a.a_scale = at<float>(ws, L.a_scale);
+  a.a_scale = at<void>(ws, L.a_scale);
   a.tile_off = at<int32_t>(ws, L.tile_off);
   return a;
 }
@@ -168,13 +171,13 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
 
 int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,
                 int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
-                float* xp_scale, void* Xq, float* x_scale, void* workspace,
+                void* xp_scale, void* Xq, void* x_scale, void* workspace,
                 size_t workspace_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!expert_ids || !X || !counts || !offsets || !dst_row || !src_tok || !Xp)
     return MOE_ERR_INVALID_ARG;
-  if (shape->precision == MOE_PREC_FP8 && (!xp_scale || !Xq || !x_scale))
+  if (shape->precision >= MOE_PREC_FP8 && (!xp_scale || !Xq || !x_scale))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   PermuteArgs a = permute_args(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp,
@@ -184,18 +187,18 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
   return hip_status(e);
 }
 
-int moe_expert_ffn(const moe_shape* shape, const void* Xp, const float* xp_scale,
-                   const int32_t* offsets, const void* Xs, const float* xs_scale,
+int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
+                   const int32_t* offsets, const void* Xs, const void* xs_scale,
                    const moe_expert_weights* weights, void* Yp, void* Ys, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if ((st = check_weights(shape, weights)) != MOE_OK) return st;
   if (!Xp || !offsets || !Yp) return MOE_ERR_INVALID_ARG;
-  if (shape->precision == MOE_PREC_FP8 && !xp_scale) return MOE_ERR_INVALID_ARG;
+  if (shape->precision >= MOE_PREC_FP8 && !xp_scale) return MOE_ERR_INVALID_ARG;
   if (shape->has_shared) {
     if (!Xs || !Ys) return MOE_ERR_INVALID_ARG;
-    if (shape->precision == MOE_PREC_FP8 && !xs_scale) return MOE_ERR_INVALID_ARG;
+    if (shape->precision >= MOE_PREC_FP8 && !xs_scale) return MOE_ERR_INVALID_ARG;
   }
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   FfnArgs a = ffn_args(shape, Xp, xp_scale, offsets, Xs, xs_scale, weights, Yp, Ys, workspace);
@@ -235,7 +238,7 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   const Layout L = make_layout(*shape);
   void* ws = workspace;
-  const bool fp8 = shape->precision == MOE_PREC_FP8;
+  const bool fp8 = shape->precision >= MOE_PREC_FP8;  // quantised activations
   int32_t* flag = at<int32_t>(ws, L.flag);
   hipError_t e = launch_clear_flag(flag, stream);
   if (e == hipSuccess && opts) {
@@ -246,15 +249,15 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
     PermuteArgs p = permute_args(shape, expert_ids, X, at<int32_t>(ws, L.counts),
                                  at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.dst_row),
                                  at<int32_t>(ws, L.src_tok), at<void>(ws, L.Xp),
-                                 fp8 ? at<float>(ws, L.xp_scale) : nullptr,
+                                 fp8 ? at<void>(ws, L.xp_scale) : nullptr,
                                  fp8 ? at<void>(ws, L.Xq) : nullptr,
-                                 fp8 ? at<float>(ws, L.x_scale) : nullptr, ws);
+                                 fp8 ? at<void>(ws, L.x_scale) : nullptr, ws);
     e = launch_permute(p, stream);
   }
   if (e == hipSuccess) {
-    FfnArgs f = ffn_args(shape, at<void>(ws, L.Xp), fp8 ? at<float>(ws, L.xp_scale) : nullptr,
+    FfnArgs f = ffn_args(shape, at<void>(ws, L.Xp), fp8 ? at<void>(ws, L.xp_scale) : nullptr,
                          at<int32_t>(ws, L.offsets), fp8 ? at<void>(ws, L.Xq) : X,
-                         fp8 ? at<float>(ws, L.x_scale) : nullptr, weights, at<void>(ws, L.Yp),
+                         fp8 ? at<void>(ws, L.x_scale) : nullptr, weights, at<void>(ws, L.Yp),
                          shape->has_shared ? at<void>(ws, L.Ys) : nullptr, ws);
     e = launch_expert_ffn(f, stream);
   }

@@ -75,6 +75,11 @@ inline size_t act_bytes(int precision) { return precision == MOE_PREC_F32 ? 4 : 
 inline size_t xp_bytes(int precision) {
   return precision == MOE_PREC_F32 ? 4 : (precision == MOE_PREC_BF16 ? 2 : 1);
 }
+inline bool is_mx(int precision) { return precision == MOE_PREC_MXFP8; }
+// bytes of the activation scales of one row of `n` elements
+inline size_t row_scale_bytes(int precision, size_t n) {
+  return is_mx(precision) ? n / 32 : (precision == MOE_PREC_FP8 ? 4 : 0);
+}
 
 // Bytes of split-K partial gate logits the router may use (0 if none).
 size_t route_partial_bytes(int T, int h, int E);
@@ -88,8 +93,8 @@ struct Layout {
   size_t tile_off;    // [E+2] int32 m-tile prefix of the grouped GEMM
   size_t counts, offsets, dst_row, src_tok;  // forward-internal dispatch results
   size_t Xp, xp_scale, Xq, x_scale;          // forward-internal dispatched rows
-  size_t A;                                  // [T*k + T*S, f] SwiGLU output
-  size_t Aq, a_scale;                        // FP8: requantised SwiGLU output
+  size_t A;                                  // [T*k + T*S, f] SwiGLU output (not for MX)
+  size_t Aq, a_scale;                        // FP8 / MX: quantised SwiGLU output
   size_t Yp, Ys;                             // forward-internal expert outputs
   size_t total;
   int nblk;
@@ -116,13 +121,14 @@ inline Layout make_layout(const moe_shape& s) {
   L.dst_row = take(rows * 4);
   L.src_tok = take(rows * 4);
   L.Xp = take(rows * h * xp_bytes(s.precision));
-  bool fp8 = s.precision == MOE_PREC_FP8;
-  L.xp_scale = take(fp8 ? rows * 4 : 0);
-  L.Xq = take(fp8 ? T * h : 0);
-  L.x_scale = take(fp8 ? T * 4 : 0);
-  L.A = take(arows * f * (fp8 ? 4 : act_bytes(s.precision)));
-  L.Aq = take(fp8 ? arows * f : 0);
-  L.a_scale = take(fp8 ? arows * 4 : 0);
+  const bool q8 = s.precision >= MOE_PREC_FP8;  // e4m3 activations (A8W8 or MX)
+  const bool mx = is_mx(s.precision);
+  L.xp_scale = take(rows * row_scale_bytes(s.precision, h));
+  L.Xq = take(q8 ? T * h : 0);
+  L.x_scale = take(T * row_scale_bytes(s.precision, h));
+  L.A = take(mx ? 0 : arows * f * (q8 ? 4 : act_bytes(s.precision)));
+  L.Aq = take(q8 ? arows * f : 0);
+  L.a_scale = take(arows * row_scale_bytes(s.precision, f));
   L.Yp = take(rows * h * act_bytes(s.precision));
   L.Ys = take(s.has_shared ? T * h * act_bytes(s.precision) : 0);
   L.total = o;
@@ -158,9 +164,9 @@ struct PermuteArgs {
   int32_t* dst_row;
   int32_t* src_tok;
   void* Xp;
-  float* xp_scale;
+  void* xp_scale;  // fp32 per row (FP8) or E8M0 bytes [rows, h/32] (MX)
   void* Xq;
-  float* x_scale;
+  void* x_scale;
   int32_t* blk_cnt;
   int32_t* local_rank;
   int32_t* flag;
@@ -170,16 +176,16 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 struct FfnArgs {
   int T, h, E, k, f, has_shared, precision;
   const void* Xp;
-  const float* xp_scale;
+  const void* xp_scale;
   const int32_t* offsets;
   const void* Xs;
-  const float* xs_scale;
+  const void* xs_scale;
   moe_expert_weights w;
   void* Yp;
   void* Ys;
-  void* A;  // [T*k + T*S, f] (fp32 for FP8)
+  void* A;  // [T*k + T*S, f] (fp32 for FP8; unused for MX)
   void* Aq;
-  float* a_scale;
+  void* a_scale;
   int32_t* tile_off;
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);

@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     int T, int h, int E, int k, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ blk_base, const int32_t* __restrict__ local_rank,
     const void* __restrict__ X, int32_t* __restrict__ dst_row, int32_t* __restrict__ src_tok,
-    void* __restrict__ Xp, float* __restrict__ xp_scale, void* __restrict__ Xq,
-    float* __restrict__ x_scale) {
+    void* __restrict__ Xp, void* __restrict__ xp_scale_v, void* __restrict__ Xq,
+    void* __restrict__ x_scale_v) {
   __shared__ int32_t s_dst[kMaxTopk];
   __shared__ float s_red[4];
   const int t = blockIdx.x;
@@ -135,7 +135,46 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     dst_row[i] = d;
     s_dst[tid] = d;
   }
-  if (PREC != MOE_PREC_FP8) {
+  if (PREC == MOE_PREC_MXFP8) {
+    // MX: groups of 32 along h share an E8M0 scale, exponent floor(log2
+    // amax) - 8; 4 consecutive threads hold a group's 32 values (8 each) and
+    // exchange their amax by xor shuffles; codes = RNE_sat(x * 2^(127-code)).
+    __syncthreads();
+    const uint16_t* xr = static_cast<const uint16_t*>(X) + static_cast<size_t>(t) * h;
+    uint8_t* xq = static_cast<uint8_t*>(Xq) + static_cast<size_t>(t) * h;
+    uint8_t* xs = static_cast<uint8_t*>(x_scale_v) + static_cast<size_t>(t) * (h / 32);
+    uint8_t* xps = static_cast<uint8_t*>(xp_scale_v);
+    // the 4 threads of a group always make the same trips (h % 32 == 0)
+    for (int c = tid * 8; c < h; c += 256 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(w[q] << 16);
+        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(f[q]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
+      const uint32_t code = static_cast<uint32_t>(e > 8 ? e - 8 : 0);
+      const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code)
+      const uint2 qv = make_uint2(f32x4_to_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                                  f32x4_to_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
+      *reinterpret_cast<uint2*>(xq + c) = qv;
+      const bool lead = (tid & 3) == 0;
+      if (lead) xs[c / 32] = static_cast<uint8_t>(code);
+      for (int j = 0; j < k; ++j) {
+        const int d = s_dst[j];
+        if (d < 0) continue;
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Xp) + static_cast<size_t>(d) * h + c) = qv;
+        if (lead) xps[static_cast<size_t>(d) * (h / 32) + c / 32] = static_cast<uint8_t>(code);
+      }
+    }
+  } else if (PREC != MOE_PREC_FP8) {
     __syncthreads();
     const int esz = (PREC == MOE_PREC_F32) ? 4 : 2;
     const int nvec = h * esz / 16;
@@ -152,6 +191,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     }
   } else {
     // A8W8: scale = max|x| / 448 (1 for a zero row), codes = RNE_sat(x / scale)
+    float* xp_scale = static_cast<float*>(xp_scale_v);
+    float* x_scale = static_cast<float*>(x_scale_v);
     const uint16_t* xr = static_cast<const uint16_t*>(X) + static_cast<size_t>(t) * h;
     float amax = 0.0f;
     for (int c = tid * 8; c < h; c += 256 * 8) {
@@ -219,6 +260,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_BF16>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
                          a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
                          a.xp_scale, a.Xq, a.x_scale);
+      break;
+    case MOE_PREC_MXFP8:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_MXFP8>, dim3(a.T), dim3(256), 0, stream, a.T,
+                         a.h, a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok,
+                         a.Xp, a.xp_scale, a.Xq, a.x_scale);
       break;
     default:
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_FP8>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,

@@ -443,10 +443,26 @@ static void swiglu_row_fp8(int hidden, int f, const uint8_t* qx, double sx, cons
 
 /* Element (c, n) of an MX weight matrix with N columns: codes [K, N] (e2m1:
  * two per byte along N), scales [K/32, N]. */
+/* Element values and scale factors as tables filled once from
+ * element_decode and ldexp (the same numbers as oracle_mx_value; a table
+ * read keeps the expert loops fast). */
+static double mx_elem_table[2][256];
+static double mx_pow2_table[256];
+static int mx_tables_ready = 0;
+static void mx_tables_init(void) {
+  if (mx_tables_ready) return;
+  for (int c = 0; c < 256; ++c) {
+    mx_elem_table[ORC_FMT_E4M3][c] = element_decode((uint8_t)c, ORC_FMT_E4M3);
+    mx_elem_table[ORC_FMT_E2M1][c] = element_decode((uint8_t)(c & 0xF), ORC_FMT_E2M1);
+    mx_pow2_table[c] = ldexp(1.0, c - 127);
+  }
+  mx_tables_ready = 1;
+}
+
 static double mx_weight(const uint8_t* W, const uint8_t* S, int N, int c, int n, int fmt) {
   size_t i = (size_t)c * N + n;
   uint8_t code = fmt == ORC_FMT_E4M3 ? W[i] : (uint8_t)((W[i / 2] >> (4 * (i & 1))) & 0xF);
-  return oracle_mx_value(code, S[(size_t)(c / 32) * N + n], fmt);
+  return mx_elem_table[fmt][code] * mx_pow2_table[S[(size_t)(c / 32) * N + n]];
 }
 
 /* The MX expert of [MM]'s MXFP block: x is quantised per group of 32 along
@@ -544,6 +560,7 @@ void oracle_layer_tokens(const oracle_layer* L, const int32_t* ids, const double
                          const int32_t* tok, double* Y) {
   int h = L->hidden, f = L->inter;
   e4m3_table_init();
+  mx_tables_init();
 #pragma omp parallel
   {
     double* xbuf = (double*)malloc(sizeof(double) * 2 * h);
@@ -586,6 +603,7 @@ void oracle_expert_rows(const oracle_layer* L, const int32_t* offsets, const int
                         int nrows, const int32_t* rows, double* Yp) {
   int h = L->hidden, f = L->inter;
   e4m3_table_init();
+  mx_tables_init();
 #pragma omp parallel
   {
     double* xbuf = (double*)malloc(sizeof(double) * 2 * h);

@@ -11,6 +11,7 @@ Workloads (T tokens, hidden h, E routed experts, top-k, inter f, shared S):
   v4pro_bf16         8192, 7168, 384, 6, 3072, 1 bf16, sigmoid + beta, alpha 2.5,
                                                  Zipf(0.8) expert load
   v4pro_fp8          as v4pro_bf16, A8W8 e4m3 experts, bf16 output
+  v4pro_mxfp8        as v4pro_bf16, MXFP8 experts (e4m3, group-32 E8M0 scales)
   decode_hash_bf16   128, 7168, 384, 6, 3072, 1  token-id hash routing
   decode_score_bf16  128, v4pro router
   ep_share_bf16      4096, 7168, 6, 6, 3072, 0   one GPU's expert-parallel share
@@ -24,7 +25,10 @@ fixture under tests/golden (written by a script that runs the CPU oracle's
 router on a calibration batch).  bf16 values are drawn in fp32 and rounded to
 nearest even by torch.  fp8 expert weights are quantised offline per output
 channel: scale = max|W[:, n]| / 448, codes = torch's float8_e4m3fn cast of
-W / scale.  Hash tables hold k distinct expert ids per token id.
+W / scale.  MXFP8 expert weights are quantised offline in groups of 32 rows
+(K) per column: E8M0 scale code = floor(log2 max|W|) - 8 + 127 (0 for a zero
+group), codes = torch's float8_e4m3fn cast of W * 2^(127 - code) clamped to
++-448.  Hash tables hold k distinct expert ids per token id.
 """
 from __future__ import annotations
 
@@ -79,6 +83,8 @@ WORKLOADS = {
                  zipf=True, family="v4pro"),
         Workload("v4pro_fp8", 8192, 7168, 384, 6, 3072, 1, "fp8", alpha=2.5, beta_range=0.1,
                  zipf=True, family="v4pro"),
+        Workload("v4pro_mxfp8", 8192, 7168, 384, 6, 3072, 1, "mxfp8", alpha=2.5,
+                 beta_range=0.1, zipf=True, family="v4pro"),
         Workload("decode_hash_bf16", 128, 7168, 384, 6, 3072, 1, "bf16", alpha=2.5, hash=True,
                  family="v4pro"),
         Workload("decode_score_bf16", 128, 7168, 384, 6, 3072, 1, "bf16", alpha=2.5,
@@ -143,21 +149,45 @@ def quantize_weight_e4m3(W: torch.Tensor):
     return q, scale.float()
 
 
+def quantize_weight_mx_e4m3(W: torch.Tensor):
+    """Offline MXFP8 quantisation of a [K, N] weight (K a multiple of 32):
+    codes [K, N] e4m3fn and E8M0 scale codes [K/32, N] uint8 (see the module
+    docstring)."""
+    Wf = W.float()
+    K, N = Wf.shape
+    g = Wf.reshape(K // 32, 32, N)
+    amax = g.abs().amax(dim=1)
+    _, ex = torch.frexp(amax)                        # amax = m * 2^ex, m in [0.5, 1)
+    code = torch.where(amax > 0, (ex - 1 - 8 + 127).clamp(0, 254), torch.zeros_like(ex))
+    q = torch.ldexp(g, (127 - code).unsqueeze(1).to(torch.float32))
+    q = q.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).reshape(K, N)
+    return q, code.to(torch.uint8)
+
+
 def _expert_weights(wl: Workload, seed, device, act_dtype):
     """W1 [E,h,2f], W2 [E,f,h] (bf16/fp32), generated one expert at a time."""
     E, h, f = wl.experts, wl.hidden, wl.inter
     fp8 = wl.precision == "fp8"
-    wdt = torch.float8_e4m3fn if fp8 else act_dtype
+    mx = wl.precision == "mxfp8"
+    wdt = torch.float8_e4m3fn if (fp8 or mx) else act_dtype
     W1 = torch.empty((E, h, 2 * f), dtype=wdt, device=device)
     W2 = torch.empty((E, f, h), dtype=wdt, device=device)
-    s1 = torch.empty((E, 2 * f), dtype=torch.float32, device=device) if fp8 else None
-    s2 = torch.empty((E, h), dtype=torch.float32, device=device) if fp8 else None
+    s1 = s2 = None
+    if fp8:
+        s1 = torch.empty((E, 2 * f), dtype=torch.float32, device=device)
+        s2 = torch.empty((E, h), dtype=torch.float32, device=device)
+    if mx:
+        s1 = torch.empty((E, h // 32, 2 * f), dtype=torch.uint8, device=device)
+        s2 = torch.empty((E, f // 32, h), dtype=torch.uint8, device=device)
     for e in range(E):
         w1 = normal((h, 2 * f), 1.0 / math.sqrt(h), seed=seed, name=f"W1.{e}", device=device,
                     dtype=act_dtype)
         w2 = normal((f, h), 1.0 / math.sqrt(f), seed=seed, name=f"W2.{e}", device=device,
                     dtype=act_dtype)
-        if fp8:
+        if mx:
+            W1[e], s1[e] = quantize_weight_mx_e4m3(w1)
+            W2[e], s2[e] = quantize_weight_mx_e4m3(w2)
+        elif fp8:
             W1[e], s1[e] = quantize_weight_e4m3(w1)
             W2[e], s2[e] = quantize_weight_e4m3(w2)
         else:

@@ -69,8 +69,11 @@ def _shape(**kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(tokens=0), INVALID), (dict(topk=0), INVALID), (dict(topk=9), INVALID),
     (dict(experts=40, topk=17), INVALID), (dict(has_shared=2), INVALID),
-    (dict(precision=3), INVALID), (dict(hidden=96), UNSUPPORTED), (dict(inter=96), UNSUPPORTED),
-    (dict(inter=192, precision="fp8"), UNSUPPORTED), (dict(experts=600, topk=2), UNSUPPORTED),
+    (dict(precision=4), INVALID), (dict(precision=-1), INVALID), (dict(hidden=96), UNSUPPORTED),
+    (dict(inter=96), UNSUPPORTED), (dict(inter=192, precision="fp8"), UNSUPPORTED),
+    (dict(hidden=384, inter=128, precision="fp8"), UNSUPPORTED),
+    (dict(hidden=384, inter=128, precision="mxfp8"), UNSUPPORTED),
+    (dict(experts=600, topk=2), UNSUPPORTED),
 ])
 def test_bad_shapes_rejected(kw, expect):
     L = _lib()
@@ -87,8 +90,13 @@ def test_workspace_size_grows_with_the_problem():
     a = moe.moe_workspace_size(_shape())
     b = moe.moe_workspace_size(_shape(tokens=128))
     c = moe.moe_workspace_size(_shape(tokens=128, has_shared=1))
-    d = moe.moe_workspace_size(_shape(tokens=128, has_shared=1, precision="fp8", inter=128))
-    assert 0 < a < b < c and d > 0 and a % 256 == 0
+    d = moe.moe_workspace_size(_shape(tokens=128, has_shared=1, precision="fp8", inter=128,
+                                      hidden=256))
+    e = moe.moe_workspace_size(_shape(tokens=128, has_shared=1, precision="mxfp8", inter=128,
+                                      hidden=256))
+    assert 0 < a < b < c and d > 0 and e > 0 and a % 256 == 0
+    # MX keeps no fp32 copy of the SwiGLU output, so it needs less than A8W8
+    assert e < d
 
 
 def test_null_pointers_and_workspace_rejected():
@@ -108,7 +116,7 @@ def test_null_pointers_and_workspace_rejected():
     # permute: null outputs, fp8 without scales
     assert L.moe_permute(C.byref(s), 16, 16, None, 16, 16, 16, 16, None, None, None, FAKE_WS, n,
                          None) == INVALID
-    s8 = _shape(precision="fp8", inter=128)
+    s8 = _shape(precision="fp8", inter=128, hidden=256)
     n8 = moe.moe_workspace_size(s8)
     assert L.moe_permute(C.byref(s8), 16, 16, 16, 16, 16, 16, 16, None, None, None, FAKE_WS, n8,
                          None) == INVALID

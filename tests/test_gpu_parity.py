@@ -26,7 +26,7 @@ from tests.helpers import bits, f64, oracle_layer, oracle_route, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2}
 DELTA = 1e-5
 
 CASES = {
@@ -34,6 +34,7 @@ CASES = {
     "llama_small": ("llama_bf16", dict(T=512, hidden=256, experts=16, inter=128)),
     "v4pro_small": ("v4pro_bf16", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_fp8_small": ("v4pro_fp8", dict(T=256, hidden=512, experts=64, inter=256)),
+    "v4pro_mxfp8_small": ("v4pro_mxfp8", dict(T=256, hidden=512, experts=64, inter=256)),
     "decode_hash_small": ("decode_hash_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "decode_score_small": ("decode_score_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "ep_share_small": ("ep_share_bf16", dict(T=600, hidden=256, inter=128)),
@@ -105,7 +106,14 @@ def test_permute_bit_exact(name):
     d = oracle.dispatch(r["ids"], wl.experts)
     for k in ("counts", "offsets", "dst_row", "src_tok"):
         assert np.array_equal(p[k].cpu().numpy(), d[k]), k
-    if wl.precision == "fp8":
+    if wl.precision == "mxfp8":
+        # bf16 inputs make the MX decision exact in any precision
+        q, s = oracle.mx_quantize(cpu["X"].double().numpy(), "e4m3")
+        assert np.array_equal(bits(p["x_scale"]), s)
+        assert np.array_equal(bits(p["Xq"]), q)
+        assert np.array_equal(bits(p["Xp"]), q[d["src_tok"]])
+        assert np.array_equal(bits(p["xp_scale"]), s[d["src_tok"]])
+    elif wl.precision == "fp8":
         q, s = oracle.quantize_rows_f32(cpu["X"].float().numpy())
         assert np.array_equal(bits(p["x_scale"]), s)
         assert np.array_equal(bits(p["Xq"]), q)
@@ -183,7 +191,8 @@ def test_forward(name):
     assert err <= TOL[wl.precision]
 
 
-@pytest.mark.parametrize("name", ["v4pro_small", "tiny_fp32", "v4pro_fp8_small"])
+@pytest.mark.parametrize("name", ["v4pro_small", "tiny_fp32", "v4pro_fp8_small",
+                                  "v4pro_mxfp8_small"])
 def test_forward_with_given_routing(name):
     """The mega_moe form: expert ids and weights are inputs (no router)."""
     _need_gpu()
@@ -209,7 +218,8 @@ def _edge(base, ids=None, **kw):
 
 
 @pytest.mark.parametrize("kind", ["one_token", "all_to_one_expert", "k_equals_E", "single_expert",
-                                  "fp8_all_to_one", "decode_one_token"])
+                                  "fp8_all_to_one", "mxfp8_all_to_one", "mxfp8_decode",
+                                  "decode_one_token"])
 def test_edge_cases(kind):
     _need_gpu()
     spec = {
@@ -220,12 +230,15 @@ def test_edge_cases(kind):
         "single_expert": ("llama_bf16", dict(T=200, hidden=128, experts=1, topk=1, inter=64)),
         "fp8_all_to_one": ("v4pro_fp8", dict(T=300, hidden=256, experts=64, inter=128, topk=1,
                                               zipf=False)),
+        "mxfp8_all_to_one": ("v4pro_mxfp8", dict(T=300, hidden=256, experts=64, inter=128,
+                                                  topk=1, zipf=False)),
+        "mxfp8_decode": ("v4pro_mxfp8", dict(T=3, hidden=512, experts=64, inter=256)),
         "decode_one_token": ("decode_hash_bf16", dict(T=1, hidden=256, experts=64, inter=128)),
     }[kind]
     cpu, L = _edge(spec[0], **spec[1])
     wl = cpu["workload"]
     _log(f"[edge] {kind} {wl}")
-    if kind in ("all_to_one_expert", "fp8_all_to_one"):
+    if kind in ("all_to_one_expert", "fp8_all_to_one", "mxfp8_all_to_one"):
         ids = np.full((wl.T, 1), 37, np.int32)       # 300 rows: 3 tiles, ragged
         G = np.full((wl.T, 1), 0.75, np.float32)
         Y, _, _ = L.forward(torch.from_numpy(ids).cuda(), torch.from_numpy(G).cuda(), route=False)
