@@ -251,9 +251,9 @@ class Layer:
     precision 'fp32': X, W float32.  'bf16': X, W uint16 bits.  'fp8': X uint16
     (bf16 bits, quantised per token inside the layer), W uint8 e4m3 codes with
     float32 per-output-channel scales.  'mxfp8' / 'mxfp4': X uint16 (bf16
-    bits, MX-quantised inside the layer), W uint8 e4m3 codes [E,K,N] / e2m1
-    code pairs [E,K,N/2] (element 2i in the low nibble), scales uint8 E8M0
-    [E,K/32,N].
+    bits, MX-quantised inside the layer).  mxfp8: W uint8 e4m3 codes [E,K,N],
+    scales uint8 E8M0 [E,K/32,N].  mxfp4: W K-contiguous e2m1 code pairs
+    [E,N,K/2] (element 2i in the low nibble), scales [E,N,K/32].
     """
 
     def __init__(self, precision, X, W1, W2, *, w1_scale=None, w2_scale=None, Ws1=None, Ws2=None,
@@ -273,15 +273,22 @@ class Layer:
         self.ws1_scale = _c(ws1_scale, sdt)
         self.ws2_scale = _c(ws2_scale, sdt)
         T, h = self.X.shape
-        E, h2, f2 = self.W1.shape
-        if precision == "mxfp4":
-            f2 *= 2  # two e2m1 codes per byte
+        if precision == "mxfp4":   # K-contiguous [E, 2f, h/2]: two e2m1 codes per byte
+            E, f2, hb = self.W1.shape
+            h2 = 2 * hb
+        else:
+            E, h2, f2 = self.W1.shape
         assert h2 == h and f2 % 2 == 0
         self.T, self.hidden, self.E, self.inter, self.k = T, h, E, f2 // 2, int(k)
-        if mx:
+        if precision == "mxfp8":
             assert h % 32 == 0 and self.inter % 32 == 0
             assert self.w1_scale.shape == (E, h // 32, f2)
             assert self.w2_scale.shape == (E, self.inter // 32, h)
+        if precision == "mxfp4":
+            assert h % 32 == 0 and self.inter % 32 == 0
+            assert self.W2.shape == (E, h, self.inter // 2)
+            assert self.w1_scale.shape == (E, f2, h // 32)
+            assert self.w2_scale.shape == (E, h, self.inter // 32)
         if precision in ("fp8", "mxfp8", "mxfp4"):
             assert self.w1_scale is not None and self.w2_scale is not None
         self._s = _Layer(T, h, E, self.k, self.inter, int(self.Ws1 is not None),

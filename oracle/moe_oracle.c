@@ -51,7 +51,9 @@
  * Element codes for tensors handed in: 0 = fp32, 1 = bf16 (raw 16-bit words),
  * 2 = fp8 e4m3fn (raw bytes).  MX tensors: e4m3 codes one per byte, e2m1
  * codes two per byte (element 2i in the low nibble), E8M0 scale codes one per
- * byte.  All arrays are host memory, row major.
+ * byte; MXFP4 weights are stored K-contiguous as on the mega_moe page
+ * (codes [E,N,K/2], scales [E,N,K/32]).  All arrays are host memory, row
+ * major.
  */
 #include <math.h>
 #include <stdint.h>
@@ -441,8 +443,10 @@ static void swiglu_row_fp8(int hidden, int f, const uint8_t* qx, double sx, cons
   for (int o = 0; o < hidden; ++o) out[o] = out[o] * (double)s_w2[o] * sa;
 }
 
-/* Element (c, n) of an MX weight matrix with N columns: codes [K, N] (e2m1:
- * two per byte along N), scales [K/32, N]. */
+/* Element (c, n) of a K x N MX weight matrix.  MXFP8 stores it K-major:
+ * codes [K, N], scales [K/32, N].  MXFP4 keeps the mega_moe page's storage,
+ * K-contiguous: codes [N, K/2] (element k of row n in byte k/2, even k in the
+ * low nibble), scales [N, K/32]. */
 /* Element values and scale factors as tables filled once from
  * element_decode and ldexp (the same numbers as oracle_mx_value; a table
  * read keeps the expert loops fast). */
@@ -459,10 +463,12 @@ static void mx_tables_init(void) {
   mx_tables_ready = 1;
 }
 
-static double mx_weight(const uint8_t* W, const uint8_t* S, int N, int c, int n, int fmt) {
-  size_t i = (size_t)c * N + n;
-  uint8_t code = fmt == ORC_FMT_E4M3 ? W[i] : (uint8_t)((W[i / 2] >> (4 * (i & 1))) & 0xF);
-  return mx_elem_table[fmt][code] * mx_pow2_table[S[(size_t)(c / 32) * N + n]];
+static double mx_weight(const uint8_t* W, const uint8_t* S, int K, int N, int c, int n, int fmt) {
+  if (fmt == ORC_FMT_E4M3)
+    return mx_elem_table[fmt][W[(size_t)c * N + n]] * mx_pow2_table[S[(size_t)(c / 32) * N + n]];
+  size_t i = (size_t)n * K + c;
+  uint8_t code = (uint8_t)((W[i / 2] >> (4 * (i & 1))) & 0xF);
+  return mx_elem_table[fmt][code] * mx_pow2_table[S[(size_t)n * (K / 32) + c / 32]];
 }
 
 /* The MX expert of [MM]'s MXFP block: x is quantised per group of 32 along
@@ -478,7 +484,7 @@ static void swiglu_row_mx(int hidden, int f, const double* x, int fmt, const uin
   for (int c = 0; c < hidden; ++c) {
     double xc = xd[c];
     if (xc == 0.0) continue;
-    for (int n = 0; n < 2 * f; ++n) h1[n] += xc * mx_weight(W1, S1, 2 * f, c, n, fmt);
+    for (int n = 0; n < 2 * f; ++n) h1[n] += xc * mx_weight(W1, S1, hidden, 2 * f, c, n, fmt);
   }
   for (int n = 0; n < f; ++n) h1[n] = silu(h1[n]) * h1[f + n];
   oracle_mx_quantize(f, h1, fmt, qbuf, sbuf);
@@ -486,7 +492,7 @@ static void swiglu_row_mx(int hidden, int f, const double* x, int fmt, const uin
   for (int n = 0; n < f; ++n) {
     double u = oracle_mx_value(qbuf[n], sbuf[n / 32], fmt);
     if (u == 0.0) continue;
-    for (int o = 0; o < hidden; ++o) out[o] += u * mx_weight(W2, S2, hidden, n, o, fmt);
+    for (int o = 0; o < hidden; ++o) out[o] += u * mx_weight(W2, S2, f, hidden, n, o, fmt);
   }
 }
 
@@ -495,10 +501,10 @@ typedef struct {
   int T, hidden, E, k, inter, has_shared;
   int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3, 3 = MXFP8, 4 = MXFP4 */
   const void* X;        /* [T,hidden]: fp32 (precision 0) or bf16 */
-  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes / e2m1 pairs */
+  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes; MXFP4: [E,2f,hidden/2] */
   const void* W2;       /* [E,f,hidden] */
-  const void* w1_scale; /* A8W8: fp32 [E,2f]; MX: E8M0 [E,hidden/32,2f] */
-  const void* w2_scale; /* A8W8: fp32 [E,hidden]; MX: E8M0 [E,f/32,hidden] */
+  const void* w1_scale; /* A8W8: fp32 [E,2f]; MXFP8: E8M0 [E,hidden/32,2f]; MXFP4 [E,2f,hidden/32] */
+  const void* w2_scale; /* A8W8: fp32 [E,hidden]; MXFP8: E8M0 [E,f/32,hidden]; MXFP4 [E,hidden,f/32] */
   const void* Ws1;      /* shared [hidden,2f] or NULL */
   const void* Ws2;      /* shared [f,hidden] */
   const void* ws1_scale;

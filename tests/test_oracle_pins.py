@@ -455,19 +455,23 @@ def test_mx_quantize_e2m1_matches_brute_force():
 
 
 def _mx_weights(rng, E, K, N, fmt):
-    """Random MX weight codes [E,K,N] (e2m1: packed [E,K,N/2], element 2i low
-    nibble) and E8M0 scales [E,K/32,N]."""
+    """Random MX weights of K x N matrices.  e4m3: codes [E,K,N], E8M0 scales
+    [E,K/32,N].  e2m1 (K-contiguous, as the MXFP4 layer stores them): code
+    pairs [E,N,K/2] (element 2i in the low nibble), scales [E,N,K/32].
+    Returns (stored codes, stored scales, dequantised [E,K,N])."""
+    scales_nk = rng.integers(112, 124, size=(E, N, K // 32)).astype(np.uint8)
     if fmt == "e4m3":
-        codes = rng.integers(0, 0x7E, size=(E, K, N)).astype(np.uint8) | \
-            (rng.integers(0, 2, size=(E, K, N)).astype(np.uint8) << 7)
-        packed = codes
+        codes_nk = rng.integers(0, 0x7E, size=(E, N, K)).astype(np.uint8) | \
+            (rng.integers(0, 2, size=(E, N, K)).astype(np.uint8) << 7)
+        stored = np.ascontiguousarray(np.swapaxes(codes_nk, 1, 2))
+        stored_sc = np.ascontiguousarray(np.swapaxes(scales_nk, 1, 2))
     else:
-        codes = rng.integers(0, 16, size=(E, K, N)).astype(np.uint8)
-        packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
-    scales = rng.integers(112, 124, size=(E, K // 32, N)).astype(np.uint8)
-    # dequantised: scale of W[e, k, n] is scales[e, k // 32, n]
-    deq = _mx_dequant(np.swapaxes(codes, 1, 2), np.swapaxes(scales, 1, 2), fmt)
-    return packed, scales, np.swapaxes(deq, 1, 2)
+        codes_nk = rng.integers(0, 16, size=(E, N, K)).astype(np.uint8)
+        stored = (codes_nk[..., 0::2] | (codes_nk[..., 1::2] << 4)).astype(np.uint8)
+        stored_sc = scales_nk
+    # dequantised: the scale of W[e, k, n] belongs to group k // 32 of column n
+    deq = _mx_dequant(codes_nk, scales_nk, fmt)
+    return stored, stored_sc, np.ascontiguousarray(np.swapaxes(deq, 1, 2))
 
 
 @pytest.mark.parametrize("prec,fmt", [("mxfp8", "e4m3"), ("mxfp4", "e2m1")])
@@ -530,8 +534,9 @@ PLANTED = {
     # e2m1 weight pairs read high nibble first
     "nibble": ("(W[i / 2] >> (4 * (i & 1)))", "(W[i / 2] >> (4 * (1 - (i & 1))))",
                lambda: test_mx_layer_is_the_dense_swiglu_of_dequantised_operands("mxfp4", "e2m1")),
-    # MX weight scale taken from the next group
-    "mxscale": ("S[(size_t)(c / 32) * N + n]", "S[(size_t)((c + 32) / 32 % (c / 32 + 1)) * N + n]",
+    # MX weight scale taken from the wrong group
+    "mxscale": ("mx_pow2_table[S[(size_t)(c / 32) * N + n]]",
+                "mx_pow2_table[S[(size_t)((c + 32) / 32 % (c / 32 + 1)) * N + n]]",
                 lambda: test_mx_layer_is_the_dense_swiglu_of_dequantised_operands("mxfp8", "e4m3")),
 }
 
