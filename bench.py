@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak) at 1 GPU"
 PEAK_HBM_GBS = 8000.0
-PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "mxfp8": 5033.2, "fp32": 157.3}
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3,
+                    "fp32": 157.3}
 
 
 def log(msg):
@@ -44,14 +45,14 @@ def stage_bytes(wl):
     Y."""
     T, h, E, k = wl.T, wl.hidden, wl.experts, wl.topk
     ab = 4 if wl.precision == "fp32" else 2             # activation / output bytes
-    q8 = wl.precision in ("fp8", "mxfp8")
-    xb = 1 if q8 else ab                                # dispatched row bytes
+    q8 = wl.precision in ("fp8", "mxfp8", "mxfp4")
+    xb = (0.5 if wl.precision == "mxfp4" else 1) if q8 else ab   # dispatched row bytes
     route = T * h * ab + h * E * ab + T * k * 8 + (T * 4 if wl.hash else 0)
     permute = 2 * T * k * 4 + T * h * ab + T * k * h * xb + 2 * T * k * 4
     if wl.precision == "fp8":      # Xq and the per-row scales
         permute += T * h + T * 4 + T * k * 4
-    if wl.precision == "mxfp8":    # Xq and the per-group E8M0 scales
-        permute += T * h + (T + T * k) * (h // 32)
+    if wl.precision in ("mxfp8", "mxfp4"):    # Xq and the per-group E8M0 scales
+        permute += T * h * xb + (T + T * k) * (h // 32)
     combine = T * k * h * ab + T * k * 8 + (T * h * ab if wl.shared else 0) + T * h * ab
     return {"route": route, "permute": permute, "combine": combine}
 
@@ -64,13 +65,13 @@ def algorithmic_work(wl, counts):
     h, f, k, T = wl.hidden, wl.inter, wl.topk, wl.T
     rows = T * k + (T if wl.shared else 0)
     flops = 2.0 * rows * (h * 2 * f + f * h)
-    q8 = wl.precision in ("fp8", "mxfp8")
-    wbytes = 1 if q8 else (4 if wl.precision == "fp32" else 2)
+    q8 = wl.precision in ("fp8", "mxfp8", "mxfp4")
+    wbytes = (0.5 if wl.precision == "mxfp4" else 1) if q8 else (4 if wl.precision == "fp32" else 2)
     xbytes = wbytes
     obytes = 4 if wl.precision == "fp32" else 2
     active = int((counts > 0).sum()) + (1 if wl.shared else 0)
     # MX: one E8M0 byte per 32 weights and per 32 input values
-    sbytes = 1.0 / 32 if wl.precision == "mxfp8" else 0.0
+    sbytes = 1.0 / 32 if wl.precision in ("mxfp8", "mxfp4") else 0.0
     weight_bytes = active * 3.0 * h * f * (wbytes + sbytes)
     act_bytes = rows * h * (xbytes + sbytes + obytes)
     return flops, weight_bytes + act_bytes, active
@@ -282,8 +283,9 @@ def main(argv=None):
     weights = moe.make_weights(inp["W1"], inp["W2"], inp["w1_scale"], inp["w2_scale"], inp["Ws1"],
                                inp["Ws2"], inp["ws1_scale"], inp["ws2_scale"])
     dev = "cuda"
-    mx = wl.precision == "mxfp8"
-    fp8 = wl.precision in ("fp8", "mxfp8")   # e4m3 activation codes
+    mx = wl.precision in ("mxfp8", "mxfp4")
+    fp4 = wl.precision == "mxfp4"
+    fp8 = wl.precision in ("fp8", "mxfp8", "mxfp4")   # quantised activation codes
     odt = torch.float32 if wl.precision == "fp32" else torch.bfloat16
     xdt = torch.float8_e4m3fn if fp8 else odt
     T, k, h, E = wl.T, wl.topk, wl.hidden, wl.experts
@@ -294,11 +296,13 @@ def main(argv=None):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     dst = torch.empty(n, dtype=torch.int32, device=dev)
     src = torch.empty(n, dtype=torch.int32, device=dev)
-    Xp = torch.empty((n, h), dtype=xdt, device=dev)
+    Xp = (torch.empty((n, h // 2), dtype=torch.uint8, device=dev) if fp4
+          else torch.empty((n, h), dtype=xdt, device=dev))
     sc_shape = (lambda r: (r, h // 32)) if mx else (lambda r: (r,))
     sc_dt = torch.uint8 if mx else torch.float32
     xps = torch.empty(sc_shape(n), dtype=sc_dt, device=dev) if fp8 else None
-    Xq = torch.empty((T, h), dtype=torch.float8_e4m3fn, device=dev) if fp8 else None
+    Xq = ((torch.empty((T, h // 2), dtype=torch.uint8, device=dev) if fp4
+           else torch.empty((T, h), dtype=torch.float8_e4m3fn, device=dev)) if fp8 else None)
     xs = torch.empty(sc_shape(T), dtype=sc_dt, device=dev) if fp8 else None
     Yp = torch.empty((n, h), dtype=odt, device=dev)
     Ys = torch.empty((T, h), dtype=odt, device=dev) if wl.shared else None
@@ -384,6 +388,7 @@ def main(argv=None):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 activations/output)",
                   "mxfp8": "mxfp8-e4m3 (group-32 E8M0 scales; bf16 input/output)",
+                  "mxfp4": "mxfp4-e2m1 (group-32 E8M0 scales; bf16 input/output)",
                   "fp32": "f32"}[prec],
         "data": "synthetic (seeded, random-init weights)",
         "config": {"workload": wl.name, "tokens": T, "hidden": h, "experts": E, "topk": k,

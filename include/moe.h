@@ -56,10 +56,17 @@
  *                      all-zero group) and its elements v / 2^exponent
  *                      rounded to nearest even, saturating at 448 (the OCP
  *                      MX rule; the page names the group size and types).
+ *       MOE_PREC_MXFP4: the same MX mode with OCP e2m1 (FP4) elements, the
+ *                      page's A4W4 scenario: two codes per byte, element 2i
+ *                      in the low nibble; exponent floor(log2(max|v|)) - 2,
+ *                      saturating at 6.  Weights are K-contiguous as the page
+ *                      stores them: W1 [E, 2*inter, hidden/2], W2 [E, hidden,
+ *                      inter/2], Ws1 [2*inter, hidden/2], Ws2 [hidden,
+ *                      inter/2]; Xp [rows, hidden/2], Xq [T, hidden/2].
  *   - Shape limits: 1 <= T; 1 <= topk <= min(16, experts) (the mega_moe
  *     constraint on top-k); experts <= 512; hidden a multiple of 128 and
- *     inter a multiple of 64 (the kernels' tile granularity); for FP8 and
- *     MXFP8 hidden a multiple of 256 and inter a multiple of 128.
+ *     inter a multiple of 64 (the kernels' tile granularity); for FP8,
+ *     MXFP8 and MXFP4 hidden a multiple of 256 and inter a multiple of 128.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -86,7 +93,8 @@ typedef enum {
   MOE_PREC_F32 = 0,
   MOE_PREC_BF16 = 1,
   MOE_PREC_FP8 = 2,
-  MOE_PREC_MXFP8 = 3
+  MOE_PREC_MXFP8 = 3,
+  MOE_PREC_MXFP4 = 4
 } moe_precision;
 
 typedef enum {
@@ -130,7 +138,11 @@ typedef struct {
  *   MOE_PREC_MXFP8: E8M0 bytes per group of 32 rows (K) and column:
  *     w1_scale [E, hidden/32, 2*inter], w2_scale [E, inter/32, hidden],
  *     ws1_scale [hidden/32, 2*inter], ws2_scale [inter/32, hidden]; the
- *     scale of W1[e, k, n] is w1_scale[e, k/32, n]. */
+ *     scale of W1[e, k, n] is w1_scale[e, k/32, n].
+ *   MOE_PREC_MXFP4: E8M0 bytes per row of the K-contiguous weights and group
+ *     of 32 along K: w1_scale [E, 2*inter, hidden/32], w2_scale [E, hidden,
+ *     inter/32], ws1_scale [2*inter, hidden/32], ws2_scale [hidden,
+ *     inter/32]. */
 typedef struct {
   const void* W1;
   const void* w1_scale;
@@ -173,6 +185,8 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
  *   along hidden); Xq [T, hidden] e4m3 and x_scale [T, hidden/32] E8M0 bytes
  *   receive that, Xp holds codes and xp_scale [T*topk, hidden/32] the scales
  *   of each row.
+ *   MOE_PREC_MXFP4: the same with e2m1 codes, two per byte: Xq [T,
+ *   hidden/2], Xp [T*topk, hidden/2], scales as for MXFP8.
  *   Otherwise xp_scale, Xq and x_scale are ignored.
  * Expert ids outside [0, E) are skipped (dst_row = -1) and flagged. */
 int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,
@@ -188,7 +202,7 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
  * be NULL.  Scales have the types moe_permute gives them.  The SwiGLU output
  * is held in the workspace: bf16 (BF16), fp32 before its per-row e4m3
  * requantisation (FP8), or MX-quantised in groups of 32 along inter as it
- * is produced (MXFP8). */
+ * is produced (MXFP8, MXFP4). */
 int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
                    const int32_t* offsets, const void* Xs, const void* xs_scale,
                    const moe_expert_weights* weights, void* Yp, void* Ys, void* workspace,

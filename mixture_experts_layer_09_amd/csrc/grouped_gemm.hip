@@ -590,6 +590,49 @@ struct DmaOps<MOE_PREC_FP8, BN> {
   }
 };
 
+// The work item of this block: its segment, m-tile and n-tile (false when
+// the block has none).  Blocks are dealt to the 8 XCDs round-robin; XCD x
+// runs either one contiguous range of items or (g.chunk > 0) chunks of
+// g.chunk items dealt to the XCDs in turn.  Items are (m-tile, n-tile) pairs,
+// m-tiles ordered by segment (tile_off); inside a segment they go in groups
+// of 1024 / BM m-tiles, n-tile major.
+template <int BM>
+__device__ __forceinline__ bool block_item(const GemmArgs& g, int& seg, int& mtile, int& nt) {
+  constexpr int GROUP_M = 1024 / BM;
+  const int E = g.E;
+  const int NT = g.n_tiles;
+  const int total = g.tile_off[E + 1] * NT;
+  int item;
+  if (g.chunk > 0) {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, C = g.chunk;
+    item = (slot / C) * (8 * C) + x * C + slot % C;
+    if (item >= total) return false;
+  } else {
+    if (static_cast<int>(blockIdx.x) >= total) return false;
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = total >> 3, rem = total & 7;
+    item = x * per + min(x, rem) + slot;
+  }
+  const int mq = item / NT;
+  int lo = 0, hi = E;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (g.tile_off[mid] <= mq)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  seg = lo;
+  const int mt_seg = g.tile_off[seg + 1] - g.tile_off[seg];
+  const int local = item - g.tile_off[seg] * NT;
+  const int grp = local / (GROUP_M * NT);
+  const int gsz = min(GROUP_M, mt_seg - grp * GROUP_M);
+  const int rin = local - grp * GROUP_M * NT;
+  nt = rin / gsz;
+  mtile = grp * GROUP_M + rin % gsz;
+  return true;
+}
+
 // MXFP8 shares the e4m3 operand layout; its MFMA takes each lane's E8M0
 // scale byte (the lane's 32 K-values are one MX group) for A and for B.
 template <int BN>
@@ -658,38 +701,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   const int wn = wave % WAVES_N;
 
   // ------------------------------------------------ tile -> segment (as above)
-  constexpr int GROUP_M = 1024 / BM;  // m-tiles of one group: 1024 rows
   const int E = g.E;
   const int NT = g.n_tiles;
-  const int total = g.tile_off[E + 1] * NT;
-  int item;
-  if (g.chunk > 0) {  // chunks of C items dealt to the XCDs in turn
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, C = g.chunk;
-    item = (slot / C) * (8 * C) + x * C + slot % C;
-    if (item >= total) return;
-  } else {
-    if (static_cast<int>(blockIdx.x) >= total) return;
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = total >> 3, rem = total & 7;
-    item = x * per + min(x, rem) + slot;
-  }
-  const int mq = item / NT;
-  int lo = 0, hi = E;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (g.tile_off[mid] <= mq)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  const int seg = lo;
-  const int mt_seg = g.tile_off[seg + 1] - g.tile_off[seg];
-  const int local = item - g.tile_off[seg] * NT;
-  const int grp = local / (GROUP_M * NT);
-  const int gsz = min(GROUP_M, mt_seg - grp * GROUP_M);
-  const int rin = local - grp * GROUP_M * NT;
-  const int nt = rin / gsz;
-  const int mtile = grp * GROUP_M + rin % gsz;
+  int seg, mtile, nt;
+  if (!block_item<BM>(g, seg, mtile, nt)) return;
 
   const bool shared = (seg == E);
   int row0, row_end;
@@ -963,6 +978,275 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
 }
 
+// MXFP4 (e2m1 x e2m1, group-32 E8M0 scales; the mega_moe page's A4W4 MXFP
+// scenario).  Both operands are K-contiguous rows: token rows [rows, K/2] and
+// weights [N, K/2] as the page stores them, so weight fragments are read the
+// way token-row fragments are, with no transposing LDS read.  A K-stage is
+// 128 elements, 64 bytes of a row; both tiles go to LDS by DMA with the
+// 64-byte-row swizzle chunk ^ ((row >> 2) & 3) (a 16-lane fragment read of
+// 16 consecutive rows then covers all banks once).  Each stage also carries
+// the rows' E8M0 scales of its 4 K-groups ([BM][4] and [BN][4], one dword
+// per row).  For 4-bit operands the 16x16x128 scaled MFMA reads lane group
+// g's 16 bytes as K 32g .. 32g+31, low nibble first, and lane group g's scale
+// covers exactly those (measured on the GPU with one-hot operands), so a
+// lane's data and scale are one MX group.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
+void grouped_gemm_mx4_kernel(GemmArgs g) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int ROWB = 64;  // bytes of one row's K-stage
+  constexpr int A_BYTES = BM * ROWB;
+  constexpr int B_BYTES = BN * ROWB;
+  constexpr int AS_OFF = A_BYTES + B_BYTES;
+  constexpr int BS_OFF = AS_OFF + BM * 4;
+  constexpr int STAGE = BS_OFF + BN * 4;
+  constexpr int A_INSTS = A_BYTES / 1024;  // 16 rows per 16-byte-lane DMA
+  constexpr int B_INSTS = B_BYTES / 1024;
+  constexpr int AS_INSTS = BM / 64;        // 64 rows per 4-byte-lane DMA
+  constexpr int BS_INSTS = BN / 64;
+  constexpr int A_OPS = A_INSTS / NW;
+  constexpr int B_OPS = B_INSTS / NW;
+  constexpr int WM = BM / WAVES_M;
+  constexpr int MT = WM / 16;
+  constexpr int NTW = BN / WAVES_N / 16;
+  static_assert(A_INSTS % NW == 0 && B_INSTS % NW == 0, "tiles must split evenly over the waves");
+  static_assert(AS_INSTS + BS_INSTS <= NW, "one scale DMA per wave at most");
+  static_assert(!SWIGLU || (NTW / 2) % 2 == 0, "MX SwiGLU epilogue: whole 32-column groups");
+
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WAVES_N;
+  const int wn = wave % WAVES_N;
+  const int E = g.E;
+  int seg, mtile, nt;
+  if (!block_item<BM>(g, seg, mtile, nt)) return;
+
+  const bool shared = (seg == E);
+  const size_t rowb = static_cast<size_t>(g.K) / 2;   // bytes of a K-contiguous row
+  const size_t sc_ld = static_cast<size_t>(g.K) / 32;  // scale bytes of a row
+  int row0, row_end;
+  const char* Abase;
+  const char* Wbase;
+  const uint8_t* asc8;
+  const uint8_t* wsc8;
+  char* obase;
+  uint8_t* osc8;
+  if (!shared) {
+    row0 = g.offsets[seg] + mtile * BM;
+    row_end = g.offsets[seg + 1];
+    Abase = static_cast<const char*>(g.A);
+    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.Nw * rowb;
+    asc8 = static_cast<const uint8_t*>(g.a_scale);
+    wsc8 = static_cast<const uint8_t*>(g.w_scale) + static_cast<size_t>(seg) * g.Nw * sc_ld;
+    obase = static_cast<char*>(g.out);
+    osc8 = static_cast<uint8_t*>(g.out_scale);
+  } else {
+    row0 = mtile * BM;
+    row_end = g.T;
+    Abase = static_cast<const char*>(g.A_sh);
+    Wbase = static_cast<const char*>(g.W_sh);
+    asc8 = static_cast<const uint8_t*>(g.a_scale_sh);
+    wsc8 = static_cast<const uint8_t*>(g.w_scale_sh);
+    obase = static_cast<char*>(g.out_sh);
+    osc8 = static_cast<uint8_t*>(g.out_scale_sh);
+  }
+  const int rows_valid = min(BM, row_end - row0);
+  const int mt_live =
+      __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
+  auto swz = [](int r) { return (r >> 2) & 3; };
+  // weight row of LDS B row nl (SwiGLU tiles: BN/2 gate rows, then the
+  // matching BN/2 up rows)
+  auto wrow = [&](int nl) {
+    if (SWIGLU) return nl < BN / 2 ? nt * (BN / 2) + nl : g.f + nt * (BN / 2) + (nl - BN / 2);
+    return nt * BN + nl;
+  };
+
+  // DMA sources (wave-uniform base + 32-bit lane offset; K-stage offset kt*64
+  // for data, kt*4 for scales, added per stage)
+  const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * rowb);
+  uint32_t a_voff[A_OPS];
+#pragma unroll
+  for (int q = 0; q < A_OPS; ++q) {
+    const int blk = wave * A_OPS + q;
+    const int r = blk * 16 + lane / 4;
+    const int c = (lane % 4) ^ swz(r);
+    a_voff[q] = static_cast<uint32_t>(min(r, row_end - 1 - row0)) * static_cast<uint32_t>(rowb) +
+                c * 16;
+  }
+  const char* b_base = uniform_ptr(Wbase);
+  uint32_t b_voff[B_OPS];
+#pragma unroll
+  for (int q = 0; q < B_OPS; ++q) {
+    const int blk = wave * B_OPS + q;
+    const int r = blk * 16 + lane / 4;
+    const int c = (lane % 4) ^ swz(r);
+    b_voff[q] = static_cast<uint32_t>(wrow(r)) * static_cast<uint32_t>(rowb) + c * 16;
+  }
+  const char* as_base = uniform_ptr(reinterpret_cast<const char*>(asc8) + static_cast<size_t>(row0) * sc_ld);
+  const char* bs_base = uniform_ptr(reinterpret_cast<const char*>(wsc8));
+  uint32_t sc_voff = 0;
+  int sc_lds = 0;
+  const bool a_sc = wave < AS_INSTS;
+  const bool b_sc = wave >= AS_INSTS && wave < AS_INSTS + BS_INSTS;
+  if (a_sc) {
+    sc_voff = static_cast<uint32_t>(min(wave * 64 + lane, row_end - 1 - row0)) *
+              static_cast<uint32_t>(sc_ld);
+    sc_lds = AS_OFF + wave * 256;
+  } else if (b_sc) {
+    sc_voff = static_cast<uint32_t>(wrow((wave - AS_INSTS) * 64 + lane)) *
+              static_cast<uint32_t>(sc_ld);
+    sc_lds = BS_OFF + (wave - AS_INSTS) * 256;
+  }
+  // only A blocks holding a valid row are fetched (wave-uniform count)
+  const int a_live = __builtin_amdgcn_readfirstlane(
+      max(0, min(A_OPS, (rows_valid + 15) / 16 - wave * A_OPS)));
+  const int ops_w = a_live + B_OPS + ((a_sc || b_sc) ? 1 : 0);
+  auto issue = [&](int kt, int slot) {
+    char* st = smem + slot * STAGE;
+#pragma unroll
+    for (int q = 0; q < A_OPS; ++q)
+      if (q < a_live)
+        dma16(a_base + static_cast<size_t>(kt) * ROWB, a_voff[q], st + (wave * A_OPS + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < B_OPS; ++q)
+      dma16(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q],
+            st + A_BYTES + (wave * B_OPS + q) * 1024);
+    if (a_sc) dma4(as_base + static_cast<size_t>(kt) * 4, sc_voff, st + sc_lds);
+    else if (b_sc) dma4(bs_base + static_cast<size_t>(kt) * 4, sc_voff, st + sc_lds);
+  };
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto bcol = [&](int j) -> int {  // first LDS B row of this wave's n-tile j
+    if (SWIGLU) {
+      const int half = BN / 2, per = BN / 2 / WAVES_N;
+      return j < NTW / 2 ? wn * per + j * 16 : half + wn * per + (j - NTW / 2) * 16;
+    }
+    return wn * (BN / WAVES_N) + j * 16;
+  };
+  const int kg = lane >> 4;  // K-group of this lane's fragment bytes
+  int a_off[MT], as_off[MT], b_off[NTW], bs_off[NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = wm * WM + i * 16 + (lane & 15);
+    a_off[i] = r * ROWB + ((kg ^ swz(r)) << 4);
+    as_off[i] = AS_OFF + r * 4 + kg;
+  }
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int r = bcol(j) + (lane & 15);
+    b_off[j] = A_BYTES + r * ROWB + ((kg ^ swz(r)) << 4);
+    bs_off[j] = BS_OFF + r * 4 + kg;
+  }
+
+  auto compute = [&](int slot) {
+    if (mt_live == 0) return;
+    const char* st = smem + slot * STAGE;
+    i32x4_t bfr[NTW], af[MT];
+    int sb[NTW], sa[MT];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) bfr[j] = *reinterpret_cast<const i32x4_t*>(st + b_off[j]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const i32x4_t*>(st + a_off[i]);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) sb[j] = *reinterpret_cast<const uint8_t*>(st + bs_off[j]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) sa[i] = *reinterpret_cast<const uint8_t*>(st + as_off[i]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const i32x8_t a8 = {af[i][0], af[i][1], af[i][2], af[i][3], 0, 0, 0, 0};
+        const i32x8_t b8 = {bfr[j][0], bfr[j][1], bfr[j][2], bfr[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
+                                                                     sa[i], 0, sb[j]);
+      }
+  };
+
+  const int KT = g.K / 128;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s);
+  for (int k0 = 0; k0 < KT; k0 += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      const int kt = k0 + s;
+      if (kt < KT) {
+        const int after = min(STAGES - 2, KT - 1 - kt);
+        wait_vmcnt_rt(after * ops_w);
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+        compute(s);
+      }
+    }
+  }
+
+  // ------------------------------------------------ epilogue
+  const int col_in = lane & 15;
+  if constexpr (SWIGLU) {
+    // SwiGLU, then MX e2m1 quantisation in groups of 32 output columns (gate
+    // tiles j, j+1 of one row: 2 values in each of the row's 16 lanes); two
+    // codes per byte, the even column's in the low nibble (its lane takes the
+    // odd neighbour's code by a shuffle).
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) continue;  // wave-uniform
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+#pragma unroll
+        for (int j = 0; j < NTW / 2; j += 2) {
+          const float u0 = silu(acc[i][j][v]) * acc[i][j + NTW / 2][v];
+          const float u1 = silu(acc[i][j + 1][v]) * acc[i][j + 1 + NTW / 2][v];
+          float amax = fmaxf(fabsf(u0), fabsf(u1));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
+          const uint32_t code = static_cast<uint32_t>(e > 2 ? e - 2 : 0);
+          const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code)
+          const uint32_t n0 = f32_to_e2m1(u0 * inv);
+          const uint32_t n1 = f32_to_e2m1(u1 * inv);
+          const uint32_t m0 = __shfl_xor(n0, 1, 64);
+          const uint32_t m1 = __shfl_xor(n1, 1, 64);
+          if (row < row_end) {
+            const int c0 = nt * (BN / 2) + bcol(j);  // first column of the group
+            uint8_t* orow = reinterpret_cast<uint8_t*>(obase) + static_cast<size_t>(row) * (g.Nout / 2);
+            if ((col_in & 1) == 0) {
+              orow[(c0 + col_in) / 2] = static_cast<uint8_t>(n0 | (m0 << 4));
+              orow[(c0 + 16 + col_in) / 2] = static_cast<uint8_t>(n1 | (m1 << 4));
+            }
+            if (col_in == 0)
+              osc8[static_cast<size_t>(row) * (g.Nout / 32) + c0 / 32] = static_cast<uint8_t>(code);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+        if (row >= row_end) continue;
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const int ncol = nt * BN + bcol(j) + col_in;
+          reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
+              f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+}
+
 // tile_off[e+1] = tile_off[e] + ceil(rows_e / BM), segment E = shared (T rows).
 __global__ __launch_bounds__(kMaxExperts) void tile_offsets_kernel(const int32_t* __restrict__ offsets,
                                                                    int E, int T_shared, int BM,
@@ -1068,7 +1352,10 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
 
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
-  if constexpr (STAGES >= 3) {
+  if constexpr (PREC == MOE_PREC_MXFP4) {
+    hipLaunchKernelGGL((grouped_gemm_mx4_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
+                       dim3(ub_m * g.n_tiles), dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+  } else if constexpr (STAGES >= 3) {
     // bf16: chunks of two m-tiles' worth of items are dealt to the XCDs in
     // turn, which evens out the XCDs' loads when a few segments (the shared
     // expert, hot experts) hold many m-tiles; e4m3 keeps contiguous ranges.
@@ -1095,9 +1382,10 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int ub_m = (rows + BM - 1) / BM + (a.E < rows ? a.E : rows) + (T_sh + BM - 1) / BM;
-  constexpr bool MX = PREC == MOE_PREC_MXFP8;
-  constexpr bool Q8 = PREC == MOE_PREC_FP8 || MX;  // e4m3 activation codes into Linear2
-  const size_t arow_bytes = static_cast<size_t>(a.f) * (Q8 ? 1 : 2);
+  constexpr bool MX = PREC == MOE_PREC_MXFP8 || PREC == MOE_PREC_MXFP4;
+  constexpr bool Q8 = PREC == MOE_PREC_FP8 || MX;  // quantised activation codes into Linear2
+  // bytes of one row of the SwiGLU output as Linear2 reads it
+  const size_t arow_bytes = PREC == MOE_PREC_MXFP4 ? a.f / 2 : static_cast<size_t>(a.f) * (Q8 ? 1 : 2);
 
   GemmArgs g1{};
   g1.A = a.Xp;
@@ -1110,7 +1398,7 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   g1.w_scale_sh = a.w.ws1_scale;
   if (MX) {  // the SwiGLU output is MX-quantised by the Linear1 epilogue
     g1.out = a.Aq;
-    g1.out_sh = static_cast<char*>(a.Aq) + static_cast<size_t>(rows) * a.f;
+    g1.out_sh = static_cast<char*>(a.Aq) + static_cast<size_t>(rows) * arow_bytes;
     g1.out_scale = a.a_scale;
     g1.out_scale_sh = static_cast<char*>(a.a_scale) + static_cast<size_t>(rows) * (a.f / 32);
   } else {
@@ -1215,6 +1503,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // MX: the 3-stage DMA pipeline at every batch size (the 16-row decode
   // kernel has no per-group scales)
   if (a.precision == MOE_PREC_MXFP8) return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
+  if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 4>(a, stream);
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 

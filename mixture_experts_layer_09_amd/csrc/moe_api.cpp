@@ -17,7 +17,7 @@ int check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->topk > s->experts || s->topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
-  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_MXFP4) return MOE_ERR_INVALID_ARG;
   if (s->experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->inter % (s->precision >= MOE_PREC_FP8 ? 128 : 64) != 0) return MOE_ERR_UNSUPPORTED;
@@ -45,7 +45,7 @@ T* at(void* ws, size_t off) {
 
 int check_weights(const moe_shape* s, const moe_expert_weights* w) {
   if (!w || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
-  const bool scaled = s->precision == MOE_PREC_FP8 || s->precision == MOE_PREC_MXFP8;
+  const bool scaled = s->precision >= MOE_PREC_FP8;
   if (scaled && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
   if (s->has_shared) {
     if (!w->Ws1 || !w->Ws2) return MOE_ERR_INVALID_ARG;

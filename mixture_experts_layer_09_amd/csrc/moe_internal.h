@@ -49,6 +49,16 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
   return static_cast<uint32_t>(w);
 }
 
+// fp32 -> OCP e2m1 (FP4) code in the low 4 bits: nearest of 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6 with ties to the even code (the midpoints 0.25, 1.25, 2.5, 5
+// round down, 0.75, 1.75, 3.5 round up), saturating at 6; the sign is bit 3.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // ---------------------------------------------------------------- wave ops
@@ -72,10 +82,15 @@ constexpr int kMaxTopk = 16;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline size_t act_bytes(int precision) { return precision == MOE_PREC_F32 ? 4 : 2; }
-inline size_t xp_bytes(int precision) {
-  return precision == MOE_PREC_F32 ? 4 : (precision == MOE_PREC_BF16 ? 2 : 1);
+// bytes of one dispatched (or quantised) row of n elements
+inline size_t xrow_bytes(int precision, size_t n) {
+  if (precision == MOE_PREC_F32) return 4 * n;
+  if (precision == MOE_PREC_BF16) return 2 * n;
+  return precision == MOE_PREC_MXFP4 ? n / 2 : n;
 }
-inline bool is_mx(int precision) { return precision == MOE_PREC_MXFP8; }
+inline bool is_mx(int precision) {
+  return precision == MOE_PREC_MXFP8 || precision == MOE_PREC_MXFP4;
+}
 // bytes of the activation scales of one row of `n` elements
 inline size_t row_scale_bytes(int precision, size_t n) {
   return is_mx(precision) ? n / 32 : (precision == MOE_PREC_FP8 ? 4 : 0);
@@ -120,14 +135,14 @@ inline Layout make_layout(const moe_shape& s) {
   L.offsets = take((E + 1) * 4);
   L.dst_row = take(rows * 4);
   L.src_tok = take(rows * 4);
-  L.Xp = take(rows * h * xp_bytes(s.precision));
-  const bool q8 = s.precision >= MOE_PREC_FP8;  // e4m3 activations (A8W8 or MX)
+  L.Xp = take(rows * xrow_bytes(s.precision, h));
+  const bool q8 = s.precision >= MOE_PREC_FP8;  // quantised activations (A8W8 or MX)
   const bool mx = is_mx(s.precision);
   L.xp_scale = take(rows * row_scale_bytes(s.precision, h));
-  L.Xq = take(q8 ? T * h : 0);
+  L.Xq = take(q8 ? T * xrow_bytes(s.precision, h) : 0);
   L.x_scale = take(T * row_scale_bytes(s.precision, h));
   L.A = take(mx ? 0 : arows * f * (q8 ? 4 : act_bytes(s.precision)));
-  L.Aq = take(q8 ? arows * f : 0);
+  L.Aq = take(q8 ? arows * xrow_bytes(s.precision, f) : 0);
   L.a_scale = take(arows * row_scale_bytes(s.precision, f));
   L.Yp = take(rows * h * act_bytes(s.precision));
   L.Ys = take(s.has_shared ? T * h * act_bytes(s.precision) : 0);

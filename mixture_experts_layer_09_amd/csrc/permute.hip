@@ -135,13 +135,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     dst_row[i] = d;
     s_dst[tid] = d;
   }
-  if (PREC == MOE_PREC_MXFP8) {
+  if (PREC == MOE_PREC_MXFP8 || PREC == MOE_PREC_MXFP4) {
     // MX: groups of 32 along h share an E8M0 scale, exponent floor(log2
-    // amax) - 8; 4 consecutive threads hold a group's 32 values (8 each) and
-    // exchange their amax by xor shuffles; codes = RNE_sat(x * 2^(127-code)).
+    // amax) - emax (8 for e4m3, 2 for e2m1); 4 consecutive threads hold a
+    // group's 32 values (8 each) and exchange their amax by xor shuffles;
+    // codes = RNE_sat(x * 2^(127-code)).  e2m1 codes go two per byte.
+    constexpr bool F4 = PREC == MOE_PREC_MXFP4;
+    constexpr int EMAX = F4 ? 2 : 8;
+    const size_t rb = F4 ? h / 2 : h;  // bytes of a quantised row
     __syncthreads();
     const uint16_t* xr = static_cast<const uint16_t*>(X) + static_cast<size_t>(t) * h;
-    uint8_t* xq = static_cast<uint8_t*>(Xq) + static_cast<size_t>(t) * h;
+    uint8_t* xq = static_cast<uint8_t*>(Xq) + static_cast<size_t>(t) * rb;
     uint8_t* xs = static_cast<uint8_t*>(x_scale_v) + static_cast<size_t>(t) * (h / 32);
     uint8_t* xps = static_cast<uint8_t*>(xp_scale_v);
     // the 4 threads of a group always make the same trips (h % 32 == 0)
@@ -160,18 +164,34 @@ __global__ __launch_bounds__(256) void scatter_kernel(
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
       const int e = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF);
-      const uint32_t code = static_cast<uint32_t>(e > 8 ? e - 8 : 0);
+      const uint32_t code = static_cast<uint32_t>(e > EMAX ? e - EMAX : 0);
       const float inv = __uint_as_float((254u - code) << 23);  // 2^(127 - code)
-      const uint2 qv = make_uint2(f32x4_to_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
-                                  f32x4_to_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
-      *reinterpret_cast<uint2*>(xq + c) = qv;
       const bool lead = (tid & 3) == 0;
       if (lead) xs[c / 32] = static_cast<uint8_t>(code);
-      for (int j = 0; j < k; ++j) {
-        const int d = s_dst[j];
-        if (d < 0) continue;
-        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Xp) + static_cast<size_t>(d) * h + c) = qv;
-        if (lead) xps[static_cast<size_t>(d) * (h / 32) + c / 32] = static_cast<uint8_t>(code);
+      if constexpr (F4) {
+        uint32_t qv = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) qv |= f32_to_e2m1(f[q] * inv) << (4 * q);
+        *reinterpret_cast<uint32_t*>(xq + c / 2) = qv;
+        for (int j = 0; j < k; ++j) {
+          const int d = s_dst[j];
+          if (d < 0) continue;
+          *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(Xp) + static_cast<size_t>(d) * rb +
+                                       c / 2) = qv;
+          if (lead) xps[static_cast<size_t>(d) * (h / 32) + c / 32] = static_cast<uint8_t>(code);
+        }
+      } else {
+        const uint2 qv =
+            make_uint2(f32x4_to_e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv),
+                       f32x4_to_e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv));
+        *reinterpret_cast<uint2*>(xq + c) = qv;
+        for (int j = 0; j < k; ++j) {
+          const int d = s_dst[j];
+          if (d < 0) continue;
+          *reinterpret_cast<uint2*>(static_cast<uint8_t*>(Xp) + static_cast<size_t>(d) * rb + c) =
+              qv;
+          if (lead) xps[static_cast<size_t>(d) * (h / 32) + c / 32] = static_cast<uint8_t>(code);
+        }
       }
     }
   } else if (PREC != MOE_PREC_FP8) {
@@ -260,6 +280,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_BF16>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
                          a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
                          a.xp_scale, a.Xq, a.x_scale);
+      break;
+    case MOE_PREC_MXFP4:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_MXFP4>, dim3(a.T), dim3(256), 0, stream, a.T,
+                         a.h, a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok,
+                         a.Xp, a.xp_scale, a.Xq, a.x_scale);
       break;
     case MOE_PREC_MXFP8:
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_MXFP8>, dim3(a.T), dim3(256), 0, stream, a.T,

@@ -12,6 +12,7 @@ Workloads (T tokens, hidden h, E routed experts, top-k, inter f, shared S):
                                                  Zipf(0.8) expert load
   v4pro_fp8          as v4pro_bf16, A8W8 e4m3 experts, bf16 output
   v4pro_mxfp8        as v4pro_bf16, MXFP8 experts (e4m3, group-32 E8M0 scales)
+  v4pro_mxfp4        as v4pro_bf16, MXFP4 experts (e2m1, group-32 E8M0 scales)
   decode_hash_bf16   128, 7168, 384, 6, 3072, 1  token-id hash routing
   decode_score_bf16  128, v4pro router
   ep_share_bf16      4096, 7168, 6, 6, 3072, 0   one GPU's expert-parallel share
@@ -28,7 +29,10 @@ channel: scale = max|W[:, n]| / 448, codes = torch's float8_e4m3fn cast of
 W / scale.  MXFP8 expert weights are quantised offline in groups of 32 rows
 (K) per column: E8M0 scale code = floor(log2 max|W|) - 8 + 127 (0 for a zero
 group), codes = torch's float8_e4m3fn cast of W * 2^(127 - code) clamped to
-+-448.  Hash tables hold k distinct expert ids per token id.
++-448.  MXFP4 weights the same way with exponent floor(log2 max|W|) - 2 and
+e2m1 codes (nearest even, saturating at 6), stored K-contiguous: codes
+[N, K/2] (element 2i of a row in the low nibble), scales [N, K/32].  Hash
+tables hold k distinct expert ids per token id.
 """
 from __future__ import annotations
 
@@ -84,6 +88,8 @@ WORKLOADS = {
         Workload("v4pro_fp8", 8192, 7168, 384, 6, 3072, 1, "fp8", alpha=2.5, beta_range=0.1,
                  zipf=True, family="v4pro"),
         Workload("v4pro_mxfp8", 8192, 7168, 384, 6, 3072, 1, "mxfp8", alpha=2.5,
+                 beta_range=0.1, zipf=True, family="v4pro"),
+        Workload("v4pro_mxfp4", 8192, 7168, 384, 6, 3072, 1, "mxfp4", alpha=2.5,
                  beta_range=0.1, zipf=True, family="v4pro"),
         Workload("decode_hash_bf16", 128, 7168, 384, 6, 3072, 1, "bf16", alpha=2.5, hash=True,
                  family="v4pro"),
@@ -164,15 +170,48 @@ def quantize_weight_mx_e4m3(W: torch.Tensor):
     return q, code.to(torch.uint8)
 
 
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def quantize_weight_mx_e2m1(W: torch.Tensor):
+    """Offline MXFP4 quantisation of a [K, N] weight (K a multiple of 32),
+    stored K-contiguous: code pairs [N, K/2] uint8 and E8M0 scale codes
+    [N, K/32] uint8 (see the module docstring)."""
+    Wt = W.float().t().contiguous()                  # [N, K]
+    N, K = Wt.shape
+    g = Wt.reshape(N, K // 32, 32)
+    amax = g.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)
+    code = torch.where(amax > 0, (ex - 1 - 2 + 127).clamp(0, 254), torch.zeros_like(ex))
+    v = torch.ldexp(g, (127 - code).unsqueeze(2).to(torch.float32)).reshape(N, K)
+    a = v.abs()
+    mag = torch.zeros_like(a, dtype=torch.uint8)
+    # nearest of 0, .5, 1, 1.5, 2, 3, 4, 6; midpoints go to the even code
+    for i, m in enumerate(_E2M1_MIDPOINTS):
+        up = (a > m) if i % 2 == 0 else (a >= m)
+        mag += up.to(torch.uint8)
+    nib = mag | (torch.signbit(v).to(torch.uint8) << 3)
+    packed = (nib[:, 0::2] | (nib[:, 1::2] << 4)).to(torch.uint8)
+    return packed, code.to(torch.uint8)
+
+
 def _expert_weights(wl: Workload, seed, device, act_dtype):
     """W1 [E,h,2f], W2 [E,f,h] (bf16/fp32), generated one expert at a time."""
     E, h, f = wl.experts, wl.hidden, wl.inter
     fp8 = wl.precision == "fp8"
     mx = wl.precision == "mxfp8"
+    mx4 = wl.precision == "mxfp4"
     wdt = torch.float8_e4m3fn if (fp8 or mx) else act_dtype
-    W1 = torch.empty((E, h, 2 * f), dtype=wdt, device=device)
-    W2 = torch.empty((E, f, h), dtype=wdt, device=device)
+    if mx4:   # K-contiguous e2m1 pairs
+        W1 = torch.empty((E, 2 * f, h // 2), dtype=torch.uint8, device=device)
+        W2 = torch.empty((E, h, f // 2), dtype=torch.uint8, device=device)
+    else:
+        W1 = torch.empty((E, h, 2 * f), dtype=wdt, device=device)
+        W2 = torch.empty((E, f, h), dtype=wdt, device=device)
     s1 = s2 = None
+    if mx4:
+        s1 = torch.empty((E, 2 * f, h // 32), dtype=torch.uint8, device=device)
+        s2 = torch.empty((E, h, f // 32), dtype=torch.uint8, device=device)
     if fp8:
         s1 = torch.empty((E, 2 * f), dtype=torch.float32, device=device)
         s2 = torch.empty((E, h), dtype=torch.float32, device=device)
@@ -184,7 +223,10 @@ def _expert_weights(wl: Workload, seed, device, act_dtype):
                     dtype=act_dtype)
         w2 = normal((f, h), 1.0 / math.sqrt(f), seed=seed, name=f"W2.{e}", device=device,
                     dtype=act_dtype)
-        if mx:
+        if mx4:
+            W1[e], s1[e] = quantize_weight_mx_e2m1(w1)
+            W2[e], s2[e] = quantize_weight_mx_e2m1(w2)
+        elif mx:
             W1[e], s1[e] = quantize_weight_mx_e4m3(w1)
             W2[e], s2[e] = quantize_weight_mx_e4m3(w2)
         elif fp8:

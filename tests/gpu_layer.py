@@ -29,8 +29,9 @@ class GpuLayer:
         self.weights = moe.make_weights(inp["W1"], inp["W2"], inp["w1_scale"], inp["w2_scale"],
                                         inp["Ws1"], inp["Ws2"], inp["ws1_scale"], inp["ws2_scale"])
         self.dev = inp["X"].device
-        self.mx = wl.precision == "mxfp8"
-        self.fp8 = wl.precision in ("fp8", "mxfp8")   # e4m3 activation codes
+        self.mx = wl.precision in ("mxfp8", "mxfp4")
+        self.fp4 = wl.precision == "mxfp4"
+        self.fp8 = wl.precision in ("fp8", "mxfp8", "mxfp4")   # quantised activation codes
         self.out_dtype = torch.float32 if wl.precision == "fp32" else torch.bfloat16
         self.xp_dtype = torch.float8_e4m3fn if self.fp8 else self.out_dtype
 
@@ -53,11 +54,16 @@ class GpuLayer:
         n = wl.T * wl.topk
         o = dict(counts=self._i32(wl.experts), offsets=self._i32(wl.experts + 1),
                  dst_row=self._i32(n), src_tok=self._i32(n),
-                 Xp=torch.empty((n, wl.hidden), dtype=self.xp_dtype, device=self.dev))
+                 Xp=(torch.empty((n, wl.hidden // 2), dtype=torch.uint8, device=self.dev)
+                     if self.fp4 else
+                     torch.empty((n, wl.hidden), dtype=self.xp_dtype, device=self.dev)))
         if self.mx:   # E8M0 bytes per group of 32 along hidden
             g = wl.hidden // 32
             o.update(xp_scale=torch.empty((n, g), dtype=torch.uint8, device=self.dev),
-                     Xq=torch.empty((wl.T, wl.hidden), dtype=torch.float8_e4m3fn, device=self.dev),
+                     Xq=(torch.empty((wl.T, wl.hidden // 2), dtype=torch.uint8, device=self.dev)
+                         if self.fp4 else
+                         torch.empty((wl.T, wl.hidden), dtype=torch.float8_e4m3fn,
+                                     device=self.dev)),
                      x_scale=torch.empty((wl.T, g), dtype=torch.uint8, device=self.dev))
         elif self.fp8:
             o.update(xp_scale=self._f32(n),

@@ -24,9 +24,9 @@ from tests.helpers import bits, f64, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
 DELTA = 1e-5
-FULL = ["v4pro_bf16", "v4pro_fp8", "v4pro_mxfp8", "llama_bf16", "decode_hash_bf16", "decode_score_bf16",
+FULL = ["v4pro_bf16", "v4pro_fp8", "v4pro_mxfp8", "v4pro_mxfp4", "llama_bf16", "decode_hash_bf16", "decode_score_bf16",
         "ep_share_bf16"]
 
 
@@ -104,9 +104,12 @@ def test_full_size_forward(name):
     rows = np.linspace(0, wl.T * wl.topk - 1, 64).astype(np.int64)
     Xp_rows = bits(p["Xp"][torch.from_numpy(rows).cuda()])
     src = d["src_tok"][rows]
-    if wl.precision == "mxfp8":
+    if wl.precision in ("mxfp8", "mxfp4"):
+        fmt = "e4m3" if wl.precision == "mxfp8" else "e2m1"
         q, s = oracle.mx_quantize(inp["X"][torch.from_numpy(src).long().cuda()].double()
-                                  .cpu().numpy(), "e4m3")
+                                  .cpu().numpy(), fmt)
+        if fmt == "e2m1":
+            q = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
         assert np.array_equal(Xp_rows, q)
         assert np.array_equal(bits(p["xp_scale"])[rows], s)
     elif wl.precision == "fp8":

@@ -26,7 +26,7 @@ from tests.helpers import bits, f64, oracle_layer, oracle_route, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
 DELTA = 1e-5
 
 CASES = {
@@ -35,6 +35,7 @@ CASES = {
     "v4pro_small": ("v4pro_bf16", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_fp8_small": ("v4pro_fp8", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_mxfp8_small": ("v4pro_mxfp8", dict(T=256, hidden=512, experts=64, inter=256)),
+    "v4pro_mxfp4_small": ("v4pro_mxfp4", dict(T=256, hidden=512, experts=64, inter=256)),
     "decode_hash_small": ("decode_hash_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "decode_score_small": ("decode_score_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "ep_share_small": ("ep_share_bf16", dict(T=600, hidden=256, inter=128)),
@@ -106,7 +107,14 @@ def test_permute_bit_exact(name):
     d = oracle.dispatch(r["ids"], wl.experts)
     for k in ("counts", "offsets", "dst_row", "src_tok"):
         assert np.array_equal(p[k].cpu().numpy(), d[k]), k
-    if wl.precision == "mxfp8":
+    if wl.precision == "mxfp4":
+        q, s = oracle.mx_quantize(cpu["X"].double().numpy(), "e2m1")
+        q = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)   # two codes per byte
+        assert np.array_equal(bits(p["x_scale"]), s)
+        assert np.array_equal(bits(p["Xq"]), q)
+        assert np.array_equal(bits(p["Xp"]), q[d["src_tok"]])
+        assert np.array_equal(bits(p["xp_scale"]), s[d["src_tok"]])
+    elif wl.precision == "mxfp8":
         # bf16 inputs make the MX decision exact in any precision
         q, s = oracle.mx_quantize(cpu["X"].double().numpy(), "e4m3")
         assert np.array_equal(bits(p["x_scale"]), s)
@@ -192,7 +200,7 @@ def test_forward(name):
 
 
 @pytest.mark.parametrize("name", ["v4pro_small", "tiny_fp32", "v4pro_fp8_small",
-                                  "v4pro_mxfp8_small"])
+                                  "v4pro_mxfp8_small", "v4pro_mxfp4_small"])
 def test_forward_with_given_routing(name):
     """The mega_moe form: expert ids and weights are inputs (no router)."""
     _need_gpu()
@@ -219,6 +227,7 @@ def _edge(base, ids=None, **kw):
 
 @pytest.mark.parametrize("kind", ["one_token", "all_to_one_expert", "k_equals_E", "single_expert",
                                   "fp8_all_to_one", "mxfp8_all_to_one", "mxfp8_decode",
+                                  "mxfp4_all_to_one", "mxfp4_decode",
                                   "decode_one_token"])
 def test_edge_cases(kind):
     _need_gpu()
@@ -233,12 +242,15 @@ def test_edge_cases(kind):
         "mxfp8_all_to_one": ("v4pro_mxfp8", dict(T=300, hidden=256, experts=64, inter=128,
                                                   topk=1, zipf=False)),
         "mxfp8_decode": ("v4pro_mxfp8", dict(T=3, hidden=512, experts=64, inter=256)),
+        "mxfp4_all_to_one": ("v4pro_mxfp4", dict(T=300, hidden=256, experts=64, inter=128,
+                                                  topk=1, zipf=False)),
+        "mxfp4_decode": ("v4pro_mxfp4", dict(T=3, hidden=512, experts=64, inter=256)),
         "decode_one_token": ("decode_hash_bf16", dict(T=1, hidden=256, experts=64, inter=128)),
     }[kind]
     cpu, L = _edge(spec[0], **spec[1])
     wl = cpu["workload"]
     _log(f"[edge] {kind} {wl}")
-    if kind in ("all_to_one_expert", "fp8_all_to_one", "mxfp8_all_to_one"):
+    if kind in ("all_to_one_expert", "fp8_all_to_one", "mxfp8_all_to_one", "mxfp4_all_to_one"):
         ids = np.full((wl.T, 1), 37, np.int32)       # 300 rows: 3 tiles, ragged
         G = np.full((wl.T, 1), 0.75, np.float32)
         Y, _, _ = L.forward(torch.from_numpy(ids).cuda(), torch.from_numpy(G).cuda(), route=False)
