@@ -1010,14 +1010,15 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
   constexpr int MT = WM / 16;
   constexpr int NTW = BN / WAVES_N / 16;
   static_assert(A_INSTS % NW == 0 && B_INSTS % NW == 0, "tiles must split evenly over the waves");
-  static_assert(AS_INSTS + BS_INSTS <= NW, "one scale DMA per wave at most");
+  constexpr int SC_INSTS = AS_INSTS + BS_INSTS;
+  constexpr int SC_OPS = (SC_INSTS + NW - 1) / NW;  // scale DMAs per wave (dealt round-robin)
   static_assert(!SWIGLU || (NTW / 2) % 2 == 0, "MX SwiGLU epilogue: whole 32-column groups");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: wave-uniform choices
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
   const int E = g.E;
@@ -1087,23 +1088,28 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
   }
   const char* as_base = uniform_ptr(reinterpret_cast<const char*>(asc8) + static_cast<size_t>(row0) * sc_ld);
   const char* bs_base = uniform_ptr(reinterpret_cast<const char*>(wsc8));
-  uint32_t sc_voff = 0;
-  int sc_lds = 0;
-  const bool a_sc = wave < AS_INSTS;
-  const bool b_sc = wave >= AS_INSTS && wave < AS_INSTS + BS_INSTS;
-  if (a_sc) {
-    sc_voff = static_cast<uint32_t>(min(wave * 64 + lane, row_end - 1 - row0)) *
-              static_cast<uint32_t>(sc_ld);
-    sc_lds = AS_OFF + wave * 256;
-  } else if (b_sc) {
-    sc_voff = static_cast<uint32_t>(wrow((wave - AS_INSTS) * 64 + lane)) *
-              static_cast<uint32_t>(sc_ld);
-    sc_lds = BS_OFF + (wave - AS_INSTS) * 256;
+  // scale DMA q of this wave is instruction q * NW + wave: A rows 64 idx ..
+  // for idx < AS_INSTS, else B rows 64 (idx - AS_INSTS) ..
+  uint32_t sc_voff[SC_OPS];
+  int sc_lds[SC_OPS];
+#pragma unroll
+  for (int q = 0; q < SC_OPS; ++q) {
+    const int idx = q * NW + wave;
+    if (idx < AS_INSTS) {
+      sc_voff[q] = static_cast<uint32_t>(min(idx * 64 + lane, row_end - 1 - row0)) *
+                   static_cast<uint32_t>(sc_ld);
+      sc_lds[q] = AS_OFF + idx * 256;
+    } else {
+      const int b = min(idx - AS_INSTS, BS_INSTS - 1);  // (unused past SC_INSTS)
+      sc_voff[q] = static_cast<uint32_t>(wrow(b * 64 + lane)) * static_cast<uint32_t>(sc_ld);
+      sc_lds[q] = BS_OFF + b * 256;
+    }
   }
+  const int sc_ops = min(SC_OPS, max(0, (SC_INSTS - wave + NW - 1) / NW));  // wave-uniform
   // only A blocks holding a valid row are fetched (wave-uniform count)
   const int a_live = __builtin_amdgcn_readfirstlane(
       max(0, min(A_OPS, (rows_valid + 15) / 16 - wave * A_OPS)));
-  const int ops_w = a_live + B_OPS + ((a_sc || b_sc) ? 1 : 0);
+  const int ops_w = a_live + B_OPS + sc_ops;
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
 #pragma unroll
@@ -1114,8 +1120,13 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
     for (int q = 0; q < B_OPS; ++q)
       dma16(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q],
             st + A_BYTES + (wave * B_OPS + q) * 1024);
-    if (a_sc) dma4(as_base + static_cast<size_t>(kt) * 4, sc_voff, st + sc_lds);
-    else if (b_sc) dma4(bs_base + static_cast<size_t>(kt) * 4, sc_voff, st + sc_lds);
+#pragma unroll
+    for (int q = 0; q < SC_OPS; ++q) {
+      if (q >= sc_ops) break;
+      const int idx = q * NW + wave;
+      dma4((idx < AS_INSTS ? as_base : bs_base) + static_cast<size_t>(kt) * 4, sc_voff[q],
+           st + sc_lds[q]);
+    }
   };
 
   f32x4_t acc[MT][NTW];
@@ -1503,7 +1514,8 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // MX: the 3-stage DMA pipeline at every batch size (the 16-row decode
   // kernel has no per-group scales)
   if (a.precision == MOE_PREC_MXFP8) return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
-  if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 4>(a, stream);
+  // MXFP4: 128 x 256 tiles on 4 waves, 3-stage ring (76.5 KB), two blocks per CU
+  if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 2, 3>(a, stream);
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 
