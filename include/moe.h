@@ -63,6 +63,9 @@
  *                      stores them: W1 [E, 2*inter, hidden/2], W2 [E, hidden,
  *                      inter/2], Ws1 [2*inter, hidden/2], Ws2 [hidden,
  *                      inter/2]; Xp [rows, hidden/2], Xq [T, hidden/2].
+ *   - Alignment: X, Wg, the weights and scales, Xp, Xq and their scales, Yp,
+ *     Ys and Y are read or written with 16-byte vector accesses and must be
+ *     16-byte aligned (MOE_ERR_INVALID_ARG otherwise; allocations are).
  *   - Shape limits: 1 <= T; 1 <= topk <= min(16, experts) (the mega_moe
  *     constraint on top-k); experts <= 512; hidden a multiple of 128 and
  *     inter a multiple of 64 (the kernels' tile granularity); for FP8,

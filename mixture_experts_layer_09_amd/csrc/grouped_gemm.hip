@@ -982,25 +982,39 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 // scenario).  Both operands are K-contiguous rows: token rows [rows, K/2] and
 // weights [N, K/2] as the page stores them, so weight fragments are read the
 // way token-row fragments are, with no transposing LDS read.  A K-stage is
-// 128 elements, 64 bytes of a row; both tiles go to LDS by DMA with the
-// 64-byte-row swizzle chunk ^ ((row >> 2) & 3) (a 16-lane fragment read of
-// 16 consecutive rows then covers all banks once).  Each stage also carries
-// the rows' E8M0 scales of its 4 K-groups ([BM][4] and [BN][4], one dword
-// per row).  For 4-bit operands the 16x16x128 scaled MFMA reads lane group
+// KS x 128 elements, KS x 64 bytes of a row: with KS = 2 every row's DMA
+// covers one whole 128-byte line, so no line is fetched for half its bytes
+// and left in L2 for the next stage.  Both tiles go to LDS by DMA with a
+// 16-byte-chunk swizzle (chunk ^ ((row >> 2) & 3) for 64-byte rows,
+// chunk ^ ((row >> 1) & 7) for 128-byte rows), so a 16-lane fragment read of
+// 16 consecutive rows covers all banks once.  Each stage also carries the
+// rows' E8M0 scales, one [rows][4] plane (one dword per row) per 128-value
+// K-step.  For 4-bit operands the 16x16x128 scaled MFMA reads lane group
 // g's 16 bytes as K 32g .. 32g+31, low nibble first, and lane group g's scale
 // covers exactly those (measured on the GPU with one-hot operands), so a
 // lane's data and scale are one MX group.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES, int KS, bool SW>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
 void grouped_gemm_mx4_kernel(GemmArgs g) {
+  static_assert(KS == 1 || KS == 2, "one or two 128-value K-steps per stage");
+  constexpr int WSTG = 4 / KS;  // SW: stages per 512-value scale window
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int ROWB = 64;  // bytes of one row's K-stage
+  constexpr int ROWB = 64 * KS;     // bytes of one row's K-stage (KS = 2: a whole 128-byte line)
+  constexpr int CH = ROWB / 16;     // 16-byte chunks of a row's K-stage
+  constexpr int RPI = 1024 / ROWB;  // rows per 16-byte-lane DMA
   constexpr int A_BYTES = BM * ROWB;
   constexpr int B_BYTES = BN * ROWB;
+  // scales, SW = false: one [rows][4] plane per K-step inside each stage;
+  // SW = true: 512-value windows, [BM][16] then [BN][16] bytes, in two
+  // buffers after the ring, each row's 16 bytes fetched by one 16-byte lane
   constexpr int AS_OFF = A_BYTES + B_BYTES;
-  constexpr int BS_OFF = AS_OFF + BM * 4;
-  constexpr int STAGE = BS_OFF + BN * 4;
-  constexpr int A_INSTS = A_BYTES / 1024;  // 16 rows per 16-byte-lane DMA
+  constexpr int BS_OFF = AS_OFF + KS * BM * 4;
+  constexpr int STAGE = SW ? A_BYTES + B_BYTES : BS_OFF + KS * BN * 4;
+  constexpr int SCW = (BM + BN) * 16;     // one scale window buffer
+  constexpr int SC_BASE = STAGES * STAGE;
+  constexpr int W_INSTS = (BM + BN) / 64;  // 16-byte-lane DMAs per window
+  constexpr int W_OPS = (W_INSTS + NW - 1) / NW;
+  constexpr int A_INSTS = A_BYTES / 1024;
   constexpr int B_INSTS = B_BYTES / 1024;
   constexpr int AS_INSTS = BM / 64;        // 64 rows per 4-byte-lane DMA
   constexpr int BS_INSTS = BN / 64;
@@ -1010,11 +1024,12 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
   constexpr int MT = WM / 16;
   constexpr int NTW = BN / WAVES_N / 16;
   static_assert(A_INSTS % NW == 0 && B_INSTS % NW == 0, "tiles must split evenly over the waves");
-  constexpr int SC_INSTS = AS_INSTS + BS_INSTS;
+  constexpr int SC_PER = AS_INSTS + BS_INSTS;       // scale DMAs of one K-step
+  constexpr int SC_INSTS = KS * SC_PER;
   constexpr int SC_OPS = (SC_INSTS + NW - 1) / NW;  // scale DMAs per wave (dealt round-robin)
   static_assert(!SWIGLU || (NTW / 2) % 2 == 0, "MX SwiGLU epilogue: whole 32-column groups");
 
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + (SW ? 2 * SCW : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1057,7 +1072,9 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
   const int rows_valid = min(BM, row_end - row0);
   const int mt_live =
       __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
-  auto swz = [](int r) { return (r >> 2) & 3; };
+  // 16-byte chunk swizzle: the 16 rows of one fragment read land on distinct
+  // bank groups (4 rows of 64 bytes, or 2 rows of 128 bytes, span all banks)
+  auto swz = [](int r) { return KS == 1 ? (r >> 2) & 3 : (r >> 1) & 7; };
   // weight row of LDS B row nl (SwiGLU tiles: BN/2 gate rows, then the
   // matching BN/2 up rows)
   auto wrow = [&](int nl) {
@@ -1065,15 +1082,15 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
     return nt * BN + nl;
   };
 
-  // DMA sources (wave-uniform base + 32-bit lane offset; K-stage offset kt*64
-  // for data, kt*4 for scales, added per stage)
+  // DMA sources (wave-uniform base + 32-bit lane offset; K-stage offset
+  // kt*ROWB for data, kt*4*KS for scales, added per stage)
   const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * rowb);
   uint32_t a_voff[A_OPS];
 #pragma unroll
   for (int q = 0; q < A_OPS; ++q) {
     const int blk = wave * A_OPS + q;
-    const int r = blk * 16 + lane / 4;
-    const int c = (lane % 4) ^ swz(r);
+    const int r = blk * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz(r);
     a_voff[q] = static_cast<uint32_t>(min(r, row_end - 1 - row0)) * static_cast<uint32_t>(rowb) +
                 c * 16;
   }
@@ -1082,36 +1099,67 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < B_OPS; ++q) {
     const int blk = wave * B_OPS + q;
-    const int r = blk * 16 + lane / 4;
-    const int c = (lane % 4) ^ swz(r);
+    const int r = blk * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz(r);
     b_voff[q] = static_cast<uint32_t>(wrow(r)) * static_cast<uint32_t>(rowb) + c * 16;
   }
   const char* as_base = uniform_ptr(reinterpret_cast<const char*>(asc8) + static_cast<size_t>(row0) * sc_ld);
   const char* bs_base = uniform_ptr(reinterpret_cast<const char*>(wsc8));
-  // scale DMA q of this wave is instruction q * NW + wave: A rows 64 idx ..
-  // for idx < AS_INSTS, else B rows 64 (idx - AS_INSTS) ..
+  // scale DMA q of this wave is instruction idx = q * NW + wave, of K-step
+  // ks = idx / SC_PER; within it, j = idx % SC_PER: A rows 64 j .. for
+  // j < AS_INSTS, else B rows 64 (j - AS_INSTS) ..
   uint32_t sc_voff[SC_OPS];
   int sc_lds[SC_OPS];
+  bool sc_a[SC_OPS];
 #pragma unroll
   for (int q = 0; q < SC_OPS; ++q) {
-    const int idx = q * NW + wave;
-    if (idx < AS_INSTS) {
-      sc_voff[q] = static_cast<uint32_t>(min(idx * 64 + lane, row_end - 1 - row0)) *
-                   static_cast<uint32_t>(sc_ld);
-      sc_lds[q] = AS_OFF + idx * 256;
+    const int idx = min(q * NW + wave, SC_INSTS - 1);  // (unused past SC_INSTS)
+    const int ks = idx / SC_PER, j = idx % SC_PER;
+    sc_a[q] = j < AS_INSTS;
+    if (j < AS_INSTS) {
+      sc_voff[q] = static_cast<uint32_t>(min(j * 64 + lane, row_end - 1 - row0)) *
+                       static_cast<uint32_t>(sc_ld) + 4 * ks;
+      sc_lds[q] = AS_OFF + ks * BM * 4 + j * 256;
     } else {
-      const int b = min(idx - AS_INSTS, BS_INSTS - 1);  // (unused past SC_INSTS)
-      sc_voff[q] = static_cast<uint32_t>(wrow(b * 64 + lane)) * static_cast<uint32_t>(sc_ld);
-      sc_lds[q] = BS_OFF + b * 256;
+      const int b = j - AS_INSTS;
+      sc_voff[q] = static_cast<uint32_t>(wrow(b * 64 + lane)) * static_cast<uint32_t>(sc_ld) + 4 * ks;
+      sc_lds[q] = BS_OFF + ks * BN * 4 + b * 256;
     }
   }
-  const int sc_ops = min(SC_OPS, max(0, (SC_INSTS - wave + NW - 1) / NW));  // wave-uniform
+  const int sc_ops = SW ? 0 : min(SC_OPS, max(0, (SC_INSTS - wave + NW - 1) / NW));  // wave-uniform
+  // SW: window DMA q of this wave is instruction idx = q * NW + wave: A rows
+  // 64 idx .. for idx < BM / 64, else B rows 64 (idx - BM / 64) ..
+  uint32_t w_voff[W_OPS];
+  int w_lds[W_OPS];
+  bool w_a[W_OPS];
+#pragma unroll
+  for (int q = 0; q < W_OPS; ++q) {
+    const int idx = min(q * NW + wave, W_INSTS - 1);  // (unused past W_INSTS)
+    w_a[q] = idx < BM / 64;
+    if (idx < BM / 64) {
+      w_voff[q] = static_cast<uint32_t>(min(idx * 64 + lane, row_end - 1 - row0)) *
+                  static_cast<uint32_t>(sc_ld);
+    } else {
+      w_voff[q] = static_cast<uint32_t>(wrow((idx - BM / 64) * 64 + lane)) * static_cast<uint32_t>(sc_ld);
+    }
+    w_lds[q] = idx * 1024;
+  }
+  const int w_ops = SW ? min(W_OPS, max(0, (W_INSTS - wave + NW - 1) / NW)) : 0;  // wave-uniform
   // only A blocks holding a valid row are fetched (wave-uniform count)
   const int a_live = __builtin_amdgcn_readfirstlane(
-      max(0, min(A_OPS, (rows_valid + 15) / 16 - wave * A_OPS)));
-  const int ops_w = a_live + B_OPS + sc_ops;
+      max(0, min(A_OPS, (rows_valid + RPI - 1) / RPI - wave * A_OPS)));
+  const int ops_w = a_live + B_OPS + sc_ops;  // DMAs per stage (SW: + w_ops at window starts)
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
+    if (SW && kt % WSTG == 0) {  // the scale window of stages kt .. kt + WSTG - 1 goes first
+      char* sw = smem + SC_BASE + ((kt / WSTG) & 1) * SCW;
+#pragma unroll
+      for (int q = 0; q < W_OPS; ++q) {
+        if (q >= w_ops) break;
+        dma16((w_a[q] ? as_base : bs_base) + static_cast<size_t>(kt / WSTG) * 16, w_voff[q],
+              sw + w_lds[q]);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < A_OPS; ++q)
       if (q < a_live)
@@ -1123,8 +1171,7 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < SC_OPS; ++q) {
       if (q >= sc_ops) break;
-      const int idx = q * NW + wave;
-      dma4((idx < AS_INSTS ? as_base : bs_base) + static_cast<size_t>(kt) * 4, sc_voff[q],
+      dma4((sc_a[q] ? as_base : bs_base) + static_cast<size_t>(kt) * 4 * KS, sc_voff[q],
            st + sc_lds[q]);
     }
   };
@@ -1148,40 +1195,53 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
   for (int i = 0; i < MT; ++i) {
     const int r = wm * WM + i * 16 + (lane & 15);
     a_off[i] = r * ROWB + ((kg ^ swz(r)) << 4);
-    as_off[i] = AS_OFF + r * 4 + kg;
+    as_off[i] = SW ? SC_BASE + r * 16 + kg : AS_OFF + r * 4 + kg;
   }
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int r = bcol(j) + (lane & 15);
     b_off[j] = A_BYTES + r * ROWB + ((kg ^ swz(r)) << 4);
-    bs_off[j] = BS_OFF + r * 4 + kg;
+    bs_off[j] = SW ? SC_BASE + BM * 16 + r * 16 + kg : BS_OFF + r * 4 + kg;
   }
 
-  auto compute = [&](int slot) {
+  // K-step ks of a stage: logical chunks 4 ks .. 4 ks + 3 of the row, i.e. the
+  // fragment offset with bit 6 flipped (rows are 128 bytes when KS = 2)
+  auto compute = [&](int slot, int kt) {
     if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
-    i32x4_t bfr[NTW], af[MT];
-    int sb[NTW], sa[MT];
+    // scale bytes of K-step ks: SW: window buffer (kt / WSTG) % 2, byte
+    // 4 KS (kt % WSTG) + 4 ks + kg of the row; else plane ks of the stage
+    const char* sc = SW ? smem + ((kt / WSTG) & 1) * SCW + (kt % WSTG) * 4 * KS : st;
+    constexpr int SA_STEP = SW ? 4 : BM * 4, SB_STEP = SW ? 4 : BN * 4;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bfr[j] = *reinterpret_cast<const i32x4_t*>(st + b_off[j]);
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x4_t bfr[NTW], af[MT];
+      int sb[NTW], sa[MT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const i32x4_t*>(st + a_off[i]);
+      for (int j = 0; j < NTW; ++j)
+        bfr[j] = *reinterpret_cast<const i32x4_t*>(st + (b_off[j] ^ (ks << 6)));
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) sb[j] = *reinterpret_cast<const uint8_t*>(st + bs_off[j]);
+      for (int i = 0; i < MT; ++i)
+        af[i] = *reinterpret_cast<const i32x4_t*>(st + (a_off[i] ^ (ks << 6)));
 #pragma unroll
-    for (int i = 0; i < MT; ++i) sa[i] = *reinterpret_cast<const uint8_t*>(st + as_off[i]);
+      for (int j = 0; j < NTW; ++j)
+        sb[j] = *reinterpret_cast<const uint8_t*>(sc + bs_off[j] + ks * SB_STEP);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i)
+        sa[i] = *reinterpret_cast<const uint8_t*>(sc + as_off[i] + ks * SA_STEP);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const i32x8_t a8 = {af[i][0], af[i][1], af[i][2], af[i][3], 0, 0, 0, 0};
-        const i32x8_t b8 = {bfr[j][0], bfr[j][1], bfr[j][2], bfr[j][3], 0, 0, 0, 0};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
-                                                                     sa[i], 0, sb[j]);
-      }
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const i32x8_t a8 = {af[i][0], af[i][1], af[i][2], af[i][3], 0, 0, 0, 0};
+          const i32x8_t b8 = {bfr[j][0], bfr[j][1], bfr[j][2], bfr[j][3], 0, 0, 0, 0};
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b8, acc[i][j], 4, 4, 0,
+                                                                       sa[i], 0, sb[j]);
+        }
+    }
   };
 
-  const int KT = g.K / 128;
+  const int KT = g.K / (128 * KS);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) issue(s, s);
@@ -1190,11 +1250,15 @@ void grouped_gemm_mx4_kernel(GemmArgs g) {
     for (int s = 0; s < STAGES; ++s) {
       const int kt = k0 + s;
       if (kt < KT) {
+        // stage kt is in LDS once at most the DMAs of the stages issued after
+        // it are in flight (vector memory loads complete in issue order)
         const int after = min(STAGES - 2, KT - 1 - kt);
-        wait_vmcnt_rt(after * ops_w);
+        int pend = 0;
+        for (int d = 1; d <= after; ++d) pend += ops_w + ((SW && (kt + d) % WSTG == 0) ? w_ops : 0);
+        wait_vmcnt_rt(pend);
         __builtin_amdgcn_s_barrier();
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-        compute(s);
+        compute(s, kt);
       }
     }
   }
@@ -1364,8 +1428,16 @@ __global__ void l2_f32_kernel(FfnArgs a, int rows_routed) {
 template <int PREC, int BM, int BN, int WAVES_M, int WAVES_N, bool SWIGLU, int STAGES>
 hipError_t launch_gemm(const GemmArgs& g, int ub_m, hipStream_t stream) {
   if constexpr (PREC == MOE_PREC_MXFP4) {
-    hipLaunchKernelGGL((grouped_gemm_mx4_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES>),
-                       dim3(ub_m * g.n_tiles), dim3(64 * WAVES_M * WAVES_N), 0, stream, g);
+    // scales in 512-value windows (one 16-byte load per row) where K % 512
+    // == 0, else per-stage 4-byte scale loads; 128-value K-stages (whole
+    // 128-byte-line stages, KS = 2, need one block per CU and measured slower)
+    const dim3 grid(ub_m * g.n_tiles), block(64 * WAVES_M * WAVES_N);
+    if (g.K % 512 == 0)
+      hipLaunchKernelGGL((grouped_gemm_mx4_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES, 1, true>),
+                         grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL((grouped_gemm_mx4_kernel<BM, BN, WAVES_M, WAVES_N, SWIGLU, STAGES, 1, false>),
+                         grid, block, 0, stream, g);
   } else if constexpr (STAGES >= 3) {
     // bf16: chunks of two m-tiles' worth of items are dealt to the XCDs in
     // turn, which evens out the XCDs' loads when a few segments (the shared
@@ -1514,8 +1586,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // MX: the 3-stage DMA pipeline at every batch size (the 16-row decode
   // kernel has no per-group scales)
   if (a.precision == MOE_PREC_MXFP8) return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
-  // MXFP4: 128 x 256 tiles on 4 waves, 3-stage ring (76.5 KB), two blocks per CU
-  if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 2, 3>(a, stream);
+  // MXFP4: 128 x 256 tiles on 8 waves, a 2-stage ring of 128-value K-stages
+  // plus two 6 KB scale windows (60 KB), two blocks per CU
+  if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 2>(a, stream);
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 

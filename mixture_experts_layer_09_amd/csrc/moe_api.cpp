@@ -3,6 +3,8 @@
 // device memory or synchronises, except moe_check_device_error.
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "moe_internal.h"
 
 using namespace moe;
@@ -10,6 +12,15 @@ using namespace moe;
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// The kernels move activations, weights and scales with 16-byte vector loads
+// and global->LDS DMAs, so those arrays must be 16-byte aligned (NULL, an
+// absent optional array, passes).
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
 
 int check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
@@ -47,6 +58,9 @@ int check_weights(const moe_shape* s, const moe_expert_weights* w) {
   if (!w || !w->W1 || !w->W2) return MOE_ERR_INVALID_ARG;
   const bool scaled = s->precision >= MOE_PREC_FP8;
   if (scaled && (!w->w1_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16({w->W1, w->w1_scale, w->W2, w->w2_scale, w->Ws1, w->ws1_scale, w->Ws2,
+                  w->ws2_scale}))
+    return MOE_ERR_INVALID_ARG;
   if (s->has_shared) {
     if (!w->Ws1 || !w->Ws2) return MOE_ERR_INVALID_ARG;
     if (scaled && (!w->ws1_scale || !w->ws2_scale))
@@ -162,6 +176,7 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
   if (st != MOE_OK) return st;
   if ((st = check_route_opts(opts)) != MOE_OK) return st;
   if (!X || !Wg || !expert_ids || !gate_weights) return MOE_ERR_INVALID_ARG;
+  if (!aligned16({X, Wg})) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   RouteArgs a = route_args(shape, opts, X, Wg, expert_ids, gate_weights, keys_out, workspace);
   hipError_t e = launch_clear_flag(a.flag, stream);
@@ -179,6 +194,7 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
     return MOE_ERR_INVALID_ARG;
   if (shape->precision >= MOE_PREC_FP8 && (!xp_scale || !Xq || !x_scale))
     return MOE_ERR_INVALID_ARG;
+  if (!aligned16({X, Xp, xp_scale, Xq, x_scale})) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   PermuteArgs a = permute_args(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp,
                                xp_scale, Xq, x_scale, workspace);
@@ -200,6 +216,7 @@ int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
     if (!Xs || !Ys) return MOE_ERR_INVALID_ARG;
     if (shape->precision >= MOE_PREC_FP8 && !xs_scale) return MOE_ERR_INVALID_ARG;
   }
+  if (!aligned16({Xp, xp_scale, Xs, xs_scale, Yp, Ys})) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   FfnArgs a = ffn_args(shape, Xp, xp_scale, offsets, Xs, xs_scale, weights, Yp, Ys, workspace);
   return hip_status(launch_expert_ffn(a, stream));
@@ -210,6 +227,7 @@ int moe_combine(const moe_shape* shape, const void* Yp, const int32_t* dst_row,
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!Yp || !dst_row || !gate_weights || !Y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16({Yp, Ys, Y})) return MOE_ERR_INVALID_ARG;
   CombineArgs a{};
   a.T = shape->tokens;
   a.h = shape->hidden;
@@ -231,6 +249,7 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
   if (st != MOE_OK) return st;
   if ((st = check_weights(shape, weights)) != MOE_OK) return st;
   if (!X || !expert_ids || !gate_weights || !Y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16({X, Wg, Y})) return MOE_ERR_INVALID_ARG;
   if (opts) {
     if ((st = check_route_opts(opts)) != MOE_OK) return st;
     if (!Wg) return MOE_ERR_INVALID_ARG;

@@ -137,6 +137,17 @@ def test_null_pointers_and_workspace_rejected():
     w = moe.moe_expert_weights(16, None, 16, None, None, None, None, None)
     assert L.moe_forward(C.byref(s), C.byref(opts), 16, None, C.byref(w), 16, 16, 16, FAKE_WS, n,
                          None) == INVALID
+    # device arrays that are not 16-byte aligned
+    assert L.moe_route(C.byref(s), C.byref(opts), 24, 16, 16, 16, None, FAKE_WS, n, None) == INVALID
+    assert L.moe_permute(C.byref(s), 16, 16, 16, 16, 16, 16, 40, None, None, None, FAKE_WS, n,
+                         None) == INVALID
+    w = moe.moe_expert_weights(16, None, 20, None, None, None, None, None)
+    assert L.moe_expert_ffn(C.byref(s), 16, None, 16, None, None, C.byref(w), 16, None, FAKE_WS, n,
+                            None) == INVALID
+    assert L.moe_combine(C.byref(s), 16, 16, 16, None, 8, None) == INVALID
+    w = moe.moe_expert_weights(16, None, 16, None, None, None, None, None)
+    assert L.moe_forward(C.byref(s), None, 16, None, C.byref(w), 16, 16, 36, FAKE_WS, n,
+                         None) == INVALID
     # check_device_error with no workspace
     assert L.moe_check_device_error(None, 0, None) == WORKSPACE
 

@@ -36,6 +36,8 @@ CASES = {
     "v4pro_fp8_small": ("v4pro_fp8", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_mxfp8_small": ("v4pro_mxfp8", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_mxfp4_small": ("v4pro_mxfp4", dict(T=256, hidden=512, experts=64, inter=256)),
+    # K = 1024 and 512: the MXFP4 kernels' 512-value scale windows, several per row
+    "v4pro_mxfp4_k1024": ("v4pro_mxfp4", dict(T=200, hidden=1024, experts=64, inter=512)),
     "decode_hash_small": ("decode_hash_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "decode_score_small": ("decode_score_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "ep_share_small": ("ep_share_bf16", dict(T=600, hidden=256, inter=128)),
