@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-PRECISIONS = {"fp32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3, "mxfp4": 4}
+PRECISIONS = {"fp32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3, "mxfp4": 4, "int8": 5}
 MX_FORMATS = {"e4m3": 0, "e2m1": 1}
 SCORES = {"sigmoid": 0, "softmax": 1, "sqrt_softplus": 2}
 
@@ -78,6 +78,7 @@ def lib():
         L.oracle_e4m3_encode.restype = C.c_uint8
         L.oracle_e4m3_encode.argtypes = [dbl]
         L.oracle_quantize_row_f32.argtypes = [i32, vp, vp, vp]
+        L.oracle_quantize_row_i8_f32.argtypes = [i32, vp, vp, vp]
         L.oracle_gate_logits.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp]
         L.oracle_affinity.argtypes = [i32, i32, i32, vp, vp]
         L.oracle_topk.argtypes = [i32, i32, i32, vp, vp, vp]
@@ -132,6 +133,20 @@ def quantize_rows_f32(X: np.ndarray):
     L = lib()
     for t in range(T):
         L.oracle_quantize_row_f32(h, _p(X[t]), _p(q[t]), C.c_void_p(s.ctypes.data + 4 * t))
+    return q, s
+
+
+def quantize_rows_i8_f32(X: np.ndarray):
+    """Per-row INT8 quantisation of the A8W8 block (s = max|x|/127, codes
+    rounded half away from zero), scale and quotient in fp32: returns
+    (codes int8, scale float32)."""
+    X = _c(X, np.float32)
+    T, h = X.shape
+    q = np.empty((T, h), np.int8)
+    s = np.empty(T, np.float32)
+    L = lib()
+    for t in range(T):
+        L.oracle_quantize_row_i8_f32(h, _p(X[t]), _p(q[t]), C.c_void_p(s.ctypes.data + 4 * t))
     return q, s
 
 
@@ -250,7 +265,8 @@ class Layer:
 
     precision 'fp32': X, W float32.  'bf16': X, W uint16 bits.  'fp8': X uint16
     (bf16 bits, quantised per token inside the layer), W uint8 e4m3 codes with
-    float32 per-output-channel scales.  'mxfp8' / 'mxfp4': X uint16 (bf16
+    float32 per-output-channel scales.  'int8': as 'fp8' with int8 weights
+    (the INT8 A8W8 block).  'mxfp8' / 'mxfp4': X uint16 (bf16
     bits, MX-quantised inside the layer).  mxfp8: W uint8 e4m3 codes [E,K,N],
     scales uint8 E8M0 [E,K/32,N].  mxfp4: W K-contiguous e2m1 code pairs
     [E,N,K/2] (element 2i in the low nibble), scales [E,N,K/32].
@@ -260,7 +276,7 @@ class Layer:
                  ws1_scale=None, ws2_scale=None, k=1):
         self.precision = precision
         mx = precision.startswith("mx")
-        wdt = {"fp32": np.float32, "bf16": np.uint16}.get(precision, np.uint8)
+        wdt = {"fp32": np.float32, "bf16": np.uint16, "int8": np.int8}.get(precision, np.uint8)
         sdt = np.uint8 if mx else np.float32
         xdt = np.float32 if precision == "fp32" else np.uint16
         self.X = _c(X, xdt)
@@ -289,7 +305,7 @@ class Layer:
             assert self.W2.shape == (E, h, self.inter // 2)
             assert self.w1_scale.shape == (E, f2, h // 32)
             assert self.w2_scale.shape == (E, h, self.inter // 32)
-        if precision in ("fp8", "mxfp8", "mxfp4"):
+        if precision in ("fp8", "int8", "mxfp8", "mxfp4"):
             assert self.w1_scale is not None and self.w2_scale is not None
         self._s = _Layer(T, h, E, self.k, self.inter, int(self.Ws1 is not None),
                          PRECISIONS[precision], _p(self.X), _p(self.W1), _p(self.W2),

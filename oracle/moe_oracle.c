@@ -35,6 +35,11 @@
  *   - fp8 (e4m3fn, OCP) replaces INT8 in the A8W8 block: the constant 127
  *     becomes 448, round-to-nearest-even with saturation; a zero row gets
  *     scale 1 and code 0;
+ *   - the INT8 A8W8 block itself ([MM] A8W8: s = max|row| / 127, codes in
+ *     [-127, 127]): its rounding ⌊z⌉ is read as round half away from zero
+ *     (the §约定 wording, 四舍五入); a zero row gets scale 1 and code 0; the
+ *     INT8 products are summed exactly as integers before the per-channel
+ *     and per-row dequantisation;
  *   - the per-token activation quantisation of X is an integer decision
  *     taken from an input, so it is done in fp32 (the kernel's precision),
  *     everything else is fp64;
@@ -49,7 +54,7 @@
  *     saturated to the element's largest magnitude (448, 6).
  *
  * Element codes for tensors handed in: 0 = fp32, 1 = bf16 (raw 16-bit words),
- * 2 = fp8 e4m3fn (raw bytes).  MX tensors: e4m3 codes one per byte, e2m1
+ * 2 = fp8 e4m3fn (raw bytes), INT8 weights as int8_t.  MX tensors: e4m3 codes one per byte, e2m1
  * codes two per byte (element 2i in the low nibble), E8M0 scale codes one per
  * byte; MXFP4 weights are stored K-contiguous as on the mega_moe page
  * (codes [E,N,K/2], scales [E,N,K/32]).  All arrays are host memory, row
@@ -412,6 +417,60 @@ void oracle_quantize_row_f32(int n, const float* x, uint8_t* q, float* scale) {
   *scale = s;
 }
 
+/* ⌊z⌉ of [MM] §约定, read as round half away from zero. */
+static double round_half_away(double v) { return round(v); /* C round: halves away from 0 */ }
+
+/* Per-token activation quantisation of the INT8 A8W8 block ([MM] A8W8, EP
+ * Dispatch): s = max|x| / 127, q = ⌊x / s⌉ in [-127, 127].  The scale and the
+ * quotient x / s are fp32 (an integer decision taken from an input, like the
+ * e4m3 form), the rounding is exact. */
+void oracle_quantize_row_i8_f32(int n, const float* x, int8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int i = 0; i < n; ++i) {
+    float a = fabsf(x[i]);
+    amax = a > amax ? a : amax;
+  }
+  float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+  for (int i = 0; i < n; ++i) {
+    double r = round_half_away((double)(x[i] / s));
+    q[i] = (int8_t)(r > 127.0 ? 127.0 : (r < -127.0 ? -127.0 : r));
+  }
+  *scale = s;
+}
+
+/* The INT8 A8W8 expert ([MM] A8W8, Expert Compute 1-3): Linear1 is the
+ * integer product Q_e W1[e] (exact), dequantised by the per-channel weight
+ * scale and the per-token scale; SwiGLU in fp64; the SwiGLU output is
+ * requantised per row (s_a = max|A| / 127, ⌊A / s_a⌉), Linear2 is again an
+ * integer product, dequantised by s^{W2} and s_a. */
+static void swiglu_row_i8(int hidden, int f, const int8_t* qx, double sx, const int8_t* Wq1,
+                          const float* s_w1, const int8_t* Wq2, const float* s_w2, double* h1,
+                          double* out) {
+  int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)(2 * f > hidden ? 2 * f : hidden));
+  for (int n = 0; n < 2 * f; ++n) acc[n] = 0;
+  for (int c = 0; c < hidden; ++c) {
+    int64_t xc = qx[c];
+    if (xc == 0) continue;
+    for (int n = 0; n < 2 * f; ++n) acc[n] += xc * (int64_t)Wq1[(size_t)c * 2 * f + n];
+  }
+  for (int n = 0; n < 2 * f; ++n) h1[n] = (double)acc[n] * (double)s_w1[n] * sx;
+  double amax = 0.0;
+  for (int n = 0; n < f; ++n) {
+    h1[n] = silu(h1[n]) * h1[f + n];
+    amax = fabs(h1[n]) > amax ? fabs(h1[n]) : amax;
+  }
+  double sa = amax > 0.0 ? amax / 127.0 : 1.0;
+  for (int o = 0; o < hidden; ++o) acc[o] = 0;
+  for (int n = 0; n < f; ++n) {
+    double r = round_half_away(h1[n] / sa);
+    int64_t qa = (int64_t)(r > 127.0 ? 127.0 : (r < -127.0 ? -127.0 : r));
+    if (qa == 0) continue;
+    for (int o = 0; o < hidden; ++o) acc[o] += qa * (int64_t)Wq2[(size_t)n * hidden + o];
+  }
+  for (int o = 0; o < hidden; ++o) out[o] = (double)acc[o] * (double)s_w2[o] * sa;
+  free(acc);
+}
+
 /* The A8W8 (e4m3) expert: x arrives quantised (q_x, s_x).  Linear1 runs on
  * codes, dequantised per output channel and per token; SwiGLU in fp64; the
  * SwiGLU output is requantised per row (s_a = max|A|/448) before Linear2,
@@ -499,11 +558,11 @@ static void swiglu_row_mx(int hidden, int f, const double* x, int fmt, const uin
 /* Everything that describes one layer.  Pointers are host memory. */
 typedef struct {
   int T, hidden, E, k, inter, has_shared;
-  int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3, 3 = MXFP8, 4 = MXFP4 */
+  int precision;        /* 0 = fp32, 1 = bf16, 2 = A8W8 e4m3, 3 = MXFP8, 4 = MXFP4, 5 = A8W8 INT8 */
   const void* X;        /* [T,hidden]: fp32 (precision 0) or bf16 */
-  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes; MXFP4: [E,2f,hidden/2] */
+  const void* W1;       /* [E,hidden,2f]: fp32 / bf16 / e4m3 codes / int8; MXFP4: [E,2f,hidden/2] */
   const void* W2;       /* [E,f,hidden] */
-  const void* w1_scale; /* A8W8: fp32 [E,2f]; MXFP8: E8M0 [E,hidden/32,2f]; MXFP4 [E,2f,hidden/32] */
+  const void* w1_scale; /* A8W8 (e4m3, INT8): fp32 [E,2f]; MXFP8: E8M0 [E,hidden/32,2f]; MXFP4 [E,2f,hidden/32] */
   const void* w2_scale; /* A8W8: fp32 [E,hidden]; MXFP8: E8M0 [E,f/32,hidden]; MXFP4 [E,hidden,f/32] */
   const void* Ws1;      /* shared [hidden,2f] or NULL */
   const void* Ws2;      /* shared [f,hidden] */
@@ -523,7 +582,7 @@ static void expert_of_token(const oracle_layer* L, int t, int e, double* xbuf, u
   const char* W1 = shared ? (const char*)L->Ws1 : (const char*)L->W1;
   const char* W2 = shared ? (const char*)L->Ws2 : (const char*)L->W2;
   int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16;
-  if (L->precision >= 3) {
+  if (L->precision == 3 || L->precision == 4) {
     int fmt = L->precision == 3 ? ORC_FMT_E4M3 : ORC_FMT_E2M1;
     size_t d1 = (size_t)h * 2 * f, d2 = (size_t)f * h; /* elements per expert */
     const uint8_t* S1 = shared ? (const uint8_t*)L->ws1_scale
@@ -544,7 +603,15 @@ static void expert_of_token(const oracle_layer* L, int t, int e, double* xbuf, u
     W1 += (size_t)e * h * 2 * f * wb;
     W2 += (size_t)e * f * h * wb;
   }
-  if (L->precision == 2) {
+  if (L->precision == 5) {
+    for (int c = 0; c < h; ++c) fbuf[c] = (float)elem(L->X, xdt, (size_t)t * h + c);
+    float sx;
+    oracle_quantize_row_i8_f32(h, fbuf, (int8_t*)qbuf, &sx);
+    const float* s1 = shared ? (const float*)L->ws1_scale : (const float*)L->w1_scale + (size_t)e * 2 * f;
+    const float* s2 = shared ? (const float*)L->ws2_scale : (const float*)L->w2_scale + (size_t)e * h;
+    swiglu_row_i8(h, f, (const int8_t*)qbuf, (double)sx, (const int8_t*)W1, s1, (const int8_t*)W2,
+                  s2, h1, out);
+  } else if (L->precision == 2) {
     for (int c = 0; c < h; ++c) fbuf[c] = (float)elem(L->X, xdt, (size_t)t * h + c);
     float sx;
     oracle_quantize_row_f32(h, fbuf, qbuf, &sx);

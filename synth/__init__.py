@@ -11,6 +11,7 @@ Workloads (T tokens, hidden h, E routed experts, top-k, inter f, shared S):
   v4pro_bf16         8192, 7168, 384, 6, 3072, 1 bf16, sigmoid + beta, alpha 2.5,
                                                  Zipf(0.8) expert load
   v4pro_fp8          as v4pro_bf16, A8W8 e4m3 experts, bf16 output
+  v4pro_int8         as v4pro_bf16, A8W8 INT8 experts (the page's INT8 block)
   v4pro_mxfp8        as v4pro_bf16, MXFP8 experts (e4m3, group-32 E8M0 scales)
   v4pro_mxfp4        as v4pro_bf16, MXFP4 experts (e2m1, group-32 E8M0 scales)
   decode_hash_bf16   128, 7168, 384, 6, 3072, 1  token-id hash routing
@@ -26,7 +27,8 @@ fixture under tests/golden (written by a script that runs the CPU oracle's
 router on a calibration batch).  bf16 values are drawn in fp32 and rounded to
 nearest even by torch.  fp8 expert weights are quantised offline per output
 channel: scale = max|W[:, n]| / 448, codes = torch's float8_e4m3fn cast of
-W / scale.  MXFP8 expert weights are quantised offline in groups of 32 rows
+W / scale; INT8 ones the same way with 127 and W / scale rounded half away
+from zero.  MXFP8 expert weights are quantised offline in groups of 32 rows
 (K) per column: E8M0 scale code = floor(log2 max|W|) - 8 + 127 (0 for a zero
 group), codes = torch's float8_e4m3fn cast of W * 2^(127 - code) clamped to
 +-448.  MXFP4 weights the same way with exponent floor(log2 max|W|) - 2 and
@@ -59,7 +61,7 @@ class Workload:
     topk: int
     inter: int
     shared: int
-    precision: str          # fp32 | bf16 | fp8
+    precision: str          # fp32 | bf16 | fp8 | int8 | mxfp8 | mxfp4
     score: str = "sigmoid"  # sigmoid | softmax | sqrt_softplus
     renorm: bool = True
     alpha: float = 1.0
@@ -86,6 +88,8 @@ WORKLOADS = {
         Workload("v4pro_bf16", 8192, 7168, 384, 6, 3072, 1, "bf16", alpha=2.5, beta_range=0.1,
                  zipf=True, family="v4pro"),
         Workload("v4pro_fp8", 8192, 7168, 384, 6, 3072, 1, "fp8", alpha=2.5, beta_range=0.1,
+                 zipf=True, family="v4pro"),
+        Workload("v4pro_int8", 8192, 7168, 384, 6, 3072, 1, "int8", alpha=2.5, beta_range=0.1,
                  zipf=True, family="v4pro"),
         Workload("v4pro_mxfp8", 8192, 7168, 384, 6, 3072, 1, "mxfp8", alpha=2.5,
                  beta_range=0.1, zipf=True, family="v4pro"),
@@ -155,6 +159,20 @@ def quantize_weight_e4m3(W: torch.Tensor):
     return q, scale.float()
 
 
+def quantize_weight_i8(W: torch.Tensor):
+    """Offline per-output-channel INT8 quantisation of a [.., K, N] weight.
+
+    scale[.., n] = max_k |W[.., k, n]| / 127 (1 where the column is zero);
+    codes = W / scale rounded half away from zero (in fp64), int8 in
+    [-127, 127]."""
+    Wf = W.double()
+    amax = Wf.abs().amax(dim=-2)
+    scale = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax))
+    v = Wf / scale.unsqueeze(-2)
+    q = torch.trunc(v + torch.copysign(torch.full_like(v, 0.5), v)).clamp_(-127, 127)
+    return q.to(torch.int8), scale.float()
+
+
 def quantize_weight_mx_e4m3(W: torch.Tensor):
     """Offline MXFP8 quantisation of a [K, N] weight (K a multiple of 32):
     codes [K, N] e4m3fn and E8M0 scale codes [K/32, N] uint8 (see the module
@@ -199,9 +217,10 @@ def _expert_weights(wl: Workload, seed, device, act_dtype):
     """W1 [E,h,2f], W2 [E,f,h] (bf16/fp32), generated one expert at a time."""
     E, h, f = wl.experts, wl.hidden, wl.inter
     fp8 = wl.precision == "fp8"
+    i8 = wl.precision == "int8"
     mx = wl.precision == "mxfp8"
     mx4 = wl.precision == "mxfp4"
-    wdt = torch.float8_e4m3fn if (fp8 or mx) else act_dtype
+    wdt = torch.float8_e4m3fn if (fp8 or mx) else (torch.int8 if i8 else act_dtype)
     if mx4:   # K-contiguous e2m1 pairs
         W1 = torch.empty((E, 2 * f, h // 2), dtype=torch.uint8, device=device)
         W2 = torch.empty((E, h, f // 2), dtype=torch.uint8, device=device)
@@ -212,7 +231,7 @@ def _expert_weights(wl: Workload, seed, device, act_dtype):
     if mx4:
         s1 = torch.empty((E, 2 * f, h // 32), dtype=torch.uint8, device=device)
         s2 = torch.empty((E, h, f // 32), dtype=torch.uint8, device=device)
-    if fp8:
+    if fp8 or i8:
         s1 = torch.empty((E, 2 * f), dtype=torch.float32, device=device)
         s2 = torch.empty((E, h), dtype=torch.float32, device=device)
     if mx:
@@ -232,6 +251,9 @@ def _expert_weights(wl: Workload, seed, device, act_dtype):
         elif fp8:
             W1[e], s1[e] = quantize_weight_e4m3(w1)
             W2[e], s2[e] = quantize_weight_e4m3(w2)
+        elif i8:
+            W1[e], s1[e] = quantize_weight_i8(w1)
+            W2[e], s2[e] = quantize_weight_i8(w2)
         else:
             W1[e] = w1
             W2[e] = w2

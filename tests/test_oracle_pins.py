@@ -257,7 +257,8 @@ def test_k_equals_E_is_the_dense_mixture(score, renorm):
     np.testing.assert_allclose(y, dense, rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "v4pro_bf16", "v4pro_fp8", "decode_hash_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "v4pro_bf16", "v4pro_fp8", "v4pro_int8",
+                                  "decode_hash_bf16"])
 def test_token_loop_equals_staged_dispatch_experts_combine(name):
     """The per-token layer equation (blog §模型与入口) and the staged
     dispatch / expert / combine definition (mega_moe §计算过程) agree."""
@@ -361,6 +362,120 @@ def test_fp8_layer_within_quantisation_error_of_exact_layer():
     y = oracle_layer(dq).tokens(r["ids"], r["G"])
     rel = np.abs(y8 - y).max(1) / np.abs(y).max(1)
     assert rel.max() < 0.1 and rel.max() > 1e-4   # lossy, but only by the fp8 rounding
+
+
+# ------------------------------------------------------------------ INT8 A8W8
+def _i8_quant_rows(v, dtype):
+    """The mega_moe page's INT8 rule restated with numpy: per row s = max|v| /
+    127 (1 for a zero row), codes = v / s rounded half away from zero, in
+    [-127, 127]; scale and quotient in `dtype`, the rounding exact."""
+    v = np.asarray(v, dtype)
+    amax = np.abs(v).max(1)
+    s = np.where(amax > 0, amax / dtype(127.0), dtype(1.0)).astype(dtype)
+    r = (v / s[:, None]).astype(np.float64)
+    q = np.clip(np.trunc(r + np.copysign(0.5, r)), -127, 127)
+    return q.astype(np.int8), s
+
+
+def _i8_weights(rng, E, K, N):
+    """Per-output-channel INT8 weights: codes [E,K,N], fp32 scales [E,N] and
+    the dequantised fp64 matrices."""
+    W = rng.standard_normal((E, K, N)) / np.sqrt(K)
+    amax = np.abs(W).max(1)
+    s = (amax / 127.0).astype(np.float32)
+    r = W / s[:, None, :].astype(np.float64)
+    q = np.clip(np.trunc(r + np.copysign(0.5, r)), -127, 127).astype(np.int8)
+    return q, s, q.astype(np.float64) * s[:, None, :].astype(np.float64)
+
+
+def test_quantize_rows_i8_rounds_half_away_from_zero():
+    # scale 1 (max 127): halves go away from zero, as ⌊z⌉ of the page's §约定 reads
+    x = np.array([[127.0, 63.5, -63.5, 0.5, -0.5, 2.5, -2.5, 1.49, -126.5, 0.0]], np.float32)
+    q, s = oracle.quantize_rows_i8_f32(x)
+    assert s[0] == 1.0
+    assert q[0].tolist() == [127, 64, -64, 1, -1, 3, -3, 1, -127, 0]
+    rng = np.random.default_rng(30)
+    X = (rng.standard_normal((16, 300)) * rng.uniform(0.01, 100, (16, 1))).astype(np.float32)
+    X[3] = 0.0
+    q, s = oracle.quantize_rows_i8_f32(X)
+    q_ref, s_ref = _i8_quant_rows(X, np.float32)
+    assert np.array_equal(s, s_ref) and np.array_equal(q, q_ref)
+    assert np.all(q[3] == 0) and s[3] == 1.0
+    assert np.all(np.abs(q).max(1)[np.arange(16) != 3] == 127)
+
+
+def test_int8_expert_is_exact_when_every_quantisation_is_lossless():
+    """Integer X rows with max 127 quantise with scale 1 to themselves, and
+    inter = 1 makes the SwiGLU output one value per row, requantised to
+    +-127 exactly: the INT8 layer then equals the exact SwiGLU with
+    dequantised weights (code * per-channel scale)."""
+    rng = np.random.default_rng(31)
+    T, h, f, E = 6, 32, 1, 3
+    X = rng.integers(-127, 128, size=(T, h)).astype(np.float64)
+    X[:, 0] = 127.0
+    Xb = _bf16(X)
+    assert np.array_equal(Xb.float().numpy(), X.astype(np.float32))  # exact in bf16
+    W1q = rng.integers(-127, 128, size=(E, h, 2 * f)).astype(np.int8)
+    W2q = rng.integers(-127, 128, size=(E, f, h)).astype(np.int8)
+    s1 = rng.uniform(1e-4, 1e-3, (E, 2 * f)).astype(np.float32)
+    s2 = rng.uniform(1e-3, 1e-2, (E, h)).astype(np.float32)
+    ids = np.array([[t % E] for t in range(T)], np.int32)
+    L = oracle.Layer("int8", bits(Xb), W1q, W2q, w1_scale=s1, w2_scale=s2, k=1)
+    y = L.tokens(ids, np.ones((T, 1)))
+    dq1 = W1q.astype(np.float64) * s1[:, None, :].astype(np.float64)
+    dq2 = W2q.astype(np.float64) * s2[:, None, :].astype(np.float64)
+    for t in range(T):
+        e = ids[t, 0]
+        ref = _np_swiglu(X[t:t + 1], dq1[e], dq2[e])
+        np.testing.assert_allclose(y[t:t + 1], ref, rtol=1e-12)
+
+
+def test_int8_layer_is_the_dense_swiglu_of_dequantised_operands():
+    """Routed and shared experts: Q8(x) -> DQ . DQ(W1) -> SwiGLU -> Q8 -> DQ
+    . DQ(W2), rebuilt with numpy matmuls and the numpy restatement of the
+    rounding rule above."""
+    rng = np.random.default_rng(32)
+    T, h, f, E, k = 5, 64, 48, 3, 2
+    Xb = _bf16(rng.standard_normal((T, h)))
+    W1, s1, dq1 = _i8_weights(rng, E, h, 2 * f)
+    W2, s2, dq2 = _i8_weights(rng, E, f, h)
+    Ws1, ss1, dqs1 = _i8_weights(rng, 1, h, 2 * f)
+    Ws2, ss2, dqs2 = _i8_weights(rng, 1, f, h)
+    ids = np.array([[t % E, (t + 1) % E] for t in range(T)], np.int32)
+    G = rng.uniform(0.1, 1.0, (T, k))
+    L = oracle.Layer("int8", bits(Xb), W1, W2, w1_scale=s1, w2_scale=s2, Ws1=Ws1[0], Ws2=Ws2[0],
+                     ws1_scale=ss1[0], ws2_scale=ss2[0], k=k)
+    y = L.tokens(ids, G)
+    xq, xs = _i8_quant_rows(Xb.float().numpy(), np.float32)
+    xd = xq.astype(np.float64) * xs[:, None].astype(np.float64)
+
+    def expert(x, d1, d2):
+        hh = x @ d1
+        u = hh[:, :f] / (1.0 + np.exp(-hh[:, :f])) * hh[:, f:]
+        uq, us = _i8_quant_rows(u, np.float64)
+        return (uq.astype(np.float64) * us[:, None]) @ d2
+
+    for t in range(T):
+        ref = expert(xd[t:t + 1], dqs1[0], dqs2[0])
+        for j in range(k):
+            ref = ref + G[t, j] * expert(xd[t:t + 1], dq1[ids[t, j]], dq2[ids[t, j]])
+        np.testing.assert_allclose(y[t:t + 1], ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+
+def test_int8_layer_within_quantisation_error_of_exact_layer():
+    inp = synth.make_inputs("v4pro_int8", T=16, hidden=256, inter=128, experts=8, zipf=False)
+    wl = inp["workload"]
+    r = oracle_route(inp)
+    y8 = oracle_layer(inp).tokens(r["ids"], r["G"])
+    dq = dict(inp)
+    dq["workload"] = wl.replace(precision="fp32")
+    dq["X"] = inp["X"].float()
+    for w, s in (("W1", "w1_scale"), ("W2", "w2_scale"), ("Ws1", "ws1_scale"), ("Ws2", "ws2_scale")):
+        dq[w] = inp[w].float() * inp[s].unsqueeze(-2)
+        dq[s] = None
+    y = oracle_layer(dq).tokens(r["ids"], r["G"])
+    rel = np.abs(y8 - y).max(1) / np.abs(y).max(1)
+    assert rel.max() < 0.1 and rel.max() > 1e-4   # lossy, but only by the INT8 rounding
 
 
 # ------------------------------------------------------------------ MX (group-32, E8M0)
@@ -534,6 +649,13 @@ PLANTED = {
     # e2m1 weight pairs read high nibble first
     "nibble": ("(W[i / 2] >> (4 * (i & 1)))", "(W[i / 2] >> (4 * (1 - (i & 1))))",
                lambda: test_mx_layer_is_the_dense_swiglu_of_dequantised_operands("mxfp4", "e2m1")),
+    # INT8 codes rounded half to even instead of half away from zero
+    "i8round": ("return round(v);", "return rint(v);",
+                lambda: test_quantize_rows_i8_rounds_half_away_from_zero()),
+    # INT8 Linear1 dequantised without the per-token activation scale
+    "i8scale": ("h1[n] = (double)acc[n] * (double)s_w1[n] * sx;",
+                "h1[n] = (double)acc[n] * (double)s_w1[n];",
+                lambda: test_int8_layer_is_the_dense_swiglu_of_dequantised_operands()),
     # MX weight scale taken from the wrong group
     "mxscale": ("mx_pow2_table[S[(size_t)(c / 32) * N + n]]",
                 "mx_pow2_table[S[(size_t)((c + 32) / 32 % (c / 32 + 1)) * N + n]]",
