@@ -28,8 +28,8 @@ if ROOT not in sys.path:
 
 METRIC = "MoE layer tokens/s and grouped-GEMM TFLOP/s (% of MFMA peak) at 1 GPU"
 PEAK_HBM_GBS = 8000.0
-PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3,
-                    "fp32": 157.3}
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "int8": 5033.2, "mxfp8": 5033.2,
+                    "mxfp4": 10066.3, "fp32": 157.3}   # int8: tera-ops/s
 
 
 def log(msg):
@@ -45,11 +45,11 @@ def stage_bytes(wl):
     Y."""
     T, h, E, k = wl.T, wl.hidden, wl.experts, wl.topk
     ab = 4 if wl.precision == "fp32" else 2             # activation / output bytes
-    q8 = wl.precision in ("fp8", "mxfp8", "mxfp4")
+    q8 = wl.precision in ("fp8", "int8", "mxfp8", "mxfp4")
     xb = (0.5 if wl.precision == "mxfp4" else 1) if q8 else ab   # dispatched row bytes
     route = T * h * ab + h * E * ab + T * k * 8 + (T * 4 if wl.hash else 0)
     permute = 2 * T * k * 4 + T * h * ab + T * k * h * xb + 2 * T * k * 4
-    if wl.precision == "fp8":      # Xq and the per-row scales
+    if wl.precision in ("fp8", "int8"):      # Xq and the per-row scales
         permute += T * h + T * 4 + T * k * 4
     if wl.precision in ("mxfp8", "mxfp4"):    # Xq and the per-group E8M0 scales
         permute += T * h * xb + (T + T * k) * (h // 32)
@@ -65,7 +65,7 @@ def algorithmic_work(wl, counts):
     h, f, k, T = wl.hidden, wl.inter, wl.topk, wl.T
     rows = T * k + (T if wl.shared else 0)
     flops = 2.0 * rows * (h * 2 * f + f * h)
-    q8 = wl.precision in ("fp8", "mxfp8", "mxfp4")
+    q8 = wl.precision in ("fp8", "int8", "mxfp8", "mxfp4")
     wbytes = (0.5 if wl.precision == "mxfp4" else 1) if q8 else (4 if wl.precision == "fp32" else 2)
     xbytes = wbytes
     obytes = 4 if wl.precision == "fp32" else 2
@@ -285,9 +285,9 @@ def main(argv=None):
     dev = "cuda"
     mx = wl.precision in ("mxfp8", "mxfp4")
     fp4 = wl.precision == "mxfp4"
-    fp8 = wl.precision in ("fp8", "mxfp8", "mxfp4")   # quantised activation codes
+    fp8 = wl.precision in ("fp8", "int8", "mxfp8", "mxfp4")   # quantised activation codes
     odt = torch.float32 if wl.precision == "fp32" else torch.bfloat16
-    xdt = torch.float8_e4m3fn if fp8 else odt
+    xdt = (torch.int8 if wl.precision == "int8" else torch.float8_e4m3fn) if fp8 else odt
     T, k, h, E = wl.T, wl.topk, wl.hidden, wl.experts
     n = T * k
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -302,7 +302,7 @@ def main(argv=None):
     sc_dt = torch.uint8 if mx else torch.float32
     xps = torch.empty(sc_shape(n), dtype=sc_dt, device=dev) if fp8 else None
     Xq = ((torch.empty((T, h // 2), dtype=torch.uint8, device=dev) if fp4
-           else torch.empty((T, h), dtype=torch.float8_e4m3fn, device=dev)) if fp8 else None)
+           else torch.empty((T, h), dtype=xdt, device=dev)) if fp8 else None)
     xs = torch.empty(sc_shape(T), dtype=sc_dt, device=dev) if fp8 else None
     Yp = torch.empty((n, h), dtype=odt, device=dev)
     Ys = torch.empty((T, h), dtype=odt, device=dev) if wl.shared else None
@@ -387,6 +387,7 @@ def main(argv=None):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 activations/output)",
+                  "int8": "i8 (int32 products; bf16 activations/output)",
                   "mxfp8": "mxfp8-e4m3 (group-32 E8M0 scales; bf16 input/output)",
                   "mxfp4": "mxfp4-e2m1 (group-32 E8M0 scales; bf16 input/output)",
                   "fp32": "f32"}[prec],

@@ -46,6 +46,10 @@
  *       MOE_PREC_FP8:  X, Wg, Yp, Ys, Y bf16; W1/W2/Ws1/Ws2 OCP e4m3fn codes
  *                      with fp32 per-output-channel scales; Xp, Xq e4m3fn
  *                      codes with fp32 per-row scales.
+ *       MOE_PREC_INT8: the mega_moe page's A8W8 block as printed: as FP8
+ *                      with int8 codes in [-127, 127] and the constant 127
+ *                      (scale = max|row| / 127, codes rounded half away from
+ *                      zero); the products are exact int32 sums.
  *       MOE_PREC_MXFP8: the mega_moe page's MXFP mode (MX block quantisation,
  *                      groups of 32 along the contraction dimension, one
  *                      E8M0 scale byte per group, value = e4m3fn(code) *
@@ -69,7 +73,8 @@
  *   - Shape limits: 1 <= T; 1 <= topk <= min(16, experts) (the mega_moe
  *     constraint on top-k); experts <= 512; hidden a multiple of 128 and
  *     inter a multiple of 64 (the kernels' tile granularity); for FP8,
- *     MXFP8 and MXFP4 hidden a multiple of 256 and inter a multiple of 128.
+ *     INT8, MXFP8 and MXFP4 hidden a multiple of 256 and inter a multiple of
+ *     128.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -97,7 +102,8 @@ typedef enum {
   MOE_PREC_BF16 = 1,
   MOE_PREC_FP8 = 2,
   MOE_PREC_MXFP8 = 3,
-  MOE_PREC_MXFP4 = 4
+  MOE_PREC_MXFP4 = 4,
+  MOE_PREC_INT8 = 5
 } moe_precision;
 
 typedef enum {
@@ -136,8 +142,9 @@ typedef struct {
 /* Expert weights.  W1 [E, hidden, 2*inter], W2 [E, inter, hidden]; shared
  * Ws1 [hidden, 2*inter], Ws2 [inter, hidden] (NULL without a shared expert).
  * Scales, ignored for F32 and BF16:
- *   MOE_PREC_FP8: fp32 per output channel: w1_scale [E, 2*inter], w2_scale
- *     [E, hidden], ws1_scale [2*inter], ws2_scale [hidden].
+ *   MOE_PREC_FP8, MOE_PREC_INT8: fp32 per output channel: w1_scale [E,
+ *     2*inter], w2_scale [E, hidden], ws1_scale [2*inter], ws2_scale
+ *     [hidden].
  *   MOE_PREC_MXFP8: E8M0 bytes per group of 32 rows (K) and column:
  *     w1_scale [E, hidden/32, 2*inter], w2_scale [E, inter/32, hidden],
  *     ws1_scale [hidden/32, 2*inter], ws2_scale [inter/32, hidden]; the
@@ -184,6 +191,8 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
  *   max|x| / 448, codes = round-to-nearest-even of x / scale, saturating);
  *   Xq [T, hidden] e4m3 and x_scale [T] fp32 receive that, Xp holds codes
  *   and xp_scale [T*topk] fp32 the scale of each row.
+ *   MOE_PREC_INT8: the same with scale = max|x| / 127 and int8 codes =
+ *   x / scale (fp32 quotient) rounded half away from zero.
  *   MOE_PREC_MXFP8: X is bf16 and is MX-quantised per token (groups of 32
  *   along hidden); Xq [T, hidden] e4m3 and x_scale [T, hidden/32] E8M0 bytes
  *   receive that, Xp holds codes and xp_scale [T*topk, hidden/32] the scales
@@ -201,10 +210,10 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
  * by offsets [E+1] (rows offsets[e] .. offsets[e+1]-1 of Xp belong to expert
  * e), fp32 accumulation.  Yp [T*topk, hidden] out (fp32 for F32, else bf16).
  * With a shared expert: Xs [T, hidden] is its input (X, or Xq with
- * xs_scale for FP8 and MXFP8) and Ys [T, hidden] its output; else both may
+ * xs_scale for the quantised precisions) and Ys [T, hidden] its output; else both may
  * be NULL.  Scales have the types moe_permute gives them.  The SwiGLU output
- * is held in the workspace: bf16 (BF16), fp32 before its per-row e4m3
- * requantisation (FP8), or MX-quantised in groups of 32 along inter as it
+ * is held in the workspace: bf16 (BF16), fp32 before its per-row e4m3 or
+ * int8 requantisation (FP8, INT8), or MX-quantised in groups of 32 along inter as it
  * is produced (MXFP8, MXFP4). */
 int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
                    const int32_t* offsets, const void* Xs, const void* xs_scale,

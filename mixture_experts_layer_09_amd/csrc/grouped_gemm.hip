@@ -39,9 +39,10 @@
 // matching BN/2 up columns, and each wave owns equal gate/up sub-tiles, so the
 // gate and up accumulators of an output element sit in the same lane.
 //
-// A8W8 (e4m3): H = C * w1_scale[e, n] * x_scale[r]; the SwiGLU output is
-// written in fp32 and requantised per row (scale = max|A[r]| / 448) by
-// requant_kernel; Linear2 dequantises with w2_scale[e, n] * a_scale[r].
+// A8W8 (e4m3, or INT8 with int32 products): H = C * w1_scale[e, n] *
+// x_scale[r]; the SwiGLU output is written in fp32 and requantised per row
+// (scale = max|A[r]| / 448, or / 127 for INT8) by requant_kernel; Linear2
+// dequantises with w2_scale[e, n] * a_scale[r].
 #include "moe_internal.h"
 
 namespace moe {
@@ -509,6 +510,7 @@ template <int BN>
 struct DmaOps<MOE_PREC_BF16, BN> {
   static constexpr int ESZ = 2, BK = 32, A_CHUNKS = 4;
   typedef bf16x8_t frag;
+  typedef f32x4_t acc_t;
   __device__ static int swz_a(int r) { return (r >> 2) & 3; }
   __device__ static int swz_b(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
   // byte offsets (inside a stage's B region) of this lane's transposing reads
@@ -547,6 +549,7 @@ template <int BN>
 struct DmaOps<MOE_PREC_FP8, BN> {
   static constexpr int ESZ = 1, BK = 128, A_CHUNKS = 8;
   typedef i32x8_t frag;
+  typedef f32x4_t acc_t;
   __device__ static int swz_a(int r) { return (r >> 1) & 7; }
   __device__ static int swz_b(int r) {
     return BN >= 256 ? (r & 7) + 8 * ((r >> 5) & 1) : ((r & 7) >> 1) + 4 * ((r >> 5) & 1);
@@ -638,6 +641,23 @@ __device__ __forceinline__ bool block_item(const GemmArgs& g, int& seg, int& mti
 template <int BN>
 struct DmaOps<MOE_PREC_MXFP8, BN> : DmaOps<MOE_PREC_FP8, BN> {};
 
+// INT8 (the A8W8 block as printed) shares the 8-bit operand layout: a stage's
+// 128 K-values per lane pair go through two 16x16x64 int8 MFMAs, the first
+// on bytes 0-15 of both fragments and the second on bytes 16-31.  A and B
+// fragments hold the same K indices at the same (lane group, byte), and an
+// MFMA pairs A and B bytes that way, so the two MFMAs sum exactly the
+// stage's 128 products, into int32.
+template <int BN>
+struct DmaOps<MOE_PREC_INT8, BN> : DmaOps<MOE_PREC_FP8, BN> {
+  typedef i32x4_t acc_t;
+  __device__ static i32x4_t mma(i32x8_t a, i32x8_t b, i32x4_t c) {
+    const i32x4_t alo = {a[0], a[1], a[2], a[3]}, ahi = {a[4], a[5], a[6], a[7]};
+    const i32x4_t blo = {b[0], b[1], b[2], b[3]}, bhi = {b[4], b[5], b[6], b[7]};
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(alo, blo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(ahi, bhi, c, 0, 0, 0);
+  }
+};
+
 __device__ __forceinline__ f32x4_t mma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
@@ -668,6 +688,8 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int A_BYTES = BM * A_ROW;
   constexpr int B_BYTES = BK * B_ROW;
   constexpr bool MX = PREC == MOE_PREC_MXFP8;
+  // A8W8 (e4m3 or INT8): per-channel and per-row fp32 scales in the epilogue
+  constexpr bool A8W8 = PREC == MOE_PREC_FP8 || PREC == MOE_PREC_INT8;
   // MX: each stage also holds the E8M0 scales of its 4 K-groups: A [BM][4]
   // (one dword per row) and B [4][BN] (one byte per group row and column)
   constexpr int AS_OFF = A_BYTES + B_BYTES;
@@ -822,11 +844,11 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     }
   };
 
-  f32x4_t acc[MT][NTW];
+  typename O::acc_t acc[MT][NTW];  // fp32, or int32 for INT8
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTW; ++j) acc[i][j] = typename O::acc_t{0, 0, 0, 0};
 
   auto bcol = [&](int j) -> int {  // first LDS column of this wave's n-tile j
     if (SWIGLU) {
@@ -947,14 +969,14 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
       if (row >= row_end) continue;
-      const float rs = (PREC == MOE_PREC_FP8) ? asc[row] : 1.0f;  // MX: scales are in the MFMA
+      const float rs = A8W8 ? asc[row] : 1.0f;  // MX: scales are in the MFMA
       if (SWIGLU) {
 #pragma unroll
         for (int j = 0; j < NTW / 2; ++j) {
           const int ncol = nt * (BN / 2) + bcol(j) + col_in;
-          float hg = acc[i][j][v];
-          float hu = acc[i][j + NTW / 2][v];
-          if (PREC == MOE_PREC_FP8) {
+          float hg = static_cast<float>(acc[i][j][v]);
+          float hu = static_cast<float>(acc[i][j + NTW / 2][v]);
+          if (A8W8) {
             hg *= wsc[ncol] * rs;
             hu *= wsc[g.f + ncol] * rs;
             reinterpret_cast<float*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
@@ -968,8 +990,8 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const int ncol = nt * BN + bcol(j) + col_in;
-          float y = acc[i][j][v];
-          if (PREC == MOE_PREC_FP8) y *= wsc[ncol] * rs;
+          float y = static_cast<float>(acc[i][j][v]);
+          if (A8W8) y *= wsc[ncol] * rs;
           reinterpret_cast<uint16_t*>(obase)[static_cast<size_t>(row) * g.Nout + ncol] =
               f32_to_bf16(y);
         }
@@ -1343,7 +1365,10 @@ __global__ __launch_bounds__(kMaxExperts) void tile_offsets_kernel(const int32_t
   if (e == E - 1) tile_off[E + 1] = s[e] + (T_shared + BM - 1) / BM;
 }
 
-// FP8: per-row requantisation of the fp32 SwiGLU output; one block per row.
+// A8W8: per-row requantisation of the fp32 SwiGLU output, scale = max|row| /
+// Q and codes of a / scale: e4m3 (Q = 448) or int8 (Q = 127, half away from
+// zero); one block per row.
+template <bool I8>
 __global__ __launch_bounds__(256) void requant_kernel(const float* __restrict__ A, int f,
                                                       uint8_t* __restrict__ Aq,
                                                       float* __restrict__ a_scale) {
@@ -1359,11 +1384,13 @@ __global__ __launch_bounds__(256) void requant_kernel(const float* __restrict__ 
   if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float s = amax > 0.0f ? amax / (I8 ? 127.0f : 448.0f) : 1.0f;
   if (threadIdx.x == 0) a_scale[r] = s;
   for (int c = threadIdx.x * 4; c < f; c += 256 * 4) {
     float4 v = *reinterpret_cast<const float4*>(a + c);
-    *reinterpret_cast<uint32_t*>(Aq + r * f + c) = f32x4_to_e4m3x4(v.x / s, v.y / s, v.z / s, v.w / s);
+    *reinterpret_cast<uint32_t*>(Aq + r * f + c) =
+        I8 ? f32x4_to_i8x4(v.x / s, v.y / s, v.z / s, v.w / s)
+           : f32x4_to_e4m3x4(v.x / s, v.y / s, v.z / s, v.w / s);
   }
 }
 
@@ -1466,7 +1493,8 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   if (err != hipSuccess) return err;
   const int ub_m = (rows + BM - 1) / BM + (a.E < rows ? a.E : rows) + (T_sh + BM - 1) / BM;
   constexpr bool MX = PREC == MOE_PREC_MXFP8 || PREC == MOE_PREC_MXFP4;
-  constexpr bool Q8 = PREC == MOE_PREC_FP8 || MX;  // quantised activation codes into Linear2
+  constexpr bool A8W8 = PREC == MOE_PREC_FP8 || PREC == MOE_PREC_INT8;
+  constexpr bool Q8 = A8W8 || MX;  // quantised activation codes into Linear2
   // bytes of one row of the SwiGLU output as Linear2 reads it
   const size_t arow_bytes = PREC == MOE_PREC_MXFP4 ? a.f / 2 : static_cast<size_t>(a.f) * (Q8 ? 1 : 2);
 
@@ -1487,7 +1515,7 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   } else {
     g1.out = a.A;
     g1.out_sh = static_cast<char*>(a.A) +
-                static_cast<size_t>(rows) * a.f * (PREC == MOE_PREC_FP8 ? 4 : 2);
+                static_cast<size_t>(rows) * a.f * (A8W8 ? 4 : 2);
   }
   g1.offsets = a.offsets;
   g1.tile_off = a.tile_off;
@@ -1503,9 +1531,9 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
 
   const void* A2 = a.A;
   const char* as2 = nullptr;
-  if (PREC == MOE_PREC_FP8) {
+  if (A8W8) {
     const int arows = rows + T_sh;
-    hipLaunchKernelGGL(requant_kernel, dim3(arows), dim3(256), 0, stream,
+    hipLaunchKernelGGL(requant_kernel<PREC == MOE_PREC_INT8>, dim3(arows), dim3(256), 0, stream,
                        static_cast<const float*>(a.A), a.f, static_cast<uint8_t*>(a.Aq),
                        static_cast<float*>(a.a_scale));
     err = hipGetLastError();
@@ -1589,6 +1617,9 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // MXFP4: 128 x 256 tiles on 8 waves, a 2-stage ring of 128-value K-stages
   // plus two 6 KB scale windows (60 KB), two blocks per CU
   if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 2>(a, stream);
+  // INT8: the e4m3 tiles (128 x 256 on 8 waves, 3-stage ring) at every batch
+  // size (the 16-row decode kernel has no int8 form)
+  if (a.precision == MOE_PREC_INT8) return run_ffn<MOE_PREC_INT8, 128, 256, 2, 4, 3>(a, stream);
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 

@@ -28,7 +28,7 @@ int check_shape(const moe_shape* s) {
     return MOE_ERR_INVALID_ARG;
   if (s->topk > s->experts || s->topk > kMaxTopk) return MOE_ERR_INVALID_ARG;
   if (s->has_shared != 0 && s->has_shared != 1) return MOE_ERR_INVALID_ARG;
-  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (s->precision < MOE_PREC_F32 || s->precision > MOE_PREC_INT8) return MOE_ERR_INVALID_ARG;
   if (s->experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->hidden % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (s->inter % (s->precision >= MOE_PREC_FP8 ? 128 : 64) != 0) return MOE_ERR_UNSUPPORTED;

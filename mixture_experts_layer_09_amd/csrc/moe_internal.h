@@ -49,6 +49,16 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, f
   return static_cast<uint32_t>(w);
 }
 
+// INT8 code of v (the A8W8 block's ⌊v⌉): rounded half away from zero
+// (roundf), clamped to [-127, 127], as the low byte of the result.
+__device__ __forceinline__ uint32_t f32_to_i8(float v) {
+  const float r = fminf(fmaxf(roundf(v), -127.0f), 127.0f);
+  return static_cast<uint32_t>(static_cast<int>(r)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t f32x4_to_i8x4(float a, float b, float c, float d) {
+  return f32_to_i8(a) | (f32_to_i8(b) << 8) | (f32_to_i8(c) << 16) | (f32_to_i8(d) << 24);
+}
+
 // fp32 -> OCP e2m1 (FP4) code in the low 4 bits: nearest of 0, 0.5, 1, 1.5,
 // 2, 3, 4, 6 with ties to the even code (the midpoints 0.25, 1.25, 2.5, 5
 // round down, 0.75, 1.75, 3.5 round up), saturating at 6; the sign is bit 3.
@@ -93,7 +103,8 @@ inline bool is_mx(int precision) {
 }
 // bytes of the activation scales of one row of `n` elements
 inline size_t row_scale_bytes(int precision, size_t n) {
-  return is_mx(precision) ? n / 32 : (precision == MOE_PREC_FP8 ? 4 : 0);
+  if (is_mx(precision)) return n / 32;
+  return (precision == MOE_PREC_FP8 || precision == MOE_PREC_INT8) ? 4 : 0;
 }
 
 // Bytes of split-K partial gate logits the router may use (0 if none).

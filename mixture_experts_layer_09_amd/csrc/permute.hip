@@ -13,10 +13,11 @@
 //      of blk_cnt[b'][e] over b' < b (the block's base row for expert e).
 //   3. scatter: one block per token; dst_row[t*k+j] = base + rank, src_tok of
 //      that row = t, and the token row is copied to each of its k rows with
-//      16-byte loads and stores.  For A8W8 the row is quantised to e4m3 once
-//      (scale = max|x| / 448) and the codes are what is copied.
-// Row order inside an expert block is ascending t*k+j: the stable order the
-// pages leave to the implementation ("any fixed order").
+//      16-byte loads and stores.  For A8W8 the row is quantised once, to
+//      e4m3 (scale = max|x| / 448) or int8 (scale = max|x| / 127), and the
+//      codes are what is copied; MX rows are quantised per 32-value group.
+// Row order inside an expert block is ascending t*k+j, a stable order; the
+// pages leave the order to the implementation as long as it is fixed.
 #include "moe_internal.h"
 
 namespace moe {
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
         }
       }
     }
-  } else if (PREC != MOE_PREC_FP8) {
+  } else if (PREC != MOE_PREC_FP8 && PREC != MOE_PREC_INT8) {
     __syncthreads();
     const int esz = (PREC == MOE_PREC_F32) ? 4 : 2;
     const int nvec = h * esz / 16;
@@ -210,7 +211,13 @@ __global__ __launch_bounds__(256) void scatter_kernel(
       }
     }
   } else {
-    // A8W8: scale = max|x| / 448 (1 for a zero row), codes = RNE_sat(x / scale)
+    // A8W8: scale = max|x| / Q (1 for a zero row), codes of x / scale: e4m3
+    // (Q = 448, RNE, saturating) or int8 (Q = 127, rounded half away from 0)
+    constexpr bool I8 = PREC == MOE_PREC_INT8;
+    constexpr float Q = I8 ? 127.0f : 448.0f;
+    auto enc4 = [](float a, float b, float c, float d) {
+      return I8 ? f32x4_to_i8x4(a, b, c, d) : f32x4_to_e4m3x4(a, b, c, d);
+    };
     float* xp_scale = static_cast<float*>(xp_scale_v);
     float* x_scale = static_cast<float*>(x_scale_v);
     const uint16_t* xr = static_cast<const uint16_t*>(X) + static_cast<size_t>(t) * h;
@@ -228,18 +235,18 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     if ((tid & 63) == 0) s_red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    const float s = amax > 0.0f ? amax / Q : 1.0f;
     if (tid == 0) x_scale[t] = s;
     if (tid < k && s_dst[tid] >= 0) xp_scale[s_dst[tid]] = s;
     uint8_t* xq = static_cast<uint8_t*>(Xq) + static_cast<size_t>(t) * h;
     for (int c = tid * 8; c < h; c += 256 * 8) {
       uint4 v = *reinterpret_cast<const uint4*>(xr + c);
       uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t lo = f32x4_to_e4m3x4(__uint_as_float(w[0] << 16) / s,
+      uint32_t lo = enc4(__uint_as_float(w[0] << 16) / s,
                                     __uint_as_float(w[0] & 0xffff0000u) / s,
                                     __uint_as_float(w[1] << 16) / s,
                                     __uint_as_float(w[1] & 0xffff0000u) / s);
-      uint32_t hi = f32x4_to_e4m3x4(__uint_as_float(w[2] << 16) / s,
+      uint32_t hi = enc4(__uint_as_float(w[2] << 16) / s,
                                     __uint_as_float(w[2] & 0xffff0000u) / s,
                                     __uint_as_float(w[3] << 16) / s,
                                     __uint_as_float(w[3] & 0xffff0000u) / s);
@@ -290,6 +297,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_MXFP8>, dim3(a.T), dim3(256), 0, stream, a.T,
                          a.h, a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok,
                          a.Xp, a.xp_scale, a.Xq, a.x_scale);
+      break;
+    case MOE_PREC_INT8:
+      hipLaunchKernelGGL(scatter_kernel<MOE_PREC_INT8>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,
+                         a.E, a.k, a.ids, a.blk_cnt, a.local_rank, a.X, a.dst_row, a.src_tok, a.Xp,
+                         a.xp_scale, a.Xq, a.x_scale);
       break;
     default:
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_FP8>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,

@@ -31,9 +31,11 @@ class GpuLayer:
         self.dev = inp["X"].device
         self.mx = wl.precision in ("mxfp8", "mxfp4")
         self.fp4 = wl.precision == "mxfp4"
-        self.fp8 = wl.precision in ("fp8", "mxfp8", "mxfp4")   # quantised activation codes
+        self.i8 = wl.precision == "int8"
+        self.fp8 = wl.precision in ("fp8", "int8", "mxfp8", "mxfp4")   # quantised activation codes
         self.out_dtype = torch.float32 if wl.precision == "fp32" else torch.bfloat16
-        self.xp_dtype = torch.float8_e4m3fn if self.fp8 else self.out_dtype
+        self.xp_dtype = (torch.int8 if self.i8 else torch.float8_e4m3fn) if self.fp8 \
+            else self.out_dtype
 
     def _i32(self, *shape):
         return torch.empty(shape, dtype=torch.int32, device=self.dev)
@@ -67,7 +69,7 @@ class GpuLayer:
                      x_scale=torch.empty((wl.T, g), dtype=torch.uint8, device=self.dev))
         elif self.fp8:
             o.update(xp_scale=self._f32(n),
-                     Xq=torch.empty((wl.T, wl.hidden), dtype=torch.float8_e4m3fn, device=self.dev),
+                     Xq=torch.empty((wl.T, wl.hidden), dtype=self.xp_dtype, device=self.dev),
                      x_scale=self._f32(wl.T))
         else:
             o.update(xp_scale=None, Xq=None, x_scale=None)

@@ -69,11 +69,13 @@ def _shape(**kw):
 @pytest.mark.parametrize("kw,expect", [
     (dict(tokens=0), INVALID), (dict(topk=0), INVALID), (dict(topk=9), INVALID),
     (dict(experts=40, topk=17), INVALID), (dict(has_shared=2), INVALID),
-    (dict(precision=5), INVALID), (dict(precision=-1), INVALID), (dict(hidden=96), UNSUPPORTED),
+    (dict(precision=6), INVALID), (dict(precision=-1), INVALID), (dict(hidden=96), UNSUPPORTED),
     (dict(inter=96), UNSUPPORTED), (dict(inter=192, precision="fp8"), UNSUPPORTED),
     (dict(hidden=384, inter=128, precision="fp8"), UNSUPPORTED),
     (dict(hidden=384, inter=128, precision="mxfp8"), UNSUPPORTED),
     (dict(hidden=384, inter=128, precision="mxfp4"), UNSUPPORTED),
+    (dict(hidden=384, inter=128, precision="int8"), UNSUPPORTED),
+    (dict(hidden=256, inter=192, precision="int8"), UNSUPPORTED),
     (dict(experts=600, topk=2), UNSUPPORTED),
 ])
 def test_bad_shapes_rejected(kw, expect):

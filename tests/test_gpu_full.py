@@ -24,9 +24,9 @@ from tests.helpers import bits, f64, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "int8": 2e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
 DELTA = 1e-5
-FULL = ["v4pro_bf16", "v4pro_fp8", "v4pro_mxfp8", "v4pro_mxfp4", "llama_bf16", "decode_hash_bf16", "decode_score_bf16",
+FULL = ["v4pro_bf16", "v4pro_fp8", "v4pro_int8", "v4pro_mxfp8", "v4pro_mxfp4", "llama_bf16", "decode_hash_bf16", "decode_score_bf16",
         "ep_share_bf16"]
 
 
@@ -112,9 +112,9 @@ def test_full_size_forward(name):
             q = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
         assert np.array_equal(Xp_rows, q)
         assert np.array_equal(bits(p["xp_scale"])[rows], s)
-    elif wl.precision == "fp8":
-        q, s = oracle.quantize_rows_f32(inp["X"][torch.from_numpy(src).long().cuda()].float()
-                                        .cpu().numpy())
+    elif wl.precision in ("fp8", "int8"):
+        quant = oracle.quantize_rows_f32 if wl.precision == "fp8" else oracle.quantize_rows_i8_f32
+        q, s = quant(inp["X"][torch.from_numpy(src).long().cuda()].float().cpu().numpy())
         assert np.array_equal(Xp_rows, q)
         assert np.array_equal(bits(p["xp_scale"])[rows], s)
     else:

@@ -26,7 +26,7 @@ from tests.helpers import bits, f64, oracle_layer, oracle_route, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
+TOL = {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2, "int8": 2e-2, "mxfp8": 5e-2, "mxfp4": 5e-2}
 DELTA = 1e-5
 
 CASES = {
@@ -34,6 +34,7 @@ CASES = {
     "llama_small": ("llama_bf16", dict(T=512, hidden=256, experts=16, inter=128)),
     "v4pro_small": ("v4pro_bf16", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_fp8_small": ("v4pro_fp8", dict(T=256, hidden=512, experts=64, inter=256)),
+    "v4pro_int8_small": ("v4pro_int8", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_mxfp8_small": ("v4pro_mxfp8", dict(T=256, hidden=512, experts=64, inter=256)),
     "v4pro_mxfp4_small": ("v4pro_mxfp4", dict(T=256, hidden=512, experts=64, inter=256)),
     # K = 1024 and 512: the MXFP4 kernels' 512-value scale windows, several per row
@@ -123,8 +124,9 @@ def test_permute_bit_exact(name):
         assert np.array_equal(bits(p["Xq"]), q)
         assert np.array_equal(bits(p["Xp"]), q[d["src_tok"]])
         assert np.array_equal(bits(p["xp_scale"]), s[d["src_tok"]])
-    elif wl.precision == "fp8":
-        q, s = oracle.quantize_rows_f32(cpu["X"].float().numpy())
+    elif wl.precision in ("fp8", "int8"):
+        quant = oracle.quantize_rows_f32 if wl.precision == "fp8" else oracle.quantize_rows_i8_f32
+        q, s = quant(cpu["X"].float().numpy())
         assert np.array_equal(bits(p["x_scale"]), s)
         assert np.array_equal(bits(p["Xq"]), q)
         assert np.array_equal(bits(p["Xp"]), q[d["src_tok"]])
@@ -202,7 +204,7 @@ def test_forward(name):
 
 
 @pytest.mark.parametrize("name", ["v4pro_small", "tiny_fp32", "v4pro_fp8_small",
-                                  "v4pro_mxfp8_small", "v4pro_mxfp4_small"])
+                                  "v4pro_int8_small", "v4pro_mxfp8_small", "v4pro_mxfp4_small"])
 def test_forward_with_given_routing(name):
     """The mega_moe form: expert ids and weights are inputs (no router)."""
     _need_gpu()
@@ -228,7 +230,8 @@ def _edge(base, ids=None, **kw):
 
 
 @pytest.mark.parametrize("kind", ["one_token", "all_to_one_expert", "k_equals_E", "single_expert",
-                                  "fp8_all_to_one", "mxfp8_all_to_one", "mxfp8_decode",
+                                  "fp8_all_to_one", "int8_all_to_one", "int8_decode",
+                                  "mxfp8_all_to_one", "mxfp8_decode",
                                   "mxfp4_all_to_one", "mxfp4_decode",
                                   "decode_one_token"])
 def test_edge_cases(kind):
@@ -241,6 +244,9 @@ def test_edge_cases(kind):
         "single_expert": ("llama_bf16", dict(T=200, hidden=128, experts=1, topk=1, inter=64)),
         "fp8_all_to_one": ("v4pro_fp8", dict(T=300, hidden=256, experts=64, inter=128, topk=1,
                                               zipf=False)),
+        "int8_all_to_one": ("v4pro_int8", dict(T=300, hidden=256, experts=64, inter=128, topk=1,
+                                                zipf=False)),
+        "int8_decode": ("v4pro_int8", dict(T=3, hidden=512, experts=64, inter=256)),
         "mxfp8_all_to_one": ("v4pro_mxfp8", dict(T=300, hidden=256, experts=64, inter=128,
                                                   topk=1, zipf=False)),
         "mxfp8_decode": ("v4pro_mxfp8", dict(T=3, hidden=512, experts=64, inter=256)),
@@ -252,7 +258,8 @@ def test_edge_cases(kind):
     cpu, L = _edge(spec[0], **spec[1])
     wl = cpu["workload"]
     _log(f"[edge] {kind} {wl}")
-    if kind in ("all_to_one_expert", "fp8_all_to_one", "mxfp8_all_to_one", "mxfp4_all_to_one"):
+    if kind in ("all_to_one_expert", "fp8_all_to_one", "int8_all_to_one", "mxfp8_all_to_one",
+                "mxfp4_all_to_one"):
         ids = np.full((wl.T, 1), 37, np.int32)       # 300 rows: 3 tiles, ragged
         G = np.full((wl.T, 1), 0.75, np.float32)
         Y, _, _ = L.forward(torch.from_numpy(ids).cuda(), torch.from_numpy(G).cuda(), route=False)
