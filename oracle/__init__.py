@@ -89,6 +89,12 @@ def lib():
         L.oracle_layer_tokens.argtypes = [C.POINTER(_Layer), vp, vp, i32, vp, vp]
         L.oracle_expert_rows.argtypes = [C.POINTER(_Layer), vp, vp, i32, vp, vp]
         L.oracle_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_backward_tokens.restype = i32
+        L.oracle_backward_tokens.argtypes = [C.POINTER(_Layer), vp, vp, vp, i32, vp, vp, vp]
+        L.oracle_backward_weights.restype = i32
+        L.oracle_backward_weights.argtypes = [C.POINTER(_Layer), vp, vp, vp, i32, vp, vp, vp]
+        L.oracle_route_backward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, i32, i32, dbl,
+                                            vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -197,6 +203,28 @@ def route(X, Wg, k, *, gate_bias=None, beta=None, score="sigmoid", renorm=True, 
                        _p(_c(token_ids, np.int32)), _p(_c(tid2eid, np.int32)), _p(ids), _p(G),
                        _p(logits), _p(keys), _p(margin))
     return {"ids": ids, "G": G, "logits": logits, "keys": keys, "margin": margin}
+
+
+def route_backward(X, Wg, ids, dG, *, gate_bias=None, score="sigmoid", renorm=True, alpha=1.0,
+                   dX=None) -> dict:
+    """Router backward for the chosen ids and dG [T,k]: dl [T,E], dWg
+    [h,E], dgate_bias [E]; adds dl Wgᵀ into dX [T,h] (fp64) when given."""
+    X = np.ascontiguousarray(X)
+    Wg = np.ascontiguousarray(Wg, dtype=X.dtype)
+    T, h = X.shape
+    E = Wg.shape[1]
+    ids = _c(ids, np.int32)
+    k = ids.shape[1]
+    dl = np.empty((T, E), np.float64)
+    dWg = np.empty((h, E), np.float64)
+    db = np.empty(E, np.float64)
+    if dX is not None:
+        assert dX.dtype == np.float64 and dX.flags.c_contiguous and dX.shape == (T, h)
+    lib().oracle_route_backward(T, h, E, k, _elem_code(X), _p(X), _p(Wg),
+                                _p(_c(gate_bias, np.float64)), SCORES[score], int(bool(renorm)),
+                                float(alpha), _p(ids), _p(_c(dG, np.float64)), _p(dl), _p(dWg),
+                                _p(db), _p(dX))
+    return {"dl": dl, "dWg": dWg, "dgate_bias": db}
 
 
 def e2m1_decode(code: int) -> float:
@@ -322,6 +350,35 @@ class Layer:
         Y = np.empty((n, self.hidden), np.float64)
         lib().oracle_layer_tokens(C.byref(self._s), _p(ids), _p(G), n, _p(tok), _p(Y))
         return Y
+
+    def backward_tokens(self, ids, G, dY, tokens=None):
+        """(dX [n,h], dG [n,k]) of the experts' side for the listed tokens."""
+        ids = _c(ids, np.int32)
+        G = _c(G, np.float64)
+        dY = _c(dY, np.float64)
+        assert dY.shape == (self.T, self.hidden)
+        tok = None if tokens is None else _c(tokens, np.int32)
+        n = self.T if tok is None else len(tok)
+        dX = np.empty((n, self.hidden), np.float64)
+        dG = np.empty((n, self.k), np.float64)
+        st = lib().oracle_backward_tokens(C.byref(self._s), _p(ids), _p(G), _p(dY), n, _p(tok),
+                                          _p(dX), _p(dG))
+        assert st == 0, "backward needs an fp32 or bf16 layer"
+        return dX, dG
+
+    def backward_weights(self, ids, G, dY, experts):
+        """(dW1 [n,h,2f], dW2 [n,f,h]) of the listed experts (E = shared)."""
+        ids = _c(ids, np.int32)
+        G = _c(G, np.float64)
+        dY = _c(dY, np.float64)
+        ex = _c(np.atleast_1d(experts), np.int32)
+        n = len(ex)
+        dW1 = np.empty((n, self.hidden, 2 * self.inter), np.float64)
+        dW2 = np.empty((n, self.inter, self.hidden), np.float64)
+        st = lib().oracle_backward_weights(C.byref(self._s), _p(ids), _p(G), _p(dY), n, _p(ex),
+                                           _p(dW1), _p(dW2))
+        assert st == 0, "backward needs an fp32 or bf16 layer"
+        return dW1, dW2
 
     def expert_rows(self, offsets, src_tok, rows=None) -> np.ndarray:
         """Yp[r] = F_e(x_{src_tok[r]}) for dispatched rows r (r >= T*k: shared)."""

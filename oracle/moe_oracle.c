@@ -719,3 +719,248 @@ void oracle_combine(int T, int k, int hidden, const double* Yp, const int32_t* d
       for (int o = 0; o < hidden; ++o) y[o] += Ys[(size_t)t * hidden + o];
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* Backward, local part  ([V4] 反向的通信: the reverse chain on one      */
+/* device, unpermute -> expert dgrad / wgrad -> permute, which sums the */
+/* k copies; [V4] dX = Ȳ Wᵀ, dW = Xᵀ Ȳ for an expert linear; [MD] §1.8  */
+/* SwiGLU backward dA = dH ⊙ U, dU = dH ⊙ A, dG = dA ⊙ [σ(G) + A ⊙ (1 − */
+/* σ(G))] with A = SiLU(G))                                             */
+/* ------------------------------------------------------------------ */
+
+/* For one row x (fp64) through expert weights W1 [h,2f], W2 [f,h] of element
+ * type wdt and the upstream gradient dy [h] of its output: the expert output
+ * y (for dG), the SwiGLU output a [f], dh1 [2f] (gradient of the Linear1
+ * pre-activations, gate then up) and dx [h].  Buffers are the caller's. */
+static void swiglu_row_backward(int hidden, int f, const double* x, int wdt, const void* W1,
+                                const void* W2, const double* dy, double* h1, double* a,
+                                double* y, double* dh1, double* dx) {
+  for (int n = 0; n < 2 * f; ++n) h1[n] = 0.0;
+  for (int c = 0; c < hidden; ++c) {
+    double xc = x[c];
+    if (xc == 0.0) continue;
+    for (int n = 0; n < 2 * f; ++n) h1[n] += xc * elem(W1, wdt, (size_t)c * 2 * f + n);
+  }
+  for (int n = 0; n < f; ++n) a[n] = silu(h1[n]) * h1[f + n];
+  for (int o = 0; o < hidden; ++o) y[o] = 0.0;
+  for (int n = 0; n < f; ++n)
+    for (int o = 0; o < hidden; ++o) y[o] += a[n] * elem(W2, wdt, (size_t)n * hidden + o);
+  /* dH (gradient of the SwiGLU output) = dy W2ᵀ, then the SwiGLU backward */
+  for (int n = 0; n < f; ++n) {
+    double dH = 0.0;
+    for (int o = 0; o < hidden; ++o) dH += dy[o] * elem(W2, wdt, (size_t)n * hidden + o);
+    double g = h1[n], u = h1[f + n];
+    double sg = sigmoid(g), act = silu(g);
+    double dA = dH * u;       /* gradient of SiLU(g) */
+    dh1[f + n] = dH * act;    /* dU */
+    dh1[n] = dA * (sg + act * (1.0 - sg));
+  }
+  /* dx = dh1 W1ᵀ */
+  for (int c = 0; c < hidden; ++c) {
+    double s = 0.0;
+    for (int n = 0; n < 2 * f; ++n) s += dh1[n] * elem(W1, wdt, (size_t)c * 2 * f + n);
+    dx[c] = s;
+  }
+}
+
+static void expert_weight_ptrs(const oracle_layer* L, int e, const char** W1, const char** W2) {
+  size_t wb = (L->precision == 0) ? 4 : 2;
+  if (e == L->E) {
+    *W1 = (const char*)L->Ws1;
+    *W2 = (const char*)L->Ws2;
+  } else {
+    *W1 = (const char*)L->W1 + (size_t)e * L->hidden * 2 * L->inter * wb;
+    *W2 = (const char*)L->W2 + (size_t)e * L->inter * L->hidden * wb;
+  }
+}
+
+/* Layer backward for the listed tokens (all when tok == NULL), fp32 / bf16
+ * layers: given dY [T, hidden] (fp64), writes dX [ntok, hidden] (the expert
+ * part: sum over j of the routed experts' dx with upstream G[t,j] dY[t], plus
+ * the shared expert's with upstream dY[t]) and dG [ntok, k] (dG[t,j] =
+ * dY[t] . F_e(x_t), the unpermute backward of the gate weights).  Returns -1
+ * for a quantised layer. */
+int oracle_backward_tokens(const oracle_layer* L, const int32_t* ids, const double* G,
+                           const double* dY, int ntok, const int32_t* tok, double* dX,
+                           double* dG) {
+  if (L->precision > 1) return -1;
+  int h = L->hidden, f = L->inter, k = L->k;
+  int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16, wdt = w_dt(L->precision);
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * h);
+    double* dy = (double*)malloc(sizeof(double) * h);
+    double* h1 = (double*)malloc(sizeof(double) * 2 * f);
+    double* a = (double*)malloc(sizeof(double) * f);
+    double* y = (double*)malloc(sizeof(double) * h);
+    double* dh1 = (double*)malloc(sizeof(double) * 2 * f);
+    double* dx = (double*)malloc(sizeof(double) * h);
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < ntok; ++i) {
+      int t = tok ? tok[i] : i;
+      double* dxt = dX + (size_t)i * h;
+      for (int c = 0; c < h; ++c) {
+        x[c] = elem(L->X, xdt, (size_t)t * h + c);
+        dxt[c] = 0.0;
+      }
+      for (int j = 0; j < k; ++j) {
+        int e = ids[(size_t)t * k + j];
+        if (e < 0 || e >= L->E) {
+          dG[(size_t)i * k + j] = 0.0;
+          continue;
+        }
+        const char *W1, *W2;
+        expert_weight_ptrs(L, e, &W1, &W2);
+        double g = G[(size_t)t * k + j];
+        for (int o = 0; o < h; ++o) dy[o] = g * dY[(size_t)t * h + o];
+        swiglu_row_backward(h, f, x, wdt, W1, W2, dy, h1, a, y, dh1, dx);
+        double s = 0.0;
+        for (int o = 0; o < h; ++o) s += dY[(size_t)t * h + o] * y[o];
+        dG[(size_t)i * k + j] = s;
+        for (int c = 0; c < h; ++c) dxt[c] += dx[c];
+      }
+      if (L->has_shared) {
+        const char *W1, *W2;
+        expert_weight_ptrs(L, L->E, &W1, &W2);
+        swiglu_row_backward(h, f, x, wdt, W1, W2, dY + (size_t)t * h, h1, a, y, dh1, dx);
+        for (int c = 0; c < h; ++c) dxt[c] += dx[c];
+      }
+    }
+    free(x);
+    free(dy);
+    free(h1);
+    free(a);
+    free(y);
+    free(dh1);
+    free(dx);
+  }
+  return 0;
+}
+
+/* Weight gradients of the listed experts (e == E: the shared expert):
+ * dW1[e] = sum over the rows r routed to e of x_r^T dh1_r  ([hidden, 2f]),
+ * dW2[e] = sum of a_r^T dy_r  ([f, hidden]), where dy_r = G[t,j] dY[t] (dY[t]
+ * for the shared expert).  Rows are visited in ascending t*k+j.  dW1 / dW2
+ * are [nexp, ...] fp64.  Returns -1 for a quantised layer. */
+int oracle_backward_weights(const oracle_layer* L, const int32_t* ids, const double* G,
+                            const double* dY, int nexp, const int32_t* experts, double* dW1,
+                            double* dW2) {
+  if (L->precision > 1) return -1;
+  int h = L->hidden, f = L->inter, k = L->k, T = L->T;
+  int xdt = L->precision == 0 ? ORC_F32 : ORC_BF16, wdt = w_dt(L->precision);
+#pragma omp parallel
+  {
+    double* x = (double*)malloc(sizeof(double) * h);
+    double* dy = (double*)malloc(sizeof(double) * h);
+    double* h1 = (double*)malloc(sizeof(double) * 2 * f);
+    double* a = (double*)malloc(sizeof(double) * f);
+    double* y = (double*)malloc(sizeof(double) * h);
+    double* dh1 = (double*)malloc(sizeof(double) * 2 * f);
+    double* dx = (double*)malloc(sizeof(double) * h);
+#pragma omp for schedule(dynamic, 1)
+    for (int q = 0; q < nexp; ++q) {
+      int e = experts[q];
+      double* w1 = dW1 + (size_t)q * h * 2 * f;
+      double* w2 = dW2 + (size_t)q * f * h;
+      for (size_t i = 0; i < (size_t)h * 2 * f; ++i) w1[i] = 0.0;
+      for (size_t i = 0; i < (size_t)f * h; ++i) w2[i] = 0.0;
+      const char *W1, *W2;
+      expert_weight_ptrs(L, e, &W1, &W2);
+      for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < (e == L->E ? 1 : k); ++j) {
+          if (e != L->E && ids[(size_t)t * k + j] != e) continue;
+          if (e == L->E && !L->has_shared) continue;
+          double g = e == L->E ? 1.0 : G[(size_t)t * k + j];
+          for (int c = 0; c < h; ++c) x[c] = elem(L->X, xdt, (size_t)t * h + c);
+          for (int o = 0; o < h; ++o) dy[o] = g * dY[(size_t)t * h + o];
+          swiglu_row_backward(h, f, x, wdt, W1, W2, dy, h1, a, y, dh1, dx);
+          for (int c = 0; c < h; ++c) {
+            if (x[c] == 0.0) continue;
+            for (int n = 0; n < 2 * f; ++n) w1[(size_t)c * 2 * f + n] += x[c] * dh1[n];
+          }
+          for (int n = 0; n < f; ++n)
+            for (int o = 0; o < h; ++o) w2[(size_t)n * h + o] += a[n] * dy[o];
+        }
+      }
+    }
+    free(x);
+    free(dy);
+    free(h1);
+    free(a);
+    free(y);
+    free(dh1);
+    free(dx);
+  }
+  return 0;
+}
+
+/* Router backward ([V4] §路由张量: the mixing weights are the selected
+ * experts' continuous affinities, α a / Σ a with renorm, else α a; the
+ * selection itself is discrete and passes no gradient).  Given the chosen ids
+ * and dG [T,k], writes dl [T,E] (gradient of the gating logits: zero outside
+ * the chosen experts for sigmoid and sqrt(softplus); softmax spreads it over
+ * all experts), and, where not NULL, dWg [hidden,E] = Xᵀ dl, dgate_bias [E] =
+ * column sums of dl, and dX [T,hidden] += dl Wgᵀ. */
+void oracle_route_backward(int T, int hidden, int E, int k, int dt, const void* X, const void* Wg,
+                           const double* gate_bias, int score_fn, int renorm, double alpha,
+                           const int32_t* ids, const double* dG, double* dl, double* dWg,
+                           double* dgate_bias, double* dX) {
+  double* logits = (double*)malloc(sizeof(double) * (size_t)T * E);
+  double* aff = (double*)malloc(sizeof(double) * (size_t)T * E);
+  double* da = (double*)malloc(sizeof(double) * (size_t)E);
+  oracle_gate_logits(T, hidden, E, dt, X, Wg, gate_bias, logits);
+  oracle_affinity(T, E, score_fn, logits, aff);
+  for (int t = 0; t < T; ++t) {
+    const double* a = aff + (size_t)t * E;
+    const double* l = logits + (size_t)t * E;
+    double* dlt = dl + (size_t)t * E;
+    for (int e = 0; e < E; ++e) da[e] = 0.0;
+    double S = 0.0, dGa = 0.0;
+    for (int j = 0; j < k; ++j) S += a[ids[(size_t)t * k + j]];
+    for (int j = 0; j < k; ++j) dGa += dG[(size_t)t * k + j] * a[ids[(size_t)t * k + j]];
+    /* G_j = α a_j / S: dG_j/da_i = α (δ_ij / S − a_j / S²) */
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      double g = dG[(size_t)t * k + j];
+      da[e] += renorm ? alpha * (g / S - dGa / (S * S)) : alpha * g;
+    }
+    if (score_fn == ORC_SOFTMAX) {
+      double s = 0.0;
+      for (int e = 0; e < E; ++e) s += da[e] * a[e];
+      for (int e = 0; e < E; ++e) dlt[e] = a[e] * (da[e] - s);
+    } else if (score_fn == ORC_SQRT_SOFTPLUS) {
+      for (int e = 0; e < E; ++e) dlt[e] = da[e] == 0.0 ? 0.0 : da[e] * sigmoid(l[e]) / (2.0 * a[e]);
+    } else {
+      for (int e = 0; e < E; ++e) dlt[e] = da[e] * a[e] * (1.0 - a[e]);
+    }
+  }
+  if (dgate_bias) {
+    for (int e = 0; e < E; ++e) dgate_bias[e] = 0.0;
+    for (int t = 0; t < T; ++t)
+      for (int e = 0; e < E; ++e) dgate_bias[e] += dl[(size_t)t * E + e];
+  }
+  if (dWg) {
+#pragma omp parallel for schedule(static)
+    for (int c = 0; c < hidden; ++c) {
+      double* w = dWg + (size_t)c * E;
+      for (int e = 0; e < E; ++e) w[e] = 0.0;
+      for (int t = 0; t < T; ++t) {
+        double xc = elem(X, dt, (size_t)t * hidden + c);
+        if (xc == 0.0) continue;
+        for (int e = 0; e < E; ++e) w[e] += xc * dl[(size_t)t * E + e];
+      }
+    }
+  }
+  if (dX) {
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t)
+      for (int c = 0; c < hidden; ++c) {
+        double s = 0.0;
+        for (int e = 0; e < E; ++e) s += dl[(size_t)t * E + e] * elem(Wg, dt, (size_t)c * E + e);
+        dX[(size_t)t * hidden + c] += s;
+      }
+  }
+  free(logits);
+  free(aff);
+  free(da);
+}

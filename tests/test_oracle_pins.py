@@ -19,6 +19,7 @@ import torch
 
 import oracle
 import synth
+from tests import test_oracle_backward_pins as bwd
 from tests.helpers import bits, oracle_layer, oracle_route
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -656,6 +657,18 @@ PLANTED = {
     "i8scale": ("h1[n] = (double)acc[n] * (double)s_w1[n] * sx;",
                 "h1[n] = (double)acc[n] * (double)s_w1[n];",
                 lambda: test_int8_layer_is_the_dense_swiglu_of_dequantised_operands()),
+    # SwiGLU backward without the A (1 - sigma(G)) term of SiLU's derivative
+    "swiglu_bwd": ("dh1[n] = dA * (sg + act * (1.0 - sg));", "dh1[n] = dA * sg;",
+                   lambda: bwd.test_expert_gradients_match_finite_differences()),
+    # renormalised gate weights differentiated as if the sum were constant
+    "renorm_bwd": ("da[e] += renorm ? alpha * (g / S - dGa / (S * S)) : alpha * g;",
+                   "da[e] += renorm ? alpha * (g / S) : alpha * g;",
+                   lambda: bwd.test_router_and_full_input_gradients_match_finite_differences(
+                       "sigmoid", True, 2.5)),
+    # permute backward keeping one copy's gradient instead of summing the k copies
+    "permute_bwd": ("for (int c = 0; c < h; ++c) dxt[c] += dx[c];",
+                    "for (int c = 0; c < h; ++c) dxt[c] = dx[c];",
+                    lambda: bwd.test_expert_gradients_match_finite_differences()),
     # MX weight scale taken from the wrong group
     "mxscale": ("mx_pow2_table[S[(size_t)(c / 32) * N + n]]",
                 "mx_pow2_table[S[(size_t)((c + 32) / 32 % (c / 32 + 1)) * N + n]]",
