@@ -234,6 +234,45 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
                 float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/* Gradients written by moe_backward (device memory, bf16 unless noted). */
+typedef struct {
+  void* dX;           /* [T, hidden] out: gradient of X (experts, and router if opts) */
+  void* dW1;          /* [E, hidden, 2*inter] out (zeros for an expert without rows) */
+  void* dW2;          /* [E, inter, hidden] out */
+  void* dWs1;         /* [hidden, 2*inter] out, shared expert (NULL without one) */
+  void* dWs2;         /* [inter, hidden] out */
+  void* dWg;          /* [hidden, E] out, or NULL (router only) */
+  float* dgate_bias;  /* [E] fp32 out, or NULL (router only) */
+  float* dG;          /* [T, topk] fp32 out: gradient of gate_weights, or NULL */
+} moe_grads;
+
+/* Bytes of device workspace that moe_backward needs (0 if the shape is
+ * invalid); 256-byte aligned, no initialisation. */
+size_t moe_backward_workspace_size(const moe_shape* shape);
+
+/* The layer's local backward (the blog "Megatron-LM 的 MoE 并行", 反向的
+ * 通信, without its collectives): given the forward's inputs and routing
+ * (expert_ids, gate_weights as moe_route wrote them, or as the caller gave
+ * them) and the upstream gradient dY [T, hidden], writes the gradients in
+ * `grads`.  It recomputes the dispatch and the expert activations (Linear1
+ * pre-activations, SwiGLU output, Yp) in the workspace, then: unpermute
+ * backward (dYp[row(t,j)] = G[t,j] dY[t], dG[t,j] = dY[t] . Yp[row]), Linear2
+ * dgrad with the SwiGLU backward of "Megatron 分布式训练全维度并行技术文档"
+ * §1.8, dW2 = Aᵀ dYp, Linear1 dgrad, dW1 = Xpᵀ dH1 (per expert; the shared
+ * expert with upstream dY), permute backward (dX[t] = sum of its k rows'
+ * gradients + the shared expert's).  With opts (the options of the forward's
+ * router) the router is differentiated too: only the chosen experts'
+ * continuous affinities carry gradient (the selection is discrete, beta gets
+ * none); dWg = Xᵀ dl, dgate_bias = column sums of dl and dl Wgᵀ is added to
+ * dX.  With opts == NULL, gate_weights are treated as inputs and dG is their
+ * gradient.  Weight gradients are fp32 sums rounded once to bf16; dX sums
+ * its parts in fp32.  BF16 layers only (MOE_ERR_UNSUPPORTED otherwise); hidden
+ * a multiple of 256, inter of 128, and with opts experts a multiple of 64. */
+int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                 const void* Wg, const moe_expert_weights* weights, const int32_t* expert_ids,
+                 const float* gate_weights, const void* dY, const moe_grads* grads,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Synchronises `stream`, then reports (and clears) the device-side error
  * flag in the workspace: MOE_ERR_DEVICE_DATA if an earlier moe_permute,
  * moe_route or moe_forward on this workspace saw an expert id outside

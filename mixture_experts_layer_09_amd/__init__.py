@@ -1,4 +1,4 @@
-"""Routed MoE layer forward pass for MI355X (gfx950): Python binding of libmoe.
+"""Routed MoE layer (forward and local backward) for MI355X (gfx950): Python binding of libmoe.
 
 The binding only marshals arguments: torch tensors give device pointers and
 the current HIP stream, and every step runs in the HIP kernels of libmoe.so
@@ -22,7 +22,8 @@ SCORE = {"sigmoid": 0, "softmax": 1, "sqrt_softplus": 2}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_DATA"}
 EXPORTED = ["moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_check_device_error", "moe_status_string"]
+            "moe_forward", "moe_check_device_error", "moe_status_string",
+            "moe_backward_workspace_size", "moe_backward"]
 
 
 class MoeError(RuntimeError):
@@ -47,6 +48,12 @@ class moe_expert_weights(C.Structure):
     _fields_ = [("W1", C.c_void_p), ("w1_scale", C.c_void_p), ("W2", C.c_void_p),
                 ("w2_scale", C.c_void_p), ("Ws1", C.c_void_p), ("ws1_scale", C.c_void_p),
                 ("Ws2", C.c_void_p), ("ws2_scale", C.c_void_p)]
+
+
+class moe_grads(C.Structure):
+    _fields_ = [("dX", C.c_void_p), ("dW1", C.c_void_p), ("dW2", C.c_void_p), ("dWs1", C.c_void_p),
+                ("dWs2", C.c_void_p), ("dWg", C.c_void_p), ("dgate_bias", C.c_void_p),
+                ("dG", C.c_void_p)]
 
 
 _lib = None
@@ -79,6 +86,12 @@ def lib():
                                   C.POINTER(moe_expert_weights), vp, vp, vp, vp, C.c_size_t, vp]
         L.moe_check_device_error.restype = i32
         L.moe_check_device_error.argtypes = [vp, C.c_size_t, vp]
+        L.moe_backward_workspace_size.restype = C.c_size_t
+        L.moe_backward_workspace_size.argtypes = [S]
+        L.moe_backward.restype = i32
+        L.moe_backward.argtypes = [S, C.POINTER(moe_route_opts), vp, vp,
+                                   C.POINTER(moe_expert_weights), vp, vp, vp,
+                                   C.POINTER(moe_grads), vp, C.c_size_t, vp]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [i32]
         _lib = L
@@ -121,6 +134,12 @@ def make_weights(W1, W2, w1_scale=None, w2_scale=None, Ws1=None, Ws2=None, ws1_s
                  ws2_scale=None) -> moe_expert_weights:
     return moe_expert_weights(_ptr(W1), _ptr(w1_scale), _ptr(W2), _ptr(w2_scale), _ptr(Ws1),
                               _ptr(ws1_scale), _ptr(Ws2), _ptr(ws2_scale))
+
+
+def make_grads(dX, dW1, dW2, dWs1=None, dWs2=None, dWg=None, dgate_bias=None,
+               dG=None) -> moe_grads:
+    return moe_grads(_ptr(dX), _ptr(dW1), _ptr(dW2), _ptr(dWs1), _ptr(dWs2), _ptr(dWg),
+                     _ptr(dgate_bias), _ptr(dG))
 
 
 # ------------------------------------------------------------------ C ABI, same names
@@ -167,6 +186,18 @@ def moe_forward(shape, opts, X, Wg, weights, expert_ids, gate_weights, Y, worksp
         workspace.numel(), _stream(stream)))
 
 
+def moe_backward_workspace_size(shape: moe_shape) -> int:
+    return int(lib().moe_backward_workspace_size(C.byref(shape)))
+
+
+def moe_backward(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads, workspace,
+                 stream=None):
+    _check("moe_backward", lib().moe_backward(
+        C.byref(shape), None if opts is None else C.byref(opts), _ptr(X), _ptr(Wg),
+        C.byref(weights), _ptr(expert_ids), _ptr(gate_weights), _ptr(dY), C.byref(grads),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 def moe_check_device_error(workspace, stream=None) -> int:
     """Returns the status (0 or MOE_ERR_DEVICE_DATA); raises on other errors."""
     st = lib().moe_check_device_error(_ptr(workspace), workspace.numel(), _stream(stream))
@@ -175,10 +206,11 @@ def moe_check_device_error(workspace, stream=None) -> int:
     return st
 
 
-def alloc_workspace(shape: moe_shape, device="cuda") -> torch.Tensor:
-    """A uint8 device tensor of moe_workspace_size bytes (torch allocations are
-    256-byte aligned)."""
-    n = moe_workspace_size(shape)
+def alloc_workspace(shape: moe_shape, device="cuda", backward=False) -> torch.Tensor:
+    """A uint8 device tensor of moe_workspace_size (or, with backward,
+    moe_backward_workspace_size) bytes; torch allocations are 256-byte
+    aligned."""
+    n = moe_backward_workspace_size(shape) if backward else moe_workspace_size(shape)
     if n == 0:
         raise MoeError("moe_workspace_size", -1)
     ws = torch.empty(n, dtype=torch.uint8, device=device)

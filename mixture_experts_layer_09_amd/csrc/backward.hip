@@ -1,0 +1,739 @@
+// backward.hip -- the layer's local backward on one GPU (bf16).
+//
+// The reverse chain of the blog "Megatron-LM 的 MoE 并行" (反向的通信) without
+// its collectives: unpermute backward (the upstream gradient dY[t] goes to
+// each of the token's k rows, weighted by G[t,j]; dG[t,j] = dY[t] . Yp[row]),
+// the experts' dgrad (dX = Ȳ Wᵀ) and wgrad (dW = Xᵀ Ȳ), the SwiGLU backward
+// of "Megatron 分布式训练全维度并行技术文档" §1.8 fused into the Linear2
+// dgrad, the permute backward summing the k copies, and the router's
+// backward through the chosen experts' continuous affinities.
+//
+// Kernels:
+//   dgrad_kernel  out[r] = dO[r] W[e]ᵀ over the expert blocks (ragged rows,
+//                 as in the forward).  Both operands are K-contiguous rows
+//                 (the gradient rows [rows, K] and the weights as stored,
+//                 [N, K]), DMA'd to LDS in 32-value K-stages (64-byte rows,
+//                 chunk swizzle (r >> 2) & 3) and read as plain 16-byte
+//                 fragments of v_mfma_f32_16x16x32_bf16.  Optional epilogue:
+//                 the SwiGLU backward, which reads the saved pre-activations.
+//   wgrad_kernel  dW[e] = A_eᵀ B_e over the rows of expert e (ragged K).  Both
+//                 operands are [rows, dim] (dim contiguous); tiles of 32 rows
+//                 go through registers (rows past the expert's block load as
+//                 zeros) into LDS and are read with the transposing
+//                 ds_read_b64_tr_b16.  An expert without rows gets zeros.
+#include "lds_dma.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) short i16x8s_t;
+
+__device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// ---------------------------------------------------------------- elementwise
+// A = SiLU(H1[:, :f]) * H1[:, f:], 8 columns per thread.
+__global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restrict__ H1, int f,
+                                                         long rows, uint16_t* __restrict__ A) {
+  const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
+  const long per = f / 8;
+  if (i >= rows * per) return;
+  const long r = i / per;
+  const int c = static_cast<int>(i % per) * 8;
+  const uint4 g = *reinterpret_cast<const uint4*>(H1 + r * 2 * f + c);
+  const uint4 u = *reinterpret_cast<const uint4*>(H1 + r * 2 * f + f + c);
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a0 = silu(bfv(gw[q] & 0xFFFF)) * bfv(uw[q] & 0xFFFF);
+    const float a1 = silu(bfv(gw[q] >> 16)) * bfv(uw[q] >> 16);
+    o[q] = f32_to_bf16(a0) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
+  }
+  *reinterpret_cast<uint4*>(A + r * f + c) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+// Unpermute backward, one block (256 threads) per token: dYp[row(t,j)] =
+// G[t,j] dY[t] and dG[t,j] = dY[t] . Yp[row(t,j)] (fp32 sums in a fixed
+// order).  h % 8 == 0.
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    int h, int k, const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Yp,
+    const int32_t* __restrict__ dst_row, const float* __restrict__ G, uint16_t* __restrict__ dYp,
+    float* __restrict__ dG) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const uint16_t* dy = dY + static_cast<size_t>(t) * h;
+  for (int j = 0; j < k; ++j) {
+    const int r = dst_row[static_cast<size_t>(t) * k + j];
+    if (r < 0) {  // skipped assignment (uniform over the block)
+      if (threadIdx.x == 0) dG[static_cast<size_t>(t) * k + j] = 0.0f;
+      continue;
+    }
+    const float g = G[static_cast<size_t>(t) * k + j];
+    const uint16_t* y = Yp + static_cast<size_t>(r) * h;
+    uint16_t* o = dYp + static_cast<size_t>(r) * h;
+    float s = 0.0f;
+    for (int c = threadIdx.x * 8; c < h; c += 256 * 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(dy + c);
+      const uint4 b = *reinterpret_cast<const uint4*>(y + c);
+      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+      uint32_t ow[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = bfv(aw[q] & 0xFFFF), a1 = bfv(aw[q] >> 16);
+        s = fmaf(a0, bfv(bw[q] & 0xFFFF), s);
+        s = fmaf(a1, bfv(bw[q] >> 16), s);
+        ow[q] = f32_to_bf16(g * a0) | (static_cast<uint32_t>(f32_to_bf16(g * a1)) << 16);
+      }
+      *reinterpret_cast<uint4*>(o + c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) dG[static_cast<size_t>(t) * k + j] = s;
+  }
+}
+
+// Router backward, one wave per token: affinities a from the recomputed keys
+// (a + beta, or a for hash routing), the gradient of the mixing weights
+// (G_j = alpha a_j / S with renorm, else alpha a_j) onto the chosen experts'
+// affinities, then onto the logits: sigmoid a(1 - a), sqrt(softplus)
+// sigma(l) / (2a) with sigma(l) = 1 - exp(-a^2), softmax a (da - sum da a).
+__global__ __launch_bounds__(256) void route_backward_kernel(
+    int T, int E, int k, const float* __restrict__ keys, const float* __restrict__ beta, int hash,
+    int score_fn, int renorm, float alpha, const int32_t* __restrict__ ids,
+    const float* __restrict__ dG, float* __restrict__ dl32, uint16_t* __restrict__ dl16) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  constexpr int kQ = kMaxExperts / 64;
+  const float* key = keys + static_cast<size_t>(t) * E;
+  auto aff = [&](int e) { return key[e] - ((beta && !hash) ? beta[e] : 0.0f); };
+  // lane j < k: choice j
+  int my_id = 0;
+  float my_g = 0.0f, my_a = 0.0f;
+  if (lane < k) {
+    my_id = ids[static_cast<size_t>(t) * k + lane];
+    my_g = dG[static_cast<size_t>(t) * k + lane];
+    my_a = (my_id >= 0 && my_id < E) ? aff(my_id) : 0.0f;
+  }
+  const float S = wave_sum(my_a);
+  const float dGa = wave_sum(my_g * my_a);
+  float a[kQ], da[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int e = lane + 64 * q;
+    a[q] = (e < E) ? aff(e) : 0.0f;
+    da[q] = 0.0f;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int id = __shfl(my_id, j, 64);
+    const float g = __shfl(my_g, j, 64);
+    const float d = renorm ? alpha * (g / S - dGa / (S * S)) : alpha * g;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+      if (lane + 64 * q == id) da[q] += d;
+  }
+  float sda = 0.0f;
+  if (score_fn == MOE_SCORE_SOFTMAX) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) sda += da[q] * a[q];
+    sda = wave_sum(sda);
+  }
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const int e = lane + 64 * q;
+    if (e >= E) continue;
+    float d;
+    if (score_fn == MOE_SCORE_SOFTMAX)
+      d = a[q] * (da[q] - sda);
+    else if (score_fn == MOE_SCORE_SQRT_SOFTPLUS)
+      d = da[q] == 0.0f ? 0.0f : da[q] * (1.0f - expf(-a[q] * a[q])) / (2.0f * a[q]);
+    else
+      d = da[q] * a[q] * (1.0f - a[q]);
+    dl32[static_cast<size_t>(t) * E + e] = d;
+    dl16[static_cast<size_t>(t) * E + e] = f32_to_bf16(d);
+  }
+}
+
+// out[e] = sum over t of dl[t, e] (one thread per expert, ascending t).
+__global__ __launch_bounds__(256) void colsum_kernel(int T, int E, const float* __restrict__ dl,
+                                                     float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.0f;
+  for (int t = 0; t < T; ++t) s += dl[static_cast<size_t>(t) * E + e];
+  out[e] = s;
+}
+
+// Permute backward, one block per token: dX[t] = sum_j dXp[row(t,j)] (+ the
+// shared expert's row) (+ the router's dl Wgᵀ row), fp32 sums, bf16 out.
+__global__ __launch_bounds__(256) void permute_backward_kernel(
+    int h, int k, const uint16_t* __restrict__ dXp, const int32_t* __restrict__ dst_row,
+    const uint16_t* __restrict__ dXs, const uint16_t* __restrict__ dXr, uint16_t* __restrict__ dX) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x * 8; c < h; c += 256 * 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+    auto add = [&](const uint16_t* p) {
+      const uint4 v = *reinterpret_cast<const uint4*>(p + c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bfv(w[q] & 0xFFFF);
+        acc[2 * q + 1] += bfv(w[q] >> 16);
+      }
+    };
+    for (int j = 0; j < k; ++j) {
+      const int r = dst_row[static_cast<size_t>(t) * k + j];
+      if (r >= 0) add(dXp + static_cast<size_t>(r) * h);
+    }
+    if (dXs) add(dXs + static_cast<size_t>(t) * h);
+    if (dXr) add(dXr + static_cast<size_t>(t) * h);
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = f32_to_bf16(acc[2 * q]) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * q + 1])) << 16);
+    *reinterpret_cast<uint4*>(dX + static_cast<size_t>(t) * h + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// tile_off[e+1] = tile_off[e] + ceil(rows_e / BM) for e < E, then the shared
+// rows (T_sh); E may be 0 (one plain segment of T_sh rows).
+__global__ __launch_bounds__(kMaxExperts) void bwd_tile_offsets_kernel(
+    const int32_t* __restrict__ offsets, int E, int T_sh, int BM, int32_t* __restrict__ tile_off) {
+  __shared__ int32_t s[kMaxExperts];
+  const int e = threadIdx.x;
+  s[e] = (e < E) ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+  __syncthreads();
+  for (int o = 1; o < kMaxExperts; o <<= 1) {
+    const int v = (e >= o) ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  if (e < E) tile_off[e + 1] = s[e];
+  if (e == 0) {
+    tile_off[0] = 0;
+    tile_off[E + 1] = (E > 0 ? s[E - 1] : 0) + (T_sh + BM - 1) / BM;
+  }
+}
+
+// ---------------------------------------------------------------- dgrad
+struct DgradArgs {
+  const void* A;      // [rows, K] bf16 gradient rows (segment blocks by offsets)
+  const void* A_sh;   // [T, K] shared rows
+  const void* W;      // [E, N, K] bf16 (K contiguous)
+  const void* W_sh;   // [N, K]
+  void* out;          // [rows, N] (SWB: [rows, 2N])
+  void* out_sh;
+  const void* h1;     // SWB: [rows, 2N] bf16 pre-activations (gate, up)
+  const void* h1_sh;
+  const int32_t* offsets;
+  const int32_t* tile_off;
+  int E, K, N, T, n_tiles;
+};
+
+// The block's (segment, m-tile, n-tile): XCD x = blockIdx % 8 runs one
+// contiguous range of items; items go in groups of 1024 / BM m-tiles, n-tile
+// major (as the forward's grouped GEMM).
+template <int BM>
+__device__ __forceinline__ bool dgrad_item(const DgradArgs& g, int& seg, int& mtile, int& nt) {
+  constexpr int GROUP_M = 1024 / BM;
+  const int E = g.E, NT = g.n_tiles;
+  const int total = g.tile_off[E + 1] * NT;
+  if (static_cast<int>(blockIdx.x) >= total) return false;
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int item = x * per + min(x, rem) + slot;
+  const int mq = item / NT;
+  int lo = 0, hi = E;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.tile_off[mid] <= mq)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  seg = lo;
+  const int mt_seg = g.tile_off[seg + 1] - g.tile_off[seg];
+  const int local = item - g.tile_off[seg] * NT;
+  const int grp = local / (GROUP_M * NT);
+  const int gsz = min(GROUP_M, mt_seg - grp * GROUP_M);
+  const int rin = local - grp * GROUP_M * NT;
+  nt = rin / gsz;
+  mtile = grp * GROUP_M + rin % gsz;
+  return true;
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool SWB>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
+void dgrad_kernel(DgradArgs g) {
+  constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int ROWB = 64;  // 32 bf16 of one row per stage
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INSTS = A_BYTES / 1024, B_INSTS = B_BYTES / 1024;  // 16 rows per DMA
+  constexpr int A_OPS = A_INSTS / NW, B_OPS = B_INSTS / NW;
+  constexpr int WM = BM / WAVES_M, MT = WM / 16, WN = BN / WAVES_N, NTW = WN / 16;
+  static_assert(A_INSTS % NW == 0 && B_INSTS % NW == 0, "tiles must split evenly over the waves");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  int seg, mtile, nt;
+  if (!dgrad_item<BM>(g, seg, mtile, nt)) return;
+  const bool shared = (seg == g.E);
+  const size_t ld = static_cast<size_t>(g.K) * 2;
+  int row0, row_end;
+  const char *Abase, *Wbase;
+  if (!shared) {
+    row0 = g.offsets[seg] + mtile * BM;
+    row_end = g.offsets[seg + 1];
+    Abase = static_cast<const char*>(g.A);
+    Wbase = static_cast<const char*>(g.W) + static_cast<size_t>(seg) * g.N * ld;
+  } else {
+    row0 = mtile * BM;
+    row_end = g.T;
+    Abase = static_cast<const char*>(g.A_sh);
+    Wbase = static_cast<const char*>(g.W_sh);
+  }
+  const int rows_valid = min(BM, row_end - row0);
+  const int mt_live = __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
+  auto swz = [](int r) { return (r >> 2) & 3; };
+
+  const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * ld);
+  const char* b_base = uniform_ptr(Wbase + static_cast<size_t>(nt) * BN * ld);
+  uint32_t a_voff[A_OPS], b_voff[B_OPS];
+#pragma unroll
+  for (int q = 0; q < A_OPS; ++q) {
+    const int r = (wave * A_OPS + q) * 16 + lane / 4;
+    a_voff[q] = static_cast<uint32_t>(min(r, row_end - 1 - row0)) * static_cast<uint32_t>(ld) +
+                ((lane % 4) ^ swz(r)) * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < B_OPS; ++q) {
+    const int r = (wave * B_OPS + q) * 16 + lane / 4;
+    b_voff[q] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld) + ((lane % 4) ^ swz(r)) * 16;
+  }
+  const int a_live = __builtin_amdgcn_readfirstlane(max(0, min(A_OPS, (rows_valid + 15) / 16 - wave * A_OPS)));
+  const int ops_w = a_live + B_OPS;
+  auto issue = [&](int kt, int slot) {
+    char* st = smem + slot * STAGE;
+#pragma unroll
+    for (int q = 0; q < A_OPS; ++q)
+      if (q < a_live) dma16(a_base + static_cast<size_t>(kt) * ROWB, a_voff[q], st + (wave * A_OPS + q) * 1024);
+#pragma unroll
+    for (int q = 0; q < B_OPS; ++q)
+      dma16(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q], st + A_BYTES + (wave * B_OPS + q) * 1024);
+  };
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int kg = lane >> 4;  // fragment chunk: K values 8 kg .. 8 kg + 7 of the stage
+  int a_off[MT], b_off[NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int r = wm * WM + i * 16 + (lane & 15);
+    a_off[i] = r * ROWB + ((kg ^ swz(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int r = wn * WN + j * 16 + (lane & 15);
+    b_off[j] = A_BYTES + r * ROWB + ((kg ^ swz(r)) << 4);
+  }
+  auto compute = [&](int slot) {
+    if (mt_live == 0) return;
+    const char* st = smem + slot * STAGE;
+    bf16x8_t bfr[NTW], af[MT];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off[j]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+
+  const int KT = g.K / 32;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s);
+  for (int k0 = 0; k0 < KT; k0 += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      const int kt = k0 + s;
+      if (kt < KT) {
+        // stage kt is in LDS once at most the stages issued after it are in flight
+        const int after = min(STAGES - 2, KT - 1 - kt);
+        wait_vmcnt_rt(after * ops_w);
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+        compute(s);
+      }
+    }
+  }
+
+  // ------------------------------------------------ epilogue
+  uint16_t* obase = static_cast<uint16_t*>(shared ? g.out_sh : g.out);
+  const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
+  const int col_in = lane & 15;
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i >= mt_live) continue;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+      if (row >= row_end) continue;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int n = nt * BN + wn * WN + j * 16 + col_in;
+        const float d = acc[i][j][v];
+        if constexpr (SWB) {
+          // dH = d; H1 = (gate G, up U); A = SiLU(G): dU = dH * A and
+          // dG = dH * U * (sigma(G) + A (1 - sigma(G)))
+          const size_t rb = static_cast<size_t>(row) * 2 * g.N;
+          const float gt = bfv(hbase[rb + n]), up = bfv(hbase[rb + g.N + n]);
+          const float sg = 1.0f / (1.0f + expf(-gt));
+          const float act = gt * sg;
+          obase[rb + n] = f32_to_bf16(d * up * (sg + act * (1.0f - sg)));
+          obase[rb + g.N + n] = f32_to_bf16(d * act);
+        } else {
+          obase[static_cast<size_t>(row) * g.N + n] = f32_to_bf16(d);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- wgrad
+struct WgradArgs {
+  const void* A;     // [rows, M] bf16 (routed rows in expert blocks)
+  const void* A_sh;  // [T, M]
+  const void* B;     // [rows, N]
+  const void* B_sh;  // [T, N]
+  void* out;         // [E, M, N] bf16
+  void* out_sh;      // [M, N]
+  const int32_t* offsets;
+  int E, M, N, T, has_shared;
+};
+
+// Swizzle of 16-byte chunks in a [32][W] bf16 tile read by ds_read_b64_tr_b16
+// (as the forward's B tiles), folded into the row's chunk count.
+template <int CH>
+__device__ __forceinline__ int wg_swz(int r) {
+  return (2 * ((r & 3) + 4 * ((r >> 3) & 1))) & (CH - 1);
+}
+
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
+void wgrad_kernel(WgradArgs g) {
+  constexpr int NW = WAVES_M * WAVES_N, NTH = 64 * NW;
+  constexpr int ACH = BM / 8, BCH = BN / 8;          // 16-byte chunks per tile row
+  constexpr int A_TILE = 32 * BM * 2, B_TILE = 32 * BN * 2;
+  constexpr int A_PT = 32 * ACH / NTH, B_PT = 32 * BCH / NTH;  // chunk loads per thread
+  static_assert(A_PT * NTH == 32 * ACH && B_PT * NTH == 32 * BCH, "tile loads must split evenly");
+  constexpr int WM = BM / WAVES_M, MT = WM / 16, WN = BN / WAVES_N, NTW = WN / 16;
+  __shared__ __attribute__((aligned(1024))) char smem[2][A_TILE + B_TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int MTt = g.M / BM, NTt = g.N / BN;
+  const int total = (g.E + g.has_shared) * MTt * NTt;
+  if (static_cast<int>(blockIdx.x) >= total) return;
+  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int item = x * per + min(x, rem) + slot;  // XCD x: a contiguous range
+  const int seg = item / (MTt * NTt);
+  const int mt = (item / NTt) % MTt, nt = item % NTt;
+  const bool shared = (seg == g.E);
+  const int k0 = shared ? 0 : g.offsets[seg];
+  const int k1 = shared ? g.T : g.offsets[seg + 1];
+  const uint16_t* Ab = static_cast<const uint16_t*>(shared ? g.A_sh : g.A) + mt * BM;
+  const uint16_t* Bb = static_cast<const uint16_t*>(shared ? g.B_sh : g.B) + nt * BN;
+  uint16_t* ob = static_cast<uint16_t*>(shared ? g.out_sh : g.out) +
+                 (shared ? 0 : static_cast<size_t>(seg) * g.M * g.N);
+
+  uint4 ra[A_PT], rb[B_PT];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < A_PT; ++q) {
+      const int i = tid + q * NTH, r = i / ACH, c = i % ACH;
+      const int row = k0 + kt * 32 + r;
+      ra[q] = row < k1 ? *reinterpret_cast<const uint4*>(Ab + static_cast<size_t>(row) * g.M + c * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < B_PT; ++q) {
+      const int i = tid + q * NTH, r = i / BCH, c = i % BCH;
+      const int row = k0 + kt * 32 + r;
+      rb[q] = row < k1 ? *reinterpret_cast<const uint4*>(Bb + static_cast<size_t>(row) * g.N + c * 8)
+                       : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+    char* st = smem[buf];
+#pragma unroll
+    for (int q = 0; q < A_PT; ++q) {
+      const int i = tid + q * NTH, r = i / ACH, c = i % ACH;
+      *reinterpret_cast<uint4*>(st + r * BM * 2 + ((c ^ wg_swz<ACH>(r)) << 4)) = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < B_PT; ++q) {
+      const int i = tid + q * NTH, r = i / BCH, c = i % BCH;
+      *reinterpret_cast<uint4*>(st + A_TILE + r * BN * 2 + ((c ^ wg_swz<BCH>(r)) << 4)) = rb[q];
+    }
+  };
+  // transposing-read offsets: lane (column p of a 16-column block, K group
+  // kgr) reads rows 8 kgr + 4 h + p / 4, 4 columns from (p % 4) * 4
+  const int kgr = lane >> 4, p = lane & 15;
+  int ao[MT][2], bo[NTW][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * kgr + 4 * h + (p >> 2);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int col = wm * WM + i * 16 + (p & 3) * 4;
+      ao[i][h] = r * BM * 2 + (((col >> 3) ^ wg_swz<ACH>(r)) << 4) + (col & 7) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int col = wn * WN + j * 16 + (p & 3) * 4;
+      bo[j][h] = A_TILE + r * BN * 2 + (((col >> 3) ^ wg_swz<BCH>(r)) << 4) + (col & 7) * 2;
+    }
+  }
+  auto frag = [](const char* st, const int (&o)[2]) {
+    const i16x4_t lo4 = ds_read_tr16(st + o[0]);
+    const i16x4_t hi4 = ds_read_tr16(st + o[1]);
+    const i16x8s_t v = i16x8s_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+
+  f32x4_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nk = (k1 - k0 + 31) / 32;
+  if (nk > 0) {
+    load(0);
+    store(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) load(kt + 1);
+    const char* st = smem[kt & 1];
+    bf16x8_t af[MT], bfr[NTW];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = frag(st, ao[i]);
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) bfr[j] = frag(st, bo[j]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NTW; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    if (kt + 1 < nk) store((kt + 1) & 1);
+    __syncthreads();
+  }
+  const int col_in = lane & 15;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int m = mt * BM + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int n = nt * BN + wn * WN + j * 16 + col_in;
+        ob[static_cast<size_t>(m) * g.N + n] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launches
+constexpr int kDgradBM = 128;
+
+hipError_t dgrad(const DgradArgs& in, int rows, int T_sh, bool swb, hipStream_t stream) {
+  DgradArgs g = in;
+  hipLaunchKernelGGL(bwd_tile_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, stream, g.offsets,
+                     g.E, T_sh, kDgradBM, const_cast<int32_t*>(g.tile_off));
+  const long ub_m = (rows + kDgradBM - 1) / kDgradBM + (g.E < rows ? g.E : rows) +
+                    (T_sh + kDgradBM - 1) / kDgradBM;
+  if (g.N % 256 == 0) {
+    g.n_tiles = g.N / 256;
+    const dim3 grid(static_cast<unsigned>(ub_m * g.n_tiles));
+    if (swb)
+      hipLaunchKernelGGL((dgrad_kernel<kDgradBM, 256, 2, 4, 3, true>), grid, dim3(512), 0, stream, g);
+    else
+      hipLaunchKernelGGL((dgrad_kernel<kDgradBM, 256, 2, 4, 3, false>), grid, dim3(512), 0, stream, g);
+  } else {
+    g.n_tiles = g.N / 128;
+    const dim3 grid(static_cast<unsigned>(ub_m * g.n_tiles));
+    if (swb)
+      hipLaunchKernelGGL((dgrad_kernel<kDgradBM, 128, 2, 2, 3, true>), grid, dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((dgrad_kernel<kDgradBM, 128, 2, 2, 3, false>), grid, dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t wgrad(const WgradArgs& g, hipStream_t stream) {
+  const long segs = g.E + g.has_shared;
+  if (g.N % 256 == 0) {
+    const long grid = segs * (g.M / 128) * (g.N / 256);
+    hipLaunchKernelGGL((wgrad_kernel<128, 256, 2, 4>), dim3(static_cast<unsigned>(grid)), dim3(512),
+                       0, stream, g);
+  } else if (g.N % 128 == 0) {
+    const long grid = segs * (g.M / 128) * (g.N / 128);
+    hipLaunchKernelGGL((wgrad_kernel<128, 128, 2, 2>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, stream, g);
+  } else {
+    const long grid = segs * (g.M / 128) * (g.N / 64);
+    hipLaunchKernelGGL((wgrad_kernel<128, 64, 2, 2>), dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, void* A, hipStream_t stream) {
+  const long n = rows * (f / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<const uint16_t*>(H1), f, rows, static_cast<uint16_t*>(A));
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
+  const int rows = a.T * a.k;
+  const int T_sh = a.has_shared ? a.T : 0;
+  const size_t h = a.h, f = a.f;
+  hipError_t e;
+  // unpermute backward: dYp and dG
+  hipLaunchKernelGGL(combine_backward_kernel, dim3(a.T), dim3(256), 0, stream, a.h, a.k,
+                     static_cast<const uint16_t*>(a.dY), static_cast<const uint16_t*>(a.Yp),
+                     a.dst_row, a.G, static_cast<uint16_t*>(a.dYp), a.dG);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // Linear2 dgrad with the SwiGLU backward: dH1 (the shared expert's
+  // upstream gradient is dY itself)
+  DgradArgs d2{};
+  d2.A = a.dYp;
+  d2.A_sh = a.dY;
+  d2.W = a.W2;
+  d2.W_sh = a.Ws2;
+  d2.out = a.dH1;
+  d2.out_sh = static_cast<char*>(a.dH1) + static_cast<size_t>(rows) * 2 * f * 2;
+  d2.h1 = a.H1;
+  d2.h1_sh = static_cast<const char*>(a.H1) + static_cast<size_t>(rows) * 2 * f * 2;
+  d2.offsets = a.offsets;
+  d2.tile_off = a.tile_b;
+  d2.E = a.E;
+  d2.K = a.h;
+  d2.N = a.f;
+  d2.T = a.T;
+  if ((e = dgrad(d2, rows, T_sh, true, stream)) != hipSuccess) return e;
+  // Linear2 wgrad: dW2[e] = A_eᵀ dYp_e (shared: Aᵀ dY)
+  WgradArgs w2{};
+  w2.A = a.Aact;
+  w2.A_sh = static_cast<const char*>(a.Aact) + static_cast<size_t>(rows) * f * 2;
+  w2.B = a.dYp;
+  w2.B_sh = a.dY;
+  w2.out = a.dW2;
+  w2.out_sh = a.dWs2;
+  w2.offsets = a.offsets;
+  w2.E = a.E;
+  w2.M = a.f;
+  w2.N = a.h;
+  w2.T = a.T;
+  w2.has_shared = a.has_shared;
+  if ((e = wgrad(w2, stream)) != hipSuccess) return e;
+  // Linear1 dgrad: dXp = dH1 W1ᵀ (shared rows after the routed ones)
+  DgradArgs d1{};
+  d1.A = a.dH1;
+  d1.A_sh = d2.out_sh;
+  d1.W = a.W1;
+  d1.W_sh = a.Ws1;
+  d1.out = a.dXp;
+  d1.out_sh = static_cast<char*>(a.dXp) + static_cast<size_t>(rows) * h * 2;
+  d1.offsets = a.offsets;
+  d1.tile_off = a.tile_b;
+  d1.E = a.E;
+  d1.K = 2 * a.f;
+  d1.N = a.h;
+  d1.T = a.T;
+  if ((e = dgrad(d1, rows, T_sh, false, stream)) != hipSuccess) return e;
+  // Linear1 wgrad: dW1[e] = Xp_eᵀ dH1_e (shared: Xᵀ dH1_sh)
+  WgradArgs w1{};
+  w1.A = a.Xp;
+  w1.A_sh = a.X;
+  w1.B = a.dH1;
+  w1.B_sh = d2.out_sh;
+  w1.out = a.dW1;
+  w1.out_sh = a.dWs1;
+  w1.offsets = a.offsets;
+  w1.E = a.E;
+  w1.M = a.h;
+  w1.N = 2 * a.f;
+  w1.T = a.T;
+  w1.has_shared = a.has_shared;
+  if ((e = wgrad(w1, stream)) != hipSuccess) return e;
+  // router: dl, dWg = Xᵀ dl, dgate_bias, dXr = dl Wgᵀ
+  const void* dXr = nullptr;
+  if (a.route) {
+    hipLaunchKernelGGL(route_backward_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.T, a.E,
+                       a.k, a.keys, a.beta, a.hash, a.score_fn, a.renorm, a.alpha, a.ids, a.dG,
+                       a.dl32, static_cast<uint16_t*>(a.dl16));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.dgate_bias) {
+      hipLaunchKernelGGL(colsum_kernel, dim3((a.E + 255) / 256), dim3(256), 0, stream, a.T, a.E,
+                         a.dl32, a.dgate_bias);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (a.dWg) {
+      WgradArgs wr{};
+      wr.A_sh = a.X;
+      wr.B_sh = a.dl16;
+      wr.out_sh = a.dWg;
+      wr.E = 0;
+      wr.M = a.h;
+      wr.N = a.E;
+      wr.T = a.T;
+      wr.has_shared = 1;
+      if ((e = wgrad(wr, stream)) != hipSuccess) return e;
+    }
+    DgradArgs dr{};
+    dr.A_sh = a.dl16;
+    dr.W_sh = a.Wg;  // [h, E] = [N, K]
+    dr.out_sh = a.dXr;
+    dr.offsets = a.offsets;  // not read with E = 0
+    dr.tile_off = a.tile_b;
+    dr.E = 0;
+    dr.K = a.E;
+    dr.N = a.h;
+    dr.T = a.T;
+    if ((e = dgrad(dr, 0, a.T, false, stream)) != hipSuccess) return e;
+    dXr = a.dXr;
+  }
+  // permute backward: dX = sum of the k rows + shared + router
+  hipLaunchKernelGGL(permute_backward_kernel, dim3(a.T), dim3(256), 0, stream, a.h, a.k,
+                     static_cast<const uint16_t*>(a.dXp), a.dst_row,
+                     a.has_shared ? static_cast<const uint16_t*>(d1.out_sh) : nullptr,
+                     static_cast<const uint16_t*>(dXr), static_cast<uint16_t*>(a.dX));
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -43,6 +43,7 @@
 // x_scale[r]; the SwiGLU output is written in fp32 and requantised per row
 // (scale = max|A[r]| / 448, or / 127 for INT8) by requant_kernel; Linear2
 // dequantises with w2_scale[e, n] * a_scale[r].
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -417,82 +418,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 // s_waitcnt vmcnt(n) leaves exactly the later stages in flight, then a plain
 // s_barrier (no fence, which would drain all of them) publishes the stage.
 
-// One DMA instruction: 16 bytes per lane from sbase + voff to LDS lds_dst +
-// 16 * lane (sbase and lds_dst are wave-uniform; lds_dst goes through M0).
-// Written as inline asm so that the compiler, which would otherwise make
-// every later LDS read wait for all DMA in flight, leaves the waiting to
-// wait_vmcnt; the memory clobber keeps LDS reads and other memory operations
-// on their side of it.
-__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
-}
-
-// As dma16 with 4 bytes per lane (LDS lds_dst + 4 * lane).
-__device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, char* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
-}
-
-// A pointer the compiler may not prove wave-uniform, moved to scalar registers.
-__device__ __forceinline__ const char* uniform_ptr(const char* p) {
-  const uint64_t v = reinterpret_cast<uintptr_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 16].
-__device__ __forceinline__ void wait_vmcnt_rt(int n) {
-  switch (n) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<1>(); break;
-    case 2: wait_vmcnt<2>(); break;
-    case 3: wait_vmcnt<3>(); break;
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 9: wait_vmcnt<9>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 11: wait_vmcnt<11>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 13: wait_vmcnt<13>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    case 15: wait_vmcnt<15>(); break;
-    default: wait_vmcnt<16>(); break;
-  }
-}
-
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
-
-__device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_t*)(p));
-}
-
-typedef __attribute__((ext_vector_type(2))) int i32x2v_t;
-
-__device__ __forceinline__ i32x2v_t ds_read_tr8(const char* p) {
-  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (__attribute__((address_space(3))) i32x2v_t*)(p));
-}
+// (dma16, dma4, uniform_ptr, wait_vmcnt, ds_read_tr16/8: lds_dma.h)
 
 // Operand layout of one precision in the DMA pipeline (see above).
 //   bf16: K-stage 32 elements; A rows 64 B (4 chunks, swizzle (r>>2)&3); B
@@ -1597,6 +1523,36 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t stream) {
+  constexpr int BM = 128;
+  const int T_sh = a.has_shared ? a.T : 0;
+  hipLaunchKernelGGL(tile_offsets_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.offsets, a.E,
+                     T_sh, BM, a.tile_off);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int ub_m = (a.rows + BM - 1) / BM + (a.E < a.rows ? a.E : a.rows) + (T_sh + BM - 1) / BM;
+  GemmArgs g{};
+  g.A = a.A;
+  g.A_sh = a.A_sh;
+  g.W = a.W;
+  g.W_sh = a.W_sh;
+  g.out = a.out;
+  g.out_sh = a.out_sh;
+  g.offsets = a.offsets;
+  g.tile_off = a.tile_off;
+  g.E = a.E;
+  g.K = a.K;
+  g.Nw = a.N;
+  g.Nout = a.N;
+  g.T = a.T;
+  if (a.N % 256 == 0) {
+    g.n_tiles = a.N / 256;
+    return launch_gemm<MOE_PREC_BF16, BM, 256, 2, 2, false, 3>(g, ub_m, stream);
+  }
+  g.n_tiles = a.N / 128;
+  return launch_gemm<MOE_PREC_BF16, BM, 128, 2, 2, false, 2>(g, ub_m, stream);
+}
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   const int rows = a.T * a.k;

@@ -296,6 +296,148 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
   return hip_status(e);
 }
 
+size_t moe_backward_workspace_size(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  return make_bwd_layout(*shape).total;
+}
+
+int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+                 const moe_expert_weights* weights, const int32_t* expert_ids,
+                 const float* gate_weights, const void* dY, const moe_grads* grads,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  // the backward GEMMs' tiles: 256-column Linear1 outputs, 128-row weight tiles
+  if (shape->hidden % 256 != 0 || shape->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_weights(shape, weights)) != MOE_OK) return st;
+  if (!X || !expert_ids || !gate_weights || !dY || !grads) return MOE_ERR_INVALID_ARG;
+  if (!grads->dX || !grads->dW1 || !grads->dW2) return MOE_ERR_INVALID_ARG;
+  if (shape->has_shared && (!grads->dWs1 || !grads->dWs2)) return MOE_ERR_INVALID_ARG;
+  if (opts) {
+    if ((st = check_route_opts(opts)) != MOE_OK) return st;
+    if (!Wg) return MOE_ERR_INVALID_ARG;
+    // the router's dWg tiles are 64 experts wide, its dgrad K-stages 32
+    if (shape->experts % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  if (!aligned16({X, Wg, dY, grads->dX, grads->dW1, grads->dW2, grads->dWs1, grads->dWs2,
+                  grads->dWg}))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
+  const BwdLayout B = make_bwd_layout(*shape);
+  if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
+  const Layout L = make_layout(*shape);
+  void* ws = workspace;
+  const int T = shape->tokens, k = shape->topk, E = shape->experts;
+  const int rows = T * k;
+  const size_t f = shape->inter;
+
+  hipError_t e = launch_clear_flag(at<int32_t>(ws, L.flag), stream);
+  // the forward's dispatch
+  if (e == hipSuccess) {
+    PermuteArgs p = permute_args(shape, expert_ids, X, at<int32_t>(ws, L.counts),
+                                 at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.dst_row),
+                                 at<int32_t>(ws, L.src_tok), at<void>(ws, L.Xp), nullptr, nullptr,
+                                 nullptr, ws);
+    e = launch_permute(p, stream);
+  }
+  // router keys (a + beta), for the router's backward
+  if (e == hipSuccess && opts) {
+    RouteArgs r = route_args(shape, opts, X, Wg, at<int32_t>(ws, B.ids_s), at<float>(ws, B.G_s),
+                             at<float>(ws, B.keys), ws);
+    e = launch_route(r, stream);
+  }
+  // recompute: H1 = X W1 per row (gate, up), A = SwiGLU(H1), Yp = A W2
+  if (e == hipSuccess) {
+    LinearArgs l1{};
+    l1.A = at<void>(ws, L.Xp);
+    l1.A_sh = X;
+    l1.W = weights->W1;
+    l1.W_sh = weights->Ws1;
+    l1.out = at<void>(ws, B.H1);
+    l1.out_sh = at<char>(ws, B.H1) + static_cast<size_t>(rows) * 2 * f * 2;
+    l1.offsets = at<int32_t>(ws, L.offsets);
+    l1.tile_off = at<int32_t>(ws, L.tile_off);
+    l1.E = E;
+    l1.K = shape->hidden;
+    l1.N = 2 * shape->inter;
+    l1.T = T;
+    l1.rows = rows;
+    l1.has_shared = shape->has_shared;
+    e = launch_grouped_linear_bf16(l1, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_swiglu_bf16(at<void>(ws, B.H1), shape->inter,
+                           static_cast<long>(rows) + (shape->has_shared ? T : 0),
+                           at<void>(ws, B.Aact), stream);
+  if (e == hipSuccess) {
+    LinearArgs l2{};
+    l2.A = at<void>(ws, B.Aact);
+    l2.W = weights->W2;
+    l2.out = at<void>(ws, L.Yp);
+    l2.offsets = at<int32_t>(ws, L.offsets);
+    l2.tile_off = at<int32_t>(ws, L.tile_off);
+    l2.E = E;
+    l2.K = shape->inter;
+    l2.N = shape->hidden;
+    l2.T = T;
+    l2.rows = rows;
+    l2.has_shared = 0;
+    e = launch_grouped_linear_bf16(l2, stream);
+  }
+  if (e == hipSuccess) {
+    BackwardArgs b{};
+    b.T = T;
+    b.h = shape->hidden;
+    b.E = E;
+    b.k = k;
+    b.f = shape->inter;
+    b.has_shared = shape->has_shared;
+    b.route = opts != nullptr;
+    if (opts) {
+      b.score_fn = opts->score_fn;
+      b.renorm = opts->renorm;
+      b.alpha = opts->alpha;
+      b.hash = (opts->token_ids && opts->tid2eid) ? 1 : 0;
+      b.beta = opts->expert_bias;
+    }
+    b.X = X;
+    b.Wg = Wg;
+    b.W1 = weights->W1;
+    b.W2 = weights->W2;
+    b.Ws1 = weights->Ws1;
+    b.Ws2 = weights->Ws2;
+    b.ids = expert_ids;
+    b.G = gate_weights;
+    b.dY = dY;
+    b.offsets = at<int32_t>(ws, L.offsets);
+    b.dst_row = at<int32_t>(ws, L.dst_row);
+    b.Xp = at<void>(ws, L.Xp);
+    b.Yp = at<void>(ws, L.Yp);
+    b.H1 = at<void>(ws, B.H1);
+    b.Aact = at<void>(ws, B.Aact);
+    b.dYp = at<void>(ws, B.dYp);
+    b.dH1 = at<void>(ws, B.dH1);
+    b.dXp = at<void>(ws, B.dXp);
+    b.dXr = at<void>(ws, B.dXr);
+    b.keys = at<float>(ws, B.keys);
+    b.dG = grads->dG ? grads->dG : at<float>(ws, B.dG);
+    b.dl32 = at<float>(ws, B.dl32);
+    b.dl16 = at<void>(ws, B.dl16);
+    b.tile_off = at<int32_t>(ws, L.tile_off);
+    b.tile_b = at<int32_t>(ws, B.tile_b);
+    b.dX = grads->dX;
+    b.dWg = opts ? grads->dWg : nullptr;
+    b.dgate_bias = opts ? grads->dgate_bias : nullptr;
+    b.dW1 = grads->dW1;
+    b.dW2 = grads->dW2;
+    b.dWs1 = grads->dWs1;
+    b.dWs2 = grads->dWs2;
+    e = launch_backward(b, stream);
+  }
+  return hip_status(e);
+}
+
 int moe_check_device_error(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < kAlign)
     return MOE_ERR_WORKSPACE;

@@ -228,4 +228,115 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream);
 
+// Plain grouped linear (bf16, fp32 accumulation, no activation): out[r] =
+// A[r] W[e] for the rows r of expert e's block [offsets[e], offsets[e+1]),
+// then the shared rows (A_sh, W_sh, out_sh; T rows) when has_shared.  W is
+// [E, K, N] (N contiguous); A rows K, out rows N elements.
+struct LinearArgs {
+  const void* A;
+  const void* A_sh;
+  const void* W;
+  const void* W_sh;
+  void* out;
+  void* out_sh;
+  const int32_t* offsets;
+  int32_t* tile_off;  // [E+2] scratch
+  int E, K, N, T, rows, has_shared;
+};
+hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t stream);
+
+// Workspace of the backward: the forward's regions (make_layout) followed by
+// the recomputed activations and the gradients in flight.
+struct BwdLayout {
+  size_t H1;       // [arows, 2f] bf16: Linear1 pre-activations (gate, up)
+  size_t Aact;     // [arows, f] bf16: SwiGLU output
+  size_t dYp;      // [rows, h] bf16: G-weighted upstream gradient per assignment
+  size_t dH1;      // [arows, 2f] bf16: gradient of the pre-activations
+  size_t dXp;      // [arows, h] bf16: dgrad of the dispatched rows (+ shared)
+  size_t dXr;      // [T, h] bf16: router part of dX
+  size_t keys;     // [T, E] fp32: recomputed router keys
+  size_t ids_s;    // [T, k] int32 scratch of the recomputed router
+  size_t G_s;      // [T, k] fp32 scratch
+  size_t dG;       // [T, k] fp32
+  size_t dl32;     // [T, E] fp32: gradient of the gating logits
+  size_t dl16;     // [T, E] bf16
+  size_t tile_b;   // [E+2] int32: m-tile prefix of the dgrad kernels
+  size_t total;
+};
+inline BwdLayout make_bwd_layout(const moe_shape& s) {
+  const Layout F = make_layout(s);
+  BwdLayout B{};
+  size_t T = s.tokens, h = s.hidden, E = s.experts, k = s.topk, f = s.inter;
+  size_t rows = T * k, arows = rows + (s.has_shared ? T : 0);
+  size_t o = F.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  B.H1 = take(arows * 2 * f * 2);
+  B.Aact = take(arows * f * 2);
+  B.dYp = take(rows * h * 2);
+  B.dH1 = take(arows * 2 * f * 2);
+  B.dXp = take(arows * h * 2);
+  B.dXr = take(T * h * 2);
+  B.keys = take(T * E * 4);
+  B.ids_s = take(T * k * 4);
+  B.G_s = take(T * k * 4);
+  B.dG = take(T * k * 4);
+  B.dl32 = take(T * E * 4);
+  B.dl16 = take(T * E * 2);
+  B.tile_b = take((E + 2) * 4);
+  B.total = o;
+  return B;
+}
+
+struct BackwardArgs {
+  int T, h, E, k, f, has_shared;
+  int route;  // 1: differentiate the router (score_fn, renorm, alpha, beta, hash below)
+  int score_fn, renorm, hash;
+  float alpha;
+  const float* beta;
+  const void* X;      // [T, h] bf16
+  const void* Wg;     // [h, E] bf16
+  const void* W1;     // [E, h, 2f]
+  const void* W2;     // [E, f, h]
+  const void* Ws1;
+  const void* Ws2;
+  const int32_t* ids; // [T, k] the forward's routing
+  const float* G;     // [T, k]
+  const void* dY;     // [T, h] bf16
+  // the forward's dispatch and recomputed activations (workspace)
+  const int32_t* offsets;
+  const int32_t* dst_row;
+  const void* Xp;
+  const void* Yp;     // [rows, h] bf16
+  // workspace regions (BwdLayout)
+  void* H1;
+  void* Aact;
+  void* dYp;
+  void* dH1;
+  void* dXp;
+  void* dXr;
+  const float* keys;
+  float* dG;
+  float* dl32;
+  void* dl16;
+  int32_t* tile_off;  // forward linears' m-tile prefix scratch
+  int32_t* tile_b;
+  // outputs
+  void* dX;
+  void* dWg;
+  float* dgate_bias;
+  void* dW1;
+  void* dW2;
+  void* dWs1;
+  void* dWs2;
+};
+// Everything after the forward recompute: combine backward, router backward
+// (when route), the experts' dgrad and wgrad, permute backward.
+hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
+// A = SiLU(H1[:, :f]) * H1[:, f:] for `rows` rows (bf16).
+hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, void* A, hipStream_t stream);
+
 }  // namespace moe
