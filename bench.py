@@ -239,6 +239,95 @@ def copy_probe(nbytes: int, reps: int = 5):
     return 0
 
 
+def backward_work(wl, counts):
+    """FLOPs and HBM bytes the local backward must do: the recomputed forward
+    (Linear1 and Linear2 over every row), the dgrad and wgrad of both linears
+    (each the forward's FLOPs again) and the router's two GEMMs; bytes: the
+    active experts' weights read once and their gradients written once, X
+    and dY read, dX written, the router's gradient."""
+    h, f, k, T, E = wl.hidden, wl.inter, wl.topk, wl.T, wl.experts
+    rows = T * k + (T if wl.shared else 0)
+    fwd = 2.0 * rows * (h * 2 * f + f * h)
+    flops = 3.0 * fwd + 2 * (2.0 * T * h * E)
+    active = int((counts > 0).sum()) + (1 if wl.shared else 0)
+    nbytes = 2 * active * 3.0 * h * f * 2 + 3 * T * h * 2 + 2 * h * E * 2
+    return flops, nbytes
+
+
+def bench_backward(args, wl, inp, shape):
+    """Times moe_backward (recompute + backward, router on) with HIP events on
+    its launch stream; one JSON line."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_09_amd as moe
+    if wl.precision != "bf16":
+        print(json.dumps({"error": "the backward is built for bf16 layers"}))
+        return 2
+    T, h, E, k, f = wl.T, wl.hidden, wl.experts, wl.topk, wl.inter
+    ws = moe.alloc_workspace(shape)
+    opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, inp["beta"], inp["gate_bias"],
+                               inp["token_ids"], inp["tid2eid"])
+    weights = moe.make_weights(inp["W1"], inp["W2"], None, None, inp["Ws1"], inp["Ws2"])
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(shape, opts, inp["X"], inp["Wg"], ids, G, None, ws)
+    gen = torch.Generator().manual_seed(4321)
+    dY = torch.randn((T, h), generator=gen).to(torch.bfloat16).cuda()
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    g = dict(dX=torch.empty((T, h), **bf), dW1=torch.empty((E, h, 2 * f), **bf),
+             dW2=torch.empty((E, f, h), **bf),
+             dWs1=torch.empty((h, 2 * f), **bf) if wl.shared else None,
+             dWs2=torch.empty((f, h), **bf) if wl.shared else None,
+             dWg=torch.empty((h, E), **bf),
+             dgate_bias=torch.empty(E, dtype=torch.float32, device="cuda"),
+             dG=torch.empty((T, k), dtype=torch.float32, device="cuda"))
+    grads = moe.make_grads(**g)
+    wsb = moe.alloc_workspace(shape, backward=True)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        moe.moe_backward(shape, opts, inp["X"], inp["Wg"], weights, ids, G, dY, grads, wsb)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(wsb) == 0
+    log(f"[bench] backward warmup done; timing {args.steps} calls")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+    flops, nbytes = backward_work(wl, counts)
+    tflops = flops / (ms / 1000.0) / 1e12
+    gbs = nbytes / (ms / 1000.0) / 1e9
+    t_mfma = flops / (PEAK_MFMA_TFLOPS["bf16"] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if t_hbm >= t_mfma else "mfma"
+    out = {
+        "metric": "MoE layer local backward (recompute + dgrad + wgrad + router) tokens/s",
+        "value": round(T / (ms / 1000.0), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4), "higher_is_better": True, "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded, random-init weights)",
+        "config": {"workload": wl.name, "tokens": T, "hidden": h, "experts": E, "topk": k,
+                   "inter": f, "shared_experts": wl.shared, "score": wl.score},
+        "backward": {"tflops": round(tflops, 1), "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS["bf16"], 4),
+                     "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                     "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "bound": bound,
+                     "frac_of_roofline": round(max(t_mfma, t_hbm) / (ms / 1000.0), 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,6 +339,8 @@ def main(argv=None):
                     help="override a workload field (exploration; e.g. --set zipf=False)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a device copy of this many bytes (counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the local backward (moe_backward, router on) instead")
     args = ap.parse_args(argv)
     if args.copy_probe:
         return copy_probe(args.copy_probe)
@@ -277,6 +368,8 @@ def main(argv=None):
     log(f"[bench] inputs ready in {time.perf_counter() - t:.1f} s")
 
     shape = moe.make_shape(wl.T, wl.hidden, wl.experts, wl.topk, wl.inter, wl.shared, wl.precision)
+    if args.backward:
+        return bench_backward(args, wl, inp, shape)
     ws = moe.alloc_workspace(shape)
     opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, inp["beta"], inp["gate_bias"],
                                inp["token_ids"], inp["tid2eid"])

@@ -162,16 +162,6 @@ __global__ __launch_bounds__(256) void route_backward_kernel(
   }
 }
 
-// out[e] = sum over t of dl[t, e] (one thread per expert, ascending t).
-__global__ __launch_bounds__(256) void colsum_kernel(int T, int E, const float* __restrict__ dl,
-                                                     float* __restrict__ out) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= E) return;
-  float s = 0.0f;
-  for (int t = 0; t < T; ++t) s += dl[static_cast<size_t>(t) * E + e];
-  out[e] = s;
-}
-
 // Permute backward, one block per token: dX[t] = sum_j dXp[row(t,j)] (+ the
 // shared expert's row) (+ the router's dl Wgᵀ row), fp32 sums, bf16 out.
 __global__ __launch_bounds__(256) void permute_backward_kernel(
@@ -428,139 +418,273 @@ struct WgradArgs {
   void* out_sh;      // [M, N]
   const int32_t* offsets;
   int E, M, N, T, has_shared;
+  int32_t* counter;  // [8] work-queue heads (one per XCD), zero at launch
 };
 
-// Swizzle of 16-byte chunks in a [32][W] bf16 tile read by ds_read_b64_tr_b16
-// (as the forward's B tiles), folded into the row's chunk count.
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (binary dispatch).
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmcnt<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID)
+      wait_vm_range<LO, MID>(n);
+    else
+      wait_vm_range<MID + 1, HI>(n);
+  }
+}
+
+// Swizzle of 16-byte chunks in a [rows][W] bf16 tile read by
+// ds_read_b64_tr_b16 (as the forward's B tiles): rows 2 apart and 8 apart
+// land on different bank groups; CH = chunks per row (16 or 8).
 template <int CH>
 __device__ __forceinline__ int wg_swz(int r) {
   return (2 * ((r & 3) + 4 * ((r >> 3) & 1))) & (CH - 1);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
+// dW[e] tile (128 x BN, BN = 128 or 64) += over the expert's rows in chunks
+// of 32: the block runs a flat sequence of (n-tile, K-chunk) steps over NG
+// n-tiles of one m-tile, each chunk DMA'd into a 4-stage LDS ring ([32][128]
+// of A and [32][BN] of B; three chunks in flight while one is multiplied);
+// the last chunk's rows past the expert's block are cleared in LDS before
+// use.  Blocks are persistent and take items from per-XCD work queues (vector
+// atomics on one counter each): XCD x owns every 8th tile of the shared
+// expert (all T rows each, so they go first) and the routed experts e = x,
+// x + 8, ..., which keeps an expert's rows in one L2; a block whose queue
+// is empty takes from the next XCD's.  The MFMA's first operand is the B
+// tile (n), its second the A tile (m); a finished tile goes through a
+// swizzled LDS buffer and leaves as 16-byte stores of whole rows.  An expert
+// without rows gets zeros.
+template <int BN, int NG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void wgrad_kernel(WgradArgs g) {
-  constexpr int NW = WAVES_M * WAVES_N, NTH = 64 * NW;
-  constexpr int ACH = BM / 8, BCH = BN / 8;          // 16-byte chunks per tile row
-  constexpr int A_TILE = 32 * BM * 2, B_TILE = 32 * BN * 2;
-  constexpr int A_PT = 32 * ACH / NTH, B_PT = 32 * BCH / NTH;  // chunk loads per thread
-  static_assert(A_PT * NTH == 32 * ACH && B_PT * NTH == 32 * BCH, "tile loads must split evenly");
-  constexpr int WM = BM / WAVES_M, MT = WM / 16, WN = BN / WAVES_N, NTW = WN / 16;
-  __shared__ __attribute__((aligned(1024))) char smem[2][A_TILE + B_TILE];
+  constexpr int BM = 128, KC = 32, STAGES = 3;
+  constexpr int TILE = KC * BM * 2;      // A: 8 KB
+  constexpr int TILE_B = KC * BN * 2;    // B: 8 or 4 KB
+  constexpr int STAGE = TILE + TILE_B;
+  constexpr int A_OPS = TILE / 1024 / 4;    // A DMAs per wave per step
+  constexpr int BCH = BN / 8;            // B chunks per row
+  constexpr int B_RPI = 1024 / (BN * 2); // B rows per DMA instruction
+  constexpr int B_OPS = TILE_B / 1024 / 4;  // B DMAs per wave per step
+  constexpr int NI = BN / 32;            // 16-column n sub-tiles per wave
+  static_assert(BN == 128 || BN == 64, "n-tile width");
+  constexpr int OCH = BN / 8;                 // 16-byte chunks of an output row
+  constexpr int OUT = STAGES * STAGE;         // staging buffer: half a finished tile
+  constexpr int NSH = (BM / 2) * OCH / 256;   // 16-byte stores of a half tile, per thread
+  constexpr int NST = 2 * NSH;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + (BM / 2) * BN * 2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int MTt = g.M / BM, NTt = g.N / BN;
-  const int total = (g.E + g.has_shared) * MTt * NTt;
-  if (static_cast<int>(blockIdx.x) >= total) return;
-  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int per = total >> 3, rem = total & 7;
-  const int item = x * per + min(x, rem) + slot;  // XCD x: a contiguous range
-  const int seg = item / (MTt * NTt);
-  const int mt = (item / NTt) % MTt, nt = item % NTt;
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves of 64 x BN / 2
+  const int MTt = g.M / BM, NTt = g.N / BN, NGt = (NTt + NG - 1) / NG;
+  const int per_seg = MTt * NGt;
+  const int xcd = blockIdx.x & 7;
+  __shared__ int s_seg, s_local;
+  int qq = 0;  // (thread 0) queues found empty so far
+  for (;;) {
+  // take the next item; the two barriers also keep this block's waves from
+  // starting an item's DMA while another still reads the previous one's LDS
+  if (tid == 0) {
+    int seg_t = -1, local_t = 0;
+    while (qq < 8) {
+      const int qx = (xcd + qq) & 7;
+      const int ns = g.has_shared ? (per_seg - qx + 7) / 8 : 0;  // shared tiles qx, qx + 8, ...
+      const int nr = (g.E - qx + 7) / 8;                         // experts qx, qx + 8, ...
+      const int i = atomicAdd(g.counter + qx, 1);
+      if (i < ns + nr * per_seg) {
+        if (i < ns) {
+          seg_t = g.E;
+          local_t = qx + 8 * i;
+        } else {
+          seg_t = qx + 8 * ((i - ns) / per_seg);
+          local_t = (i - ns) % per_seg;
+        }
+        break;
+      }
+      ++qq;
+    }
+    s_seg = seg_t;
+    s_local = local_t;
+  }
+  __syncthreads();
+  const int seg = s_seg, local = s_local;
+  __syncthreads();
+  if (seg < 0) return;  // every queue is empty (the same for the whole block)
+  const int mt = local / NGt, ng = local % NGt;
+  const int nt0 = ng * NG, nts = min(NG, NTt - nt0);
   const bool shared = (seg == g.E);
   const int k0 = shared ? 0 : g.offsets[seg];
   const int k1 = shared ? g.T : g.offsets[seg + 1];
-  const uint16_t* Ab = static_cast<const uint16_t*>(shared ? g.A_sh : g.A) + mt * BM;
-  const uint16_t* Bb = static_cast<const uint16_t*>(shared ? g.B_sh : g.B) + nt * BN;
+  const int nkc = (k1 - k0 + KC - 1) / KC;
+  const char* Ab = static_cast<const char*>(shared ? g.A_sh : g.A) + static_cast<size_t>(mt) * BM * 2;
+  const char* Bb = static_cast<const char*>(shared ? g.B_sh : g.B);
   uint16_t* ob = static_cast<uint16_t*>(shared ? g.out_sh : g.out) +
                  (shared ? 0 : static_cast<size_t>(seg) * g.M * g.N);
+  const size_t lda = static_cast<size_t>(g.M) * 2, ldb = static_cast<size_t>(g.N) * 2;
 
-  uint4 ra[A_PT], rb[B_PT];
-  auto load = [&](int kt) {
+  // DMA of one step: A 8 instructions of 4 rows x 256 B (2 per wave), B 8 or
+  // 4 of 4 or 8 rows (2 or 1 per wave); rows past the chunk's valid ones
+  // repeat its last valid row
+  auto issue = [&](int s, int st) {
+    const int nt = nt0 + s / nkc, kc = s % nkc;
+    const int rb = k0 + kc * KC, kv = min(KC, k1 - rb);
+    const char* a_src = uniform_ptr(Ab + static_cast<size_t>(rb) * lda);
+    const char* b_src = uniform_ptr(Bb + static_cast<size_t>(rb) * ldb + static_cast<size_t>(nt) * BN * 2);
+    char* dst = smem + st * STAGE;
 #pragma unroll
-    for (int q = 0; q < A_PT; ++q) {
-      const int i = tid + q * NTH, r = i / ACH, c = i % ACH;
-      const int row = k0 + kt * 32 + r;
-      ra[q] = row < k1 ? *reinterpret_cast<const uint4*>(Ab + static_cast<size_t>(row) * g.M + c * 8)
-                       : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < A_OPS; ++q) {
+      const int blk = wave * A_OPS + q;
+      const int r = blk * 4 + lane / 16;
+      const int c = (lane & 15) ^ wg_swz<16>(r);
+      const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
+      dma16(a_src, rr * static_cast<uint32_t>(lda) + c * 16, dst + blk * 1024);
     }
 #pragma unroll
-    for (int q = 0; q < B_PT; ++q) {
-      const int i = tid + q * NTH, r = i / BCH, c = i % BCH;
-      const int row = k0 + kt * 32 + r;
-      rb[q] = row < k1 ? *reinterpret_cast<const uint4*>(Bb + static_cast<size_t>(row) * g.N + c * 8)
-                       : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-    char* st = smem[buf];
-#pragma unroll
-    for (int q = 0; q < A_PT; ++q) {
-      const int i = tid + q * NTH, r = i / ACH, c = i % ACH;
-      *reinterpret_cast<uint4*>(st + r * BM * 2 + ((c ^ wg_swz<ACH>(r)) << 4)) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < B_PT; ++q) {
-      const int i = tid + q * NTH, r = i / BCH, c = i % BCH;
-      *reinterpret_cast<uint4*>(st + A_TILE + r * BN * 2 + ((c ^ wg_swz<BCH>(r)) << 4)) = rb[q];
+    for (int q = 0; q < B_OPS; ++q) {
+      const int blk = wave * B_OPS + q;
+      const int r = blk * B_RPI + lane / BCH;
+      const int c = (lane % BCH) ^ wg_swz<BCH>(r);
+      const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
+      dma16(b_src, rr * static_cast<uint32_t>(ldb) + c * 16, dst + TILE + blk * 1024);
     }
   };
-  // transposing-read offsets: lane (column p of a 16-column block, K group
-  // kgr) reads rows 8 kgr + 4 h + p / 4, 4 columns from (p % 4) * 4
+  // transposing reads: 16-column block at col0, K rows 8 kgr + 4 h + p / 4
   const int kgr = lane >> 4, p = lane & 15;
-  int ao[MT][2], bo[NTW][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 8 * kgr + 4 * h + (p >> 2);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int col = wm * WM + i * 16 + (p & 3) * 4;
-      ao[i][h] = r * BM * 2 + (((col >> 3) ^ wg_swz<ACH>(r)) << 4) + (col & 7) * 2;
-    }
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-      const int col = wn * WN + j * 16 + (p & 3) * 4;
-      bo[j][h] = A_TILE + r * BN * 2 + (((col >> 3) ^ wg_swz<BCH>(r)) << 4) + (col & 7) * 2;
-    }
-  }
-  auto frag = [](const char* st, const int (&o)[2]) {
-    const i16x4_t lo4 = ds_read_tr16(st + o[0]);
-    const i16x4_t hi4 = ds_read_tr16(st + o[1]);
+  auto toff = [&](int col0, int ks, int h, int W) {
+    const int r = 32 * ks + 8 * kgr + 4 * h + (p >> 2);  // (ks = 0: one MFMA step per chunk)
+    const int col = col0 + (p & 3) * 4;
+    const int sw = W == 128 ? wg_swz<16>(r) : wg_swz<8>(r);
+    return r * W * 2 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
+  };
+  auto frag = [&](const char* base, int col0, int ks, int W) {
+    const i16x4_t lo4 = ds_read_tr16(base + toff(col0, ks, 0, W));
+    const i16x4_t hi4 = ds_read_tr16(base + toff(col0, ks, 1, W));
     const i16x8s_t v = i16x8s_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8_t, v);
   };
 
-  f32x4_t acc[MT][NTW];
+  f32x4_t acc[NI][4];  // [n sub-tile i][m sub-tile j]
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int nk = (k1 - k0 + 31) / 32;
-  if (nk > 0) {
-    load(0);
-    store(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load(kt + 1);
-    const char* st = smem[kt & 1];
-    bf16x8_t af[MT], bfr[NTW];
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  // a finished tile, in two halves of 64 rows (the waves with wm = 0, then
+  // wm = 1): acc -> swizzled staging rows -> 16-byte stores of whole rows
+  auto store = [&](int nt) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) af[i] = frag(st, ao[i]);
+    for (int half = 0; half < 2; ++half) {
+      if (wm == half) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bfr[j] = frag(st, bo[j]);
+        for (int j = 0; j < 4; ++j) {
+          const int ml = j * 16 + p;  // row inside the half
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    if (kt + 1 < nk) store((kt + 1) & 1);
-    __syncthreads();
-  }
-  const int col_in = lane & 15;
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int m = mt * BM + wm * WM + i * 16 + (lane >> 4) * 4 + v;
-#pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int n = nt * BN + wn * WN + j * 16 + col_in;
-        ob[static_cast<size_t>(m) * g.N + n] = f32_to_bf16(acc[i][j][v]);
+          for (int i = 0; i < NI; ++i) {
+            const int nl = wn * (BN / 2) + i * 16 + 4 * kgr;
+            const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
+            const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
+            *reinterpret_cast<uint2*>(smem + OUT + ml * BN * 2 + (((nl >> 3) ^ (ml & (OCH - 1))) << 4) +
+                                      (nl & 7) * 2) = make_uint2(lo, hi);
+          }
+        }
       }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < NSH; ++q) {
+        const int idx = tid + q * 256, r = idx / OCH, c = idx % OCH;
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + OUT + r * BN * 2 + ((c ^ (r & (OCH - 1))) << 4));
+        *reinterpret_cast<uint4*>(ob + static_cast<size_t>(mt * BM + half * 64 + r) * g.N + nt * BN + c * 8) = v;
+      }
+      __syncthreads();  // the staging rows are free again
     }
+  };
+  zero_acc();
+  if (nkc == 0) {  // no rows: zero gradients
+    for (int t = 0; t < nts; ++t)
+#pragma unroll
+      for (int q = 0; q < NST; ++q) {
+        const int idx = tid + q * 256, r = idx / OCH, c = idx % OCH;
+        *reinterpret_cast<uint4*>(ob + static_cast<size_t>(mt * BM + r) * g.N + (nt0 + t) * BN + c * 8) =
+            make_uint4(0, 0, 0, 0);
+      }
+    continue;
+  }
+  const int steps = nts * nkc;
+  const int ops = A_OPS + B_OPS;  // DMAs of one step, per wave
+
+#pragma unroll
+  for (int q = 0; q < STAGES - 1; ++q)
+    if (q < steps) issue(q, q);
+  for (int s = 0; s < steps; ++s) {
+    const int st = s % STAGES;
+    // chunk s is in LDS once at most the memory operations issued after its
+    // DMAs are in flight: the next chunks' DMAs and the tile stores of the
+    // three steps since (stores count in vmcnt too, in issue order)
+    int after = min(STAGES - 2, steps - 1 - s) * ops;
+#pragma unroll
+    for (int d = 1; d < STAGES; ++d)
+      if (s - d >= 0 && (s - d) % nkc == nkc - 1) after += NST;
+    wait_vm_range<0, 63>(min(after, 63));
+    __builtin_amdgcn_s_barrier();  // ... for every wave; all are done with chunk s - 1
+    if (s + STAGES - 1 < steps) issue(s + STAGES - 1, (s + STAGES - 1) % STAGES);
+    const int kc = s % nkc;
+    const int kv = min(KC, k1 - (k0 + kc * KC));
+    char* base = smem + st * STAGE;
+    if (kv < KC) {  // rows past the expert's block: clear the A rows
+      for (int i = tid; i < (KC - kv) * 16; i += 256)
+        *reinterpret_cast<uint4*>(base + (kv + i / 16) * 256 + (i % 16) * 16) = make_uint4(0, 0, 0, 0);
+      __syncthreads();
+    }
+    {
+      constexpr int ks = 0;
+      bf16x8_t bn[NI], am[4];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) bn[i] = frag(base + TILE, wn * (BN / 2) + i * 16, ks, BN);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) am[j] = frag(base, wm * 64 + j * 16, ks, 128);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bn[i], am[j], acc[i][j], 0, 0, 0);
+    }
+    if (kc == nkc - 1) {
+      store(nt0 + s / nkc);
+      zero_acc();
+    }
+  }
+  }  // item loop
+}
+
+// Gating-bias gradient: column sums of dl [T, E] in two fixed-order passes.
+// Pass 1: block (expert group of 64, 256-row chunk); wave w sums rows w, w +
+// 4, ... of the chunk; the 4 wave sums are added in order.
+__global__ __launch_bounds__(256) void colsum_partial_kernel(int T, int E, const float* __restrict__ dl,
+                                                             float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int t0 = blockIdx.y * 256;
+  float s = 0.0f;
+  if (e < E)
+    for (int t = t0 + w; t < min(T, t0 + 256); t += 4) s += dl[static_cast<size_t>(t) * E + e];
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && e < E)
+    part[static_cast<size_t>(blockIdx.y) * E + e] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+// Pass 2: out[e] = sum over the chunks, in chunk order.
+__global__ __launch_bounds__(256) void colsum_final_kernel(int nchunk, int E, const float* __restrict__ part,
+                                                           float* __restrict__ out) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.0f;
+  for (int c = 0; c < nchunk; ++c) s += part[static_cast<size_t>(c) * E + e];
+  out[e] = s;
 }
 
 // ---------------------------------------------------------------- launches
@@ -590,21 +714,16 @@ hipError_t dgrad(const DgradArgs& in, int rows, int T_sh, bool swb, hipStream_t 
   return hipGetLastError();
 }
 
+__global__ void zero_counter_kernel(int32_t* c) { c[threadIdx.x] = 0; }
+
 hipError_t wgrad(const WgradArgs& g, hipStream_t stream) {
-  const long segs = g.E + g.has_shared;
-  if (g.N % 256 == 0) {
-    const long grid = segs * (g.M / 128) * (g.N / 256);
-    hipLaunchKernelGGL((wgrad_kernel<128, 256, 2, 4>), dim3(static_cast<unsigned>(grid)), dim3(512),
-                       0, stream, g);
-  } else if (g.N % 128 == 0) {
-    const long grid = segs * (g.M / 128) * (g.N / 128);
-    hipLaunchKernelGGL((wgrad_kernel<128, 128, 2, 2>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, stream, g);
-  } else {
-    const long grid = segs * (g.M / 128) * (g.N / 64);
-    hipLaunchKernelGGL((wgrad_kernel<128, 64, 2, 2>), dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, stream, g);
-  }
+  constexpr int NG = 4;                  // n-tiles per item
+  constexpr unsigned kBlocks = 256 * 2;  // persistent: two blocks per CU
+  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(8), 0, stream, g.counter);
+  if (g.N % 128 == 0)
+    hipLaunchKernelGGL((wgrad_kernel<128, NG>), dim3(kBlocks), dim3(256), 0, stream, g);
+  else  // N % 64 == 0 (the router's experts)
+    hipLaunchKernelGGL((wgrad_kernel<64, NG>), dim3(kBlocks), dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -660,6 +779,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   w2.N = a.h;
   w2.T = a.T;
   w2.has_shared = a.has_shared;
+  w2.counter = a.wq;
   if ((e = wgrad(w2, stream)) != hipSuccess) return e;
   // Linear1 dgrad: dXp = dH1 W1ᵀ (shared rows after the routed ones)
   DgradArgs d1{};
@@ -690,6 +810,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   w1.N = 2 * a.f;
   w1.T = a.T;
   w1.has_shared = a.has_shared;
+  w1.counter = a.wq;
   if ((e = wgrad(w1, stream)) != hipSuccess) return e;
   // router: dl, dWg = Xᵀ dl, dgate_bias, dXr = dl Wgᵀ
   const void* dXr = nullptr;
@@ -698,9 +819,13 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
                        a.k, a.keys, a.beta, a.hash, a.score_fn, a.renorm, a.alpha, a.ids, a.dG,
                        a.dl32, static_cast<uint16_t*>(a.dl16));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.dgate_bias) {
-      hipLaunchKernelGGL(colsum_kernel, dim3((a.E + 255) / 256), dim3(256), 0, stream, a.T, a.E,
-                         a.dl32, a.dgate_bias);
+    if (a.dgate_bias) {  // partial sums in the keys region ([T, E], read only by dl above)
+      const int nchunk = (a.T + 255) / 256;
+      float* part = const_cast<float*>(a.keys);
+      hipLaunchKernelGGL(colsum_partial_kernel, dim3((a.E + 63) / 64, nchunk), dim3(256), 0, stream,
+                         a.T, a.E, a.dl32, part);
+      hipLaunchKernelGGL(colsum_final_kernel, dim3((a.E + 255) / 256), dim3(256), 0, stream, nchunk,
+                         a.E, part, a.dgate_bias);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (a.dWg) {
@@ -713,6 +838,7 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
       wr.N = a.E;
       wr.T = a.T;
       wr.has_shared = 1;
+      wr.counter = a.wq;
       if ((e = wgrad(wr, stream)) != hipSuccess) return e;
     }
     DgradArgs dr{};

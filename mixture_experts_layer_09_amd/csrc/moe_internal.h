@@ -261,6 +261,7 @@ struct BwdLayout {
   size_t dl32;     // [T, E] fp32: gradient of the gating logits
   size_t dl16;     // [T, E] bf16
   size_t tile_b;   // [E+2] int32: m-tile prefix of the dgrad kernels
+  size_t wq;       // int32 [8] work-queue heads of the wgrad kernel
   size_t total;
 };
 inline BwdLayout make_bwd_layout(const moe_shape& s) {
@@ -287,6 +288,7 @@ inline BwdLayout make_bwd_layout(const moe_shape& s) {
   B.dl32 = take(T * E * 4);
   B.dl16 = take(T * E * 2);
   B.tile_b = take((E + 2) * 4);
+  B.wq = take(8 * 4);
   B.total = o;
   return B;
 }
@@ -324,6 +326,7 @@ struct BackwardArgs {
   void* dl16;
   int32_t* tile_off;  // forward linears' m-tile prefix scratch
   int32_t* tile_b;
+  int32_t* wq;
   // outputs
   void* dX;
   void* dWg;

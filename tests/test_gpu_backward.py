@@ -116,3 +116,86 @@ def test_backward_parity(name):
     _log(f"[backward] {name}: " + ", ".join(f"{k} {v:.3e}" for k, v in err.items()))
     for k, v in err.items():
         assert v <= TOL, (k, v)
+
+
+def test_backward_full_size_v4pro():
+    """moe_backward at the V4-Pro size (T = 8192, h = 7168, 384 experts, top-6,
+    f = 3072, shared expert, router on), as the benchmark's backward run times
+    it.  Checked: dX (experts' and router's parts) and dG on sampled tokens
+    (the hottest expert's ragged tail, the coldest experts, first and last
+    token), dW1 / dW2 of the two least-loaded active experts, and zero
+    gradients for experts without rows."""
+    _need_gpu()
+    import gc
+    from tests.test_gpu_full import _sample_tokens
+    inp = synth.make_inputs("v4pro_bf16", device="cuda")
+    wl = inp["workload"]
+    T, h, E, k, f = wl.T, wl.hidden, wl.experts, wl.topk, wl.inter
+    shape = moe.make_shape(T, h, E, k, f, wl.shared, "bf16")
+    opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, inp["beta"], inp["gate_bias"])
+    weights = moe.make_weights(inp["W1"], inp["W2"], None, None, inp["Ws1"], inp["Ws2"])
+    ws = moe.alloc_workspace(shape)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(shape, opts, inp["X"], inp["Wg"], ids, G, None, ws)
+    gen = torch.Generator().manual_seed(4321)
+    dY = torch.randn((T, h), generator=gen).to(torch.bfloat16)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    g = dict(dX=torch.empty((T, h), **bf), dW1=torch.empty((E, h, 2 * f), **bf),
+             dW2=torch.empty((E, f, h), **bf), dWs1=torch.empty((h, 2 * f), **bf),
+             dWs2=torch.empty((f, h), **bf), dWg=torch.empty((h, E), **bf),
+             dgate_bias=torch.empty(E, dtype=torch.float32, device="cuda"),
+             dG=torch.empty((T, k), dtype=torch.float32, device="cuda"))
+    wsb = moe.alloc_workspace(shape, backward=True)
+    _log("[backward full] v4pro_bf16: moe_backward")
+    moe.moe_backward(shape, opts, inp["X"], inp["Wg"], weights, ids, G, dY.cuda(),
+                     moe.make_grads(**g), wsb)
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(wsb) == 0
+    ids_h = ids.cpu().numpy()
+    G_h = G.cpu().double().numpy()
+    dY_h = dY.double().numpy()
+    counts = np.bincount(ids_h.ravel(), minlength=E)
+    inactive = np.nonzero(counts == 0)[0]
+    for e in inactive:
+        assert not g["dW1"][int(e)].any() and not g["dW2"][int(e)].any()
+
+    # sampled tokens: experts' part and router part of dX, and dG
+    toks = _sample_tokens(ids_h, counts)
+    experts = sorted(set(int(e) for e in ids_h[toks].ravel()))
+    remap = np.full(E, -1, np.int32)
+    remap[experts] = np.arange(len(experts), dtype=np.int32)
+    idx = torch.tensor(experts, dtype=torch.long, device="cuda")
+    tsel = torch.from_numpy(toks).long().cuda()
+    X_s = bits(inp["X"][tsel])
+    L = oracle.Layer("bf16", X_s, bits(inp["W1"].index_select(0, idx)),
+                     bits(inp["W2"].index_select(0, idx)), Ws1=bits(inp["Ws1"]), Ws2=bits(inp["Ws2"]),
+                     k=k)
+    _log(f"[backward full] oracle on {len(toks)} sampled tokens")
+    dX, dG = L.backward_tokens(remap[ids_h[toks]], G_h[toks], dY_h[toks])
+    oracle.route_backward(X_s, bits(inp["Wg"]), ids_h[toks], dG, gate_bias=f64(inp["gate_bias"]),
+                          score=wl.score, renorm=wl.renorm, alpha=wl.alpha, dX=dX)
+    err_x = row_rel_err(f64(g["dX"])[toks], dX)
+    err_g = float(np.abs(f64(g["dG"])[toks] - dG).max() / np.abs(dG).max())
+    _log(f"[backward full] dX {err_x:.3e}, dG {err_g:.3e}")
+    assert err_x <= TOL and err_g <= TOL
+    del L
+    gc.collect()
+
+    # weight gradients of the two least-loaded active experts (all their rows)
+    active = np.nonzero(counts > 0)[0]
+    cold = [int(e) for e in active[np.argsort(counts[active], kind="stable")[:2]]]
+    remap = np.full(E, -1, np.int32)
+    remap[cold] = np.arange(len(cold), dtype=np.int32)
+    idx = torch.tensor(cold, dtype=torch.long, device="cuda")
+    L = oracle.Layer("bf16", bits(inp["X"]), bits(inp["W1"].index_select(0, idx)),
+                     bits(inp["W2"].index_select(0, idx)), k=k)
+    _log(f"[backward full] oracle dW of experts {cold} ({counts[cold].tolist()} rows)")
+    dW1, dW2 = L.backward_weights(remap[ids_h], G_h, dY_h, list(range(len(cold))))
+    e1 = row_rel_err(f64(g["dW1"][idx]).reshape(-1, 2 * f), dW1.reshape(-1, 2 * f))
+    e2 = row_rel_err(f64(g["dW2"][idx]).reshape(-1, h), dW2.reshape(-1, h))
+    _log(f"[backward full] dW1 {e1:.3e}, dW2 {e2:.3e}")
+    assert e1 <= TOL and e2 <= TOL
+    del inp, g, wsb, ws, L
+    gc.collect()
+    torch.cuda.empty_cache()
