@@ -17,10 +17,12 @@
 //                 fragments of v_mfma_f32_16x16x32_bf16.  Optional epilogue:
 //                 the SwiGLU backward, which reads the saved pre-activations.
 //   wgrad_kernel  dW[e] = A_eᵀ B_e over the rows of expert e (ragged K).  Both
-//                 operands are [rows, dim] (dim contiguous); tiles of 32 rows
-//                 go through registers (rows past the expert's block load as
-//                 zeros) into LDS and are read with the transposing
-//                 ds_read_b64_tr_b16.  An expert without rows gets zeros.
+//                 operands are [rows, dim] (dim contiguous); chunks of 32 rows
+//                 are DMA'd to LDS (rows past the expert's block cleared) and
+//                 read with the transposing ds_read_b64_tr_b16.  Tiles are
+//                 scheduled statically in groups of 64 per XCD so that the
+//                 blocks sharing a chunk read it together.  An expert without
+//                 rows gets zeros.
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -418,7 +420,6 @@ struct WgradArgs {
   void* out_sh;      // [M, N]
   const int32_t* offsets;
   int E, M, N, T, has_shared;
-  int32_t* counter;  // [8] work-queue heads (one per XCD), zero at launch
 };
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (binary dispatch).
@@ -443,220 +444,287 @@ __device__ __forceinline__ int wg_swz(int r) {
   return (2 * ((r & 3) + 4 * ((r >> 3) & 1))) & (CH - 1);
 }
 
-// dW[e] tile (128 x BN, BN = 128 or 64) += over the expert's rows in chunks
-// of 32: the block runs a flat sequence of (n-tile, K-chunk) steps over NG
-// n-tiles of one m-tile, each chunk DMA'd into a 4-stage LDS ring ([32][128]
-// of A and [32][BN] of B; three chunks in flight while one is multiplied);
-// the last chunk's rows past the expert's block are cleared in LDS before
-// use.  Blocks are persistent and take items from per-XCD work queues (vector
-// atomics on one counter each): XCD x owns every 8th tile of the shared
-// expert (all T rows each, so they go first) and the routed experts e = x,
-// x + 8, ..., which keeps an expert's rows in one L2; a block whose queue
-// is empty takes from the next XCD's.  The MFMA's first operand is the B
-// tile (n), its second the A tile (m); a finished tile goes through a
-// swizzled LDS buffer and leaves as 16-byte stores of whole rows.  An expert
-// without rows gets zeros.
-template <int BN, int NG>
+// dW[e] = A_eᵀ B_e, A_e and B_e the rows of segment e (the shared expert's
+// segment: all T rows of A_sh and B_sh).  The 128 x BN output tiles of a
+// segment are taken in groups of 8 m-tiles by 8 n-tiles, and the groups of
+// all segments, shared expert first, are dealt round-robin to the 8 XCDs.
+// Block b runs on XCD b % 8 and takes tile b / 8 of every group its XCD
+// holds (m-tile (b / 8) % 8, n-tile b / 64 inside it): the 64 blocks of
+// an XCD work through one group at a time, over the same rows at about the
+// same time, so each 32-row chunk of A or B they read comes from HBM into
+// that XCD's L2 once for 8 blocks.  A block's tiles form one flat sequence
+// of 32-row K chunks (a segment without rows counts one empty chunk), DMA'd
+// into a STAGES-deep LDS ring; a chunk's rows past the segment are cleared in
+// LDS before use.  The MFMA's first operand is the B tile (n), its second the
+// A tile (m); a finished tile goes through a swizzled LDS buffer and leaves as
+// 16-byte stores of whole rows.
+template <int BN, int STAGES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void wgrad_kernel(WgradArgs g) {
-  constexpr int BM = 128, KC = 32, STAGES = 3;
+  constexpr int BM = 128, KC = 32;
   constexpr int TILE = KC * BM * 2;      // A: 8 KB
   constexpr int TILE_B = KC * BN * 2;    // B: 8 or 4 KB
   constexpr int STAGE = TILE + TILE_B;
-  constexpr int A_OPS = TILE / 1024 / 4;    // A DMAs per wave per step
+  constexpr int A_OPS = TILE / 1024 / 4;    // A DMAs per wave per chunk
   constexpr int BCH = BN / 8;            // B chunks per row
   constexpr int B_RPI = 1024 / (BN * 2); // B rows per DMA instruction
-  constexpr int B_OPS = TILE_B / 1024 / 4;  // B DMAs per wave per step
-  constexpr int NI = BN / 32;            // 16-column n sub-tiles per wave
+  constexpr int B_OPS = TILE_B / 1024 / 4;  // B DMAs per wave per chunk
+  constexpr int NB = BN / 64;            // 32-column n blocks per wave
   static_assert(BN == 128 || BN == 64, "n-tile width");
   constexpr int OCH = BN / 8;                 // 16-byte chunks of an output row
-  constexpr int OUT = STAGES * STAGE;         // staging buffer: half a finished tile
   constexpr int NSH = (BM / 2) * OCH / 256;   // 16-byte stores of a half tile, per thread
   constexpr int NST = 2 * NSH;
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE + (BM / 2) * BN * 2];
+  constexpr int OPS = A_OPS + B_OPS;          // DMAs of one chunk, per wave
+  static_assert((STAGES - 2) * OPS + (STAGES - 1) * NST <= 63, "vmcnt range");
+  static_assert((BM / 2) * BN * 2 <= STAGE, "half a tile is staged in one ring stage");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves of 64 x BN / 2
-  const int MTt = g.M / BM, NTt = g.N / BN, NGt = (NTt + NG - 1) / NG;
-  const int per_seg = MTt * NGt;
-  const int xcd = blockIdx.x & 7;
-  __shared__ int s_seg, s_local;
-  int qq = 0;  // (thread 0) queues found empty so far
-  for (;;) {
-  // take the next item; the two barriers also keep this block's waves from
-  // starting an item's DMA while another still reads the previous one's LDS
-  if (tid == 0) {
-    int seg_t = -1, local_t = 0;
-    while (qq < 8) {
-      const int qx = (xcd + qq) & 7;
-      const int ns = g.has_shared ? (per_seg - qx + 7) / 8 : 0;  // shared tiles qx, qx + 8, ...
-      const int nr = (g.E - qx + 7) / 8;                         // experts qx, qx + 8, ...
-      const int i = atomicAdd(g.counter + qx, 1);
-      if (i < ns + nr * per_seg) {
-        if (i < ns) {
-          seg_t = g.E;
-          local_t = qx + 8 * i;
-        } else {
-          seg_t = qx + 8 * ((i - ns) / per_seg);
-          local_t = (i - ns) % per_seg;
-        }
-        break;
-      }
-      ++qq;
-    }
-    s_seg = seg_t;
-    s_local = local_t;
-  }
-  __syncthreads();
-  const int seg = s_seg, local = s_local;
-  __syncthreads();
-  if (seg < 0) return;  // every queue is empty (the same for the whole block)
-  const int mt = local / NGt, ng = local % NGt;
-  const int nt0 = ng * NG, nts = min(NG, NTt - nt0);
-  const bool shared = (seg == g.E);
-  const int k0 = shared ? 0 : g.offsets[seg];
-  const int k1 = shared ? g.T : g.offsets[seg + 1];
-  const int nkc = (k1 - k0 + KC - 1) / KC;
-  const char* Ab = static_cast<const char*>(shared ? g.A_sh : g.A) + static_cast<size_t>(mt) * BM * 2;
-  const char* Bb = static_cast<const char*>(shared ? g.B_sh : g.B);
-  uint16_t* ob = static_cast<uint16_t*>(shared ? g.out_sh : g.out) +
-                 (shared ? 0 : static_cast<size_t>(seg) * g.M * g.N);
-  const size_t lda = static_cast<size_t>(g.M) * 2, ldb = static_cast<size_t>(g.N) * 2;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;  // 512 blocks: 64 per XCD
+  const int MTt = g.M / BM, NTt = g.N / BN;
+  const int ngm = (MTt + 7) / 8, ngn = (NTt + 7) / 8;  // a segment's groups: ngm x ngn
+  const int nseg = g.E + (g.has_shared ? 1 : 0);
+  const int sm = slot & 7, sn = slot >> 3;  // this block's tile in a group
+  const uint32_t lda = static_cast<uint32_t>(g.M) * 2, ldb = static_cast<uint32_t>(g.N) * 2;
 
-  // DMA of one step: A 8 instructions of 4 rows x 256 B (2 per wave), B 8 or
-  // 4 of 4 or 8 rows (2 or 1 per wave); rows past the chunk's valid ones
-  // repeat its last valid row
-  auto issue = [&](int s, int st) {
-    const int nt = nt0 + s / nkc, kc = s % nkc;
-    const int rb = k0 + kc * KC, kv = min(KC, k1 - rb);
-    const char* a_src = uniform_ptr(Ab + static_cast<size_t>(rb) * lda);
-    const char* b_src = uniform_ptr(Bb + static_cast<size_t>(rb) * ldb + static_cast<size_t>(nt) * BN * 2);
-    char* dst = smem + st * STAGE;
-#pragma unroll
-    for (int q = 0; q < A_OPS; ++q) {
-      const int blk = wave * A_OPS + q;
-      const int r = blk * 4 + lane / 16;
-      const int c = (lane & 15) ^ wg_swz<16>(r);
-      const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
-      dma16(a_src, rr * static_cast<uint32_t>(lda) + c * 16, dst + blk * 1024);
+  // position in the block's sequence: group (gm, gn) of segment sg (the
+  // shared expert's first), whose tile for this block is m-tile 8 gm + sm,
+  // n-tile 8 gn + sn of segment seg, and its chunk kc of nkc, which starts
+  // at A row a and B row b with rem rows left in the segment.  This XCD's
+  // groups are every 8th in (sg, gm, gn) order, so the walk is additions
+  // with carries (no divisions in the loop).
+  struct Cur {
+    int sg, gm, gn, seg, nkc, kc, rem;  // sg >= nseg: past the end
+    const char* a;
+    const char* b;
+  };
+  auto carry = [&](Cur c) -> Cur {
+    while (c.gn >= ngn) {
+      c.gn -= ngn;
+      ++c.gm;
     }
+    while (c.gm >= ngm) {
+      c.gm -= ngm;
+      ++c.sg;
+    }
+    return c;
+  };
+  // from group (sg, gm, gn) on, this XCD's first group with a tile for this
+  // block (a segment's last row or column of groups may be short)
+  auto settle = [&](Cur c) -> Cur {
+    for (;;) {
+      if (c.sg >= nseg) return c;
+      if (c.gm * 8 + sm < MTt && c.gn * 8 + sn < NTt) break;
+      c.gn += 8;
+      c = carry(c);
+    }
+    const bool sh = g.has_shared && c.sg == 0;
+    c.seg = sh ? g.E : c.sg - (g.has_shared ? 1 : 0);
+    int k0 = 0, k1 = g.T;
+    if (!sh) scalar_load2(g.offsets + c.seg, k0, k1);
+    c.rem = k1 - k0;
+    c.nkc = max(1, (c.rem + KC - 1) / KC);
+    c.kc = 0;
+    if (c.rem == 0) k0 = 0;  // no rows: the chunk's DMA reads row 0 (not multiplied)
+    c.a = static_cast<const char*>(sh ? g.A_sh : g.A) + static_cast<size_t>(k0) * lda +
+          static_cast<size_t>(c.gm * 8 + sm) * BM * 2;
+    c.b = static_cast<const char*>(sh ? g.B_sh : g.B) + static_cast<size_t>(k0) * ldb +
+          static_cast<size_t>(c.gn * 8 + sn) * BN * 2;
+    return c;
+  };
+  auto advance = [&](Cur c) -> Cur {
+    if (++c.kc < c.nkc) {
+      c.rem -= KC;
+      c.a += static_cast<size_t>(KC) * lda;
+      c.b += static_cast<size_t>(KC) * ldb;
+      return c;
+    }
+    c.gn += 8;
+    return settle(carry(c));
+  };
+
+  // DMA of one chunk: A 8 instructions of 4 rows x 256 B (2 per wave), B 8 or
+  // 4 of 4 or 8 rows (2 or 1 per wave), each lane one swizzled 16-byte piece.
+  // Rows past the chunk's valid ones repeat its last valid row; a segment
+  // without rows reads row 0 (the chunk is not multiplied).
+  uint32_t a_off[A_OPS], b_off[B_OPS];  // a full chunk's per-lane offsets
 #pragma unroll
-    for (int q = 0; q < B_OPS; ++q) {
-      const int blk = wave * B_OPS + q;
-      const int r = blk * B_RPI + lane / BCH;
-      const int c = (lane % BCH) ^ wg_swz<BCH>(r);
-      const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
-      dma16(b_src, rr * static_cast<uint32_t>(ldb) + c * 16, dst + TILE + blk * 1024);
+  for (int q = 0; q < A_OPS; ++q) {
+    const int r = (wave * A_OPS + q) * 4 + lane / 16;
+    a_off[q] = r * lda + (((lane & 15) ^ wg_swz<16>(r)) << 4);
+  }
+#pragma unroll
+  for (int q = 0; q < B_OPS; ++q) {
+    const int r = (wave * B_OPS + q) * B_RPI + lane / BCH;
+    b_off[q] = r * ldb + (((lane % BCH) ^ wg_swz<BCH>(r)) << 4);
+  }
+  const uint32_t lds0 = lds_address(smem);
+  auto issue = [&](Cur c, int st) {
+    const int kv = max(1, min(KC, c.rem));
+    const uint32_t dst = lds0 + st * STAGE;
+    if (kv == KC) {
+#pragma unroll
+      for (int q = 0; q < A_OPS; ++q) dma16_at(c.a, a_off[q], dst + (wave * A_OPS + q) * 1024);
+#pragma unroll
+      for (int q = 0; q < B_OPS; ++q) dma16_at(c.b, b_off[q], dst + TILE + (wave * B_OPS + q) * 1024);
+    } else {
+#pragma unroll
+      for (int q = 0; q < A_OPS; ++q) {
+        const int r = (wave * A_OPS + q) * 4 + lane / 16;
+        const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
+        dma16_at(c.a, rr * lda + (((lane & 15) ^ wg_swz<16>(r)) << 4), dst + (wave * A_OPS + q) * 1024);
+      }
+#pragma unroll
+      for (int q = 0; q < B_OPS; ++q) {
+        const int r = (wave * B_OPS + q) * B_RPI + lane / BCH;
+        const uint32_t rr = static_cast<uint32_t>(min(r, kv - 1));
+        dma16_at(c.b, rr * ldb + (((lane % BCH) ^ wg_swz<BCH>(r)) << 4), dst + TILE + (wave * B_OPS + q) * 1024);
+      }
     }
   };
-  // transposing reads: 16-column block at col0, K rows 8 kgr + 4 h + p / 4
+  // v_mfma_f32_32x32x16_bf16 fragments (8 K-consecutive values per lane) by
+  // transposing reads: 32 columns from col0 and the 16 K rows from 16 kh;
+  // lane group g = lane / 16 reads rows 8 (g >> 1) + 4 h + p / 4 of the 16
+  // columns from col0 + 16 (g & 1), so lane l holds column col0 + l % 32 at
+  // K rows 16 kh + 8 (l / 32) + 0..7 (the same for both operands).  The
+  // per-lane offsets inside a stage are computed once.
   const int kgr = lane >> 4, p = lane & 15;
-  auto toff = [&](int col0, int ks, int h, int W) {
-    const int r = 32 * ks + 8 * kgr + 4 * h + (p >> 2);  // (ks = 0: one MFMA step per chunk)
-    const int col = col0 + (p & 3) * 4;
+  auto toff = [&](int col0, int kh, int h, int W) {
+    const int r = 16 * kh + 8 * (kgr >> 1) + 4 * h + (p >> 2);
+    const int col = col0 + 16 * (kgr & 1) + (p & 3) * 4;
     const int sw = W == 128 ? wg_swz<16>(r) : wg_swz<8>(r);
     return r * W * 2 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
   };
-  auto frag = [&](const char* base, int col0, int ks, int W) {
-    const i16x4_t lo4 = ds_read_tr16(base + toff(col0, ks, 0, W));
-    const i16x4_t hi4 = ds_read_tr16(base + toff(col0, ks, 1, W));
+  int offB[2][NB][2], offA[2][2][2];  // [kh][block][h]
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) offB[kh][i][h] = TILE + toff(wn * (BN / 2) + i * 32, kh, h, BN);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) offA[kh][j][h] = toff(wm * 64 + j * 32, kh, h, 128);
+    }
+  auto frag = [&](const char* base, int o0, int o1) {
+    const i16x4_t lo4 = ds_read_tr16(base + o0);
+    const i16x4_t hi4 = ds_read_tr16(base + o1);
     const i16x8s_t v = i16x8s_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8_t, v);
   };
 
-  f32x4_t acc[NI][4];  // [n sub-tile i][m sub-tile j]
+  // acc[i][j]: the 32 x 32 block (n block i, m block j); lane l holds m =
+  // l % 32 and, in elements 4 q .. 4 q + 3, the 4 consecutive n from
+  // 8 q + 4 (l / 32)
+  f32x16_t acc[NB][2];
   auto zero_acc = [&]() {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NB; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   };
   // a finished tile, in two halves of 64 rows (the waves with wm = 0, then
-  // wm = 1): acc -> swizzled staging rows -> 16-byte stores of whole rows
-  auto store = [&](int nt) {
+  // wm = 1): acc -> swizzled staging rows in the ring stage just multiplied
+  // (its next DMA is issued after the step's barrier) -> 16-byte stores of
+  // whole rows.  Sharing the ring leaves LDS for a deeper ring, and so more
+  // steps between a tile's stores and the first wait on a DMA issued after
+  // them (stores and DMAs share vmcnt, in issue order).
+  auto store = [&](Cur c, char* stg) {
+    uint16_t* ob = static_cast<uint16_t*>(c.seg == g.E ? g.out_sh : g.out) +
+                   (c.seg == g.E ? 0 : static_cast<size_t>(c.seg) * g.M * g.N);
+    __syncthreads();  // every wave is done reading the stage
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       if (wm == half) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int ml = j * 16 + p;  // row inside the half
+        for (int j = 0; j < 2; ++j) {
+          const int ml = j * 32 + (lane & 31);  // row inside the half
 #pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            const int nl = wn * (BN / 2) + i * 16 + 4 * kgr;
-            const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
-            const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
-            *reinterpret_cast<uint2*>(smem + OUT + ml * BN * 2 + (((nl >> 3) ^ (ml & (OCH - 1))) << 4) +
-                                      (nl & 7) * 2) = make_uint2(lo, hi);
-          }
+          for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int nl = wn * (BN / 2) + i * 32 + 8 * q + 4 * (lane >> 5);
+              const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+              const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+              *reinterpret_cast<uint2*>(stg + ml * BN * 2 + (((nl >> 3) ^ (ml & (OCH - 1))) << 4) +
+                                        (nl & 7) * 2) = make_uint2(lo, hi);
+            }
         }
       }
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < NSH; ++q) {
-        const int idx = tid + q * 256, r = idx / OCH, c = idx % OCH;
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + OUT + r * BN * 2 + ((c ^ (r & (OCH - 1))) << 4));
-        *reinterpret_cast<uint4*>(ob + static_cast<size_t>(mt * BM + half * 64 + r) * g.N + nt * BN + c * 8) = v;
+        const int idx = tid + q * 256, r = idx / OCH, cc = idx % OCH;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + r * BN * 2 + ((cc ^ (r & (OCH - 1))) << 4));
+        *reinterpret_cast<uint4*>(ob + static_cast<size_t>((c.gm * 8 + sm) * BM + half * 64 + r) * g.N +
+                                  (c.gn * 8 + sn) * BN + cc * 8) = v;
       }
       __syncthreads();  // the staging rows are free again
     }
   };
-  zero_acc();
-  if (nkc == 0) {  // no rows: zero gradients
-    for (int t = 0; t < nts; ++t)
-#pragma unroll
-      for (int q = 0; q < NST; ++q) {
-        const int idx = tid + q * 256, r = idx / OCH, c = idx % OCH;
-        *reinterpret_cast<uint4*>(ob + static_cast<size_t>(mt * BM + r) * g.N + (nt0 + t) * BN + c * 8) =
-            make_uint4(0, 0, 0, 0);
-      }
-    continue;
-  }
-  const int steps = nts * nkc;
-  const int ops = A_OPS + B_OPS;  // DMAs of one step, per wave
 
+  Cur ci = settle(carry(Cur{0, 0, xcd, 0, 0, 0, 0, nullptr, nullptr}));  // the next chunk to DMA
+  if (ci.sg >= nseg) return;  // no tile for this block
+  Cur cc = ci;             // the next chunk to multiply
+  zero_acc();
+  int n_iss = 0;  // chunks DMA'd so far
 #pragma unroll
   for (int q = 0; q < STAGES - 1; ++q)
-    if (q < steps) issue(q, q);
-  for (int s = 0; s < steps; ++s) {
+    if (ci.sg < nseg) {
+      issue(ci, q);
+      ci = advance(ci);
+      ++n_iss;
+    }
+  uint32_t ends = 0;  // bit d - 1: the chunk d steps back ended a tile (its stores follow)
+  for (int s = 0;; ++s) {
     const int st = s % STAGES;
     // chunk s is in LDS once at most the memory operations issued after its
-    // DMAs are in flight: the next chunks' DMAs and the tile stores of the
-    // three steps since (stores count in vmcnt too, in issue order)
-    int after = min(STAGES - 2, steps - 1 - s) * ops;
-#pragma unroll
-    for (int d = 1; d < STAGES; ++d)
-      if (s - d >= 0 && (s - d) % nkc == nkc - 1) after += NST;
-    wait_vm_range<0, 63>(min(after, 63));
+    // DMAs are in flight: the later chunks' DMAs and the tile stores of the
+    // STAGES - 1 steps since (stores count in vmcnt too, in issue order)
+    const int after = (n_iss - 1 - s) * OPS + NST * __builtin_popcount(ends & ((1u << (STAGES - 1)) - 1));
+    wait_vm_range<0, 63>(after);
     __builtin_amdgcn_s_barrier();  // ... for every wave; all are done with chunk s - 1
-    if (s + STAGES - 1 < steps) issue(s + STAGES - 1, (s + STAGES - 1) % STAGES);
-    const int kc = s % nkc;
-    const int kv = min(KC, k1 - (k0 + kc * KC));
+    if (ci.sg < nseg) {
+      issue(ci, (s + STAGES - 1) % STAGES);
+      ci = advance(ci);
+      ++n_iss;
+    }
+    const int kv = min(KC, cc.rem);
     char* base = smem + st * STAGE;
-    if (kv < KC) {  // rows past the expert's block: clear the A rows
-      for (int i = tid; i < (KC - kv) * 16; i += 256)
-        *reinterpret_cast<uint4*>(base + (kv + i / 16) * 256 + (i % 16) * 16) = make_uint4(0, 0, 0, 0);
-      __syncthreads();
+    if (kv > 0) {
+      if (kv < KC) {  // rows past the segment: clear the A rows
+        for (int i = tid; i < (KC - kv) * 16; i += 256)
+          *reinterpret_cast<uint4*>(base + (kv + i / 16) * 256 + (i % 16) * 16) = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+      }
+      bf16x8_t bn[2][NB], am[2][2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bn[kh][i] = frag(base, offB[kh][i][0], offB[kh][i][1]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) am[kh][j] = frag(base, offA[kh][j][0], offA[kh][j][1]);
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bn[kh][i], am[kh][j], acc[i][j], 0, 0, 0);
     }
-    {
-      constexpr int ks = 0;
-      bf16x8_t bn[NI], am[4];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) bn[i] = frag(base + TILE, wn * (BN / 2) + i * 16, ks, BN);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) am[j] = frag(base, wm * 64 + j * 16, ks, 128);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bn[i], am[j], acc[i][j], 0, 0, 0);
-    }
-    if (kc == nkc - 1) {
-      store(nt0 + s / nkc);
+    const bool end = cc.kc == cc.nkc - 1;
+    if (end) {
+      store(cc, base);
       zero_acc();
     }
+    ends = (ends << 1) | (end ? 1u : 0u);
+    cc = advance(cc);
+    if (cc.sg >= nseg) break;
   }
-  }  // item loop
 }
 
 // Gating-bias gradient: column sums of dl [T, E] in two fixed-order passes.
@@ -714,16 +782,12 @@ hipError_t dgrad(const DgradArgs& in, int rows, int T_sh, bool swb, hipStream_t 
   return hipGetLastError();
 }
 
-__global__ void zero_counter_kernel(int32_t* c) { c[threadIdx.x] = 0; }
-
 hipError_t wgrad(const WgradArgs& g, hipStream_t stream) {
-  constexpr int NG = 4;                  // n-tiles per item
-  constexpr unsigned kBlocks = 256 * 2;  // persistent: two blocks per CU
-  hipLaunchKernelGGL(zero_counter_kernel, dim3(1), dim3(8), 0, stream, g.counter);
+  constexpr unsigned kBlocks = 512;  // 64 per XCD, two per CU
   if (g.N % 128 == 0)
-    hipLaunchKernelGGL((wgrad_kernel<128, NG>), dim3(kBlocks), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((wgrad_kernel<128, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
   else  // N % 64 == 0 (the router's experts)
-    hipLaunchKernelGGL((wgrad_kernel<64, NG>), dim3(kBlocks), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL((wgrad_kernel<64, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
@@ -779,7 +843,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   w2.N = a.h;
   w2.T = a.T;
   w2.has_shared = a.has_shared;
-  w2.counter = a.wq;
   if ((e = wgrad(w2, stream)) != hipSuccess) return e;
   // Linear1 dgrad: dXp = dH1 W1ᵀ (shared rows after the routed ones)
   DgradArgs d1{};
@@ -810,7 +873,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   w1.N = 2 * a.f;
   w1.T = a.T;
   w1.has_shared = a.has_shared;
-  w1.counter = a.wq;
   if ((e = wgrad(w1, stream)) != hipSuccess) return e;
   // router: dl, dWg = Xᵀ dl, dgate_bias, dXr = dl Wgᵀ
   const void* dXr = nullptr;
@@ -838,7 +900,6 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
       wr.N = a.E;
       wr.T = a.T;
       wr.has_shared = 1;
-      wr.counter = a.wq;
       if ((e = wgrad(wr, stream)) != hipSuccess) return e;
     }
     DgradArgs dr{};

@@ -23,6 +23,20 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* ld
                : "memory");
 }
 
+// As dma16 with the LDS destination given as an LDS address (wave-uniform),
+// which spares the generic-to-LDS pointer conversion in a hot loop.
+__device__ __forceinline__ void dma16_at(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
+}
+
+// The LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
 // As dma16 with 4 bytes per lane (LDS lds_dst + 4 * lane).
 __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, char* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
@@ -39,6 +53,17 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Two consecutive int32 at a wave-uniform address, read through the scalar
+// cache.  The compiler turns a plain load of memory that the kernel might
+// also write into a vector load, and its wait (vmcnt(0)) would drain every
+// DMA and store this wave has in flight; this one waits on lgkmcnt only.
+__device__ __forceinline__ void scalar_load2(const int32_t* p, int& a, int& b) {
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  a = static_cast<int>(static_cast<uint32_t>(v));
+  b = static_cast<int>(static_cast<uint32_t>(v >> 32));
 }
 
 // s_waitcnt vmcnt(n) with the other counters left free (gfx9 encoding).

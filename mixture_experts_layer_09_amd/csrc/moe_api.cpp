@@ -426,7 +426,6 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
     b.dl16 = at<void>(ws, B.dl16);
     b.tile_off = at<int32_t>(ws, L.tile_off);
     b.tile_b = at<int32_t>(ws, B.tile_b);
-    b.wq = at<int32_t>(ws, B.wq);
     b.dX = grads->dX;
     b.dWg = opts ? grads->dWg : nullptr;
     b.dgate_bias = opts ? grads->dgate_bias : nullptr;

@@ -13,6 +13,7 @@ namespace moe {
 // ---------------------------------------------------------------- vectors
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
@@ -28,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
+}
+
+// Two fp32 -> bf16 (round to nearest even) packed low, high, by the
+// hardware conversion v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) float f2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 b2;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
 }
 
 // fp32 -> OCP e4m3fn code, round to nearest even, saturating at +-448.  The
@@ -261,7 +270,6 @@ struct BwdLayout {
   size_t dl32;     // [T, E] fp32: gradient of the gating logits
   size_t dl16;     // [T, E] bf16
   size_t tile_b;   // [E+2] int32: m-tile prefix of the dgrad kernels
-  size_t wq;       // int32 [8] work-queue heads of the wgrad kernel
   size_t total;
 };
 inline BwdLayout make_bwd_layout(const moe_shape& s) {
@@ -288,7 +296,6 @@ inline BwdLayout make_bwd_layout(const moe_shape& s) {
   B.dl32 = take(T * E * 4);
   B.dl16 = take(T * E * 2);
   B.tile_b = take((E + 2) * 4);
-  B.wq = take(8 * 4);
   B.total = o;
   return B;
 }
@@ -326,7 +333,6 @@ struct BackwardArgs {
   void* dl16;
   int32_t* tile_off;  // forward linears' m-tile prefix scratch
   int32_t* tile_b;
-  int32_t* wq;
   // outputs
   void* dX;
   void* dWg;
