@@ -437,11 +437,14 @@ __device__ __forceinline__ void wait_vm_range(int n) {
 }
 
 // Swizzle of 16-byte chunks in a [rows][W] bf16 tile read by
-// ds_read_b64_tr_b16 (as the forward's B tiles): rows 2 apart and 8 apart
-// land on different bank groups; CH = chunks per row (16 or 8).
+// ds_read_b64_tr_b16 for 32x32 fragments (as the forward's B tiles): half a
+// read is 4 consecutive K rows x 4 chunks, which must fall on distinct
+// banks.  256-byte rows (CH = 16 chunks) all start on bank 0: XOR by
+// 4 (r % 4).  128-byte rows (CH = 8): rows r and r + 1 already use opposite
+// bank halves, so rows r and r + 2 get chunk sets 4 apart.
 template <int CH>
 __device__ __forceinline__ int wg_swz(int r) {
-  return (2 * ((r & 3) + 4 * ((r >> 3) & 1))) & (CH - 1);
+  return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
 // dW[e] = A_eᵀ B_e, A_e and B_e the rows of segment e (the shared expert's

@@ -33,7 +33,8 @@
 // weight bytes in flight; each thread loads a 4 x 16-byte weight block into
 // registers and writes it transposed (v_perm byte shuffles), and the next
 // K-tile is prefetched into registers while the current one is multiplied.
-//   bf16: v_mfma_f32_16x16x32_bf16 (a lane holds 8 K-consecutive elements)
+//   bf16: v_mfma_f32_16x16x32_bf16 (decode) and v_mfma_f32_32x32x16_bf16
+//         (prefill; twice the rate), a lane holding 8 K-consecutive elements
 //   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (32 per lane)
 // For SwiGLU an N-tile of BN columns holds BN/2 gate columns and the
 // matching BN/2 up columns, and each wave owns equal gate/up sub-tiles, so the
@@ -408,9 +409,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 // LDS layout of one stage:
 //   A: BM rows x 64 bytes; 16-byte chunk c of row r at c ^ ((r >> 2) & 3)
 //      (an MFMA read of 16 consecutive rows then covers all 64 banks);
-//   B: 32 rows (k) x BN*2 bytes; chunk c of row r at c ^ 2 s(r),
-//      s(r) = (r & 3) + 4 ((r >> 3) & 1), which makes each transposing load
-//      touch every bank exactly twice.
+//   B: 32 rows (k) x BN*2 bytes; chunk c of row r at c ^ 4 (r & 3), so that
+//      each half of a transposing load (4 K rows x 64 bytes) touches every
+//      bank once.
 // The swizzles are applied on the global side: lane i of a DMA instruction
 // fetches the chunk that belongs at LDS position i.
 //
@@ -432,50 +433,77 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void grouped_gemm_kernel(Ge
 template <int PREC, int BN>
 struct DmaOps;
 
+// bf16 multiplies 32 x 32 output tiles with v_mfma_f32_32x32x16_bf16 (twice
+// the rate of the 16x16x32 form on gfx950): a stage's 32 K-values are two
+// 16-deep halves kh, and in each a lane holds row (or column) lane % 32 at K
+// 16 kh + 8 (lane / 32) + 0..7, for A and for B alike.  The accumulator's
+// element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+struct Bf16Pair {
+  bf16x8_t k0, k1;
+};
+
 template <int BN>
 struct DmaOps<MOE_PREC_BF16, BN> {
   static constexpr int ESZ = 2, BK = 32, A_CHUNKS = 4;
-  typedef bf16x8_t frag;
-  typedef f32x4_t acc_t;
+  static constexpr int TM = 32, NV = 16;  // MFMA tile and accumulator elements per lane
+  typedef Bf16Pair frag;
+  typedef f32x16_t acc_t;
+  __device__ static int row_of(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+  __device__ static int col_of(int lane) { return lane & 31; }
   __device__ static int swz_a(int r) { return (r >> 2) & 3; }
-  __device__ static int swz_b(int r) { return 2 * ((r & 3) + 4 * ((r >> 3) & 1)); }
-  // byte offsets (inside a stage's B region) of this lane's transposing reads
+  // B chunk swizzle: a transposing read's 32-lane half covers 4 consecutive
+  // K rows x 4 chunks (64 bytes); XOR by 4 (r % 4) gives the 4 rows disjoint
+  // chunk sets, 16 chunks on 64 distinct banks (rows start on bank 0)
+  __device__ static int swz_b(int r) { return 4 * (r & 3); }
+  // byte offsets (inside a stage's B region) of this lane's transposing
+  // reads: lane group g reads rows 16 kh + 8 (g >> 1) + 4 h + p / 4 of the
+  // 16 columns from col0 + 16 (g & 1)
   template <int B_ROW>
   __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
     const int g = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = 8 * g + 4 * h + (p >> 2);
-      const int col = col0 + (p & 3) * 4;  // element
-      o[h] = r * B_ROW + (((col >> 3) ^ swz_b(r)) << 4) + (col & 7) * 2;
-    }
-    o[2] = o[3] = 0;
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 16 * kh + 8 * (g >> 1) + 4 * h + (p >> 2);
+        const int col = col0 + 16 * (g & 1) + (p & 3) * 4;  // element
+        o[2 * kh + h] = r * B_ROW + (((col >> 3) ^ swz_b(r)) << 4) + (col & 7) * 2;
+      }
   }
-  __device__ static frag load_b(const char* st, const int (&o)[4]) {
-    const i16x4_t lo4 = ds_read_tr16(st + o[0]);
-    const i16x4_t hi4 = ds_read_tr16(st + o[1]);
+  __device__ static bf16x8_t tr_pair(const char* st, int o0, int o1) {
+    const i16x4_t lo4 = ds_read_tr16(st + o0);
+    const i16x4_t hi4 = ds_read_tr16(st + o1);
     typedef __attribute__((ext_vector_type(8))) short i16x8_t;
     const i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8_t, v);
   }
+  __device__ static frag load_b(const char* st, const int (&o)[4]) {
+    return frag{tr_pair(st, o[0], o[1]), tr_pair(st, o[2], o[3])};
+  }
+  // row r of the tile: 16-byte chunk 2 kh + lane / 32 (K 16 kh + 8 (lane / 32))
   template <int A_ROW>
   __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
-    o[0] = r * A_ROW + (((lane >> 4) ^ swz_a(r)) << 4);
-    o[1] = 0;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) o[kh] = r * A_ROW + (((2 * kh + (lane >> 5)) ^ swz_a(r)) << 4);
   }
   __device__ static frag load_a(const char* st, const int (&o)[2]) {
-    return *reinterpret_cast<const bf16x8_t*>(st + o[0]);
+    return frag{*reinterpret_cast<const bf16x8_t*>(st + o[0]), *reinterpret_cast<const bf16x8_t*>(st + o[1])};
   }
-  __device__ static f32x4_t mma(frag a, frag b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  __device__ static f32x16_t mma(frag a, frag b, f32x16_t c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.k0, b.k0, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.k1, b.k1, c, 0, 0, 0);
   }
 };
 
 template <int BN>
 struct DmaOps<MOE_PREC_FP8, BN> {
   static constexpr int ESZ = 1, BK = 128, A_CHUNKS = 8;
+  // 16 x 16 tiles: element v of lane l is row 4 (l / 16) + v, column l % 16
+  static constexpr int TM = 16, NV = 4;
   typedef i32x8_t frag;
   typedef f32x4_t acc_t;
+  __device__ static int row_of(int lane, int v) { return 4 * (lane >> 4) + v; }
+  __device__ static int col_of(int lane) { return lane & 15; }
   __device__ static int swz_a(int r) { return (r >> 1) & 7; }
   __device__ static int swz_b(int r) {
     return BN >= 256 ? (r & 7) + 8 * ((r >> 5) & 1) : ((r & 7) >> 1) + 4 * ((r >> 5) & 1);
@@ -629,9 +657,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int A_RPI = 1024 / A_ROW;     // A rows per DMA instruction
   constexpr int B_CHUNKS = B_ROW / 16;    // 16-byte chunks per B row
   constexpr int B_RPI = 1024 / B_ROW;     // B rows per DMA instruction
+  constexpr int TM = O::TM;  // MFMA tile (rows = columns)
   constexpr int WM = BM / WAVES_M;
-  constexpr int MT = WM / 16;
-  constexpr int NTW = BN / WAVES_N / 16;
+  constexpr int MT = WM / TM;
+  constexpr int NTW = BN / WAVES_N / TM;
+  static_assert(WM % TM == 0 && (BN / WAVES_N) % TM == 0, "wave tile in MFMA tiles");
+  static_assert(!MX || TM == 16, "MX epilogue and scales use the 16 x 16 layout");
   static_assert(B_INSTS % NW == 0, "B stage must split evenly over the waves");
   static_assert(A_BYTES % 1024 == 0 || A_INSTS == 1, "A stage granularity");
   static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
@@ -692,7 +723,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   const int rows_valid = min(BM, row_end - row0);
   // wave-uniform: keep it scalar so the skip below is a scalar branch
   const int mt_live =
-      __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
+      __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + TM - 1) / TM)));
   const size_t a_ld = static_cast<size_t>(g.K) * ESZ;
   const size_t w_ld = static_cast<size_t>(g.Nw) * ESZ;
 
@@ -774,14 +805,14 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = typename O::acc_t{0, 0, 0, 0};
+    for (int j = 0; j < NTW; ++j) acc[i][j] = typename O::acc_t{};
 
   auto bcol = [&](int j) -> int {  // first LDS column of this wave's n-tile j
     if (SWIGLU) {
       const int half = BN / 2, per = BN / 2 / WAVES_N;
-      return j < NTW / 2 ? wn * per + j * 16 : half + wn * per + (j - NTW / 2) * 16;
+      return j < NTW / 2 ? wn * per + j * TM : half + wn * per + (j - NTW / 2) * TM;
     }
-    return wn * (BN / WAVES_N) + j * 16;
+    return wn * (BN / WAVES_N) + j * TM;
   };
 
   int b_off[NTW][4];
@@ -793,7 +824,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
   int a_off[MT][2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) O::template a_offsets<A_ROW>(wm * WM + i * 16 + (lane & 15), lane, a_off[i]);
+  for (int i = 0; i < MT; ++i) O::template a_offsets<A_ROW>(wm * WM + i * TM + (lane & (TM - 1)), lane, a_off[i]);
   // MX: LDS byte of this lane's scale for A row tile i / B column tile j
   int as_off[MT], bs_off[NTW];
 #pragma unroll
@@ -855,7 +886,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------ epilogue
-  const int col_in = lane & 15;
+  const int col_in = O::col_of(lane);
   if constexpr (MX && SWIGLU) {
     // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
     // gate tiles (j, j+1) of one row, i.e. 2 values in each of the 16 lanes
@@ -892,8 +923,8 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   for (int i = 0; i < MT; ++i) {
     if (i >= mt_live) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+    for (int v = 0; v < O::NV; ++v) {
+      const int row = row0 + wm * WM + i * TM + O::row_of(lane, v);
       if (row >= row_end) continue;
       const float rs = A8W8 ? asc[row] : 1.0f;  // MX: scales are in the MFMA
       if (SWIGLU) {
