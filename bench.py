@@ -173,7 +173,8 @@ def cpu_model() -> str:
 
 
 TRAFFIC_SOURCES = ("mixture_experts_layer_09_amd/csrc/grouped_gemm.hip",
-                   "mixture_experts_layer_09_amd/csrc/moe_internal.h")
+                   "mixture_experts_layer_09_amd/csrc/moe_internal.h",
+                   "mixture_experts_layer_09_amd/csrc/lds_dma.h")
 
 
 def grouped_gemm_source_hash() -> str:
