@@ -30,6 +30,7 @@ namespace moe {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) short i16x8s_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 __device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
@@ -662,8 +663,11 @@ void wgrad_kernel(WgradArgs g) {
       for (int q = 0; q < NSH; ++q) {
         const int idx = tid + q * 256, r = idx / OCH, cc = idx % OCH;
         const uint4 v = *reinterpret_cast<const uint4*>(stg + r * BN * 2 + ((cc ^ (r & (OCH - 1))) << 4));
-        *reinterpret_cast<uint4*>(ob + static_cast<size_t>((c.gm * 8 + sm) * BM + half * 64 + r) * g.N +
-                                  (c.gn * 8 + sn) * BN + cc * 8) = v;
+        // non-temporal: the dW stream would otherwise evict the A and B
+        // chunks that the group's other blocks are about to read from L2
+        __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4_t*>(ob + static_cast<size_t>((c.gm * 8 + sm) * BM + half * 64 + r) * g.N +
+                                                               (c.gn * 8 + sn) * BN + cc * 8));
       }
       __syncthreads();  // the staging rows are free again
     }
