@@ -771,7 +771,14 @@ hipError_t dgrad(const DgradArgs& in, int rows, int T_sh, bool swb, hipStream_t 
                      g.E, T_sh, kDgradBM, const_cast<int32_t*>(g.tile_off));
   const long ub_m = (rows + kDgradBM - 1) / kDgradBM + (g.E < rows ? g.E : rows) +
                     (T_sh + kDgradBM - 1) / kDgradBM;
-  if (g.N % 256 == 0) {
+  if (!swb && g.N % 512 == 0 && static_cast<long>(rows) < 256L * g.E) {
+    // about one m-tile of rows per expert: 512-wide n-tiles halve the
+    // re-reads of the gradient rows (one per n-tile), as in the forward
+    // (measured slower for Linear2's dgrad, whose N = inter gives 6 n-tiles)
+    g.n_tiles = g.N / 512;
+    const dim3 grid(static_cast<unsigned>(ub_m * g.n_tiles));
+    hipLaunchKernelGGL((dgrad_kernel<kDgradBM, 512, 2, 4, 3, false>), grid, dim3(512), 0, stream, g);
+  } else if (g.N % 256 == 0) {
     g.n_tiles = g.N / 256;
     const dim3 grid(static_cast<unsigned>(ub_m * g.n_tiles));
     if (swb)

@@ -1577,6 +1577,12 @@ hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t stream) {
   g.Nw = a.N;
   g.Nout = a.N;
   g.T = a.T;
+  // tile width as the expert FFN chooses it (about one m-tile of rows per
+  // expert: 512-wide n-tiles halve the re-reads of token-row tiles)
+  if (a.N % 512 == 0 && static_cast<long>(a.rows) < 256L * a.E) {
+    g.n_tiles = a.N / 512;
+    return launch_gemm<MOE_PREC_BF16, BM, 512, 2, 4, false, 3>(g, ub_m, stream);
+  }
   if (a.N % 256 == 0) {
     g.n_tiles = a.N / 256;
     return launch_gemm<MOE_PREC_BF16, BM, 256, 2, 2, false, 3>(g, ub_m, stream);
