@@ -14,7 +14,7 @@
 //                 (the gradient rows [rows, K] and the weights as stored,
 //                 [N, K]), DMA'd to LDS in 32-value K-stages (64-byte rows,
 //                 chunk swizzle (r >> 2) & 3) and read as plain 16-byte
-//                 fragments of v_mfma_f32_16x16x32_bf16.  Optional epilogue:
+//                 fragments of v_mfma_f32_32x32x16_bf16.  Optional epilogue:
 //                 the SwiGLU backward, which reads the saved pre-activations.
 //   wgrad_kernel  dW[e] = A_eᵀ B_e over the rows of expert e (ragged K).  Both
 //                 operands are [rows, dim] (dim contiguous); chunks of 32 rows
@@ -274,7 +274,8 @@ void dgrad_kernel(DgradArgs g) {
   constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB, STAGE = A_BYTES + B_BYTES;
   constexpr int A_INSTS = A_BYTES / 1024, B_INSTS = B_BYTES / 1024;  // 16 rows per DMA
   constexpr int A_OPS = A_INSTS / NW, B_OPS = B_INSTS / NW;
-  constexpr int WM = BM / WAVES_M, MT = WM / 16, WN = BN / WAVES_N, NTW = WN / 16;
+  // 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16, two per 32-value stage)
+  constexpr int WM = BM / WAVES_M, MT = WM / 32, WN = BN / WAVES_N, NTW = WN / 32;
   static_assert(A_INSTS % NW == 0 && B_INSTS % NW == 0, "tiles must split evenly over the waves");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
@@ -299,7 +300,7 @@ void dgrad_kernel(DgradArgs g) {
     Wbase = static_cast<const char*>(g.W_sh);
   }
   const int rows_valid = min(BM, row_end - row0);
-  const int mt_live = __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 15) / 16)));
+  const int mt_live = __builtin_amdgcn_readfirstlane(max(0, min(MT, (rows_valid - wm * WM + 31) / 32)));
   auto swz = [](int r) { return (r >> 2) & 3; };
 
   const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * ld);
@@ -328,36 +329,48 @@ void dgrad_kernel(DgradArgs g) {
       dma16(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q], st + A_BYTES + (wave * B_OPS + q) * 1024);
   };
 
-  f32x4_t acc[MT][NTW];
+  f32x16_t acc[MT][NTW];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int kg = lane >> 4;  // fragment chunk: K values 8 kg .. 8 kg + 7 of the stage
-  int a_off[MT], b_off[NTW];
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
+  // fragments: lane l holds row (or column) l % 32 at K 16 kh + 8 (l / 32)
+  // + 0..7 of the stage, i.e. 16-byte chunk 2 kh + l / 32 of the row, for A
+  // and W alike; element v of an accumulator is row 8 (v / 4) + 4 (l / 32) +
+  // v % 4, column l % 32
+  int a_off[MT][2], b_off[NTW][2];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int r = wm * WM + i * 16 + (lane & 15);
-    a_off[i] = r * ROWB + ((kg ^ swz(r)) << 4);
-  }
+  for (int kh = 0; kh < 2; ++kh) {
+    const int ch = 2 * kh + (lane >> 5);
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) {
-    const int r = wn * WN + j * 16 + (lane & 15);
-    b_off[j] = A_BYTES + r * ROWB + ((kg ^ swz(r)) << 4);
+    for (int i = 0; i < MT; ++i) {
+      const int r = wm * WM + i * 32 + (lane & 31);
+      a_off[i][kh] = r * ROWB + ((ch ^ swz(r)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int r = wn * WN + j * 32 + (lane & 31);
+      b_off[j][kh] = A_BYTES + r * ROWB + ((ch ^ swz(r)) << 4);
+    }
   }
   auto compute = [&](int slot) {
     if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
-    bf16x8_t bfr[NTW], af[MT];
+    bf16x8_t bfr[NTW][2], af[MT][2];
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + b_off[j]);
+    for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i]);
+      for (int j = 0; j < NTW; ++j) bfr[j][kh] = *reinterpret_cast<const bf16x8_t*>(st + b_off[j][kh]);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i) af[i][kh] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][kh]);
+    }
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][kh], bfr[j][kh], acc[i][j], 0, 0, 0);
   };
 
   const int KT = g.K / 32;
@@ -382,17 +395,17 @@ void dgrad_kernel(DgradArgs g) {
   // ------------------------------------------------ epilogue
   uint16_t* obase = static_cast<uint16_t*>(shared ? g.out_sh : g.out);
   const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
-  const int col_in = lane & 15;
+  const int col_in = lane & 31;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
     if (i >= mt_live) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row0 + wm * WM + i * 16 + (lane >> 4) * 4 + v;
+    for (int v = 0; v < 16; ++v) {
+      const int row = row0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (row >= row_end) continue;
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        const int n = nt * BN + wn * WN + j * 16 + col_in;
+        const int n = nt * BN + wn * WN + j * 32 + col_in;
         const float d = acc[i][j][v];
         if constexpr (SWB) {
           // dH = d; H1 = (gate G, up U); A = SiLU(G): dU = dH * A and
