@@ -305,6 +305,36 @@ def bench_backward(args, wl, inp, shape):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1000.0 / args.steps
     ms = e0.elapsed_time(e1) / args.steps
+    # saved activations: the training forward keeps what moe_backward
+    # recomputes, and moe_backward_saved starts from there
+    Yt = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
+
+    def fwd_train():
+        moe.moe_forward_train(shape, opts, inp["X"], inp["Wg"], weights, ids, G, Yt, wsb)
+
+    def bwd_saved():
+        moe.moe_backward_saved(shape, opts, inp["X"], inp["Wg"], weights, ids, G, dY, grads, wsb)
+
+    def timed(fn, pre=None):
+        tot = 0.0
+        for _ in range(args.steps):
+            if pre:
+                pre()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            tot += a.elapsed_time(b)
+        return tot / args.steps
+
+    fwd_train()
+    bwd_saved()
+    torch.cuda.synchronize()
+    ft_ms = timed(fwd_train)
+    bs_ms = timed(bwd_saved, pre=fwd_train)
+    assert moe.moe_check_device_error(wsb) == 0
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
     flops, nbytes = backward_work(wl, counts)
     tflops = flops / (ms / 1000.0) / 1e12
@@ -324,6 +354,11 @@ def bench_backward(args, wl, inp, shape):
                      "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                      "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "bound": bound,
                      "frac_of_roofline": round(max(t_mfma, t_hbm) / (ms / 1000.0), 4)},
+        # moe_backward_saved after moe_forward_train (activations kept instead of
+        # recomputed): its own time per call, and the training forward's
+        "saved_activations": {"backward_ms": round(bs_ms, 4),
+                              "tokens_per_s": round(T / (bs_ms / 1000.0), 1),
+                              "forward_train_ms": round(ft_ms, 4)},
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -273,6 +273,33 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
                  const float* gate_weights, const void* dY, const moe_grads* grads,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Training forward: steps 1-5 as moe_forward, for the layers and shapes
+ * that moe_backward takes, on a backward workspace (moe_backward_workspace_size
+ * bytes), keeping there what the backward reads: the dispatch, Linear1's
+ * pre-activations H1 (gate, up) and the SwiGLU output A of every routed and
+ * shared row, the routed experts' outputs Yp and, with opts, the router's
+ * keys.  H1 is written out in bf16 and SwiGLU applied to it (the values the
+ * backward differentiates), not fused into Linear1's epilogue as in
+ * moe_forward, so Y agrees with moe_forward to bf16 rounding of H1.
+ * Arguments and errors as moe_forward, plus those of moe_backward's shape
+ * limits. */
+int moe_forward_train(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                      const void* Wg, const moe_expert_weights* weights, int32_t* expert_ids,
+                      float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* moe_backward on saved activations: the same gradients, without the
+ * recompute (dispatch, router keys, Linear1, SwiGLU, Linear2).  The
+ * workspace must hold the moe_forward_train of the same shape, X, weights,
+ * routing and opts, unchanged since (the library cannot check this; anything
+ * else gives wrong gradients, not an error).  Arguments and errors as
+ * moe_backward. */
+int moe_backward_saved(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                       const void* Wg, const moe_expert_weights* weights,
+                       const int32_t* expert_ids, const float* gate_weights, const void* dY,
+                       const moe_grads* grads, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
 /* Synchronises `stream`, then reports (and clears) the device-side error
  * flag in the workspace: MOE_ERR_DEVICE_DATA if an earlier moe_permute,
  * moe_route or moe_forward on this workspace saw an expert id outside

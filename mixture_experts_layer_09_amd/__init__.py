@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
           -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_DATA"}
 EXPORTED = ["moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_forward", "moe_check_device_error", "moe_status_string",
-            "moe_backward_workspace_size", "moe_backward"]
+            "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
+            "moe_backward_saved"]
 
 
 class MoeError(RuntimeError):
@@ -92,6 +93,10 @@ def lib():
         L.moe_backward.argtypes = [S, C.POINTER(moe_route_opts), vp, vp,
                                    C.POINTER(moe_expert_weights), vp, vp, vp,
                                    C.POINTER(moe_grads), vp, C.c_size_t, vp]
+        L.moe_forward_train.restype = i32
+        L.moe_forward_train.argtypes = L.moe_forward.argtypes
+        L.moe_backward_saved.restype = i32
+        L.moe_backward_saved.argtypes = L.moe_backward.argtypes
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [i32]
         _lib = L
@@ -193,6 +198,24 @@ def moe_backward_workspace_size(shape: moe_shape) -> int:
 def moe_backward(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads, workspace,
                  stream=None):
     _check("moe_backward", lib().moe_backward(
+        C.byref(shape), None if opts is None else C.byref(opts), _ptr(X), _ptr(Wg),
+        C.byref(weights), _ptr(expert_ids), _ptr(gate_weights), _ptr(dY), C.byref(grads),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def moe_forward_train(shape, opts, X, Wg, weights, expert_ids, gate_weights, Y, workspace,
+                      stream=None):
+    """moe_forward that keeps the activations moe_backward_saved reads, in a
+    backward workspace (alloc_workspace(shape, backward=True))."""
+    _check("moe_forward_train", lib().moe_forward_train(
+        C.byref(shape), None if opts is None else C.byref(opts), _ptr(X), _ptr(Wg),
+        C.byref(weights), _ptr(expert_ids), _ptr(gate_weights), _ptr(Y), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+
+
+def moe_backward_saved(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads,
+                       workspace, stream=None):
+    _check("moe_backward_saved", lib().moe_backward_saved(
         C.byref(shape), None if opts is None else C.byref(opts), _ptr(X), _ptr(Wg),
         C.byref(weights), _ptr(expert_ids), _ptr(gate_weights), _ptr(dY), C.byref(grads),
         _ptr(workspace), workspace.numel(), _stream(stream)))

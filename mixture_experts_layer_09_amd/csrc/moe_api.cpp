@@ -301,10 +301,13 @@ size_t moe_backward_workspace_size(const moe_shape* shape) {
   return make_bwd_layout(*shape).total;
 }
 
-int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
-                 const moe_expert_weights* weights, const int32_t* expert_ids,
-                 const float* gate_weights, const void* dY, const moe_grads* grads,
-                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Shape, argument and workspace checks of moe_backward and its saved form.
+int check_backward(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+                   const moe_expert_weights* weights, const int32_t* expert_ids,
+                   const float* gate_weights, const void* dY, const moe_grads* grads,
+                   void* workspace, size_t workspace_bytes) {
   int st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (shape->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
@@ -324,30 +327,38 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
                   grads->dWg}))
     return MOE_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
-  const BwdLayout B = make_bwd_layout(*shape);
-  if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < make_bwd_layout(*shape).total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// The dispatch, the router keys (with opts) and H1 = Xp W1 (routed and shared
+// rows), A = SwiGLU(H1), into a backward workspace; Yp = A W2 for the routed
+// rows and, with Ys != NULL, the shared expert's output too.  Routing: with
+// route_out the router runs and writes it (the training forward), else it
+// runs into scratch for its keys only (the recompute).
+hipError_t recompute(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+                     const moe_expert_weights* weights, const int32_t* expert_ids,
+                     int32_t* ids_out, float* g_out, void* Ys, void* ws, hipStream_t stream) {
   const Layout L = make_layout(*shape);
-  void* ws = workspace;
+  const BwdLayout B = make_bwd_layout(*shape);
   const int T = shape->tokens, k = shape->topk, E = shape->experts;
   const int rows = T * k;
   const size_t f = shape->inter;
-
-  hipError_t e = launch_clear_flag(at<int32_t>(ws, L.flag), stream);
-  // the forward's dispatch
+  hipError_t e = hipSuccess;
+  // router keys (a + beta) for the router's backward; the training forward's
+  // routing itself
+  if (opts) {
+    RouteArgs r = route_args(shape, opts, X, Wg, ids_out ? ids_out : at<int32_t>(ws, B.ids_s),
+                             g_out ? g_out : at<float>(ws, B.G_s), at<float>(ws, B.keys), ws);
+    e = launch_route(r, stream);
+  }
   if (e == hipSuccess) {
-    PermuteArgs p = permute_args(shape, expert_ids, X, at<int32_t>(ws, L.counts),
+    PermuteArgs p = permute_args(shape, ids_out ? ids_out : expert_ids, X, at<int32_t>(ws, L.counts),
                                  at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.dst_row),
                                  at<int32_t>(ws, L.src_tok), at<void>(ws, L.Xp), nullptr, nullptr,
                                  nullptr, ws);
     e = launch_permute(p, stream);
   }
-  // router keys (a + beta), for the router's backward
-  if (e == hipSuccess && opts) {
-    RouteArgs r = route_args(shape, opts, X, Wg, at<int32_t>(ws, B.ids_s), at<float>(ws, B.G_s),
-                             at<float>(ws, B.keys), ws);
-    e = launch_route(r, stream);
-  }
-  // recompute: H1 = X W1 per row (gate, up), A = SwiGLU(H1), Yp = A W2
   if (e == hipSuccess) {
     LinearArgs l1{};
     l1.A = at<void>(ws, L.Xp);
@@ -373,8 +384,11 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
   if (e == hipSuccess) {
     LinearArgs l2{};
     l2.A = at<void>(ws, B.Aact);
+    l2.A_sh = at<char>(ws, B.Aact) + static_cast<size_t>(rows) * f * 2;
     l2.W = weights->W2;
+    l2.W_sh = weights->Ws2;
     l2.out = at<void>(ws, L.Yp);
+    l2.out_sh = Ys;
     l2.offsets = at<int32_t>(ws, L.offsets);
     l2.tile_off = at<int32_t>(ws, L.tile_off);
     l2.E = E;
@@ -382,60 +396,140 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
     l2.N = shape->hidden;
     l2.T = T;
     l2.rows = rows;
-    l2.has_shared = 0;
+    l2.has_shared = (Ys != nullptr && shape->has_shared) ? 1 : 0;
     e = launch_grouped_linear_bf16(l2, stream);
   }
+  return e;
+}
+
+// Everything after the recompute, on the activations in the workspace.
+hipError_t backward_from_saved(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                               const void* Wg, const moe_expert_weights* weights,
+                               const int32_t* expert_ids, const float* gate_weights, const void* dY,
+                               const moe_grads* grads, void* ws, hipStream_t stream) {
+  const Layout L = make_layout(*shape);
+  const BwdLayout B = make_bwd_layout(*shape);
+  BackwardArgs b{};
+  b.T = shape->tokens;
+  b.h = shape->hidden;
+  b.E = shape->experts;
+  b.k = shape->topk;
+  b.f = shape->inter;
+  b.has_shared = shape->has_shared;
+  b.route = opts != nullptr;
+  if (opts) {
+    b.score_fn = opts->score_fn;
+    b.renorm = opts->renorm;
+    b.alpha = opts->alpha;
+    b.hash = (opts->token_ids && opts->tid2eid) ? 1 : 0;
+    b.beta = opts->expert_bias;
+  }
+  b.X = X;
+  b.Wg = Wg;
+  b.W1 = weights->W1;
+  b.W2 = weights->W2;
+  b.Ws1 = weights->Ws1;
+  b.Ws2 = weights->Ws2;
+  b.ids = expert_ids;
+  b.G = gate_weights;
+  b.dY = dY;
+  b.offsets = at<int32_t>(ws, L.offsets);
+  b.dst_row = at<int32_t>(ws, L.dst_row);
+  b.Xp = at<void>(ws, L.Xp);
+  b.Yp = at<void>(ws, L.Yp);
+  b.H1 = at<void>(ws, B.H1);
+  b.Aact = at<void>(ws, B.Aact);
+  b.dYp = at<void>(ws, B.dYp);
+  b.dH1 = at<void>(ws, B.dH1);
+  b.dXp = at<void>(ws, B.dXp);
+  b.dXr = at<void>(ws, B.dXr);
+  b.keys = at<float>(ws, B.keys);
+  b.dG = grads->dG ? grads->dG : at<float>(ws, B.dG);
+  b.dl32 = at<float>(ws, B.dl32);
+  b.dl16 = at<void>(ws, B.dl16);
+  b.tile_off = at<int32_t>(ws, L.tile_off);
+  b.tile_b = at<int32_t>(ws, B.tile_b);
+  b.dX = grads->dX;
+  b.dWg = opts ? grads->dWg : nullptr;
+  b.dgate_bias = opts ? grads->dgate_bias : nullptr;
+  b.dW1 = grads->dW1;
+  b.dW2 = grads->dW2;
+  b.dWs1 = grads->dWs1;
+  b.dWs2 = grads->dWs2;
+  return launch_backward(b, stream);
+}
+
+}  // namespace
+
+int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
+                 const moe_expert_weights* weights, const int32_t* expert_ids,
+                 const float* gate_weights, const void* dY, const moe_grads* grads,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_backward(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads,
+                                workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  const Layout L = make_layout(*shape);
+  hipError_t e = launch_clear_flag(at<int32_t>(workspace, L.flag), stream);
+  if (e == hipSuccess)
+    e = recompute(shape, opts, X, Wg, weights, expert_ids, nullptr, nullptr, nullptr, workspace,
+                  stream);
+  if (e == hipSuccess)
+    e = backward_from_saved(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads,
+                            workspace, stream);
+  return hip_status(e);
+}
+
+int moe_forward_train(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                      const void* Wg, const moe_expert_weights* weights, int32_t* expert_ids,
+                      float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->precision != MOE_PREC_BF16) return MOE_ERR_UNSUPPORTED;
+  if (shape->hidden % 256 != 0 || shape->inter % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_weights(shape, weights)) != MOE_OK) return st;
+  if (!X || !expert_ids || !gate_weights || !Y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16({X, Wg, Y})) return MOE_ERR_INVALID_ARG;
+  if (opts) {
+    if ((st = check_route_opts(opts)) != MOE_OK) return st;
+    if (!Wg) return MOE_ERR_INVALID_ARG;
+    if (shape->experts % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  if (!workspace || !aligned(workspace, kAlign)) return MOE_ERR_WORKSPACE;
+  if (workspace_bytes < make_bwd_layout(*shape).total) return MOE_ERR_WORKSPACE;
+  const Layout L = make_layout(*shape);
+  void* ws = workspace;
+  hipError_t e = launch_clear_flag(at<int32_t>(ws, L.flag), stream);
+  if (e == hipSuccess)
+    e = recompute(shape, opts, X, Wg, weights, expert_ids, opts ? expert_ids : nullptr,
+                  opts ? gate_weights : nullptr, shape->has_shared ? at<void>(ws, L.Ys) : nullptr,
+                  ws, stream);
   if (e == hipSuccess) {
-    BackwardArgs b{};
-    b.T = T;
-    b.h = shape->hidden;
-    b.E = E;
-    b.k = k;
-    b.f = shape->inter;
-    b.has_shared = shape->has_shared;
-    b.route = opts != nullptr;
-    if (opts) {
-      b.score_fn = opts->score_fn;
-      b.renorm = opts->renorm;
-      b.alpha = opts->alpha;
-      b.hash = (opts->token_ids && opts->tid2eid) ? 1 : 0;
-      b.beta = opts->expert_bias;
-    }
-    b.X = X;
-    b.Wg = Wg;
-    b.W1 = weights->W1;
-    b.W2 = weights->W2;
-    b.Ws1 = weights->Ws1;
-    b.Ws2 = weights->Ws2;
-    b.ids = expert_ids;
-    b.G = gate_weights;
-    b.dY = dY;
-    b.offsets = at<int32_t>(ws, L.offsets);
-    b.dst_row = at<int32_t>(ws, L.dst_row);
-    b.Xp = at<void>(ws, L.Xp);
-    b.Yp = at<void>(ws, L.Yp);
-    b.H1 = at<void>(ws, B.H1);
-    b.Aact = at<void>(ws, B.Aact);
-    b.dYp = at<void>(ws, B.dYp);
-    b.dH1 = at<void>(ws, B.dH1);
-    b.dXp = at<void>(ws, B.dXp);
-    b.dXr = at<void>(ws, B.dXr);
-    b.keys = at<float>(ws, B.keys);
-    b.dG = grads->dG ? grads->dG : at<float>(ws, B.dG);
-    b.dl32 = at<float>(ws, B.dl32);
-    b.dl16 = at<void>(ws, B.dl16);
-    b.tile_off = at<int32_t>(ws, L.tile_off);
-    b.tile_b = at<int32_t>(ws, B.tile_b);
-    b.dX = grads->dX;
-    b.dWg = opts ? grads->dWg : nullptr;
-    b.dgate_bias = opts ? grads->dgate_bias : nullptr;
-    b.dW1 = grads->dW1;
-    b.dW2 = grads->dW2;
-    b.dWs1 = grads->dWs1;
-    b.dWs2 = grads->dWs2;
-    e = launch_backward(b, stream);
+    CombineArgs c{};
+    c.T = shape->tokens;
+    c.h = shape->hidden;
+    c.k = shape->topk;
+    c.precision = shape->precision;
+    c.Yp = at<void>(ws, L.Yp);
+    c.dst_row = at<int32_t>(ws, L.dst_row);
+    c.G = gate_weights;
+    c.Ys = shape->has_shared ? at<void>(ws, L.Ys) : nullptr;
+    c.Y = Y;
+    e = launch_combine(c, stream);
   }
   return hip_status(e);
+}
+
+int moe_backward_saved(const moe_shape* shape, const moe_route_opts* opts, const void* X,
+                       const void* Wg, const moe_expert_weights* weights,
+                       const int32_t* expert_ids, const float* gate_weights, const void* dY,
+                       const moe_grads* grads, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  const int st = check_backward(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads,
+                                workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  return hip_status(backward_from_saved(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY,
+                                        grads, workspace, stream));
 }
 
 int moe_check_device_error(void* workspace, size_t workspace_bytes, hipStream_t stream) {

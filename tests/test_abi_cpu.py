@@ -173,8 +173,10 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
         moe.lib()
 
 
-def test_backward_rejects_out_of_contract_arguments():
+@pytest.mark.parametrize("entry", ["moe_backward", "moe_backward_saved"])
+def test_backward_rejects_out_of_contract_arguments(entry):
     L = _lib()
+    fn = getattr(L, entry)
     s = _shape(hidden=256, inter=128, experts=64, topk=2, has_shared=1)
     n = moe.moe_backward_workspace_size(s)
     assert n > moe.moe_workspace_size(s)
@@ -187,18 +189,39 @@ def test_backward_rejects_out_of_contract_arguments():
     for bad in (_shape(hidden=256, inter=128, experts=64, precision="fp8"),
                 _shape(hidden=256, inter=128, experts=64, precision="fp32"),
                 _shape(hidden=128, inter=128, experts=64), _shape(hidden=256, inter=64, experts=64)):
-        assert L.moe_backward(*args(bad)) == UNSUPPORTED
+        assert fn(*args(bad)) == UNSUPPORTED
     # router gradients need experts in multiples of 64; without options they are not asked for
     s40 = _shape(hidden=256, inter=128, experts=40, topk=2, has_shared=1)
     n40 = moe.moe_backward_workspace_size(s40)
-    assert L.moe_backward(*args(s40, nb=n40)) == UNSUPPORTED
+    assert fn(*args(s40, nb=n40)) == UNSUPPORTED
     # missing gradient outputs, shared-expert gradients missing, misaligned arrays
-    assert L.moe_backward(*args(s, grads=None)) == INVALID
+    assert fn(*args(s, grads=None)) == INVALID
     g2 = moe.moe_grads(16, 16, 16, None, 16, 16, 16, 16)
-    assert L.moe_backward(*args(s, grads=C.byref(g2))) == INVALID
+    assert fn(*args(s, grads=C.byref(g2))) == INVALID
     g3 = moe.moe_grads(16, 24, 16, 16, 16, 16, 16, 16)
-    assert L.moe_backward(*args(s, grads=C.byref(g3))) == INVALID
+    assert fn(*args(s, grads=C.byref(g3))) == INVALID
     # workspace: misaligned or smaller than moe_backward_workspace_size
-    assert L.moe_backward(*args(s, ws=FAKE_WS + 8)) == WORKSPACE
-    assert L.moe_backward(*args(s, nb=n - 1)) == WORKSPACE
-    assert L.moe_backward(*args(s, nb=moe.moe_workspace_size(s))) == WORKSPACE
+    assert fn(*args(s, ws=FAKE_WS + 8)) == WORKSPACE
+    assert fn(*args(s, nb=n - 1)) == WORKSPACE
+    assert fn(*args(s, nb=moe.moe_workspace_size(s))) == WORKSPACE
+
+
+def test_training_forward_rejects_out_of_contract_arguments():
+    L = _lib()
+    s = _shape(hidden=256, inter=128, experts=64, topk=2, has_shared=1)
+    n = moe.moe_backward_workspace_size(s)
+    opts = moe.make_route_opts()
+    w = moe.moe_expert_weights(16, None, 16, None, 16, None, 16, None)
+    args = lambda shape, o=C.byref(opts), Y=16, ws=FAKE_WS, nb=n: (  # noqa: E731
+        C.byref(shape), o, 16, 16, C.byref(w), 16, 16, Y, ws, nb, None)
+    # the layers and shapes the backward takes
+    for bad in (_shape(hidden=256, inter=128, experts=64, precision="fp8"),
+                _shape(hidden=128, inter=128, experts=64), _shape(hidden=256, inter=64, experts=64)):
+        assert L.moe_forward_train(*args(bad)) == UNSUPPORTED
+    s40 = _shape(hidden=256, inter=128, experts=40, topk=2, has_shared=1)
+    assert L.moe_forward_train(*args(s40, nb=moe.moe_backward_workspace_size(s40))) == UNSUPPORTED
+    assert L.moe_forward_train(*args(s, Y=None)) == INVALID
+    assert L.moe_forward_train(*args(s, Y=24)) == INVALID
+    # a forward-sized workspace does not hold the saved activations
+    assert L.moe_forward_train(*args(s, nb=moe.moe_workspace_size(s))) == WORKSPACE
+    assert L.moe_forward_train(*args(s, ws=FAKE_WS + 8)) == WORKSPACE

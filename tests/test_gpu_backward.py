@@ -45,7 +45,9 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def run_case(name):
+def run_case(name, saved=False):
+    """moe_backward on the case; with saved, moe_forward_train then
+    moe_backward_saved (also returns the training forward's Y)."""
     base, kw, with_router = CASES[name]
     cpu = synth.make_inputs(base, **kw)
     wl = cpu["workload"]
@@ -72,22 +74,37 @@ def run_case(name):
              dG=torch.empty((T, k), dtype=torch.float32, device="cuda"))
     grads = moe.make_grads(**g)
     wsb = moe.alloc_workspace(shape, backward=True)
-    _log(f"[backward] {name}: moe_backward T={T} h={h} E={E} k={k} f={f} router={with_router}")
-    moe.moe_backward(shape, opts if with_router else None, gpu["X"], gpu["Wg"], weights, ids, G,
-                     dYg, grads, wsb)
+    o = opts if with_router else None
+    Y = None
+    if saved:
+        _log(f"[backward] {name}: moe_forward_train + moe_backward_saved T={T} h={h} E={E} k={k} "
+             f"f={f} router={with_router}")
+        Y = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
+        moe.moe_forward_train(shape, o, gpu["X"], gpu["Wg"], weights, ids, G, Y, wsb)
+        moe.moe_backward_saved(shape, o, gpu["X"], gpu["Wg"], weights, ids, G, dYg, grads, wsb)
+    else:
+        _log(f"[backward] {name}: moe_backward T={T} h={h} E={E} k={k} f={f} router={with_router}")
+        moe.moe_backward(shape, o, gpu["X"], gpu["Wg"], weights, ids, G, dYg, grads, wsb)
     torch.cuda.synchronize()
     assert moe.moe_check_device_error(wsb) == 0
-    return cpu, wl, ids.cpu().numpy(), G.cpu().double().numpy(), dY.double().numpy(), g, with_router
+    out = (cpu, wl, ids.cpu().numpy(), G.cpu().double().numpy(), dY.double().numpy(), g, with_router)
+    return out + (Y,) if saved else out
 
 
+@pytest.mark.parametrize("saved", [False, True], ids=["recompute", "saved"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_backward_parity(name):
+def test_backward_parity(name, saved):
     _need_gpu()
-    cpu, wl, ids, G, dY, g, with_router = run_case(name)
+    res = run_case(name, saved)
+    cpu, wl, ids, G, dY, g, with_router = res[:7]
     L = oracle.Layer("bf16", bits(cpu["X"]), bits(cpu["W1"]), bits(cpu["W2"]), Ws1=bits(cpu["Ws1"]),
                      Ws2=bits(cpu["Ws2"]), k=wl.topk)
-    dX, dG = L.backward_tokens(ids, G, dY)
     err = {}
+    if saved:  # the training forward's output, at the bf16 forward tolerance
+        err_y = row_rel_err(f64(res[7]), L.tokens(ids, G))
+        _log(f"[backward] {name}: training forward Y {err_y:.3e}")
+        assert err_y <= 2e-2
+    dX, dG = L.backward_tokens(ids, G, dY)
     # dG[t,j] is a dot product over hidden (k values per token, which can all
     # be small by cancellation): normalised by its largest magnitude
     err["dG"] = float(np.abs(f64(g["dG"]) - dG).max() / np.abs(dG).max())
@@ -196,6 +213,31 @@ def test_backward_full_size_v4pro():
     e2 = row_rel_err(f64(g["dW2"][idx]).reshape(-1, h), dW2.reshape(-1, h))
     _log(f"[backward full] dW1 {e1:.3e}, dW2 {e2:.3e}")
     assert e1 <= TOL and e2 <= TOL
-    del inp, g, wsb, ws, L
+    del L
+    gc.collect()
+
+    # saved activations: the training forward keeps what moe_backward
+    # recomputes (the same kernels on the same inputs), so every gradient is
+    # bit-identical; its Y matches moe_forward's to bf16 rounding
+    _log("[backward full] moe_forward_train + moe_backward_saved")
+    g2 = {kk: torch.empty_like(v) for kk, v in g.items()}
+    Yt = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
+    ids2 = torch.empty_like(ids)
+    G2 = torch.empty_like(G)
+    moe.moe_forward_train(shape, opts, inp["X"], inp["Wg"], weights, ids2, G2, Yt, wsb)
+    moe.moe_backward_saved(shape, opts, inp["X"], inp["Wg"], weights, ids2, G2, dY.cuda(),
+                           moe.make_grads(**g2), wsb)
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(wsb) == 0
+    assert torch.equal(ids2, ids) and torch.equal(G2, G)
+    for kk in g:
+        assert torch.equal(g2[kk], g[kk]), kk
+    Yf = torch.empty_like(Yt)
+    moe.moe_forward(shape, opts, inp["X"], inp["Wg"], weights, ids2, G2, Yf, ws)
+    torch.cuda.synchronize()
+    err_y = row_rel_err(f64(Yt), f64(Yf))
+    _log(f"[backward full] training forward vs moe_forward: {err_y:.3e}")
+    assert err_y <= 2e-2
+    del inp, g, g2, wsb, ws
     gc.collect()
     torch.cuda.empty_cache()
