@@ -329,12 +329,13 @@ def bench_backward(args, wl, inp, shape):
             tot += a.elapsed_time(b)
         return tot / args.steps
 
-    fwd_train()
-    bwd_saved()
-    torch.cuda.synchronize()
-    ft_ms = timed(fwd_train)
-    bs_ms = timed(bwd_saved, pre=fwd_train)
-    assert moe.moe_check_device_error(wsb) == 0
+    if not args.no_saved:
+        fwd_train()
+        bwd_saved()
+        torch.cuda.synchronize()
+        ft_ms = timed(fwd_train)
+        bs_ms = timed(bwd_saved, pre=fwd_train)
+        assert moe.moe_check_device_error(wsb) == 0
     counts = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
     flops, nbytes = backward_work(wl, counts)
     tflops = flops / (ms / 1000.0) / 1e12
@@ -356,9 +357,9 @@ def bench_backward(args, wl, inp, shape):
                      "frac_of_roofline": round(max(t_mfma, t_hbm) / (ms / 1000.0), 4)},
         # moe_backward_saved after moe_forward_train (activations kept instead of
         # recomputed): its own time per call, and the training forward's
-        "saved_activations": {"backward_ms": round(bs_ms, 4),
-                              "tokens_per_s": round(T / (bs_ms / 1000.0), 1),
-                              "forward_train_ms": round(ft_ms, 4)},
+        "saved_activations": None if args.no_saved else {
+            "backward_ms": round(bs_ms, 4), "tokens_per_s": round(T / (bs_ms / 1000.0), 1),
+            "forward_train_ms": round(ft_ms, 4)},
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -377,6 +378,9 @@ def main(argv=None):
                     help="only run a device copy of this many bytes (counter calibration)")
     ap.add_argument("--backward", action="store_true",
                     help="time the local backward (moe_backward, router on) instead")
+    ap.add_argument("--no-saved", action="store_true",
+                    help="with --backward: skip the saved-activation pair (moe_forward_train, "
+                         "moe_backward_saved)")
     args = ap.parse_args(argv)
     if args.copy_probe:
         return copy_probe(args.copy_probe)
