@@ -19,10 +19,11 @@
 //   wgrad_kernel  dW[e] = A_eᵀ B_e over the rows of expert e (ragged K).  Both
 //                 operands are [rows, dim] (dim contiguous); chunks of 32 rows
 //                 are DMA'd to LDS (rows past the expert's block cleared) and
-//                 read with the transposing ds_read_b64_tr_b16.  Tiles are
-//                 scheduled statically in groups of 64 per XCD so that the
-//                 blocks sharing a chunk read it together.  An expert without
-//                 rows gets zeros.
+//                 read with the transposing ds_read_b64_tr_b16 as fragments
+//                 of v_mfma_f32_32x32x16_bf16.  Tiles are scheduled
+//                 statically in groups of 64 per XCD so that the blocks
+//                 sharing a chunk read it together; the dW stores are
+//                 non-temporal.  An expert without rows gets zeros.
 #include "lds_dma.h"
 #include "moe_internal.h"
 
@@ -468,13 +469,13 @@ __device__ __forceinline__ int wg_swz(int r) {
 // Block b runs on XCD b % 8 and takes tile b / 8 of every group its XCD
 // holds (m-tile (b / 8) % 8, n-tile b / 64 inside it): the 64 blocks of
 // an XCD work through one group at a time, over the same rows at about the
-// same time, so each 32-row chunk of A or B they read comes from HBM into
-// that XCD's L2 once for 8 blocks.  A block's tiles form one flat sequence
-// of 32-row K chunks (a segment without rows counts one empty chunk), DMA'd
-// into a STAGES-deep LDS ring; a chunk's rows past the segment are cleared in
-// LDS before use.  The MFMA's first operand is the B tile (n), its second the
-// A tile (m); a finished tile goes through a swizzled LDS buffer and leaves as
-// 16-byte stores of whole rows.
+// same time, so the 8 blocks that read a 32-row chunk of A or B do so while
+// it is in that XCD's L2.  A block's tiles form one flat sequence of 32-row
+// K chunks (a segment without rows counts one empty chunk), DMA'd into a
+// STAGES-deep LDS ring; a chunk's rows past the segment are cleared in LDS
+// before use.  v_mfma_f32_32x32x16_bf16, first operand the B tile (n), second
+// the A tile (m).  A finished tile is staged, swizzled, in the ring stage
+// just multiplied and leaves as non-temporal 16-byte stores of whole rows.
 template <int BN, int STAGES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void wgrad_kernel(WgradArgs g) {
