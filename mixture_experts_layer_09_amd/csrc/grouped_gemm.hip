@@ -547,6 +547,58 @@ struct DmaOps<MOE_PREC_FP8, BN> {
   }
 };
 
+// e4m3 with 512-wide n-tiles: 32 x 32 tiles on the scaled 32x32x64 MFMA
+// (unit scales), K-stages of 64 values, so that a stage (8 KB of A, 32 KB of
+// B) is the bf16 512-wide kernel's and three fit in LDS.  A lane holds row
+// (or column) lane % 32 at K 32 (lane / 32) + 0..31: for A two 16-byte chunks
+// of its 64-byte row, for B four transposing 8-bit reads of 8 K-rows each,
+// byte j of either at K 32 (lane / 32) + j; with unit scales the MFMA's own
+// K order does not matter, only that A and B agree.  B rows are 512 bytes
+// (32 chunks); half a transposing read covers 8 consecutive K-rows x 2
+// chunks, which the swizzle chunk ^ 2 (r % 8) puts on 64 distinct banks.
+template <>
+struct DmaOps<MOE_PREC_FP8, 512> {
+  static constexpr int ESZ = 1, BK = 64, A_CHUNKS = 4;
+  static constexpr int TM = 32, NV = 16;
+  typedef i32x8_t frag;
+  typedef f32x16_t acc_t;
+  __device__ static int row_of(int lane, int v) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+  __device__ static int col_of(int lane) { return lane & 31; }
+  __device__ static int swz_a(int r) { return (r >> 2) & 3; }
+  __device__ static int swz_b(int r) { return 2 * (r & 7); }
+  template <int B_ROW>
+  __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int r = 32 * (g >> 1) + 8 * h + (p >> 1);
+      const int col = col0 + 16 * (g & 1) + 8 * (p & 1);  // byte
+      o[h] = r * B_ROW + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+    }
+  }
+  __device__ static frag load_b(const char* st, const int (&o)[4]) {
+    const i32x2v_t a = ds_read_tr8(st + o[0]);
+    const i32x2v_t b = ds_read_tr8(st + o[1]);
+    const i32x2v_t c = ds_read_tr8(st + o[2]);
+    const i32x2v_t d = ds_read_tr8(st + o[3]);
+    return i32x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+  template <int A_ROW>
+  __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
+    const int c0 = 2 * (lane >> 5);
+    o[0] = r * A_ROW + ((c0 ^ swz_a(r)) << 4);
+    o[1] = r * A_ROW + (((c0 + 1) ^ swz_a(r)) << 4);
+  }
+  __device__ static frag load_a(const char* st, const int (&o)[2]) {
+    const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(st + o[0]);
+    const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(st + o[1]);
+    return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __device__ static f32x16_t mma(frag a, frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
 // The work item of this block: its segment, m-tile and n-tile (false when
 // the block has none).  Blocks are dealt to the 8 XCDs round-robin; XCD x
 // runs either one contiguous range of items or (g.chunk > 0) chunks of
@@ -1536,9 +1588,13 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
     return wide ? run_ffn<PREC, 16, 256, 1, 4, 1>(a, stream)
                 : run_ffn<PREC, 16, 128, 1, 4, 1>(a, stream);
   if constexpr (PREC == MOE_PREC_FP8) {
-    // e4m3: 128 x 256 tiles on 8 waves (64 x 64 per wave): the 3-stage ring
-    // (144 KB) allows one block per CU, and 8 waves give two per SIMD to
-    // cover each other's LDS and DMA waits
+    // e4m3: 128 x 512 tiles on 8 waves (64 x 128 per wave, 32x32x64 MFMA,
+    // 64-value stages) where hidden and 2 * inter allow, which halves the
+    // re-reads of token-row tiles (one per n-tile) against 256-wide tiles;
+    // else 128 x 256 (64 x 64 per wave, 16x16x128, 128-value stages).  Either
+    // ring takes most of the LDS (120 / 144 KB): one block per CU, and its 8
+    // waves are two per SIMD to cover each other's LDS and DMA waits
+    if ((a.h % 512 == 0) && ((2 * a.f) % 512 == 0)) return run_ffn<PREC, 128, 512, 2, 4, 3>(a, stream);
     return run_ffn<PREC, 128, 256, 2, 4, 3>(a, stream);
   } else {
     if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
