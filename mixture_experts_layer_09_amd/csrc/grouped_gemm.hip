@@ -664,6 +664,24 @@ struct DmaOps<MOE_PREC_INT8, BN> : DmaOps<MOE_PREC_FP8, BN> {
   }
 };
 
+typedef __attribute__((ext_vector_type(16))) int i32x16_t;
+
+// INT8 on the 128 x 512 tiles: the e4m3 32x32 operand layout, a stage's 64
+// K-values per lane pair through two 32x32x32 int8 MFMAs (bytes 0-15 of both
+// fragments, then bytes 16-31).  As for the 16x16 form, A and B hold the same
+// K index at the same (lane, byte), so the pair sums exactly the stage's
+// products, into int32.
+template <>
+struct DmaOps<MOE_PREC_INT8, 512> : DmaOps<MOE_PREC_FP8, 512> {
+  typedef i32x16_t acc_t;
+  __device__ static i32x16_t mma(i32x8_t a, i32x8_t b, i32x16_t c) {
+    const i32x4_t alo = {a[0], a[1], a[2], a[3]}, ahi = {a[4], a[5], a[6], a[7]};
+    const i32x4_t blo = {b[0], b[1], b[2], b[3]}, bhi = {b[4], b[5], b[6], b[7]};
+    c = __builtin_amdgcn_mfma_i32_32x32x32_i8(alo, blo, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(ahi, bhi, c, 0, 0, 0);
+  }
+};
+
 __device__ __forceinline__ f32x4_t mma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
@@ -1666,9 +1684,14 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   // MXFP4: 128 x 256 tiles on 8 waves, a 2-stage ring of 128-value K-stages
   // plus two 6 KB scale windows (60 KB), two blocks per CU
   if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 2>(a, stream);
-  // INT8: the e4m3 tiles (128 x 256 on 8 waves, 3-stage ring) at every batch
-  // size (the 16-row decode kernel has no int8 form)
-  if (a.precision == MOE_PREC_INT8) return run_ffn<MOE_PREC_INT8, 128, 256, 2, 4, 3>(a, stream);
+  // INT8: the e4m3 tiles (128 x 512 where hidden and 2 * inter allow, else
+  // 128 x 256; 8 waves, 3-stage ring) at every batch size (the 16-row decode
+  // kernel has no int8 form)
+  if (a.precision == MOE_PREC_INT8) {
+    if ((a.h % 512 == 0) && ((2 * a.f) % 512 == 0))
+      return run_ffn<MOE_PREC_INT8, 128, 512, 2, 4, 3>(a, stream);
+    return run_ffn<MOE_PREC_INT8, 128, 256, 2, 4, 3>(a, stream);
+  }
   return dispatch_ffn<MOE_PREC_FP8>(a, stream);
 }
 

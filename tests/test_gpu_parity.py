@@ -233,7 +233,8 @@ def _edge(base, ids=None, **kw):
                                   "fp8_all_to_one", "int8_all_to_one", "int8_decode",
                                   "mxfp8_all_to_one", "mxfp8_decode",
                                   "mxfp4_all_to_one", "mxfp4_decode",
-                                  "decode_one_token"])
+                                  "decode_one_token", "bf16_wide_tiles", "fp8_wide_tiles",
+                                  "int8_wide_tiles"])
 def test_edge_cases(kind):
     _need_gpu()
     spec = {
@@ -254,6 +255,11 @@ def test_edge_cases(kind):
                                                   topk=1, zipf=False)),
         "mxfp4_decode": ("v4pro_mxfp4", dict(T=3, hidden=512, experts=64, inter=256)),
         "decode_one_token": ("decode_hash_bf16", dict(T=1, hidden=256, experts=64, inter=128)),
+        # 128 x 512 tiles: two n-tiles per linear, K of 1024 and 512, Zipf load
+        # (the hottest expert holds 4 m-tiles, the last one ragged)
+        "bf16_wide_tiles": ("v4pro_bf16", dict(T=512, hidden=1024, experts=64, inter=512)),
+        "fp8_wide_tiles": ("v4pro_fp8", dict(T=512, hidden=1024, experts=64, inter=512)),
+        "int8_wide_tiles": ("v4pro_int8", dict(T=512, hidden=1024, experts=64, inter=512)),
     }[kind]
     cpu, L = _edge(spec[0], **spec[1])
     wl = cpu["workload"]
