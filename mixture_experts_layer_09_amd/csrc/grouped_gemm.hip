@@ -1596,11 +1596,14 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
 template <int PREC>
 hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
   const int rows = a.T * a.k;
-  // Decode-sized batches (a few rows per expert) stream weights with 16-row
-  // tiles and one LDS stage, so more blocks fit on a CU; prefill batches use
-  // the 3-stage DMA pipeline.  N tiles of 256 need hidden and 2*inter to be
-  // multiples of 256, else 128.
-  const bool small = static_cast<long>(rows) < 16L * a.E;
+  // Decode-sized batches (a few rows per expert) are weight streams.  For
+  // bf16 with 512-wide n-tiles the 3-stage DMA pipeline streams them fastest
+  // (only an expert's live rows are fetched and multiplied, and one block per
+  // CU keeps 120 KB of weight slices in flight); otherwise they run 16-row
+  // tiles with one LDS stage, so more blocks fit on a CU.  N tiles of 256
+  // need hidden and 2*inter to be multiples of 256, else 128.
+  const bool w512 = (a.h % 512 == 0) && ((2 * a.f) % 512 == 0);
+  const bool small = static_cast<long>(rows) < 16L * a.E && !(PREC == MOE_PREC_BF16 && w512);
   const bool wide = (a.h % 256 == 0) && ((2 * a.f) % 256 == 0);
   if (small)
     return wide ? run_ffn<PREC, 16, 256, 1, 4, 1>(a, stream)
@@ -1616,11 +1619,10 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
     return run_ffn<PREC, 128, 256, 2, 4, 3>(a, stream);
   } else {
     if (!wide) return run_ffn<PREC, 128, 128, 2, 2, 2>(a, stream);
-    // About one m-tile of rows per expert: every m-tile's token rows are read
-    // once per n-tile, so 512-wide n-tiles on 8 waves halve that traffic.
-    // With more rows per expert the weight tiles dominate and two 4-wave
-    // blocks of 128 x 256 per CU are faster.
-    const bool w512 = (a.h % 512 == 0) && ((2 * a.f) % 512 == 0);
+    // About one m-tile of rows per expert or fewer: every m-tile's token rows
+    // are read once per n-tile, so 512-wide n-tiles on 8 waves halve that
+    // traffic.  With more rows per expert the weight tiles dominate and two
+    // 4-wave blocks of 128 x 256 per CU are faster.
     if (w512 && static_cast<long>(rows) < 256L * a.E)
       return run_ffn<PREC, 128, 512, 2, 4, 3>(a, stream);
     return run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream);
