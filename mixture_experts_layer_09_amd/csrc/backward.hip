@@ -435,6 +435,7 @@ struct WgradArgs {
   void* out_sh;      // [M, N]
   const int32_t* offsets;
   int E, M, N, T, has_shared;
+  int strip_rows;  // routed segments of at most this many rows go to wgrad_strip_kernel (-1: none)
 };
 
 // s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63] (binary dispatch).
@@ -530,18 +531,29 @@ void wgrad_kernel(WgradArgs g) {
     return c;
   };
   // from group (sg, gm, gn) on, this XCD's first group with a tile for this
-  // block (a segment's last row or column of groups may be short)
+  // block (a segment's last row or column of groups may be short), skipping
+  // the routed segments that wgrad_strip_kernel takes
   auto settle = [&](Cur c) -> Cur {
+    int k0 = 0, k1 = g.T;
+    bool sh = false;
     for (;;) {
       if (c.sg >= nseg) return c;
-      if (c.gm * 8 + sm < MTt && c.gn * 8 + sn < NTt) break;
+      if (c.gm * 8 + sm < MTt && c.gn * 8 + sn < NTt) {
+        sh = g.has_shared && c.sg == 0;
+        c.seg = sh ? g.E : c.sg - (g.has_shared ? 1 : 0);
+        k0 = 0;
+        k1 = g.T;
+        if (!sh) scalar_load2(g.offsets + c.seg, k0, k1);
+        if (sh || k1 - k0 > g.strip_rows) break;
+        // on to this XCD's first group past the segment
+        const int left = ngm * ngn - (c.gm * ngn + c.gn);
+        c.gn += 8 * ((left + 7) / 8);
+        c = carry(c);
+        continue;
+      }
       c.gn += 8;
       c = carry(c);
     }
-    const bool sh = g.has_shared && c.sg == 0;
-    c.seg = sh ? g.E : c.sg - (g.has_shared ? 1 : 0);
-    int k0 = 0, k1 = g.T;
-    if (!sh) scalar_load2(g.offsets + c.seg, k0, k1);
     c.rem = k1 - k0;
     c.nkc = max(1, (c.rem + KC - 1) / KC);
     c.kc = 0;
@@ -748,6 +760,249 @@ void wgrad_kernel(WgradArgs g) {
   }
 }
 
+// dW[e] for the routed segments of at most strip_rows (<= 128) rows, most of
+// the experts of a prefill batch.  A 128 x 128 tile over K = such a
+// segment's rows reads about as many bytes of A and B as it writes, so a
+// tile-by-tile walk reads about as much as it writes unless L2 catches the
+// re-reads.  Here a block takes a strip: one m-tile of one segment (128
+// columns of A_e).  The strip's rows of A_e are DMA'd into LDS once and kept
+// there while the block walks every n-tile of dW[e], streaming 32-row chunks
+// of B_e (the segment's rows, the n-tile's columns) through a STAGES-deep
+// ring; each wave stages its part of a finished tile in LDS of its own and
+// stores it as whole 128-byte lines.  The small segments are
+// dealt to the 8 XCDs in turn (block b runs on XCD b % 8) and an XCD's 64
+// blocks take its strips in order, so a segment's strips (M / 128 of them)
+// run together on one XCD and read the same B_e rows, at most 128 x N
+// values, through its L2.  A segment without rows gets zero tiles.
+template <int STAGES, int RS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void wgrad_strip_kernel(WgradArgs g) {
+  constexpr int BM = 128, BN = 128, KC = 32;
+  constexpr int CH = KC * 256;                // one 32-row chunk of 256-byte rows (A or B)
+  constexpr int OPS = CH / 1024 / 4;          // DMAs per wave per chunk
+  constexpr int NA = RS / KC;                 // A chunks of a strip, at most
+  constexpr int NB = BN / 64;                 // 32-column n blocks per wave
+  constexpr int NST = 8;                      // 16-byte stores of a tile, per thread
+  constexpr int B_OFF = NA * CH;
+  constexpr int STG_OFF = B_OFF + STAGES * CH;
+  constexpr int LDS_BYTES = STG_OFF + 4 * 4096;  // a 32 x 64 staging block per wave
+  static_assert(RS % KC == 0 && BM == 128 && BN == 128, "strip shape");
+  static_assert((STAGES - 2) * OPS + (STAGES - 1) * NST <= 63, "vmcnt range");
+  static_assert(LDS_BYTES + kMaxExperts / 8 * 4 + 16 <= 81920, "two blocks per CU");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  __shared__ int list[kMaxExperts / 8];  // this XCD's segments, in order
+  __shared__ int wsum[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // 2 x 2 waves of 64 x 64
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;  // 512 blocks: 64 per XCD
+  const int MTt = g.M / BM, NTt = g.N / BN;
+  const uint32_t lda = static_cast<uint32_t>(g.M) * 2, ldb = static_cast<uint32_t>(g.N) * 2;
+
+  // the small segments, numbered in expert order by a block-wide scan (two
+  // experts per thread); number i goes to XCD i % 8
+  const int e0 = 2 * tid, e1 = e0 + 1;
+  const int f0 = (e0 < g.E && g.offsets[e0 + 1] - g.offsets[e0] <= g.strip_rows) ? 1 : 0;
+  const int f1 = (e1 < g.E && g.offsets[e1 + 1] - g.offsets[e1] <= g.strip_rows) ? 1 : 0;
+  int v = f0 + f1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int i0 = before + v - f0 - f1;  // number of e0 among the small segments
+  if (f0 && i0 % 8 == xcd) list[i0 / 8] = e0;
+  if (f1 && (i0 + f0) % 8 == xcd) list[(i0 + f0) / 8] = e1;
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  const int nlist = (total - xcd + 7) / 8;  // numbers i < total with i % 8 == xcd
+  __syncthreads();
+
+  // per-lane DMA and fragment offsets, as in wgrad_kernel: rows of 16
+  // swizzled 16-byte chunks; lane l holds column l % 32 at K rows
+  // 16 kh + 8 (l / 32) + 0..7 of both operands
+  int rq[OPS];
+  uint32_t cq[OPS];
+#pragma unroll
+  for (int q = 0; q < OPS; ++q) {
+    rq[q] = (wave * OPS + q) * 4 + lane / 16;
+    cq[q] = static_cast<uint32_t>(((lane & 15) ^ wg_swz<16>(rq[q])) << 4);
+  }
+  const uint32_t lds0 = lds_address(smem);
+  const int kgr = lane >> 4, p = lane & 15;
+  auto toff = [&](int col0, int kh, int h) {
+    const int r = 16 * kh + 8 * (kgr >> 1) + 4 * h + (p >> 2);
+    const int col = col0 + 16 * (kgr & 1) + (p & 3) * 4;
+    return r * 256 + (((col >> 3) ^ wg_swz<16>(r)) << 4) + (col & 7) * 2;
+  };
+  int offB[2][NB][2], offA[2][2][2];  // [kh][block][h]
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) offB[kh][i][h] = B_OFF + toff(wn * (BN / 2) + i * 32, kh, h);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) offA[kh][j][h] = toff(wm * 64 + j * 32, kh, h);
+    }
+  auto frag = [&](const char* base, int o0, int o1) {
+    const i16x4_t lo4 = ds_read_tr16(base + o0);
+    const i16x4_t hi4 = ds_read_tr16(base + o1);
+    const i16x8s_t w = i16x8s_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8_t, w);
+  };
+  f32x16_t acc[NB][2];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  };
+  // tile (mt, n) of dW[e] at ob.  Each wave stages its own 64 x 64 part, 32
+  // rows at a time, in its own 4 KB of LDS (128-byte rows, 16-byte chunk c
+  // of row r at c ^ ((r >> 1) & 7), which keeps both the 8-byte writes and
+  // the 16-byte reads free of bank conflicts) and stores it as whole 128-byte
+  // lines, non-temporal; no block-wide barrier.
+  char* wstg = smem + STG_OFF + wave * 4096;
+  auto store = [&](uint16_t* ob, int mt, int n) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ml = lane & 31;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = 4 * i + q;  // columns 8 c .. 8 c + 7 of the wave's 64
+          const uint32_t lo = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+          const uint32_t hi = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          *reinterpret_cast<uint2*>(wstg + ml * 128 + ((c ^ ((ml >> 1) & 7)) << 4) + (lane >> 5) * 8) =
+              make_uint2(lo, hi);
+        }
+      // the wave's LDS operations run in order: once its writes are done,
+      // its reads see them (the memory clobber keeps the compiler's order)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = (lane >> 3) + 8 * k, ch = lane & 7;
+        const uint4 w = *reinterpret_cast<const uint4*>(wstg + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+        __builtin_nontemporal_store(u32x4_t{w.x, w.y, w.z, w.w},
+                                    reinterpret_cast<u32x4_t*>(ob + static_cast<size_t>(mt * BM + wm * 64 + j * 32 + r) * g.N +
+                                                               n * BN + wn * 64 + ch * 8));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+    }
+  };
+
+  const int nstrips = nlist * MTt;
+  for (int s = slot; s < nstrips; s += 64) {
+    const int li = s / MTt, mt = s - li * MTt;
+    const int e = __builtin_amdgcn_readfirstlane(list[li]);
+    int k0, k1;
+    scalar_load2(g.offsets + e, k0, k1);
+    const int R = k1 - k0;
+    uint16_t* ob = static_cast<uint16_t*>(g.out) + static_cast<size_t>(e) * g.M * g.N;
+    zero_acc();
+    if (R == 0) {
+      for (int n = 0; n < NTt; ++n) store(ob, mt, n);
+      continue;
+    }
+    const int nkc = (R + KC - 1) / KC;
+    // the strip's A rows (rows past the segment repeat its last row and are
+    // cleared below, before the first multiply)
+    const char* a_src = static_cast<const char*>(g.A) + static_cast<size_t>(k0) * lda + mt * BM * 2;
+    for (int kc = 0; kc < nkc; ++kc) {
+      const int kv = min(KC, R - kc * KC);
+#pragma unroll
+      for (int q = 0; q < OPS; ++q)
+        dma16_at(a_src + static_cast<size_t>(kc) * KC * lda,
+                 static_cast<uint32_t>(min(rq[q], kv - 1)) * lda + cq[q],
+                 lds0 + kc * CH + (wave * OPS + q) * 1024);
+    }
+    // B chunks in (n-tile, chunk) order: chunk kc of n-tile n is rows
+    // 32 kc .. of the segment, columns n BN ..
+    const char* b_src = static_cast<const char*>(g.B) + static_cast<size_t>(k0) * ldb;
+    auto issue = [&](int n, int kc, int st) {
+      const int kv = min(KC, R - kc * KC);
+#pragma unroll
+      for (int q = 0; q < OPS; ++q)
+        dma16_at(b_src + static_cast<size_t>(kc) * KC * ldb + n * BN * 2,
+                 static_cast<uint32_t>(min(rq[q], kv - 1)) * ldb + cq[q],
+                 lds0 + B_OFF + st * CH + (wave * OPS + q) * 1024);
+    };
+    const int nsteps = NTt * nkc;
+    int in_ = 0, ikc = 0, n_iss = 0;  // the next chunk to DMA
+#pragma unroll
+    for (int q = 0; q < STAGES - 1; ++q)
+      if (n_iss < nsteps) {
+        issue(in_, ikc, q);
+        if (++ikc == nkc) {
+          ikc = 0;
+          ++in_;
+        }
+        ++n_iss;
+      }
+    int cn = 0, ckc = 0;  // the chunk to multiply
+    uint32_t ends = 0;    // bit d - 1: the step d back ended a tile (its stores follow)
+    for (int t = 0; t < nsteps; ++t) {
+      const int st = t % STAGES;
+      // chunk t (and, issued before it, the strip's A rows) is in LDS once at
+      // most the memory operations issued after it are in flight
+      const int after = (n_iss - 1 - t) * OPS + NST * __builtin_popcount(ends & ((1u << (STAGES - 1)) - 1));
+      wait_vm_range<0, 63>(after);
+      __builtin_amdgcn_s_barrier();  // ... for every wave; all are done with chunk t - 1
+      if (t == 0 && R % KC != 0) {  // A rows past the segment: clear
+        const int kv = R % KC;
+        char* al = smem + (nkc - 1) * CH;
+        for (int i = tid; i < (KC - kv) * 16; i += 256)
+          *reinterpret_cast<uint4*>(al + (kv + i / 16) * 256 + (i % 16) * 16) = make_uint4(0, 0, 0, 0);
+        __syncthreads();
+      }
+      if (n_iss < nsteps) {
+        issue(in_, ikc, (t + STAGES - 1) % STAGES);
+        if (++ikc == nkc) {
+          ikc = 0;
+          ++in_;
+        }
+        ++n_iss;
+      }
+      const char* abase = smem + ckc * CH;
+      const char* bbase = smem + st * CH;
+      bf16x8_t bn[2][NB], am[2][2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bn[kh][i] = frag(bbase, offB[kh][i][0], offB[kh][i][1]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) am[kh][j] = frag(abase, offA[kh][j][0], offA[kh][j][1]);
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bn[kh][i], am[kh][j], acc[i][j], 0, 0, 0);
+      const bool end = ckc == nkc - 1;
+      if (end) {
+        store(ob, mt, cn);
+        zero_acc();
+      }
+      ends = (ends << 1) | (end ? 1u : 0u);
+      if (++ckc == nkc) {
+        ckc = 0;
+        ++cn;
+      }
+    }
+    __syncthreads();  // every wave is done with the strip's A rows and B chunks
+  }
+}
+
 // Gating-bias gradient: column sums of dl [T, E] in two fixed-order passes.
 // Pass 1: block (expert group of 64, 256-row chunk); wave w sums rows w, w +
 // 4, ... of the chunk; the 4 wave sums are added in order.
@@ -810,12 +1065,21 @@ hipError_t dgrad(const DgradArgs& in, int rows, int T_sh, bool swb, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t wgrad(const WgradArgs& g, hipStream_t stream) {
+// The strip kernel: ring depth and the most rows of a segment it takes.
+constexpr int kStripStages = 3, kStripRows = 128;
+
+hipError_t wgrad(const WgradArgs& in, hipStream_t stream) {
   constexpr unsigned kBlocks = 512;  // 64 per XCD, two per CU
+  WgradArgs g = in;
+  const bool strips = g.E > 0 && g.N % 128 == 0 && g.M % 128 == 0;
+  g.strip_rows = strips ? kStripRows : -1;
   if (g.N % 128 == 0)
     hipLaunchKernelGGL((wgrad_kernel<128, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
   else  // N % 64 == 0 (the router's experts)
     hipLaunchKernelGGL((wgrad_kernel<64, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
+  if (strips)
+    hipLaunchKernelGGL((wgrad_strip_kernel<kStripStages, kStripRows>), dim3(kBlocks), dim3(256), 0,
+                       stream, g);
   return hipGetLastError();
 }
 
