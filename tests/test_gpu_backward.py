@@ -1,7 +1,7 @@
 """GPU parity of the local backward (moe_backward) against the oracle.
 
-Routing comes from the GPU router (moe_route), the upstream gradient dY is a
-seeded bf16 tensor; the oracle differentiates the same layer (bf16 values) at
+Routing comes from the GPU router (moe_route), or is given with set expert
+loads (ROUTING); the upstream gradient dY is a seeded bf16 tensor; the oracle differentiates the same layer (bf16 values) at
 the same routing in fp64: dX (experts' part plus, with router options, the
 router's), dG, the weight gradients of every expert and of the shared expert,
 and the router's dWg and gating-bias gradient.
@@ -33,7 +33,15 @@ CASES = {
     "sqrt_softplus_bwd": ("v4pro_bf16", dict(T=150, hidden=256, experts=64, inter=128,
                                              score="sqrt_softplus"), True),
     "hash_bwd": ("decode_hash_bf16", dict(T=40, hidden=512, experts=64, inter=256), True),
+    # given top-1 routing with the expert loads below: the wgrad kernels split
+    # the routed experts at 128 rows (a strip kernel up to 128, the tile walk
+    # above, with the shared expert), and rows come in 32-row chunks
+    "wgrad_split_bwd": ("v4pro_bf16", dict(T=1050, hidden=1024, experts=12, inter=1024, topk=1,
+                                           zipf=False), False),
 }
+# rows per expert of the cases with given routing
+ROUTING = {"wgrad_split_bwd": [0, 1, 31, 32, 33, 64, 127, 128, 129, 200, 300, 5]}
+_ORACLE_DW = {}  # (case) -> the oracle's dW1, dW2 (the same for both modes)
 
 
 def _log(msg):
@@ -58,9 +66,18 @@ def run_case(name, saved=False):
                                gpu["token_ids"], gpu["tid2eid"])
     weights = moe.make_weights(gpu["W1"], gpu["W2"], None, None, gpu["Ws1"], gpu["Ws2"])
     ws = moe.alloc_workspace(shape)
-    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    G = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    moe.moe_route(shape, opts, gpu["X"], gpu["Wg"], ids, G, None, ws)
+    if name in ROUTING:  # seeded token order, weights in [0.25, 1)
+        counts = ROUTING[name]
+        assert sum(counts) == T * k and len(counts) == E and k == 1
+        rng = np.random.default_rng(7)
+        e_of_tok = np.repeat(np.arange(E, dtype=np.int32), counts)
+        rng.shuffle(e_of_tok)
+        ids = torch.from_numpy(e_of_tok.reshape(T, 1)).cuda()
+        G = torch.from_numpy(rng.uniform(0.25, 1.0, (T, 1)).astype(np.float32)).cuda()
+    else:
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        G = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        moe.moe_route(shape, opts, gpu["X"], gpu["Wg"], ids, G, None, ws)
     gen = torch.Generator().manual_seed(1234)
     dY = torch.randn((T, h), generator=gen).to(torch.bfloat16)
     dYg = dY.cuda()
@@ -117,7 +134,9 @@ def test_backward_parity(name, saved):
         err["dgate_bias"] = float(np.abs(db - b["dgate_bias"]).max() / np.abs(b["dgate_bias"]).max())
     err["dX"] = row_rel_err(f64(g["dX"]), dX)
     experts = list(range(wl.experts)) + ([wl.experts] if wl.shared else [])
-    dW1, dW2 = L.backward_weights(ids, G, dY, experts)
+    if name not in _ORACLE_DW:
+        _ORACLE_DW[name] = L.backward_weights(ids, G, dY, experts)
+    dW1, dW2 = _ORACLE_DW[name]
     gw1 = f64(g["dW1"])
     gw2 = f64(g["dW2"])
     if wl.shared:
@@ -140,7 +159,8 @@ def test_backward_full_size_v4pro():
     f = 3072, shared expert, router on), as the benchmark's backward run times
     it.  Checked: dX (experts' and router's parts) and dG on sampled tokens
     (the hottest expert's ragged tail, the coldest experts, first and last
-    token), dW1 / dW2 of the two least-loaded active experts, and zero
+    token), dW1 / dW2 of the two least-loaded active experts (strip kernel)
+    and of the least-loaded expert above 128 rows (tile walk), and zero
     gradients for experts without rows."""
     _need_gpu()
     import gc
@@ -199,9 +219,12 @@ def test_backward_full_size_v4pro():
     del L
     gc.collect()
 
-    # weight gradients of the two least-loaded active experts (all their rows)
+    # weight gradients (all their rows) of the two least-loaded active experts
+    # and of the least-loaded one above 128 rows
     active = np.nonzero(counts > 0)[0]
     cold = [int(e) for e in active[np.argsort(counts[active], kind="stable")[:2]]]
+    above = np.nonzero(counts > 128)[0]
+    cold.append(int(above[np.argmin(counts[above])]))
     remap = np.full(E, -1, np.int32)
     remap[cold] = np.arange(len(cold), dtype=np.int32)
     idx = torch.tensor(cold, dtype=torch.long, device="cuda")
