@@ -645,7 +645,42 @@ __device__ __forceinline__ bool block_item(const GemmArgs& g, int& seg, int& mti
 // MXFP8 shares the e4m3 operand layout; its MFMA takes each lane's E8M0
 // scale byte (the lane's 32 K-values are one MX group) for A and for B.
 template <int BN>
-struct DmaOps<MOE_PREC_MXFP8, BN> : DmaOps<MOE_PREC_FP8, BN> {};
+struct DmaOps<MOE_PREC_MXFP8, BN> : DmaOps<MOE_PREC_FP8, BN> {
+  __device__ static f32x4_t mma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  }
+};
+
+// MXFP8 on the 128 x 512 tiles.  The scaled 32x32x64 form takes K 0..31 of
+// the stage from bytes 0-15 of both lane groups and K 32..63 from bytes
+// 16-31, and lane l's scale for row (column) l % 32 and K group l / 32
+// (measured on the GPU with one-hot operands and per-lane scales).  So lane
+// group G holds K 16 G .. 16 G + 15 in bytes 0-15 and K 32 + 16 G .. in bytes
+// 16-31 (A: 16-byte chunks G and G + 2 of the row; B: the transposing reads
+// from those K rows), and each lane passes the scale of its row or column
+// and group l / 32.
+template <>
+struct DmaOps<MOE_PREC_MXFP8, 512> : DmaOps<MOE_PREC_FP8, 512> {
+  template <int B_ROW>
+  __device__ static void b_offsets(int lane, int col0, int (&o)[4]) {
+    const int g = lane >> 4, p = lane & 15, G = g >> 1;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int r = 8 * h + 16 * G + 16 * (h >> 1) + (p >> 1);
+      const int col = col0 + 16 * (g & 1) + 8 * (p & 1);  // byte
+      o[h] = r * B_ROW + (((col >> 4) ^ swz_b(r)) << 4) + (col & 15);
+    }
+  }
+  template <int A_ROW>
+  __device__ static void a_offsets(int r, int lane, int (&o)[2]) {
+    const int G = lane >> 5;
+    o[0] = r * A_ROW + ((G ^ swz_a(r)) << 4);
+    o[1] = r * A_ROW + (((G + 2) ^ swz_a(r)) << 4);
+  }
+  __device__ static f32x16_t mma_mx(i32x8_t a, i32x8_t b, f32x16_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  }
+};
 
 // INT8 (the A8W8 block as printed) shares the 8-bit operand layout: a stage's
 // 128 K-values per lane pair go through two 16x16x64 int8 MFMAs, the first
@@ -682,10 +717,6 @@ struct DmaOps<MOE_PREC_INT8, 512> : DmaOps<MOE_PREC_FP8, 512> {
   }
 };
 
-__device__ __forceinline__ f32x4_t mma_mx(i32x8_t a, i32x8_t b, f32x4_t c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
-}
-
 // E8M0 code of the MX group scale for an e4m3 group whose largest magnitude
 // is amax (fp32): floor(log2 amax) - 8, i.e. the biased exponent minus 8,
 // clamped at 0 (all-zero and tiny groups); and 2^(127 - code) as a float.
@@ -714,11 +745,13 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr bool MX = PREC == MOE_PREC_MXFP8;
   // A8W8 (e4m3 or INT8): per-channel and per-row fp32 scales in the epilogue
   constexpr bool A8W8 = PREC == MOE_PREC_FP8 || PREC == MOE_PREC_INT8;
-  // MX: each stage also holds the E8M0 scales of its 4 K-groups: A [BM][4]
-  // (one dword per row) and B [4][BN] (one byte per group row and column)
+  // MX: each stage also holds the E8M0 scales of its KG K-groups: A [BM][4]
+  // (per row the aligned dword that holds them: K / 32 is a multiple of 4)
+  // and B [KG][BN] (one byte per group row and column)
+  constexpr int KG = BK / 32;
   constexpr int AS_OFF = A_BYTES + B_BYTES;
   constexpr int BS_OFF = AS_OFF + (MX ? BM * 4 : 0);
-  constexpr int STAGE = BS_OFF + (MX ? 4 * BN : 0);
+  constexpr int STAGE = BS_OFF + (MX ? KG * BN : 0);
   constexpr int AS_INSTS = MX ? BM / 64 : 0;  // dword DMA: 64 rows per instruction
   constexpr int A_INSTS = (A_BYTES + 1023) / 1024;
   constexpr int B_INSTS = B_BYTES / 1024;
@@ -732,13 +765,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int MT = WM / TM;
   constexpr int NTW = BN / WAVES_N / TM;
   static_assert(WM % TM == 0 && (BN / WAVES_N) % TM == 0, "wave tile in MFMA tiles");
-  static_assert(!MX || TM == 16, "MX epilogue and scales use the 16 x 16 layout");
   static_assert(B_INSTS % NW == 0, "B stage must split evenly over the waves");
   static_assert(A_BYTES % 1024 == 0 || A_INSTS == 1, "A stage granularity");
   static_assert(!SWIGLU || (NTW % 2 == 0), "SwiGLU needs gate/up pairs per wave");
-  static_assert(!MX || (BN == 256 && BM % 64 == 0 && NW > AS_INSTS),
+  static_assert(!MX || (KG * BN == 1024 && BM % 64 == 0 && NW > AS_INSTS && KG <= 4),
                 "MX scale DMA: one 1 KB instruction for B, 64-row ones for A");
-  static_assert(!MX || !SWIGLU || (NTW / 2) % 2 == 0,
+  static_assert(!MX || !SWIGLU || TM == 32 || (NTW / 2) % 2 == 0,
                 "MX SwiGLU epilogue: whole 32-column groups per wave");
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
@@ -845,9 +877,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
               static_cast<uint32_t>(sc_ld);
     bs_base = uniform_ptr(reinterpret_cast<const char*>(wsc8) +
                           static_cast<size_t>(nt) * (SWIGLU ? BN / 2 : BN));
-    const int nl = (lane % 16) * 16;
+    constexpr int CPR = BN / 16;  // 16-byte chunks of a group row
+    const int nl = (lane % CPR) * 16;
     const int col = (SWIGLU && nl >= BN / 2) ? g.f + (nl - BN / 2) : nl;
-    bs_voff = static_cast<uint32_t>(lane / 16) * static_cast<uint32_t>(g.Nw) + col;
+    bs_voff = static_cast<uint32_t>(lane / CPR) * static_cast<uint32_t>(g.Nw) + col;
     ops_sc = (wave <= AS_INSTS) ? 1 : 0;
   }
   const int ops_w = a_live + B_OPS + ops_sc;
@@ -865,9 +898,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     }
     if constexpr (MX) {
       if (wave < AS_INSTS)
-        dma4(as_base + static_cast<size_t>(kt) * 4, as_voff, st + AS_OFF + wave * 256);
+        dma4(as_base + ((static_cast<size_t>(kt) * KG) & ~static_cast<size_t>(3)), as_voff,
+             st + AS_OFF + wave * 256);
       else if (wave == AS_INSTS)
-        dma16(bs_base + static_cast<size_t>(kt) * 4 * g.Nw, bs_voff, st + BS_OFF);
+        dma16(bs_base + static_cast<size_t>(kt) * KG * g.Nw, bs_voff, st + BS_OFF);
     }
   };
 
@@ -898,15 +932,15 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   // MX: LDS byte of this lane's scale for A row tile i / B column tile j
   int as_off[MT], bs_off[NTW];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) as_off[i] = AS_OFF + (wm * WM + i * 16 + (lane & 15)) * 4 + (lane >> 4);
+  for (int i = 0; i < MT; ++i) as_off[i] = AS_OFF + (wm * WM + i * TM + (lane & (TM - 1))) * 4 + lane / TM;
 #pragma unroll
-  for (int j = 0; j < NTW; ++j) bs_off[j] = BS_OFF + (lane >> 4) * BN + bcol(j) + (lane & 15);
+  for (int j = 0; j < NTW; ++j) bs_off[j] = BS_OFF + (lane / TM) * BN + bcol(j) + (lane & (TM - 1));
 
   // A wave with any live row multiplies all of its MT row tiles (rows past the
   // segment only feed accumulators that are never stored); a wave with none
   // skips the stage's reads and MFMAs.  A single branch lets every fragment
   // read of the stage issue before the first MFMA.
-  auto compute = [&](int slot) {
+  auto compute = [&](int slot, int kt) {
     if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
     typename O::frag bfr[NTW];
@@ -917,14 +951,15 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     for (int i = 0; i < MT; ++i) af[i] = O::load_a(st, a_off[i]);
     if constexpr (MX) {
       int sa[MT], sb[NTW];
+      const int a_sub = (kt * KG) & 3;  // the stage's first group inside the row's dword
 #pragma unroll
-      for (int i = 0; i < MT; ++i) sa[i] = *reinterpret_cast<const uint8_t*>(st + as_off[i]);
+      for (int i = 0; i < MT; ++i) sa[i] = *reinterpret_cast<const uint8_t*>(st + as_off[i] + a_sub);
 #pragma unroll
       for (int j = 0; j < NTW; ++j) sb[j] = *reinterpret_cast<const uint8_t*>(st + bs_off[j]);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = mma_mx(af[i], bfr[j], acc[i][j], sa[i], sb[j]);
+        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma_mx(af[i], bfr[j], acc[i][j], sa[i], sb[j]);
     } else {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -950,13 +985,43 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
         wait_vmcnt_rt(after * ops_w);
         __builtin_amdgcn_s_barrier();
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-        compute(s);
+        compute(s, kt);
       }
     }
   }
 
   // ------------------------------------------------ epilogue
   const int col_in = O::col_of(lane);
+  if constexpr (MX && SWIGLU && TM == 32) {
+    // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
+    // gate tile j of one row, one value in each of the 32 lanes that hold the
+    // row (lanes 0-31 or 32-63); their amax goes round them by xor shuffles.
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) continue;  // wave-uniform
+#pragma unroll
+      for (int v = 0; v < O::NV; ++v) {
+        const int row = row0 + wm * WM + i * TM + O::row_of(lane, v);
+#pragma unroll
+        for (int j = 0; j < NTW / 2; ++j) {
+          const float u = silu(acc[i][j][v]) * acc[i][j + NTW / 2][v];
+          float amax = fabsf(u);
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          const uint32_t code = mx_e4m3_code(amax);
+          const float inv = mx_inv_scale(code);
+          if (row < row_end) {
+            const int c0 = nt * (BN / 2) + bcol(j);  // first column of the group
+            uint8_t* orow = reinterpret_cast<uint8_t*>(obase) + static_cast<size_t>(row) * g.Nout;
+            orow[c0 + col_in] = static_cast<uint8_t>(f32_to_e4m3(u * inv));
+            if (col_in == 0)
+              osc8[static_cast<size_t>(row) * (g.Nout / 32) + c0 / 32] = static_cast<uint8_t>(code);
+          }
+        }
+      }
+    }
+    return;
+  }
   if constexpr (MX && SWIGLU) {
     // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
     // gate tiles (j, j+1) of one row, i.e. 2 values in each of the 16 lanes
@@ -1682,7 +1747,12 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
   if (a.precision == MOE_PREC_BF16) return dispatch_ffn<MOE_PREC_BF16>(a, stream);
   // MX: the 3-stage DMA pipeline at every batch size (the 16-row decode
   // kernel has no per-group scales)
-  if (a.precision == MOE_PREC_MXFP8) return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
+  if (a.precision == MOE_PREC_MXFP8) {
+    // 128 x 512 tiles (32x32x64 scaled MFMA) where hidden and 2 * inter allow
+    if ((a.h % 512 == 0) && ((2 * a.f) % 512 == 0))
+      return run_ffn<MOE_PREC_MXFP8, 128, 512, 2, 4, 3>(a, stream);
+    return run_ffn<MOE_PREC_MXFP8, 128, 256, 2, 4, 3>(a, stream);
+  }
   // MXFP4: 128 x 256 tiles on 8 waves, a 2-stage ring of 128-value K-stages
   // plus two 6 KB scale windows (60 KB), two blocks per CU
   if (a.precision == MOE_PREC_MXFP4) return run_ffn<MOE_PREC_MXFP4, 128, 256, 2, 4, 2>(a, stream);

@@ -234,7 +234,7 @@ def _edge(base, ids=None, **kw):
                                   "mxfp8_all_to_one", "mxfp8_decode",
                                   "mxfp4_all_to_one", "mxfp4_decode",
                                   "decode_one_token", "bf16_wide_tiles", "fp8_wide_tiles",
-                                  "int8_wide_tiles"])
+                                  "int8_wide_tiles", "mxfp8_wide_tiles"])
 def test_edge_cases(kind):
     _need_gpu()
     spec = {
@@ -260,6 +260,7 @@ def test_edge_cases(kind):
         "bf16_wide_tiles": ("v4pro_bf16", dict(T=512, hidden=1024, experts=64, inter=512)),
         "fp8_wide_tiles": ("v4pro_fp8", dict(T=512, hidden=1024, experts=64, inter=512)),
         "int8_wide_tiles": ("v4pro_int8", dict(T=512, hidden=1024, experts=64, inter=512)),
+        "mxfp8_wide_tiles": ("v4pro_mxfp8", dict(T=512, hidden=1024, experts=64, inter=512)),
     }[kind]
     cpu, L = _edge(spec[0], **spec[1])
     wl = cpu["workload"]
