@@ -489,13 +489,17 @@ void wgrad_kernel(WgradArgs g) {
   constexpr int B_RPI = 1024 / (BN * 2); // B rows per DMA instruction
   constexpr int B_OPS = TILE_B / 1024 / 4;  // B DMAs per wave per chunk
   constexpr int NB = BN / 64;            // 32-column n blocks per wave
-  static_assert(BN == 128 || BN == 64, "n-tile width");
+  static_assert(BN == 256 || BN == 128 || BN == 64, "n-tile width");
   constexpr int OCH = BN / 8;                 // 16-byte chunks of an output row
-  constexpr int NSH = (BM / 2) * OCH / 256;   // 16-byte stores of a half tile, per thread
-  constexpr int NST = 2 * NSH;
+  // a finished tile is staged in NPH phases of PR rows: halves, or quarters
+  // where half a tile is more than a ring stage
+  constexpr int NPH = (BM / 2) * BN * 2 <= STAGE ? 2 : 4;
+  constexpr int PR = BM / NPH;
+  constexpr int NSH = PR * OCH / 256;         // 16-byte stores of a phase, per thread
+  constexpr int NST = NPH * NSH;
   constexpr int OPS = A_OPS + B_OPS;          // DMAs of one chunk, per wave
   static_assert((STAGES - 2) * OPS + (STAGES - 1) * NST <= 63, "vmcnt range");
-  static_assert((BM / 2) * BN * 2 <= STAGE, "half a tile is staged in one ring stage");
+  static_assert(PR * BN * 2 <= STAGE, "a staging phase fits in one ring stage");
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -543,7 +547,10 @@ void wgrad_kernel(WgradArgs g) {
         c.seg = sh ? g.E : c.sg - (g.has_shared ? 1 : 0);
         k0 = 0;
         k1 = g.T;
-        if (!sh) scalar_load2(g.offsets + c.seg, k0, k1);
+        if (!sh)  // (the pointer made explicitly wave-uniform: an operand of a scalar load)
+          scalar_load2(reinterpret_cast<const int32_t*>(
+                           uniform_ptr(reinterpret_cast<const char*>(g.offsets + c.seg))),
+                       k0, k1);
         if (sh || k1 - k0 > g.strip_rows) break;
         // on to this XCD's first group past the segment
         const int left = ngm * ngn - (c.gm * ngn + c.gn);
@@ -624,7 +631,7 @@ void wgrad_kernel(WgradArgs g) {
   auto toff = [&](int col0, int kh, int h, int W) {
     const int r = 16 * kh + 8 * (kgr >> 1) + 4 * h + (p >> 2);
     const int col = col0 + 16 * (kgr & 1) + (p & 3) * 4;
-    const int sw = W == 128 ? wg_swz<16>(r) : wg_swz<8>(r);
+    const int sw = W >= 128 ? wg_swz<16>(r) : wg_swz<8>(r);  // 256 or 512-byte rows alike
     return r * W * 2 + (((col >> 3) ^ sw) << 4) + (col & 7) * 2;
   };
   int offB[2][NB][2], offA[2][2][2];  // [kh][block][h]
@@ -667,11 +674,12 @@ void wgrad_kernel(WgradArgs g) {
                    (c.seg == g.E ? 0 : static_cast<size_t>(c.seg) * g.M * g.N);
     __syncthreads();  // every wave is done reading the stage
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
+    for (int ph = 0; ph < NPH; ++ph) {
+      if (wm == ph / (NPH / 2)) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int ml = j * 32 + (lane & 31);  // row inside the half
+          if (NPH == 4 && j != (ph & 1)) continue;
+          const int ml = (NPH == 4 ? 0 : j * 32) + (lane & 31);  // row inside the phase
 #pragma unroll
           for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -692,7 +700,7 @@ void wgrad_kernel(WgradArgs g) {
         // non-temporal: the dW stream would otherwise evict the A and B
         // chunks that the group's other blocks are about to read from L2
         __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
-                                    reinterpret_cast<u32x4_t*>(ob + static_cast<size_t>((c.gm * 8 + sm) * BM + half * 64 + r) * g.N +
+                                    reinterpret_cast<u32x4_t*>(ob + static_cast<size_t>((c.gm * 8 + sm) * BM + ph * PR + r) * g.N +
                                                                (c.gn * 8 + sn) * BN + cc * 8));
       }
       __syncthreads();  // the staging rows are free again
@@ -1073,7 +1081,9 @@ hipError_t wgrad(const WgradArgs& in, hipStream_t stream) {
   WgradArgs g = in;
   const bool strips = g.E > 0 && g.N % 128 == 0 && g.M % 128 == 0;
   g.strip_rows = strips ? kStripRows : -1;
-  if (g.N % 128 == 0)
+  if (strips && g.N % 256 == 0)  // the experts above strip_rows and the shared expert: long K
+    hipLaunchKernelGGL((wgrad_kernel<256, 3>), dim3(kBlocks), dim3(256), 0, stream, g);
+  else if (g.N % 128 == 0)
     hipLaunchKernelGGL((wgrad_kernel<128, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
   else  // N % 64 == 0 (the router's experts)
     hipLaunchKernelGGL((wgrad_kernel<64, 5>), dim3(kBlocks), dim3(256), 0, stream, g);
