@@ -923,23 +923,23 @@ void wgrad_strip_kernel(WgradArgs g) {
     const int nkc = (R + KC - 1) / KC;
     // the strip's A rows (rows past the segment repeat its last row and are
     // cleared below, before the first multiply)
-    const char* a_src = static_cast<const char*>(g.A) + static_cast<size_t>(k0) * lda + mt * BM * 2;
+    const char* a_src = uniform_ptr(static_cast<const char*>(g.A) + static_cast<size_t>(k0) * lda + mt * BM * 2);
     for (int kc = 0; kc < nkc; ++kc) {
       const int kv = min(KC, R - kc * KC);
 #pragma unroll
       for (int q = 0; q < OPS; ++q)
-        dma16_at(a_src + static_cast<size_t>(kc) * KC * lda,
+        dma16_at(uniform_ptr(a_src + static_cast<size_t>(kc) * KC * lda),
                  static_cast<uint32_t>(min(rq[q], kv - 1)) * lda + cq[q],
                  lds0 + kc * CH + (wave * OPS + q) * 1024);
     }
     // B chunks in (n-tile, chunk) order: chunk kc of n-tile n is rows
     // 32 kc .. of the segment, columns n BN ..
-    const char* b_src = static_cast<const char*>(g.B) + static_cast<size_t>(k0) * ldb;
+    const char* b_src = uniform_ptr(static_cast<const char*>(g.B) + static_cast<size_t>(k0) * ldb);
     auto issue = [&](int n, int kc, int st) {
       const int kv = min(KC, R - kc * KC);
 #pragma unroll
       for (int q = 0; q < OPS; ++q)
-        dma16_at(b_src + static_cast<size_t>(kc) * KC * ldb + n * BN * 2,
+        dma16_at(uniform_ptr(b_src + static_cast<size_t>(kc) * KC * ldb + n * BN * 2),
                  static_cast<uint32_t>(min(rq[q], kv - 1)) * ldb + cq[q],
                  lds0 + B_OFF + st * CH + (wave * OPS + q) * 1024);
     };
