@@ -343,10 +343,15 @@ struct RoutePlan {
 };
 RoutePlan route_plan(int T, int h, int E) {
   RoutePlan p;
-  p.bm = (T >= 4096 && E <= 384) ? 32 : 16;
+  // large batches: 64-token blocks, each block's gate-weight slice read once
+  // per 64 tokens instead of 32 (the slices come from L2 and that traffic
+  // bounded the kernel), with at most 4 K-splits (more splits write and
+  // re-read more partial logits)
+  p.bm = (T >= 8192 && E <= 384) ? 64 : (T >= 4096 && E <= 384) ? 32 : 16;
   const int mtiles = (T + p.bm - 1) / p.bm;
+  const int max_splits = p.bm == 64 ? 4 : 1 << 20;
   p.splits = 1;
-  while (mtiles * p.splits < 1024 && h / (p.splits * 2) >= 128 &&
+  while (mtiles * p.splits < 1024 && p.splits < max_splits && h / (p.splits * 2) >= 128 &&
          (h / (p.splits * 2)) % kBK == 0)
     p.splits *= 2;
   return p;
@@ -398,6 +403,7 @@ size_t route_partial_bytes(int T, int h, int E) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const RoutePlan p = route_plan(a.T, a.h, a.E);
+  if (p.bm == 64) return launch_bm<64>(a, p.splits, stream);
   return p.bm == 32 ? launch_bm<32>(a, p.splits, stream) : launch_bm<16>(a, p.splits, stream);
 }
 
