@@ -1,6 +1,7 @@
 """Benchmark of the routed MoE layer forward pass on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --backward [--no-saved] [--workload NAME]   (the local backward)
     python bench.py --copy-probe BYTES     (HBM counter calibration only)
 
 A step is one whole layer forward (route -> permute -> expert FFN -> combine,
