@@ -1183,9 +1183,9 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
                        a.k, a.keys, a.beta, a.hash, a.score_fn, a.renorm, a.alpha, a.ids, a.dG,
                        a.dl32, static_cast<uint16_t*>(a.dl16));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (a.dgate_bias) {  // partial sums in the keys region ([T, E], read only by dl above)
+    if (a.dgate_bias) {  // partial sums in a region of their own: the saved keys stay intact
       const int nchunk = (a.T + 255) / 256;
-      float* part = const_cast<float*>(a.keys);
+      float* part = a.colsum;
       hipLaunchKernelGGL(colsum_partial_kernel, dim3((a.E + 63) / 64, nchunk), dim3(256), 0, stream,
                          a.T, a.E, a.dl32, part);
       hipLaunchKernelGGL(colsum_final_kernel, dim3((a.E + 255) / 256), dim3(256), 0, stream, nchunk,

@@ -13,14 +13,15 @@ namespace moe {
 // Written as inline asm so that the compiler, which would otherwise make
 // every later LDS read wait for all DMA in flight, leaves the waiting to
 // wait_vmcnt; the memory clobber keeps LDS reads and other memory operations
-// on their side of it.
+// on their side of it, and m0 is declared clobbered so that the compiler
+// keeps no value of its own there across the instruction.
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // As dma16 with the LDS destination given as an LDS address (wave-uniform),
@@ -29,7 +30,7 @@ __device__ __forceinline__ void dma16_at(const char* sbase, uint32_t voff, uint3
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // The LDS address of a __shared__ object.
@@ -44,7 +45,7 @@ __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, char* lds
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory");
+               : "memory", "m0");
 }
 
 // A pointer the compiler may not prove wave-uniform, moved to scalar registers.

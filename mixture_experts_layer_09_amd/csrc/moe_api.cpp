@@ -449,6 +449,7 @@ hipError_t backward_from_saved(const moe_shape* shape, const moe_route_opts* opt
   b.dl16 = at<void>(ws, B.dl16);
   b.tile_off = at<int32_t>(ws, L.tile_off);
   b.tile_b = at<int32_t>(ws, B.tile_b);
+  b.colsum = at<float>(ws, B.colsum);
   b.dX = grads->dX;
   b.dWg = opts ? grads->dWg : nullptr;
   b.dgate_bias = opts ? grads->dgate_bias : nullptr;

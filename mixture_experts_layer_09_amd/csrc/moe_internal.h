@@ -270,6 +270,7 @@ struct BwdLayout {
   size_t dl32;     // [T, E] fp32: gradient of the gating logits
   size_t dl16;     // [T, E] bf16
   size_t tile_b;   // [E+2] int32: m-tile prefix of the dgrad kernels
+  size_t colsum;   // [ceil(T/256), E] fp32: partial column sums of dl (gating bias gradient)
   size_t total;
 };
 inline BwdLayout make_bwd_layout(const moe_shape& s) {
@@ -296,6 +297,7 @@ inline BwdLayout make_bwd_layout(const moe_shape& s) {
   B.dl32 = take(T * E * 4);
   B.dl16 = take(T * E * 2);
   B.tile_b = take((E + 2) * 4);
+  B.colsum = take((T + 255) / 256 * E * 4);
   B.total = o;
   return B;
 }
@@ -333,6 +335,7 @@ struct BackwardArgs {
   void* dl16;
   int32_t* tile_off;  // forward linears' m-tile prefix scratch
   int32_t* tile_b;
+  float* colsum;      // [ceil(T/256), E] partial column sums of dl
   // outputs
   void* dX;
   void* dWg;

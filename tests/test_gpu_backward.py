@@ -154,6 +154,49 @@ def test_backward_parity(name, saved):
         assert v <= TOL, (k, v)
 
 
+def test_backward_saved_twice_bit_identical():
+    """Two moe_backward_saved calls after one moe_forward_train (a new dY, a
+    retry, gradient accumulation) read the same saved activations: with the
+    router on and the gating-bias gradient requested, the second call's
+    gradients equal the first's bit for bit (the backward writes none of the
+    regions that the training forward filled)."""
+    _need_gpu()
+    base, kw, _ = CASES["v4pro_bwd"]
+    cpu = synth.make_inputs(base, **kw)
+    wl = cpu["workload"]
+    gpu = to_device(cpu)
+    T, h, E, k, f = wl.T, wl.hidden, wl.experts, wl.topk, wl.inter
+    shape = moe.make_shape(T, h, E, k, f, wl.shared, "bf16")
+    opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, gpu["beta"], gpu["gate_bias"])
+    weights = moe.make_weights(gpu["W1"], gpu["W2"], None, None, gpu["Ws1"], gpu["Ws2"])
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    Y = torch.empty((T, h), dtype=torch.bfloat16, device="cuda")
+    gen = torch.Generator().manual_seed(99)
+    dY = torch.randn((T, h), generator=gen).to(torch.bfloat16).cuda()
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+
+    def fresh():
+        return dict(dX=torch.empty((T, h), **bf), dW1=torch.empty((E, h, 2 * f), **bf),
+                    dW2=torch.empty((E, f, h), **bf), dWs1=torch.empty((h, 2 * f), **bf),
+                    dWs2=torch.empty((f, h), **bf), dWg=torch.empty((h, E), **bf),
+                    dgate_bias=torch.empty(E, dtype=torch.float32, device="cuda"),
+                    dG=torch.empty((T, k), dtype=torch.float32, device="cuda"))
+    wsb = moe.alloc_workspace(shape, backward=True)
+    _log(f"[backward] saved twice: T={T} h={h} E={E} k={k} f={f} router=True dgate_bias=True")
+    moe.moe_forward_train(shape, opts, gpu["X"], gpu["Wg"], weights, ids, G, Y, wsb)
+    g1, g2 = fresh(), fresh()
+    moe.moe_backward_saved(shape, opts, gpu["X"], gpu["Wg"], weights, ids, G, dY,
+                           moe.make_grads(**g1), wsb)
+    moe.moe_backward_saved(shape, opts, gpu["X"], gpu["Wg"], weights, ids, G, dY,
+                           moe.make_grads(**g2), wsb)
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(wsb) == 0
+    for name in g1:
+        assert torch.equal(g1[name], g2[name]), name
+    assert g1["dgate_bias"].abs().max().item() > 0
+
+
 def test_backward_full_size_v4pro():
     """moe_backward at the V4-Pro size (T = 8192, h = 7168, 384 experts, top-6,
     f = 3072, shared expert, router on), as the benchmark's backward run times

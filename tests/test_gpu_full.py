@@ -2,13 +2,18 @@
 benchmark times (moe_forward and the four entry points it chains).
 
 Checked on every token: the router's selection (exact at every clear margin,
-and equal to the top-k of the kernel's own keys everywhere), the dispatch
-(counts, offsets, row maps bit-exact against the oracle on the same ids) and
-the copies into Xp (bit-exact on sampled rows).  Checked on sampled tokens:
+and equal to the top-k of the kernel's own keys everywhere; the tokens whose
+ids differ from the oracle's are listed, and must all be near ties), the
+dispatch (counts, offsets, row maps bit-exact against the oracle on the same
+ids) and the copies into Xp (bit-exact on sampled rows).  Checked on about
+260 dispatched rows spread evenly over all T*k rows (so over every m-tile
+group and every chunk of work dealt to an XCD), the hottest expert's last
+row and the coldest experts' first rows: the expert FFN output Yp, and on 64
+tokens the shared expert's Ys, each against the oracle's expert FFN with one
+expert's weights copied to the host at a time.  Checked on sampled tokens:
 the layer output against the oracle, with samples chosen to cover the
 hottest expert's last (ragged) tile, the coldest active experts and the
-shared expert.  The oracle receives host copies of only the experts the
-sampled tokens use.
+shared expert.
 """
 from __future__ import annotations
 
@@ -45,6 +50,59 @@ def _sample_tokens(ids: np.ndarray, counts: np.ndarray, n_each: int = 4) -> np.n
     cold_tok = [int(np.nonzero((ids == e).any(axis=1))[0][0]) for e in cold]
     toks = np.unique(np.concatenate([hot_tok, cold_tok, [0, T - 1]])).astype(np.int32)
     return toks
+
+
+def _sample_rows(counts: np.ndarray, n: int = 256) -> np.ndarray:
+    """Dispatched rows spread evenly over [0, T*k) (every m-tile group and
+    every chunk of work items dealt to an XCD holds some of them), plus the
+    last row of the hottest expert (its ragged tail) and the first row of each
+    of the four coldest active experts."""
+    total = int(counts.sum())
+    off = np.concatenate([[0], np.cumsum(counts)])
+    rows = np.linspace(0, total - 1, min(n, total)).astype(np.int64)
+    hot = int(np.argmax(counts))
+    active = np.nonzero(counts > 0)[0]
+    cold = active[np.argsort(counts[active], kind="stable")[:4]]
+    extra = [off[hot + 1] - 1] + [off[e] for e in cold]
+    return np.unique(np.concatenate([rows, extra])).astype(np.int64)
+
+
+def _expert_oracle(inp, e, X_rows):
+    """oracle.Layer of one expert (e = E: the shared expert) on the given rows."""
+    wl = inp["workload"]
+    if e == wl.experts:
+        pick = lambda w: None if w is None else bits(w)[None]  # noqa: E731
+        W1, W2, s1, s2 = (pick(inp["Ws1"]), pick(inp["Ws2"]), pick(inp["ws1_scale"]),
+                          pick(inp["ws2_scale"]))
+    else:
+        pick = lambda w: None if w is None else bits(w[e:e + 1])  # noqa: E731
+        W1, W2, s1, s2 = (pick(inp["W1"]), pick(inp["W2"]), pick(inp["w1_scale"]),
+                          pick(inp["w2_scale"]))
+    return oracle.Layer(wl.precision, X_rows, W1, W2, w1_scale=s1, w2_scale=s2, k=1)
+
+
+def _check_expert_rows(inp, d, Yp, Ys, rows, toks_sh):
+    """Yp on the sampled dispatched rows and Ys on the sampled tokens against
+    the oracle's expert FFN, one expert at a time (only that expert's weights
+    are copied to the host)."""
+    wl = inp["workload"]
+    seg = np.searchsorted(d["offsets"], rows, side="right") - 1
+    worst = 0.0
+    for e in np.unique(seg):
+        rr = rows[seg == e]
+        src = torch.from_numpy(d["src_tok"][rr]).long().cuda()
+        Lx = _expert_oracle(inp, int(e), bits(inp["X"][src]))
+        n = len(rr)
+        ref = Lx.expert_rows(np.array([0, n], np.int32), np.arange(n, dtype=np.int32))
+        got = f64(Yp[torch.from_numpy(rr).cuda()])
+        worst = max(worst, row_rel_err(got, ref))
+    if Ys is not None:
+        tt = torch.from_numpy(toks_sh).long().cuda()
+        Lx = _expert_oracle(inp, wl.experts, bits(inp["X"][tt]))
+        n = len(toks_sh)
+        ref = Lx.expert_rows(np.array([0, n], np.int32), np.arange(n, dtype=np.int32))
+        worst = max(worst, row_rel_err(f64(Ys[tt]), ref))
+    return worst, len(np.unique(seg))
 
 
 def _oracle_on_tokens(inp, ids, G, toks):
@@ -95,7 +153,13 @@ def test_full_size_forward(name):
     same = (ids == r["ids"]).all(axis=1)
     np.testing.assert_allclose(G_g.cpu().numpy()[same], r["G"][same],
                                atol=1e-5 * max(1.0, wl.alpha), rtol=1e-5)
-    _log(f"[full] {name}: near-tie tokens {int((~sure).sum())}")
+    differ = np.nonzero(~same)[0]
+    assert (~sure[differ]).all()   # only near ties may differ
+    _log(f"[full] {name}: near-tie tokens {int((~sure).sum())} (oracle margin < {DELTA:g}); "
+         f"tokens whose ids differ from the oracle: {len(differ)}")
+    for t in differ:
+        _log(f"[full] {name}:   token {t}: margin {r['margin'][t]:.3e}, kernel ids "
+             f"{ids[t].tolist()}, oracle ids {r['ids'][t].tolist()}")
 
     # dispatch on every assignment, copies on sampled rows
     d = oracle.dispatch(ids, wl.experts)
@@ -119,6 +183,18 @@ def test_full_size_forward(name):
         assert np.array_equal(bits(p["xp_scale"])[rows], s)
     else:
         assert np.array_equal(Xp_rows, bits(inp["X"][torch.from_numpy(src).long().cuda()]))
+
+    # the expert FFN on dispatched rows spread over the whole tile grid
+    Yp, Ys = L.expert_ffn(p)
+    torch.cuda.synchronize()
+    rows = _sample_rows(d["counts"])
+    toks_sh = np.linspace(0, wl.T - 1, min(64, wl.T)).astype(np.int64)
+    err_rows, n_exp = _check_expert_rows(inp, d, Yp, Ys, rows, toks_sh if wl.shared else None)
+    _log(f"[full] {name}: expert FFN on {len(rows)} sampled rows of {n_exp} experts"
+         f"{' and ' + str(len(toks_sh)) + ' shared rows' if wl.shared else ''}: "
+         f"max row-relative error {err_rows:.3e}")
+    assert err_rows <= TOL[wl.precision]
+    del Yp, Ys
 
     # the whole layer as the benchmark runs it
     _log(f"[full] {name}: moe_forward")

@@ -42,6 +42,9 @@ CASES = {
     "decode_hash_small": ("decode_hash_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "decode_score_small": ("decode_score_bf16", dict(T=16, hidden=512, experts=64, inter=256)),
     "ep_share_small": ("ep_share_bf16", dict(T=600, hidden=256, inter=128)),
+    # the DeepSeek-V4 affinity sqrt(softplus(l)) with the V4-Pro router
+    "v4pro_sqrt_softplus_small": ("v4pro_bf16", dict(T=256, hidden=512, experts=64, inter=256,
+                                                     score="sqrt_softplus")),
 }
 
 
