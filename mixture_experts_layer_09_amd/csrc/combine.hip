@@ -52,50 +52,77 @@ __global__ __launch_bounds__(256) void combine_kernel(int h, int k,
       reinterpret_cast<float4*>(static_cast<float*>(Y) + static_cast<size_t>(t) * h)[v] = acc;
     }
   } else {
+    // two 16-byte column chunks per thread and trip; a trip issues the loads
+    // of up to 8 expert rows and the shared row for both chunks before it
+    // uses any of them
     const int nv = h / 8;
-    for (int v = threadIdx.x; v < nv; v += 256) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      // groups of 8 rows: all loads of a group are issued before any is used
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (int v0 = threadIdx.x; v0 < nv; v0 += 512) {
+      const int v1 = v0 + 256;
+      const bool has1 = v1 < nv;
+      float acc[2][8];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[c][q] = 0.0f;
+      uint4 s0 = zero, s1 = zero;
       for (int j0 = 0; j0 < k; j0 += 8) {
-        uint4 yr[8];
+        uint4 y0[8], y1[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int j = j0 + q;
           const int r = (j < k) ? s_row[j] : -1;
-          yr[q] = make_uint4(0u, 0u, 0u, 0u);
-          if (r >= 0)
-            yr[q] = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Yp) +
-                                                   static_cast<size_t>(r) * h)[v];
+          y0[q] = zero;
+          y1[q] = zero;
+          if (r >= 0) {
+            const uint4* row = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Yp) +
+                                                              static_cast<size_t>(r) * h);
+            y0[q] = row[v0];
+            if (has1) y1[q] = row[v1];
+          }
+        }
+        if (j0 == 0 && Ys) {
+          const uint4* srow = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Ys) +
+                                                             static_cast<size_t>(t) * h);
+          s0 = srow[v0];
+          if (has1) s1 = srow[v1];
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int j = j0 + q;
           if (j >= k || s_row[j] < 0) continue;
           const float g = s_g[j];
-          uint32_t w[4] = {yr[q].x, yr[q].y, yr[q].z, yr[q].w};
+          const uint32_t w0[4] = {y0[q].x, y0[q].y, y0[q].z, y0[q].w};
+          const uint32_t w1[4] = {y1[q].x, y1[q].y, y1[q].z, y1[q].w};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            acc[2 * c] = fmaf(g, __uint_as_float(w[c] << 16), acc[2 * c]);
-            acc[2 * c + 1] = fmaf(g, __uint_as_float(w[c] & 0xffff0000u), acc[2 * c + 1]);
+            acc[0][2 * c] = fmaf(g, __uint_as_float(w0[c] << 16), acc[0][2 * c]);
+            acc[0][2 * c + 1] = fmaf(g, __uint_as_float(w0[c] & 0xffff0000u), acc[0][2 * c + 1]);
+            acc[1][2 * c] = fmaf(g, __uint_as_float(w1[c] << 16), acc[1][2 * c]);
+            acc[1][2 * c + 1] = fmaf(g, __uint_as_float(w1[c] & 0xffff0000u), acc[1][2 * c + 1]);
           }
         }
       }
-      if (Ys) {
-        uint4 s = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(Ys) +
-                                                 static_cast<size_t>(t) * h)[v];
-        uint32_t w[4] = {s.x, s.y, s.z, s.w};
+      const uint4 sv[2] = {s0, s1};
+      uint4* yrow = reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + static_cast<size_t>(t) * h);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += __uint_as_float(w[q] << 16);
-          acc[2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+      for (int c = 0; c < 2; ++c) {
+        if (c == 1 && !has1) break;
+        if (Ys) {
+          const uint32_t w[4] = {sv[c].x, sv[c].y, sv[c].z, sv[c].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[c][2 * q] += __uint_as_float(w[q] << 16);
+            acc[c][2 * q + 1] += __uint_as_float(w[q] & 0xffff0000u);
+          }
         }
+        uint4 o;
+        o.x = f32_to_bf16(acc[c][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[c][1])) << 16);
+        o.y = f32_to_bf16(acc[c][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[c][3])) << 16);
+        o.z = f32_to_bf16(acc[c][4]) | (static_cast<uint32_t>(f32_to_bf16(acc[c][5])) << 16);
+        o.w = f32_to_bf16(acc[c][6]) | (static_cast<uint32_t>(f32_to_bf16(acc[c][7])) << 16);
+        yrow[c == 0 ? v0 : v1] = o;
       }
-      uint4 o;
-      o.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
-      o.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
-      o.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
-      o.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
-      reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + static_cast<size_t>(t) * h)[v] = o;
     }
   }
 }

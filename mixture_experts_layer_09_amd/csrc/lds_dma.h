@@ -14,7 +14,11 @@ namespace moe {
 // every later LDS read wait for all DMA in flight, leaves the waiting to
 // wait_vmcnt; the memory clobber keeps LDS reads and other memory operations
 // on their side of it, and m0 is declared clobbered so that the compiler
-// keeps no value of its own there across the instruction.
+// keeps no value of its own there across the instruction (clang notes that
+// m0 is a reserved register, which it only ever sets right before its own
+// uses; the clobber is recorded all the same, so the note is silenced here).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, char* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_dst)));
@@ -47,6 +51,8 @@ __device__ __forceinline__ void dma4(const char* sbase, uint32_t voff, char* lds
                : "v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // A pointer the compiler may not prove wave-uniform, moved to scalar registers.
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {

@@ -94,7 +94,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ---------------------------------------------------------------- workspace
 constexpr size_t kAlign = 256;
-constexpr int kPermChunk = 256;  // assignments per dispatch block
+constexpr int kPermChunk = 2048;   // assignments per counting block of the dispatch
+constexpr int kPermThreads = 1024; // its threads: two assignments each
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 
@@ -116,7 +117,13 @@ inline size_t row_scale_bytes(int precision, size_t n) {
   return (precision == MOE_PREC_FP8 || precision == MOE_PREC_INT8) ? 4 : 0;
 }
 
-// Bytes of split-K partial gate logits the router may use (0 if none).
+// The router's launch plan: tokens per block and K-splits of the gating
+// linear (route_plan.cpp), and the bytes of split-K partial gate logits it
+// uses in the workspace (0 if none).
+struct RoutePlan {
+  int bm, splits;
+};
+RoutePlan route_plan(int T, int h, int E);
 size_t route_partial_bytes(int T, int h, int E);
 
 // Byte offsets of every region inside the caller's workspace.

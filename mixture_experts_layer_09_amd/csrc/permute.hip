@@ -4,10 +4,15 @@
 // blog post, §计数与重排).
 //
 // Three kernels, no global atomics, deterministic:
-//   1. count_rank: block b takes assignments [b*256, (b+1)*256) of the flat
-//      array ids[T*k]; it writes its per-expert counts blk_cnt[b][e] and the
-//      rank of each assignment among the block's earlier assignments to the
-//      same expert (one pass over LDS per thread; broadcast reads).
+//   1. count_rank: block b takes assignments [b*2048, (b+1)*2048) of the flat
+//      array ids[T*k] as 32 groups of 64 (one per wave and round).  Inside a
+//      group a lane finds its rank among the group's earlier lanes with the
+//      same expert by reading the 64 lanes' experts in turn; the group's per-expert counts go to LDS,
+//      a scan over the 32 groups per expert turns them into group bases, and
+//      the block writes its per-expert counts blk_cnt[b][e] and each
+//      assignment's rank among the block's earlier assignments to the same
+//      expert.  Large blocks keep the per-block count table short, so the
+//      single-block scan that follows reads few rows of it.
 //   2. scan: one block turns blk_cnt into counts[e], offsets[e] (exclusive
 //      prefix over experts) and, in place, blk_cnt[b][e] = offsets[e] + sum
 //      of blk_cnt[b'][e] over b' < b (the block's base row for expert e).
@@ -23,38 +28,67 @@
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(kPermChunk) void count_rank_kernel(const int32_t* __restrict__ ids,
-                                                                int n, int E,
-                                                                int32_t* __restrict__ blk_cnt,
-                                                                int32_t* __restrict__ local_rank,
-                                                                int32_t* __restrict__ flag) {
-  __shared__ int32_t s_ids[kPermChunk];
-  __shared__ int32_t s_cnt[kMaxExperts];
+__global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t* __restrict__ ids,
+                                                                  int n, int E,
+                                                                  int32_t* __restrict__ blk_cnt,
+                                                                  int32_t* __restrict__ local_rank,
+                                                                  int32_t* __restrict__ flag) {
+  constexpr int kGroups = kPermChunk / 64;  // groups of 64 assignments
+  constexpr int kRounds = kPermChunk / kPermThreads;
+  __shared__ int32_t s_cnt[kGroups][kMaxExperts];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int base = blockIdx.x * kPermChunk;
-  const int i = base + tid;
-  int e = -1;
-  if (i < n) {
-    e = ids[i];
-    if (e < 0 || e >= E) {
-      flag[0] = 1;  // every writer stores the same value
-      e = -1;
+  for (int x = tid; x < kGroups * kMaxExperts; x += kPermThreads) (&s_cnt[0][0])[x] = 0;
+  int e[kRounds], rank[kRounds];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = base + r * kPermThreads + tid;
+    int v = -1;
+    if (i < n) {
+      v = ids[i];
+      if (v < 0 || v >= E) {
+        flag[0] = 1;  // every writer stores the same value
+        v = -1;
+      }
     }
+    e[r] = v;
   }
-  s_ids[tid] = e;
-  for (int x = tid; x < E; x += kPermChunk) s_cnt[x] = 0;
+  __syncthreads();  // s_cnt cleared
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    // rank among the group's earlier lanes with the same expert, and the
+    // group's count of that expert
+    int rk = 0, cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const int o = __builtin_amdgcn_readlane(e[r], j);
+      const int eq = (o == e[r]) ? 1 : 0;
+      rk += (j < lane) ? eq : 0;
+      cnt += eq;
+    }
+    rank[r] = rk;
+    if (e[r] >= 0 && rk == cnt - 1) s_cnt[r * (kPermThreads / 64) + wave][e[r]] = cnt;
+  }
   __syncthreads();
-  // rank among earlier assignments of this block to the same expert
-  int rank = 0;
-  for (int j = 0; j < tid; ++j) rank += (s_ids[j] == e) ? 1 : 0;
-  if (i < n) local_rank[i] = (e >= 0) ? rank : -1;
-  // the last assignment of each expert in the block knows the block's count
-  bool last = (e >= 0);
-  for (int j = tid + 1; j < kPermChunk && last; ++j) last = (s_ids[j] != e);
-  if (last) s_cnt[e] = rank + 1;
+  // per expert: exclusive scan over the groups, in group order
+  for (int x = tid; x < E; x += kPermThreads) {
+    int run = 0;
+    for (int g = 0; g < kGroups; ++g) {
+      const int c = s_cnt[g][x];
+      s_cnt[g][x] = run;
+      run += c;
+    }
+    blk_cnt[static_cast<size_t>(blockIdx.x) * E + x] = run;
+  }
   __syncthreads();
-  for (int x = tid; x < E; x += kPermChunk)
-    blk_cnt[static_cast<size_t>(blockIdx.x) * E + x] = s_cnt[x];
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = base + r * kPermThreads + tid;
+    if (i < n)
+      local_rank[i] = (e[r] >= 0) ? s_cnt[r * (kPermThreads / 64) + wave][e[r]] + rank[r] : -1;
+  }
 }
 
 // One block of 512 threads; E <= 512, one thread per expert.  The loops over
@@ -273,8 +307,8 @@ hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int n = a.T * a.k;
-  hipLaunchKernelGGL(count_rank_kernel, dim3(a.nblk), dim3(kPermChunk), 0, stream, a.ids, n, a.E,
-                     a.blk_cnt, a.local_rank, a.flag);
+  hipLaunchKernelGGL(count_rank_kernel, dim3(a.nblk), dim3(kPermThreads), 0, stream, a.ids, n,
+                     a.E, a.blk_cnt, a.local_rank, a.flag);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.nblk, a.E, a.blk_cnt,
                      a.counts, a.offsets);
   switch (a.precision) {

@@ -336,27 +336,6 @@ __global__ __launch_bounds__(kThreads) void route_epilogue_kernel(RouteArgs a, i
   route_token<EP>(a, t, lane, lg);
 }
 
-// Router launch plan: BM tokens per block; K split in powers of two (each
-// part >= 128 and a multiple of 32) until the grid has >= 1024 blocks.
-struct RoutePlan {
-  int bm, splits;
-};
-RoutePlan route_plan(int T, int h, int E) {
-  RoutePlan p;
-  // large batches: 64-token blocks, each block's gate-weight slice read once
-  // per 64 tokens instead of 32 (the slices come from L2 and that traffic
-  // bounded the kernel), with at most 4 K-splits (more splits write and
-  // re-read more partial logits)
-  p.bm = (T >= 8192 && E <= 384) ? 64 : (T >= 4096 && E <= 384) ? 32 : 16;
-  const int mtiles = (T + p.bm - 1) / p.bm;
-  const int max_splits = p.bm == 64 ? 4 : 1 << 20;
-  p.splits = 1;
-  while (mtiles * p.splits < 1024 && p.splits < max_splits && h / (p.splits * 2) >= 128 &&
-         (h / (p.splits * 2)) % kBK == 0)
-    p.splits *= 2;
-  return p;
-}
-
 template <int BM, int EP>
 hipError_t launch_ep(const RouteArgs& a, int splits, hipStream_t stream) {
   const int mtiles = (a.T + BM - 1) / BM;
@@ -395,11 +374,6 @@ hipError_t launch_bm(const RouteArgs& a, int splits, hipStream_t stream) {
 }
 
 }  // namespace
-
-size_t route_partial_bytes(int T, int h, int E) {
-  const RoutePlan p = route_plan(T, h, E);
-  return p.splits > 1 ? static_cast<size_t>(p.splits) * T * E * 4 : 0;
-}
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   const RoutePlan p = route_plan(a.T, a.h, a.E);

@@ -27,7 +27,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB points the loader at another build of moe_oracle.c (the
+# sanitizer test builds one with AddressSanitizer and UBSan)
+_LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 PRECISIONS = {"fp32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3, "mxfp4": 4, "int8": 5}
