@@ -94,7 +94,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels implement */
   MOE_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned or too small */
   MOE_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
-  MOE_ERR_DEVICE_DATA = -5  /* device data broke the contract (bad expert id) */
+  MOE_ERR_DEVICE_DATA = -5, /* device data broke the contract (bad expert id) */
+  MOE_ERR_SCRATCH = -6      /* larger than the static scratch of moe_permute_no_alloc */
 } moe_status;
 
 typedef enum {
@@ -205,6 +206,25 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
                 int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
                 void* xp_scale, void* Xq, void* x_scale, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same dispatch and the same outputs as moe_permute;
+ * its scratch (an error flag, the per-block expert counts and the in-block
+ * ranks) is a static device array of the library, about 1.3 MiB on each GPU
+ * the library runs on, held until the process ends.  At most
+ * MOE_NO_ALLOC_MAX_ASSIGNMENTS assignments (tokens * topk); a larger call
+ * returns MOE_ERR_SCRATCH and launches nothing.  Every call on one GPU uses
+ * that GPU's single array, which keeps the last call's contents: calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * give wrong results; calls ordered on one stream are safe.  Expert ids
+ * outside [0, E) are skipped (dst_row = -1, not counted) as in moe_permute,
+ * but with no workspace moe_check_device_error cannot report them.  Nothing
+ * is allocated, on the host or on the device. */
+#define MOE_NO_ALLOC_MAX_ASSIGNMENTS 262144
+int moe_permute_no_alloc(const moe_shape* shape, const int32_t* expert_ids, const void* X,
+                         int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok,
+                         void* Xp, void* xp_scale, void* Xq, void* x_scale, hipStream_t stream);
 
 /* Step 4: grouped Linear1 -> SwiGLU -> Linear2 over the expert blocks given
  * by offsets [E+1] (rows offsets[e] .. offsets[e+1]-1 of Xp belong to expert

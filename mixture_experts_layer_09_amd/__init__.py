@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 PREC = {"fp32": 0, "bf16": 1, "fp8": 2, "mxfp8": 3, "mxfp4": 4, "int8": 5}
 SCORE = {"sigmoid": 0, "softmax": 1, "sqrt_softplus": 2}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
-          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_DATA"}
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_DEVICE_DATA",
+          -6: "MOE_ERR_SCRATCH"}
+NO_ALLOC_MAX_ASSIGNMENTS = 262144   # MOE_NO_ALLOC_MAX_ASSIGNMENTS
 EXPORTED = ["moe_workspace_size", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
             "moe_forward", "moe_check_device_error", "moe_status_string",
             "moe_backward_workspace_size", "moe_backward", "moe_forward_train",
-            "moe_backward_saved"]
+            "moe_backward_saved", "moe_permute_no_alloc"]
 
 
 class MoeError(RuntimeError):
@@ -77,6 +79,8 @@ def lib():
                                 vp]
         L.moe_permute.restype = i32
         L.moe_permute.argtypes = [S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
+        L.moe_permute_no_alloc.restype = i32
+        L.moe_permute_no_alloc.argtypes = [S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_expert_ffn.restype = i32
         L.moe_expert_ffn.argtypes = [S, vp, vp, vp, vp, vp, C.POINTER(moe_expert_weights), vp, vp,
                                      vp, C.c_size_t, vp]
@@ -168,6 +172,14 @@ def moe_permute(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp, xp_
         C.byref(shape), _ptr(expert_ids), _ptr(X), _ptr(counts), _ptr(offsets), _ptr(dst_row),
         _ptr(src_tok), _ptr(Xp), _ptr(xp_scale), _ptr(Xq), _ptr(x_scale), _ptr(workspace),
         workspace.numel(), _stream(stream)))
+
+
+def moe_permute_no_alloc(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp, xp_scale,
+                         Xq, x_scale, stream=None):
+    """moe_permute with the library's static scratch instead of a workspace."""
+    _check("moe_permute_no_alloc", lib().moe_permute_no_alloc(
+        C.byref(shape), _ptr(expert_ids), _ptr(X), _ptr(counts), _ptr(offsets), _ptr(dst_row),
+        _ptr(src_tok), _ptr(Xp), _ptr(xp_scale), _ptr(Xq), _ptr(x_scale), _stream(stream)))
 
 
 def moe_expert_ffn(shape, Xp, xp_scale, offsets, Xs, xs_scale, weights, Yp, Ys, workspace,

@@ -108,7 +108,7 @@ RouteArgs route_args(const moe_shape* s, const moe_route_opts* o, const void* X,
 
 PermuteArgs permute_args(const moe_shape* s, const int32_t* ids, const void* X, int32_t* counts,
                          int32_t* offsets, int32_t* dst_row, int32_t* src_tok, void* Xp,
-                         void* xp_scale, void* Xq, void* x_scale, void* ws) {
+                         void* xp_scale, void* Xq, void* x_scale, void* ws /* may be NULL */) {
   Layout L = make_layout(*s);
   PermuteArgs a{};
   a.T = s->tokens;
@@ -127,9 +127,11 @@ PermuteArgs permute_args(const moe_shape* s, const int32_t* ids, const void* X, 
   a.xp_scale = xp_scale;
   a.Xq = Xq;
   a.x_scale = x_scale;
-  a.blk_cnt = at<int32_t>(ws, L.blk_cnt);
-  a.local_rank = at<int32_t>(ws, L.local_rank);
-  a.flag = at<int32_t>(ws, L.flag);
+  if (ws) {
+    a.blk_cnt = at<int32_t>(ws, L.blk_cnt);
+    a.local_rank = at<int32_t>(ws, L.local_rank);
+    a.flag = at<int32_t>(ws, L.flag);
+  }
   return a;
 }
 
@@ -201,6 +203,23 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
   hipError_t e = launch_clear_flag(a.flag, stream);
   if (e == hipSuccess) e = launch_permute(a, stream);
   return hip_status(e);
+}
+
+int moe_permute_no_alloc(const moe_shape* shape, const int32_t* expert_ids, const void* X,
+                         int32_t* counts, int32_t* offsets, int32_t* dst_row, int32_t* src_tok,
+                         void* Xp, void* xp_scale, void* Xq, void* x_scale, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!expert_ids || !X || !counts || !offsets || !dst_row || !src_tok || !Xp)
+    return MOE_ERR_INVALID_ARG;
+  if (shape->precision >= MOE_PREC_FP8 && (!xp_scale || !Xq || !x_scale))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16({X, Xp, xp_scale, Xq, x_scale})) return MOE_ERR_INVALID_ARG;
+  if (static_cast<long long>(shape->tokens) * shape->topk > MOE_NO_ALLOC_MAX_ASSIGNMENTS)
+    return MOE_ERR_SCRATCH;
+  PermuteArgs a = permute_args(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp,
+                               xp_scale, Xq, x_scale, nullptr);
+  return hip_status(launch_permute_no_alloc(a, stream));
 }
 
 int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
@@ -557,6 +576,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ERR_HIP: return "HIP runtime or launch error";
     case MOE_ERR_DEVICE_DATA: return "device data out of contract (expert or token id)";
+    case MOE_ERR_SCRATCH: return "problem larger than the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }

@@ -214,6 +214,9 @@ struct PermuteArgs {
   int32_t* flag;
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+// launch_permute with the flag, per-block counts and ranks in the library's
+// static scratch of this device (a's workspace pointers are ignored).
+hipError_t launch_permute_no_alloc(PermuteArgs a, hipStream_t stream);
 
 struct FfnArgs {
   int T, h, E, k, f, has_shared, precision;

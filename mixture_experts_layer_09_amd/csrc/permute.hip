@@ -23,10 +23,24 @@
 //      codes are what is copied; MX rows are quantised per 32-value group.
 // Row order inside an expert block is ascending t*k+j, a stable order; the
 // pages leave the order to the implementation as long as it is fixed.
+#include <atomic>
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+// Scratch of the dispatch without a workspace (moe_permute_no_alloc), one
+// copy per GPU: the error flag, the per-block expert counts and the in-block
+// ranks of at most MOE_NO_ALLOC_MAX_ASSIGNMENTS assignments and kMaxExperts
+// experts.
+constexpr size_t kNoAllocFlagBytes = 256;
+constexpr size_t kNoAllocBlkBytes =
+    static_cast<size_t>((MOE_NO_ALLOC_MAX_ASSIGNMENTS + kPermChunk - 1) / kPermChunk) * kMaxExperts * 4;
+constexpr size_t kNoAllocRankBytes = static_cast<size_t>(MOE_NO_ALLOC_MAX_ASSIGNMENTS) * 4;
+constexpr size_t kNoAllocScratchBytes = kNoAllocFlagBytes + kNoAllocBlkBytes + kNoAllocRankBytes;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t* __restrict__ ids,
                                                                   int n, int E,
@@ -298,7 +312,51 @@ __global__ __launch_bounds__(256) void scatter_kernel(
 
 __global__ void clear_flag_kernel(int32_t* flag) { flag[0] = 0; }
 
+// The device address of this device's `scratch` (in host code the array's
+// name is only a stand-in), looked up once per device, with it current.
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_of_current_device(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  char* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (q == nullptr) return hipErrorInvalidSymbol;
+      p = static_cast<char*>(q);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_permute_no_alloc(PermuteArgs a, hipStream_t stream) {
+  if (static_cast<long long>(a.T) * a.k > MOE_NO_ALLOC_MAX_ASSIGNMENTS || a.E > kMaxExperts)
+    return hipErrorInvalidValue;
+  char* s = nullptr;
+  hipError_t e = scratch_of_current_device(&s);
+  if (e != hipSuccess) return e;
+  a.flag = reinterpret_cast<int32_t*>(s);
+  a.blk_cnt = reinterpret_cast<int32_t*>(s + kNoAllocFlagBytes);
+  a.local_rank = reinterpret_cast<int32_t*>(s + kNoAllocFlagBytes + kNoAllocBlkBytes);
+  // the flag is cleared by a kernel (no memset node under graph capture);
+  // the counts and ranks are written whole by every call before they are read
+  e = launch_clear_flag(a.flag, stream);
+  if (e == hipSuccess) e = launch_permute(a, stream);
+  return e;
+}
 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
   hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, stream, flag);

@@ -108,6 +108,18 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_permute_no_alloc(PermuteArgs a, hipStream_t stream) {
+  // the kernels' scratch is the library's static array, not a workspace
+  static int32_t flag;
+  static std::vector<int32_t> blk, rank;
+  blk.assign(static_cast<size_t>(a.nblk) * a.E, 0);
+  rank.assign(static_cast<size_t>(a.T) * a.k, 0);
+  a.flag = &flag;
+  a.blk_cnt = blk.data();
+  a.local_rank = rank.data();
+  return launch_permute(a, stream);
+}
+
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t) {
   new_launch();
   const size_t T = a.T, h = a.h, E = a.E, k = a.k, f = a.f, rows = T * k;
@@ -309,6 +321,12 @@ void run_shape(int T, int h, int E, int k, int f, int shared, int prec, bool has
                      static_cast<int32_t*>(offsets.p), static_cast<int32_t*>(dst.p),
                      static_cast<int32_t*>(src.p), Xp.p, q8 ? xps.p : nullptr, q8 ? Xq.p : nullptr,
                      q8 ? xs.p : nullptr, W, ws_bytes, nullptr), MOE_OK, "permute");
+  expect(moe_permute_no_alloc(&s, static_cast<int32_t*>(ids.p), X.p, static_cast<int32_t*>(counts.p),
+                              static_cast<int32_t*>(offsets.p), static_cast<int32_t*>(dst.p),
+                              static_cast<int32_t*>(src.p), Xp.p, q8 ? xps.p : nullptr,
+                              q8 ? Xq.p : nullptr, q8 ? xs.p : nullptr, nullptr),
+         static_cast<long long>(T) * k <= MOE_NO_ALLOC_MAX_ASSIGNMENTS ? MOE_OK : MOE_ERR_SCRATCH,
+         "permute_no_alloc");
   expect(moe_expert_ffn(&s, Xp.p, q8 ? xps.p : nullptr, static_cast<int32_t*>(offsets.p),
                         shared ? (q8 ? Xq.p : X.p) : nullptr, shared && q8 ? xs.p : nullptr, &w,
                         Yp.p, shared ? Ys.p : nullptr, W, ws_bytes, nullptr), MOE_OK, "expert_ffn");

@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     _lib()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert moe.moe_status_string(st) != "unknown status"
     assert moe.moe_status_string(7) == "unknown status"
 
@@ -225,3 +225,25 @@ def test_training_forward_rejects_out_of_contract_arguments():
     # a forward-sized workspace does not hold the saved activations
     assert L.moe_forward_train(*args(s, nb=moe.moe_workspace_size(s))) == WORKSPACE
     assert L.moe_forward_train(*args(s, ws=FAKE_WS + 8)) == WORKSPACE
+
+
+def test_permute_no_alloc_host_checks():
+    """moe_permute_no_alloc rejects out-of-contract arguments and calls larger
+    than its static scratch on the host, before any launch."""
+    L = _lib()
+    vp = C.c_void_p
+    a = vp(FAKE_WS)
+    s = _shape()
+    args = [a] * 10 + [None]
+    # NULL ids
+    assert L.moe_permute_no_alloc(C.byref(s), None, *args[1:]) == INVALID
+    # misaligned X
+    assert L.moe_permute_no_alloc(C.byref(s), a, vp(FAKE_WS + 2), *args[2:]) == INVALID
+    # fp8 without the scale and code arrays
+    s8 = _shape(hidden=256, inter=128, precision="fp8")
+    assert L.moe_permute_no_alloc(C.byref(s8), a, a, a, a, a, a, a, None, None, None,
+                                  None) == INVALID
+    # more assignments than the scratch holds
+    big = _shape(tokens=moe.NO_ALLOC_MAX_ASSIGNMENTS // 2 + 1, topk=2)
+    assert L.moe_permute_no_alloc(C.byref(big), *args) == -6
+    assert "scratch" in moe.moe_status_string(-6)
