@@ -13,6 +13,15 @@ stream between the four calls give per-stage times inside the timed region;
 the grouped GEMM stage (moe_expert_ffn: Linear1+SwiGLU and Linear2) is the
 dominant one and carries the roofline figures.
 
+The same JSON line carries, measured in the same process: `routing`, the
+router's ids on every token against the oracle's fp64 routing (the tokens
+that differ, all of which must be near ties, and the near-tie count);
+`cpu_baseline`, the oracle timed on a bounded sample; and `workloads`, the
+other configurations (decode-shaped with hash and with score routing, the
+Llama-shaped layer, one GPU's expert-parallel share, V4-Pro A8W8 e4m3), each
+with its step time, stage times and the grouped GEMM's roofline figures
+(--no-workloads leaves them out).
+
 Prints one JSON line.  Runs on one GPU only: --gpus N with N > 1 exits.
 """
 from __future__ import annotations
@@ -373,6 +382,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="v4pro_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="measure the selected workload only (not the other configurations)")
+    ap.add_argument("--no-routing-check", action="store_true",
+                    help="skip the oracle's routing of every token (the 'routing' field)")
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=VALUE",
                     help="override a workload field (exploration; e.g. --set zipf=False)")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -411,6 +424,88 @@ def main(argv=None):
     shape = moe.make_shape(wl.T, wl.hidden, wl.experts, wl.topk, wl.inter, wl.shared, wl.precision)
     if args.backward:
         return bench_backward(args, wl, inp, shape)
+    out, ids, cnt = measure_forward(wl, inp, args.steps, args.warmup,
+                                    traffic=measured_traffic(wl.name) if not args.set else None)
+    out = {"metric": METRIC, "value": out.pop("value"), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, **out}
+    if not args.no_routing_check:
+        out["routing"] = routing_check(wl, inp, ids)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, ids, cnt)
+    out["hbm_copy_probe_gbs"] = device_copy_gbs()
+    if not args.no_workloads and not args.set:
+        del inp
+        torch.cuda.empty_cache()
+        out["workloads"] = other_workloads([w for w in EXTRA_WORKLOADS if w != wl.name], args)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# The other configurations, measured in the same run as the headline one:
+# decode-shaped batches (hash and score routing), the Llama-shaped layer, one
+# GPU's expert-parallel share and the V4-Pro A8W8 e4m3 layer.
+EXTRA_WORKLOADS = ["decode_hash_bf16", "decode_score_bf16", "llama_bf16", "ep_share_bf16",
+                   "v4pro_fp8"]
+
+
+def other_workloads(names, args) -> dict:
+    """measure_forward on each named workload (inputs generated, measured and
+    freed one workload at a time); a short summary per workload."""
+    import torch
+
+    import synth
+    res = {}
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        log(f"[bench] workload {name}: generating")
+        inp = synth.make_inputs(wl, device="cuda")
+        torch.cuda.synchronize()
+        m, _, _ = measure_forward(wl, inp, args.steps, args.warmup,
+                                  traffic=measured_traffic(name), with_forward=False)
+        r = m["roofline"]
+        res[name] = {"tokens_per_s": m["value"], "ms_per_step": m["ms_per_step"],
+                     "stages_ms": m["stages_ms"], "expert_ffn_ms": m["stages_ms"]["expert_ffn"],
+                     "bound": r["bound"], "roofline_frac": r["frac"],
+                     "frac_of_roofline": r["frac_of_roofline"], "achieved": r["achieved"],
+                     "unit": r["unit"], "traffic": r["traffic"],
+                     "grouped_gemm": m["grouped_gemm"], "layer_hbm": m["layer_hbm"],
+                     "config": m["config"]}
+        del inp
+        torch.cuda.empty_cache()
+    return res
+
+
+def routing_check(wl, inp, ids) -> dict:
+    """The router's ids against the oracle's fp64 routing of every token: the
+    tokens whose ids differ (all must be near ties: oracle margin between the
+    k-th and (k+1)-th key below 1e-5) and the number of near ties."""
+    import numpy as np
+
+    import oracle
+    from tests.helpers import bits, f64
+    t0 = time.perf_counter()
+    r = oracle.route(bits(inp["X"]), bits(inp["Wg"]), wl.topk, gate_bias=f64(inp["gate_bias"]),
+                     beta=f64(inp["beta"]), score=wl.score, renorm=wl.renorm, alpha=wl.alpha,
+                     token_ids=bits(inp["token_ids"]), tid2eid=bits(inp["tid2eid"]))
+    near = r["margin"] < 1e-5
+    differ = np.nonzero((ids != r["ids"]).any(axis=1))[0]
+    log(f"[bench] routing check: {len(differ)} of {wl.T} tokens differ from the oracle, "
+        f"{int(near.sum())} near ties ({time.perf_counter() - t0:.1f} s)")
+    return {"tokens": wl.T, "checked_against": "oracle fp64 routing of every token",
+            "near_tie_delta": 1e-5, "near_ties": int(near.sum()),
+            "differ_from_oracle": [int(t) for t in differ],
+            "differ_all_near_ties": bool(near[differ].all()) if len(differ) else True,
+            "exact_at_clear_margin": bool((ids[~near] == r["ids"][~near]).all())}
+
+
+def measure_forward(wl, inp, steps, warmup, traffic=None, with_forward=True):
+    """Times the layer step (the four C-ABI calls moe_forward makes) with HIP
+    events on the launch stream; returns (summary dict, ids [T,k], counts)."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_09_amd as moe
+    shape = moe.make_shape(wl.T, wl.hidden, wl.experts, wl.topk, wl.inter, wl.shared, wl.precision)
     ws = moe.alloc_workspace(shape)
     opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, inp["beta"], inp["gate_bias"],
                                inp["token_ids"], inp["tid2eid"])
@@ -445,7 +540,7 @@ def main(argv=None):
     Xs_in = (Xq if fp8 else X) if wl.shared else None
     xs_in = xs if (fp8 and wl.shared) else None
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
 
     def step(ev=None):
         if ev:
@@ -463,31 +558,33 @@ def main(argv=None):
         if ev:
             ev[4].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     assert moe.moe_check_device_error(ws) == 0
-    log(f"[bench] warmup done; timing {args.steps} steps")
+    log(f"[bench] {wl.name}: warmup done; timing {steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    ms_per_step = (t1 - t0) * 1000.0 / steps
     stage_ms = np.array([[e[s].elapsed_time(e[s + 1]) for s in range(4)] for e in evs]).mean(0)
-    log(f"[bench] {ms_per_step:.3f} ms/step; stages (route, permute, ffn, combine) ms: "
-        f"{np.round(stage_ms, 4).tolist()}")
+    log(f"[bench] {wl.name}: {ms_per_step:.3f} ms/step; stages (route, permute, ffn, combine) "
+        f"ms: {np.round(stage_ms, 4).tolist()}")
 
-    # moe_forward (one call for all four stages) over the same inputs
-    for _ in range(2):
-        moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
-    torch.cuda.synchronize()
-    tf0 = time.perf_counter()
-    for _ in range(args.steps):
-        moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
-    torch.cuda.synchronize()
-    fwd_ms = (time.perf_counter() - tf0) * 1000.0 / args.steps
+    fwd_ms = None
+    if with_forward:
+        # moe_forward (one call for all four stages) over the same inputs
+        for _ in range(2):
+            moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
+        torch.cuda.synchronize()
+        tf0 = time.perf_counter()
+        for _ in range(steps):
+            moe.moe_forward(shape, opts, X, inp["Wg"], weights, ids, G, Y, ws)
+        torch.cuda.synchronize()
+        fwd_ms = (time.perf_counter() - tf0) * 1000.0 / steps
 
     cnt = counts.cpu().numpy()
     flops, nbytes, active = algorithmic_work(wl, cnt)
@@ -500,13 +597,11 @@ def main(argv=None):
     bound = "hbm" if t_hbm >= t_mfma else "mfma"
     if bound == "hbm":
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS[prec],
                 "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
-                "traffic": None}
-    traffic = measured_traffic(wl.name) if not args.set else None
-    roof["traffic"] = traffic
+                "traffic": traffic}
     roof.update({"kernel": "moe_expert_ffn (grouped Linear1+SwiGLU, Linear2)",
                  "traffic_over_algorithmic": (round(traffic / nbytes, 3) if traffic else None),
                  "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
@@ -514,11 +609,9 @@ def main(argv=None):
                  "frac_of_roofline": round(max(t_mfma, t_hbm) / ffn_s, 4)})
     sbytes = stage_bytes(wl)
     layer_bytes = nbytes + sum(sbytes.values())
-    copy_gbs = device_copy_gbs()
-    value = T / (ms_per_step / 1000.0)
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "value": round(T / (ms_per_step / 1000.0), 1),
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8-e4m3 (bf16 activations/output)",
                   "int8": "i8 (int32 products; bf16 activations/output)",
@@ -530,14 +623,13 @@ def main(argv=None):
                    "inter": wl.inter, "shared_experts": wl.shared, "score": wl.score,
                    "renorm": wl.renorm, "alpha": wl.alpha, "routing": "hash" if wl.hash else "score",
                    "expert_load": "zipf(0.8)" if wl.zipf else "random gate",
-                   "active_experts": active,
-                   **({"overrides": args.set} if args.set else {})},
+                   "active_experts": active},
         "grouped_gemm": {"tflops": round(tflops, 1),
                          "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS[prec], 4),
                          "hbm_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)},
         "stages_ms": {"route": round(stage_ms[0], 4), "permute": round(stage_ms[1], 4),
                       "expert_ffn": round(stage_ms[2], 4), "combine": round(stage_ms[3], 4)},
-        "moe_forward_ms": round(fwd_ms, 4),
+        "moe_forward_ms": None if fwd_ms is None else round(fwd_ms, 4),
         "stages_hbm": {name: {"gbs": round(b / (stage_ms[i] / 1000.0) / 1e9, 1),
                               "frac_hbm_peak": round(b / (stage_ms[i] / 1000.0) / 1e9
                                                      / PEAK_HBM_GBS, 4),
@@ -547,13 +639,11 @@ def main(argv=None):
                       "frac_hbm_peak": round(layer_bytes / (ms_per_step / 1000.0) / 1e9
                                              / PEAK_HBM_GBS, 4),
                       "algorithmic_bytes": layer_bytes},
-        "hbm_copy_probe_gbs": copy_gbs,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, ids.cpu().numpy(), cnt)
-    print(json.dumps(out), flush=True)
-    return 0
+    ids_h = ids.cpu().numpy()
+    del ws, Xp, Yp, Ys, Y, xps, Xq, xs
+    return out, ids_h, cnt
 
 
 if __name__ == "__main__":
