@@ -181,9 +181,7 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
   if (!aligned16({X, Wg})) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   RouteArgs a = route_args(shape, opts, X, Wg, expert_ids, gate_weights, keys_out, workspace);
-  hipError_t e = launch_clear_flag(a.flag, stream);
-  if (e == hipSuccess) e = launch_route(a, stream);
-  return hip_status(e);
+  return hip_status(launch_route(a, stream));  // clears the error flag first
 }
 
 int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X,

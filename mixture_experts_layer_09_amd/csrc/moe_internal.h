@@ -117,14 +117,15 @@ inline size_t row_scale_bytes(int precision, size_t n) {
   return (precision == MOE_PREC_FP8 || precision == MOE_PREC_INT8) ? 4 : 0;
 }
 
-// The router's launch plan: tokens per block and K-splits of the gating
-// linear (route_plan.cpp), and the bytes of split-K partial gate logits it
-// uses in the workspace (0 if none).
+// The router's launch plan: which gate kernel, tokens per block and
+// K-splits of the gating linear (route_plan.cpp), and the bytes of fp32
+// partial gate logits it uses in the workspace (0 if none).
 struct RoutePlan {
+  int dma;  // 1: DMA-fed bf16 gate GEMM + top-k kernel; 0: register-staged gate kernel
   int bm, splits;
 };
-RoutePlan route_plan(int T, int h, int E);
-size_t route_partial_bytes(int T, int h, int E);
+RoutePlan route_plan(int T, int h, int E, int precision);
+size_t route_partial_bytes(int T, int h, int E, int precision);
 
 // Byte offsets of every region inside the caller's workspace.
 struct Layout {
@@ -154,7 +155,7 @@ inline Layout make_layout(const moe_shape& s) {
     return at;
   };
   L.flag = take(kAlign);
-  L.part = take(route_partial_bytes(s.tokens, s.hidden, s.experts));
+  L.part = take(route_partial_bytes(s.tokens, s.hidden, s.experts, s.precision));
   L.blk_cnt = take(static_cast<size_t>(L.nblk) * E * 4);
   L.local_rank = take(rows * 4);
   L.tile_off = take((E + 2) * 4);
@@ -195,6 +196,7 @@ struct RouteArgs {
   int32_t* flag;
   float* part;  // workspace for split-K partial logits
 };
+// Clears the error flag a.flag, then routes (hash routing may set the flag).
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 struct PermuteArgs {

@@ -23,6 +23,7 @@
 // rounds of a wave-wide argmax by shuffles (ties to the lower expert id),
 // weights alpha * a / sum a (or alpha * a).  Hash routing reads the selection
 // from tid2eid and keeps the weights.
+#include "lds_dma.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -32,16 +33,10 @@ constexpr int kThreads = 256;
 constexpr int kBK = 32;                  // K elements per LDS tile
 constexpr int kARow = kBK * 2 + 16;      // bytes per padded token row
 
-typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((ext_vector_type(8))) short i16x8_t;
 
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
-}
-
-__device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) i16x4_t*)(p));
 }
 
 // The routing of one token from its logits (lane l holds logits of experts
@@ -336,6 +331,353 @@ __global__ __launch_bounds__(kThreads) void route_epilogue_kernel(RouteArgs a, i
   route_token<EP>(a, t, lane, lg);
 }
 
+// ------------------------------------------------------------ DMA gate GEMM
+// bf16, E a multiple of 128 (E <= 512): a block of 8 waves owns BM (64 or
+// 128) tokens and all E experts over one K range.  K-stages of 32 go global -> LDS by
+// asynchronous DMA (global_load_lds_dwordx4) into a 3-stage ring with the
+// waits written out (s_waitcnt vmcnt for the later stages, then s_barrier):
+// token rows as 64-byte pieces, gate-weight rows ([h, E], E contiguous) as
+// they are, read as MFMA B fragments by the transposing ds_read_b64_tr_b16.
+// The waves split the tile 2 (tokens) x 4 (experts); each multiplies its
+// BM / 64 x E / 128 tiles of 32 x 32 with two v_mfma_f32_32x32x16_bf16 per stage (a lane holds row or
+// column lane % 32 at K 16 kh + 8 (lane / 32) + 0..7 of half kh, the same in
+// A and B, so the instruction's own K order does not matter).  XOR chunk
+// swizzles: token rows (r >> 2) & 3, weight rows 4 (r % 4) (a transposing
+// read's half covers 4 consecutive K rows x 4 chunks; the XOR keeps a chunk
+// inside its aligned group of 16, so rows of E / 8 chunks work).  Every block
+// writes its fp32 partial logits part[split][t][e]; route_topk_kernel sums
+// the splits and routes.
+// The ring is as deep as 140 KB of LDS allows (up to 6 stages): a block
+// streams its gate-weight slice from L2 and its token rows from HBM at
+// latencies that only many stages in flight cover.  Block (0, 0) clears the
+// device error flag first (route_topk_kernel, which runs after, may set it).
+template <int EP, int BM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
+  constexpr int BK = 32, NW = 8, WN = 4;
+  constexpr int MT = BM / 64;  // 32-row MFMA tiles per wave (2 x 4 waves)
+  constexpr int STAGE_BYTES = BM * BK * 2 + BK * EP * 2;
+  constexpr int STAGES = (143360 / STAGE_BYTES) < 6 ? (143360 / STAGE_BYTES) : 6;
+  constexpr int NTW = EP / (32 * WN);  // 32-column MFMA tiles per wave
+  constexpr int A_ROW = BK * 2;        // bytes of a token row piece
+  constexpr int B_ROW = EP * 2;        // bytes of a gate-weight K row
+  constexpr int A_BYTES = BM * A_ROW;
+  constexpr int B_BYTES = BK * B_ROW;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_INSTS = A_BYTES / 1024;
+  constexpr int B_INSTS = B_BYTES / 1024;
+  constexpr int INSTS = A_INSTS + B_INSTS;
+  constexpr int MAX_OPS = (INSTS + NW - 1) / NW;
+  constexpr int B_CHUNKS = B_ROW / 16;  // 16-byte chunks of a weight row
+  static_assert(EP % 128 == 0 && EP <= 512 && B_CHUNKS % 16 == 0, "expert columns");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 1024 == 0, "DMA granularity");
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.flag[0] = 0;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int wm = wave / WN, wn = wave % WN;
+  const int T = a.T, h = a.h, E = a.E;
+  const int m0 = blockIdx.x * BM;
+  const int split = blockIdx.y;
+  const int k0 = split * kchunk;
+  const int KT = kchunk / BK;
+  const size_t x_ld = static_cast<size_t>(h) * 2;
+  const size_t w_ld = static_cast<size_t>(E) * 2;
+  // DMA: instruction q of a stage (q < A_INSTS: token rows, else weight rows)
+  // is issued by wave q % NW; this wave's per-lane source offsets
+  const char* a_base = uniform_ptr(static_cast<const char*>(a.X) + static_cast<size_t>(m0) * x_ld +
+                                   static_cast<size_t>(k0) * 2);
+  const char* b_base = uniform_ptr(static_cast<const char*>(a.Wg) + static_cast<size_t>(k0) * w_ld);
+  uint32_t voff[MAX_OPS];
+  int ops = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_OPS; ++i) {
+    const int q = wave + i * NW;
+    voff[i] = 0;
+    if (q < A_INSTS) {
+      const int r = q * (1024 / A_ROW) + lane / 4;
+      const int c = (lane % 4) ^ ((r >> 2) & 3);
+      voff[i] = static_cast<uint32_t>(min(m0 + r, T - 1) - m0) * static_cast<uint32_t>(x_ld) + c * 16;
+      ++ops;
+    } else if (q < INSTS) {
+      const int s = (q - A_INSTS) * 64 + lane;
+      const int r = s / B_CHUNKS;
+      const int c = (s % B_CHUNKS) ^ (4 * (r & 3));
+      voff[i] = static_cast<uint32_t>(r) * static_cast<uint32_t>(w_ld) + c * 16;
+      ++ops;
+    }
+  }
+  auto issue = [&](int kt, int slot) {
+    char* st = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < MAX_OPS; ++i) {
+      const int q = wave + i * NW;
+      if (q < A_INSTS)
+        dma16(a_base + static_cast<size_t>(kt) * A_ROW, voff[i], st + q * 1024);
+      else if (q < INSTS)
+        dma16(b_base + static_cast<size_t>(kt) * BK * w_ld, voff[i], st + q * 1024);
+    }
+  };
+  // fragment offsets (within a stage): A rows wm * BM / 2 + 32 i + lane % 32;
+  // B columns of this wave's NTW tiles
+  int a_off[MT][2];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int ar = wm * (BM / 2) + 32 * i + (lane & 31);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+      a_off[i][kh] = ar * A_ROW + (((2 * kh + (lane >> 5)) ^ ((ar >> 2) & 3)) << 4);
+  }
+  int b_off[NTW][4];
+  {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int col0 = wn * (EP / WN) + j * 32;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = 16 * kh + 8 * (g >> 1) + 4 * hh + (p >> 2);
+          const int col = col0 + 16 * (g & 1) + (p & 3) * 4;
+          b_off[j][2 * kh + hh] = A_BYTES + r * B_ROW + (((col >> 3) ^ (4 * (r & 3))) << 4) + (col & 7) * 2;
+        }
+    }
+  }
+  f32x16_t acc[MT][NTW];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x16_t{};
+  auto tr_pair = [](const char* st, int o0, int o1) {
+    const i16x4_t lo4 = ds_read_tr16(st + o0);
+    const i16x4_t hi4 = ds_read_tr16(st + o1);
+    const i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  auto compute = [&](int slot) {
+    const char* st = smem + slot * STAGE;
+    bf16x8_t bk0[NTW], bk1[NTW];
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      bk0[j] = tr_pair(st, b_off[j][0], b_off[j][1]);
+      bk1[j] = tr_pair(st, b_off[j][2], b_off[j][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const bf16x8_t ak0 = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][0]);
+      const bf16x8_t ak1 = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][1]);
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0, bk0[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1, bk1[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  // K loop, unrolled by STAGES so that every slot is a constant LDS range
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < KT) issue(s, s);
+  for (int kt0 = 0; kt0 < KT; kt0 += STAGES) {
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) {
+      const int kt = kt0 + s;
+      if (kt < KT) {
+        const int after = min(STAGES - 2, KT - 1 - kt);
+        wait_vmcnt_rt(after * ops);
+        __builtin_amdgcn_s_barrier();
+        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+        compute(s);
+      }
+    }
+  }
+  // partial logits: element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4
+  // of the wave's 32 rows, column l % 32 of tile j
+  float* out = part + static_cast<size_t>(split) * T * E;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int e = wn * (EP / WN) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int t = m0 + wm * (BM / 2) + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (t < T) out[static_cast<size_t>(t) * E + e] = acc[i][j][v];
+      }
+    }
+}
+
+// Routing of 4 tokens per wave (one wave per block, so that the blocks
+// spread over every CU), 16 lanes per token: lane p of a token's group
+// holds experts p + 16 q (q < EP / 16).  Logits are the split partials summed
+// in split order (+ the gating bias); affinity, key = a + beta; k rounds of
+// a 16-lane argmax by xor shuffles (key descending, equal keys to the lower
+// id), the winner's lane marks it taken; the weights' denominator sums the
+// chosen affinities in choice order.  Hash routing reads the choice from
+// tid2eid and takes the chosen affinities from their lanes.
+template <int EP>
+__global__ __launch_bounds__(64) void route_topk_kernel(RouteArgs a, int splits,
+                                                        const float* __restrict__ part) {
+  constexpr int Q = EP / 16;
+  static_assert(Q <= 32, "experts per lane");
+  const int lane = threadIdx.x & 63;
+  const int p = lane & 15;
+  const int t = blockIdx.x * 4 + (lane >> 4);  // one wave (4 tokens) per block
+  const int T = a.T, E = a.E, k = a.k;
+  const bool live = t < T;  // not wave-uniform: every lane takes part in the shuffles
+  const bool hash = (a.token_ids != nullptr && a.tid2eid != nullptr);
+  float av[Q], key[Q];
+  // logits: the splits summed in split order; every load of a split is
+  // issued before any is added
+#pragma unroll
+  for (int q = 0; q < Q; ++q) av[q] = 0.0f;
+  // two splits at a time, every load of both issued before any add
+  const size_t tt = live ? t : 0;
+  int sp = 0;
+  for (; sp + 1 < splits; sp += 2) {
+    const float* r0 = part + (static_cast<size_t>(sp) * T + tt) * E;
+    const float* r1 = r0 + static_cast<size_t>(T) * E;
+    float v0[Q], v1[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const bool ok = live && p + 16 * q < E;
+      v0[q] = ok ? r0[p + 16 * q] : 0.0f;
+      v1[q] = ok ? r1[p + 16 * q] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) av[q] = (av[q] + v0[q]) + v1[q];
+  }
+  if (sp < splits) {
+    const float* r0 = part + (static_cast<size_t>(sp) * T + tt) * E;
+    float v0[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) v0[q] = (live && p + 16 * q < E) ? r0[p + 16 * q] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) av[q] += v0[q];
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = p + 16 * q;
+    av[q] = (e < E) ? av[q] + (a.gate_bias ? a.gate_bias[e] : 0.0f) : -INFINITY;
+  }
+  // affinities with the hardware exp2 and reciprocal (a few ulp; the keys
+  // stay within 1e-6 of the exact values)
+  if (a.score_fn == MOE_SCORE_SOFTMAX) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) m = fmaxf(m, av[q]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    float z = 0.0f;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      av[q] = (p + 16 * q < E) ? __expf(av[q] - m) : 0.0f;
+      z += av[q];
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 16);
+    const float rz = __builtin_amdgcn_rcpf(z);
+#pragma unroll
+    for (int q = 0; q < Q; ++q) av[q] = av[q] * rz;
+  } else if (a.score_fn == MOE_SCORE_SQRT_SOFTPLUS) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float l = av[q];
+      const float sp = l > 0.0f ? l + log1pf(expf(-l)) : log1pf(expf(l));
+      av[q] = (p + 16 * q < E) ? sqrtf(sp) : 0.0f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      av[q] = (p + 16 * q < E) ? __builtin_amdgcn_rcpf(1.0f + __expf(-av[q])) : 0.0f;
+  }
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    const int e = p + 16 * q;
+    key[q] = (e < E) ? av[q] + ((a.beta && !hash) ? a.beta[e] : 0.0f) : -INFINITY;
+    if (a.keys && live && e < E) a.keys[static_cast<size_t>(t) * E + e] = key[q];
+  }
+  int my_id = -1;
+  float my_a = 0.0f, den = 0.0f;
+  if (!hash) {
+    // branch-free selection: a taken (or absent) expert competes with key
+    // -inf, which a real key always beats in the group reduction (E >= k)
+    uint32_t taken = 0u;
+    for (int j = 0; j < k; ++j) {
+      float bk = -INFINITY, ba = 0.0f;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int e = p + 16 * q;
+        const float kq = ((taken >> q) & 1u) ? -INFINITY : key[q];
+        const bool b = (kq > bk) || (kq == bk && e < bi);
+        bk = b ? kq : bk;
+        bi = b ? e : bi;
+        ba = b ? av[q] : ba;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float ok = __shfl_xor(bk, o, 16);
+        const int oi = __shfl_xor(bi, o, 16);
+        const float oa = __shfl_xor(ba, o, 16);
+        if (better(ok, oi, bk, bi)) {
+          bk = ok;
+          bi = oi;
+          ba = oa;
+        }
+      }
+      taken |= ((bi & 15) == p) ? (1u << (bi >> 4)) : 0u;
+      den += ba;
+      if (p == j) {
+        my_id = bi;
+        my_a = ba;
+      }
+    }
+  } else {
+    const int tok = live ? a.token_ids[t] : -1;
+    const bool ok_tok = tok >= 0 && tok < a.vocab;
+    for (int j = 0; j < k; ++j) {
+      int e = ok_tok ? a.tid2eid[static_cast<size_t>(tok) * k + j] : -1;
+      if (e < 0 || e >= E) e = -1;
+      const int qs = e >= 0 ? e >> 4 : 0;
+      float mine = 0.0f;
+#pragma unroll
+      for (int q = 0; q < Q; ++q)
+        if (q == qs) mine = av[q];
+      float v = __shfl(mine, e >= 0 ? (e & 15) : 0, 16);
+      if (e < 0) v = 0.0f;
+      den += v;
+      if (p == j) {
+        my_id = e;
+        my_a = v;
+      }
+    }
+    if (live && p < k && my_id < 0) a.flag[0] = 1;
+  }
+  if (live && p < k) {
+    a.ids[static_cast<size_t>(t) * k + p] = my_id;
+    const float g = a.renorm ? a.alpha * my_a / den : a.alpha * my_a;
+    a.G[static_cast<size_t>(t) * k + p] = (my_id >= 0) ? g : 0.0f;
+  }
+}
+
+template <int EP>
+hipError_t launch_dma_route(const RouteArgs& a, int bm, int splits, hipStream_t stream) {
+  const int mtiles = (a.T + bm - 1) / bm;
+  if (bm == 128)
+    hipLaunchKernelGGL((gate_dma_kernel<EP, 128>), dim3(mtiles, splits), dim3(512), 0, stream, a,
+                       a.h / splits, a.part);
+  else
+    hipLaunchKernelGGL((gate_dma_kernel<EP, 64>), dim3(mtiles, splits), dim3(512), 0, stream, a,
+                       a.h / splits, a.part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_topk_kernel<EP>, dim3((a.T + 3) / 4), dim3(64), 0, stream, a, splits,
+                     static_cast<const float*>(a.part));
+  return hipGetLastError();
+}
+
 template <int BM, int EP>
 hipError_t launch_ep(const RouteArgs& a, int splits, hipStream_t stream) {
   const int mtiles = (a.T + BM - 1) / BM;
@@ -376,7 +718,17 @@ hipError_t launch_bm(const RouteArgs& a, int splits, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
-  const RoutePlan p = route_plan(a.T, a.h, a.E);
+  const RoutePlan p = route_plan(a.T, a.h, a.E, a.precision);
+  if (p.dma) {
+    switch (a.E) {
+      case 128: return launch_dma_route<128>(a, p.bm, p.splits, stream);
+      case 256: return launch_dma_route<256>(a, p.bm, p.splits, stream);
+      case 384: return launch_dma_route<384>(a, p.bm, p.splits, stream);
+      default: return launch_dma_route<512>(a, p.bm, p.splits, stream);
+    }
+  }
+  hipError_t e = launch_clear_flag(a.flag, stream);
+  if (e != hipSuccess) return e;
   if (p.bm == 64) return launch_bm<64>(a, p.splits, stream);
   return p.bm == 32 ? launch_bm<32>(a, p.splits, stream) : launch_bm<16>(a, p.splits, stream);
 }

@@ -81,7 +81,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t) {
   touch(a.G, T * k * 4);
   touch(a.keys, a.keys ? T * E * 4 : 0);
   touch(a.flag, 4);
-  touch(a.part, route_partial_bytes(a.T, a.h, a.E));
+  *a.flag = 0;  // the router clears the error flag first
+  touch(a.part, route_partial_bytes(a.T, a.h, a.E, a.precision));
   ++g_launches;
   return hipSuccess;
 }

@@ -45,6 +45,19 @@ CASES = {
     # the DeepSeek-V4 affinity sqrt(softplus(l)) with the V4-Pro router
     "v4pro_sqrt_softplus_small": ("v4pro_bf16", dict(T=256, hidden=512, experts=64, inter=256,
                                                      score="sqrt_softplus")),
+    # expert counts that take the DMA gate GEMM and the 16-lane top-k kernel
+    # (E a multiple of 128): ragged token tiles, one and several K-splits,
+    # every score function and hash routing
+    "route_dma_e384": ("v4pro_bf16", dict(T=300, hidden=512, experts=384, inter=128)),
+    "route_dma_e128_softmax": ("llama_bf16", dict(T=260, hidden=1024, experts=128, inter=128)),
+    "route_dma_e256_sqrt_softplus": ("v4pro_bf16", dict(T=130, hidden=256, experts=256, inter=128,
+                                                        zipf=False, score="sqrt_softplus")),
+    "route_dma_e512": ("v4pro_bf16", dict(T=70, hidden=768, experts=512, topk=8, inter=128,
+                                          zipf=False)),
+    "decode_hash_e384": ("decode_hash_bf16", dict(T=20, hidden=512, experts=384, inter=128)),
+    # 128-token gate blocks (T >= 4096), a ragged last block
+    "route_dma_bm128": ("v4pro_bf16", dict(T=4100, hidden=256, experts=128, inter=128,
+                                           zipf=False)),
 }
 
 
