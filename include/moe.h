@@ -172,6 +172,8 @@ typedef struct {
 size_t moe_workspace_size(const moe_shape* shape);
 
 /* Steps 1-2: gating linear, affinity, bias-for-selection top-k, weights.
+ * Source: "Megatron-LM 的 MoE 并行：以 DeepSeek-V4 为例" §路由张量 and §Hash 路由;
+ * "Megatron 分布式训练全维度并行技术文档" §4.1-§4.2 (softmax top-k router).
  *   X [T, hidden] (fp32 for F32, else bf16), Wg [hidden, E] same type.
  *   expert_ids [T, topk] int32 out, gate_weights [T, topk] fp32 out.
  *   keys_out [T, E] fp32 out or NULL: the selection keys a + beta as the
@@ -183,6 +185,8 @@ int moe_route(const moe_shape* shape, const moe_route_opts* opts, const void* X,
               size_t workspace_bytes, hipStream_t stream);
 
 /* Step 3: dispatch (a permutation with duplication).
+ * Source: CANN "mega_moe" page §计算过程, EP Dispatch (and its A8W8 and MXFP
+ * blocks for the quantised X); "Megatron-LM 的 MoE 并行" §计数与重排.
  *   counts [E] out: assignments per expert; offsets [E+1] out: exclusive
  *   prefix sum; dst_row [T*topk] out: destination row of assignment t*k+j
  *   (rows of one expert are contiguous and ordered by ascending t*k+j);
@@ -227,6 +231,8 @@ int moe_permute_no_alloc(const moe_shape* shape, const int32_t* expert_ids, cons
                          void* Xp, void* xp_scale, void* Xq, void* x_scale, hipStream_t stream);
 
 /* Step 4: grouped Linear1 -> SwiGLU -> Linear2 over the expert blocks given
+ * [source: CANN "mega_moe" page §计算过程, Expert Compute and its A8W8 / MXFP
+ * blocks; "Megatron-LM 的 MoE 并行" §ETP 里的矩阵 and §模型与入口 (shared expert)]
  * by offsets [E+1] (rows offsets[e] .. offsets[e+1]-1 of Xp belong to expert
  * e), fp32 accumulation.  Yp [T*topk, hidden] out (fp32 for F32, else bf16).
  * With a shared expert: Xs [T, hidden] is its input (X, or Xq with
@@ -241,12 +247,16 @@ int moe_expert_ffn(const moe_shape* shape, const void* Xp, const void* xp_scale,
                    size_t workspace_bytes, hipStream_t stream);
 
 /* Step 5: Y[t] = sum_{j ascending} G[t,j] * Yp[dst_row[t*k+j]] (+ Ys[t]),
+ * [source: CANN "mega_moe" page §计算过程, Token Combine; "Megatron-LM 的 MoE
+ * 并行" §模型与入口 (the layer equation, shared expert at weight 1)]
  * fp32 accumulation, rounded once to the output type.  Rows with dst_row < 0
  * are skipped.  Ys may be NULL. */
 int moe_combine(const moe_shape* shape, const void* Yp, const int32_t* dst_row,
                 const float* gate_weights, const void* Ys, void* Y, hipStream_t stream);
 
 /* Steps 1-5.  With opts != NULL the router runs and writes expert_ids and
+ * [source: the layer equation of "Megatron-LM 的 MoE 并行" §模型与入口, computed by
+ * the four steps above]
  * gate_weights; with opts == NULL they are inputs (the mega_moe form, which
  * takes the routing as given) and Wg is not read.  Y [T, hidden] out. */
 int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* X,
