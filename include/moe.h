@@ -331,9 +331,13 @@ int moe_backward_saved(const moe_shape* shape, const moe_route_opts* opts, const
                        hipStream_t stream);
 
 /* Synchronises `stream`, then reports (and clears) the device-side error
- * flag in the workspace: MOE_ERR_DEVICE_DATA if an earlier moe_permute,
- * moe_route or moe_forward on this workspace saw an expert id outside
- * [0, E) or a token id outside [0, vocab); MOE_OK otherwise. */
+ * flag in the workspace: MOE_ERR_DEVICE_DATA if the most recent moe_route,
+ * moe_permute, moe_forward, moe_forward_train or moe_backward on this
+ * workspace saw an expert id outside [0, E) or a token id outside
+ * [0, vocab); MOE_OK otherwise.  Each of those calls clears the flag when it
+ * starts (the workspace needs no initialisation) and covers all of its own
+ * steps, so a caller that runs moe_route and then moe_permute on one
+ * workspace checks after moe_route to see the router's errors. */
 int moe_check_device_error(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a moe_status value. */

@@ -335,3 +335,13 @@ def test_bad_token_ids_are_flagged():
     assert L.device_error() == -5
     assert (ids[2] == -1).all() and (G[2] == 0).all()
     assert (ids[3] >= 0).all()
+    # moe_forward reports its router's bad token id too (it covers all its
+    # steps), and a clean call afterwards clears the flag again
+    Y = torch.empty((wl.T, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    _log("[bad token id] hash forward")
+    moe.moe_forward(L.shape, opts, gpu["X"], gpu["Wg"], L.weights, ids, G, Y, L.ws)
+    torch.cuda.synchronize()
+    assert L.device_error() == -5
+    moe.moe_route(L.shape, L.opts, gpu["X"], gpu["Wg"], ids, G, None, L.ws)
+    torch.cuda.synchronize()
+    assert L.device_error() == 0
