@@ -13,7 +13,7 @@ tokens the shared expert's Ys, each against the oracle's expert FFN with one
 expert's weights copied to the host at a time.  Checked on sampled tokens:
 the layer output against the oracle, with samples chosen to cover the
 hottest expert's last (ragged) tile, the coldest active experts and the
-shared expert.
+shared expert.  A second moe_forward must give bit-identical outputs.
 """
 from __future__ import annotations
 
@@ -201,6 +201,12 @@ def test_full_size_forward(name):
     Y, ids_f, G_f = L.forward()
     torch.cuda.synchronize()
     assert torch.equal(ids_f, ids_g) and torch.equal(G_f, G_g)
+    # deterministic at full size too: a second call gives the same bits
+    Y2, ids_2, G_2 = L.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(ids_2, ids_f) and torch.equal(G_2, G_f)
+    assert torch.equal(Y2.view(torch.uint8), Y.view(torch.uint8))
+    del Y2
     counts = d["counts"]
     toks = _sample_tokens(ids, counts)
     _log(f"[full] {name}: oracle on {len(toks)} sampled tokens")
