@@ -58,6 +58,15 @@ CASES = {
     # 128-token gate blocks (T >= 4096), a ragged last block
     "route_dma_bm128": ("v4pro_bf16", dict(T=4100, hidden=256, experts=128, inter=128,
                                            zipf=False)),
+    # the shape limits: top-16 (the most the ABI takes) over 512 experts on
+    # the DMA router (32 experts per lane, a 32-bit taken mask), over 64
+    # experts on the other router, and by hash
+    "max_topk16_e512": ("v4pro_bf16", dict(T=96, hidden=512, experts=512, topk=16, inter=128,
+                                           zipf=False)),
+    "max_topk16_e64_softmax": ("llama_bf16", dict(T=128, hidden=256, experts=64, topk=16,
+                                                  inter=128)),
+    "max_topk16_hash": ("decode_hash_bf16", dict(T=24, hidden=512, experts=64, topk=16,
+                                                 inter=128)),
 }
 
 
