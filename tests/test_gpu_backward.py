@@ -33,6 +33,9 @@ CASES = {
     "sqrt_softplus_bwd": ("v4pro_bf16", dict(T=150, hidden=256, experts=64, inter=128,
                                              score="sqrt_softplus"), True),
     "hash_bwd": ("decode_hash_bf16", dict(T=40, hidden=512, experts=64, inter=256), True),
+    # top-16 (the most the ABI takes) over 128 experts, the router differentiated
+    "topk16_bwd": ("v4pro_bf16", dict(T=64, hidden=256, experts=128, topk=16, inter=128,
+                                      zipf=False), True),
     # given top-1 routing with the expert loads below: the wgrad kernels split
     # the routed experts at 128 rows (a strip kernel up to 128, the tile walk
     # above, with the shared expert), and rows come in 32-row chunks
