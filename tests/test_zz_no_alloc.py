@@ -5,8 +5,8 @@ Two calls in a row on one GPU, the second with fewer tokens and fewer
 per-block count rows than the first, in bf16 and in the quantised e4m3
 layout: every output (counts, offsets, row maps, the copied or quantised
 rows and their scales) bit-identical to moe_permute's on the same ids, and
-both equal to the oracle's dispatch.  A call larger than the scratch is
-refused on the host.
+both equal to the oracle's dispatch; the same at exactly the scratch's limit
+(over 512 experts).  A call larger than the scratch is refused on the host.
 """
 from __future__ import annotations
 
@@ -67,6 +67,44 @@ def test_no_alloc_permute_equals_moe_permute(base):
         for k in ("counts", "offsets", "dst_row"):
             assert np.array_equal(out[k].cpu().numpy(), d[k]), k
         assert L.device_error() == -5      # moe_permute's workspace saw the bad id
+
+
+def test_no_alloc_permute_at_its_limit():
+    """Exactly MOE_NO_ALLOC_MAX_ASSIGNMENTS assignments over the most experts
+    the ABI takes (512): the scratch's per-block count table and rank array
+    are full."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    k, E, h = 8, 512, 128
+    T = moe.NO_ALLOC_MAX_ASSIGNMENTS // k
+    assert T * k == moe.NO_ALLOC_MAX_ASSIGNMENTS
+    g = torch.Generator().manual_seed(20260)
+    ids_cpu = torch.randint(0, E, (T, k), generator=g, dtype=torch.int32)
+    X = torch.randn((T, h), generator=g).to(torch.bfloat16).cuda()
+    ids = ids_cpu.cuda()
+    shape = moe.make_shape(T, h, E, k, 64, 0, "bf16")
+    ws = moe.alloc_workspace(shape)
+    n = T * k
+
+    def bufs():
+        i32 = dict(dtype=torch.int32, device="cuda")
+        return dict(counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                    dst_row=torch.empty(n, **i32), src_tok=torch.empty(n, **i32),
+                    Xp=torch.empty((n, h), dtype=torch.bfloat16, device="cuda"))
+
+    _log(f"[no-alloc] at the limit: T={T} k={k} E={E}: moe_permute, then moe_permute_no_alloc")
+    ref, out = bufs(), bufs()
+    moe.moe_permute(shape, ids, X, ref["counts"], ref["offsets"], ref["dst_row"], ref["src_tok"],
+                    ref["Xp"], None, None, None, ws)
+    moe.moe_permute_no_alloc(shape, ids, X, out["counts"], out["offsets"], out["dst_row"],
+                             out["src_tok"], out["Xp"], None, None, None)
+    torch.cuda.synchronize()
+    for key in ref:
+        assert torch.equal(out[key].view(torch.uint8), ref[key].view(torch.uint8)), key
+    d = oracle.dispatch(ids_cpu.numpy(), E)
+    for key in ("counts", "offsets", "dst_row", "src_tok"):
+        assert np.array_equal(out[key].cpu().numpy(), d[key]), key
+    assert moe.moe_check_device_error(ws) == 0
 
 
 def test_no_alloc_permute_refuses_more_than_its_scratch():
