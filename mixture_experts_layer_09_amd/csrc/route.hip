@@ -509,112 +509,122 @@ void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
 }
 
 // Routing of 4 tokens per wave (one wave per block, so that the blocks
-// spread over every CU), 16 lanes per token: lane p of a token's group
-// holds experts p + 16 q (q < EP / 16).  Logits are the split partials summed
-// in split order (+ the gating bias); affinity, key = a + beta; k rounds of
-// a 16-lane argmax by xor shuffles (key descending, equal keys to the lower
+// spread over every CU), 16 lanes per token.  E equals EP here (the DMA gate
+// GEMM runs only for E a multiple of 128 up to 512, one instance per E).  Lane
+// p of a token's group holds the 4 experts 64 q + 4 p + c (c < 4) of every
+// 64-expert group q, in slot 4 q + c, so that its loads of partial logits
+// are 16 bytes each.  Logits are the split partials summed in
+// split order (+ the gating bias); affinity, key = a + beta; k rounds of a
+// 16-lane argmax by xor shuffles (key descending, equal keys to the lower
 // id), the winner's lane marks it taken; the weights' denominator sums the
 // chosen affinities in choice order.  Hash routing reads the choice from
 // tid2eid and takes the chosen affinities from their lanes.
 template <int EP>
 __global__ __launch_bounds__(64) void route_topk_kernel(RouteArgs a, int splits,
                                                         const float* __restrict__ part) {
-  constexpr int Q = EP / 16;
+  constexpr int G = EP / 64;  // 64-expert groups
+  constexpr int Q = 4 * G;    // experts per lane
   static_assert(Q <= 32, "experts per lane");
   const int lane = threadIdx.x & 63;
   const int p = lane & 15;
   const int t = blockIdx.x * 4 + (lane >> 4);  // one wave (4 tokens) per block
-  const int T = a.T, E = a.E, k = a.k;
+  const int T = a.T, k = a.k;
   const bool live = t < T;  // not wave-uniform: every lane takes part in the shuffles
   const bool hash = (a.token_ids != nullptr && a.tid2eid != nullptr);
-  float av[Q], key[Q];
-  // logits: the splits summed in split order; every load of a split is
-  // issued before any is added
-#pragma unroll
-  for (int q = 0; q < Q; ++q) av[q] = 0.0f;
-  // two splits at a time, every load of both issued before any add
   const size_t tt = live ? t : 0;
-  int sp = 0;
-  for (; sp + 1 < splits; sp += 2) {
-    const float* r0 = part + (static_cast<size_t>(sp) * T + tt) * E;
-    const float* r1 = r0 + static_cast<size_t>(T) * E;
-    float v0[Q], v1[Q];
+  auto ld4 = [&](const float* row, int g) {
+    return *reinterpret_cast<const f32x4_t*>(row + 64 * g + 4 * p);
+  };
+  float av[Q], key[Q];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const bool ok = live && p + 16 * q < E;
-      v0[q] = ok ? r0[p + 16 * q] : 0.0f;
-      v1[q] = ok ? r1[p + 16 * q] : 0.0f;
+  for (int s = 0; s < Q; ++s) av[s] = 0.0f;
+  // four splits at a time, every load of the four issued before any add;
+  // the adds go in split order
+  int sp = 0;
+  for (; sp + 3 < splits; sp += 4) {
+    f32x4_t v[4][G];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* r = part + (static_cast<size_t>(sp + u) * T + tt) * EP;
+#pragma unroll
+      for (int g = 0; g < G; ++g) v[u][g] = ld4(r, g);
     }
 #pragma unroll
-    for (int q = 0; q < Q; ++q) av[q] = (av[q] + v0[q]) + v1[q];
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) av[4 * g + c] += v[u][g][c];
   }
-  if (sp < splits) {
-    const float* r0 = part + (static_cast<size_t>(sp) * T + tt) * E;
-    float v0[Q];
+  for (; sp < splits; ++sp) {
+    const float* r = part + (static_cast<size_t>(sp) * T + tt) * EP;
+    f32x4_t v0[G];
 #pragma unroll
-    for (int q = 0; q < Q; ++q) v0[q] = (live && p + 16 * q < E) ? r0[p + 16 * q] : 0.0f;
+    for (int g = 0; g < G; ++g) v0[g] = ld4(r, g);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) av[q] += v0[q];
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) av[4 * g + c] += v0[g][c];
   }
+  if (a.gate_bias) {
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int e = p + 16 * q;
-    av[q] = (e < E) ? av[q] + (a.gate_bias ? a.gate_bias[e] : 0.0f) : -INFINITY;
+    for (int s = 0; s < Q; ++s) av[s] += a.gate_bias[64 * (s >> 2) + 4 * p + (s & 3)];
   }
   // affinities with the hardware exp2 and reciprocal (a few ulp; the keys
   // stay within 1e-6 of the exact values)
   if (a.score_fn == MOE_SCORE_SOFTMAX) {
     float m = -INFINITY;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) m = fmaxf(m, av[q]);
+    for (int s = 0; s < Q; ++s) m = fmaxf(m, av[s]);
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
     float z = 0.0f;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      av[q] = (p + 16 * q < E) ? __expf(av[q] - m) : 0.0f;
-      z += av[q];
+    for (int s = 0; s < Q; ++s) {
+      av[s] = __expf(av[s] - m);
+      z += av[s];
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 16);
     const float rz = __builtin_amdgcn_rcpf(z);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) av[q] = av[q] * rz;
+    for (int s = 0; s < Q; ++s) av[s] = av[s] * rz;
   } else if (a.score_fn == MOE_SCORE_SQRT_SOFTPLUS) {
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const float l = av[q];
-      const float sp = l > 0.0f ? l + log1pf(expf(-l)) : log1pf(expf(l));
-      av[q] = (p + 16 * q < E) ? sqrtf(sp) : 0.0f;
+    for (int s = 0; s < Q; ++s) {
+      const float l = av[s];
+      const float sp1 = l > 0.0f ? l + log1pf(expf(-l)) : log1pf(expf(l));
+      av[s] = sqrtf(sp1);
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-      av[q] = (p + 16 * q < E) ? __builtin_amdgcn_rcpf(1.0f + __expf(-av[q])) : 0.0f;
+    for (int s = 0; s < Q; ++s) av[s] = __builtin_amdgcn_rcpf(1.0f + __expf(-av[s]));
   }
+  const bool use_beta = a.beta && !hash;
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    const int e = p + 16 * q;
-    key[q] = (e < E) ? av[q] + ((a.beta && !hash) ? a.beta[e] : 0.0f) : -INFINITY;
-    if (a.keys && live && e < E) a.keys[static_cast<size_t>(t) * E + e] = key[q];
+  for (int s = 0; s < Q; ++s)
+    key[s] = av[s] + (use_beta ? a.beta[64 * (s >> 2) + 4 * p + (s & 3)] : 0.0f);
+  if (a.keys && live) {
+#pragma unroll
+    for (int s = 0; s < Q; ++s) a.keys[static_cast<size_t>(t) * EP + 64 * (s >> 2) + 4 * p + (s & 3)] = key[s];
   }
   int my_id = -1;
   float my_a = 0.0f, den = 0.0f;
   if (!hash) {
-    // branch-free selection: a taken (or absent) expert competes with key
-    // -inf, which a real key always beats in the group reduction (E >= k)
+    // branch-free selection: a taken expert competes with key -inf, which a
+    // real key always beats in the group reduction (E >= k)
     uint32_t taken = 0u;
     for (int j = 0; j < k; ++j) {
       float bk = -INFINITY, ba = 0.0f;
       int bi = 0x7fffffff;
 #pragma unroll
-      for (int q = 0; q < Q; ++q) {
-        const int e = p + 16 * q;
-        const float kq = ((taken >> q) & 1u) ? -INFINITY : key[q];
+      for (int s = 0; s < Q; ++s) {
+        const int e = 64 * (s >> 2) + 4 * p + (s & 3);
+        const float kq = ((taken >> s) & 1u) ? -INFINITY : key[s];
         const bool b = (kq > bk) || (kq == bk && e < bi);
         bk = b ? kq : bk;
         bi = b ? e : bi;
-        ba = b ? av[q] : ba;
+        ba = b ? av[s] : ba;
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
@@ -627,7 +637,7 @@ __global__ __launch_bounds__(64) void route_topk_kernel(RouteArgs a, int splits,
           ba = oa;
         }
       }
-      taken |= ((bi & 15) == p) ? (1u << (bi >> 4)) : 0u;
+      taken |= (((bi >> 2) & 15) == p) ? (1u << ((4 * (bi >> 6) + (bi & 3)) & 31)) : 0u;
       den += ba;
       if (p == j) {
         my_id = bi;
@@ -639,13 +649,13 @@ __global__ __launch_bounds__(64) void route_topk_kernel(RouteArgs a, int splits,
     const bool ok_tok = tok >= 0 && tok < a.vocab;
     for (int j = 0; j < k; ++j) {
       int e = ok_tok ? a.tid2eid[static_cast<size_t>(tok) * k + j] : -1;
-      if (e < 0 || e >= E) e = -1;
-      const int qs = e >= 0 ? e >> 4 : 0;
+      if (e < 0 || e >= EP) e = -1;
+      const int se = e >= 0 ? 4 * (e >> 6) + (e & 3) : 0;
       float mine = 0.0f;
 #pragma unroll
-      for (int q = 0; q < Q; ++q)
-        if (q == qs) mine = av[q];
-      float v = __shfl(mine, e >= 0 ? (e & 15) : 0, 16);
+      for (int s = 0; s < Q; ++s)
+        if (s == se) mine = av[s];
+      float v = __shfl(mine, e >= 0 ? ((e >> 2) & 15) : 0, 16);
       if (e < 0) v = 0.0f;
       den += v;
       if (p == j) {
@@ -664,6 +674,7 @@ __global__ __launch_bounds__(64) void route_topk_kernel(RouteArgs a, int splits,
 
 template <int EP>
 hipError_t launch_dma_route(const RouteArgs& a, int bm, int splits, hipStream_t stream) {
+  if (a.E != EP) return hipErrorInvalidValue;  // route_topk_kernel takes E == EP
   const int mtiles = (a.T + bm - 1) / bm;
   if (bm == 128)
     hipLaunchKernelGGL((gate_dma_kernel<EP, 128>), dim3(mtiles, splits), dim3(512), 0, stream, a,
