@@ -258,7 +258,12 @@ int moe_combine(const moe_shape* shape, const void* Yp, const int32_t* dst_row,
  * [source: the layer equation of "Megatron-LM 的 MoE 并行" §模型与入口, computed by
  * the four steps above]
  * gate_weights; with opts == NULL they are inputs (the mega_moe form, which
- * takes the routing as given) and Wg is not read.  Y [T, hidden] out. */
+ * takes the routing as given) and Wg is not read.  Y [T, hidden] out, the
+ * same bits as the four entry points chained.  For BF16 with hidden and
+ * 2*inter multiples of 256 (and, unless both are multiples of 512, at least
+ * 16 rows per expert on average) and T*hidden*2 <= 2^32 - 1, step 3 writes
+ * only the row maps: Linear1 reads each routed row as its token's row of X
+ * (through the row -> token map) instead of from a permuted copy. */
 int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* X,
                 const void* Wg, const moe_expert_weights* weights, int32_t* expert_ids,
                 float* gate_weights, void* Y, void* workspace, size_t workspace_bytes,

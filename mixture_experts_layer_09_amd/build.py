@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "route_plan.cpp", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
+SOURCES = ["moe_api.cpp", "route_plan.cpp", "ffn_plan.cpp", "route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
            "backward.hip"]
 ARCH = "gfx950"
 

@@ -83,6 +83,8 @@ struct GemmArgs {
   const int32_t* tile_off;
   int E, K, Nw, Nout, f, T, n_tiles;
   int chunk;  // DMA kernel: items per XCD chunk (0: one contiguous range per XCD)
+  // DMA kernel, bf16: routed row r is row gather[r] of A (null: row r of A)
+  const int32_t* gather;
 };
 
 template <int PREC>
@@ -837,15 +839,21 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   // offset added per stage) plus a 32-bit per-lane offset.  A: instruction
   // blk covers rows A_RPI blk .. + A_RPI - 1 of the tile (clamped to the
   // segment's last row).
-  const char* a_base = uniform_ptr(Abase + static_cast<size_t>(row0) * a_ld);
+  // A gathered routed rows (bf16): the base is the first token row and each
+  // lane's offset is its row's token times the row pitch (host-checked to
+  // stay below 2^32).
+  const int32_t* gat = nullptr;
+  if constexpr (PREC == MOE_PREC_BF16) gat = shared ? nullptr : g.gather;
+  const char* a_base = uniform_ptr(gat ? Abase : Abase + static_cast<size_t>(row0) * a_ld);
   uint32_t a_voff[A_OPS];
 #pragma unroll
   for (int q = 0; q < A_OPS; ++q) {
     const int blk = (wave * A_OPS + q) % A_INSTS;
     const int r = blk * A_RPI + lane / O::A_CHUNKS;
     const int c = (lane % O::A_CHUNKS) ^ O::swz_a(r);
-    a_voff[q] = static_cast<uint32_t>(min(r, row_end - 1 - row0)) * static_cast<uint32_t>(a_ld) +
-                c * 16;
+    const int rr = min(r, row_end - 1 - row0);
+    const uint32_t row = gat ? static_cast<uint32_t>(gat[row0 + rr]) : static_cast<uint32_t>(rr);
+    a_voff[q] = row * static_cast<uint32_t>(a_ld) + c * 16;
   }
   const char* b_base = uniform_ptr(
       Wbase + static_cast<size_t>(nt) * (SWIGLU ? BN / 2 : BN) * ESZ);
@@ -1663,7 +1671,8 @@ hipError_t run_ffn(const FfnArgs& a, hipStream_t stream) {
   const size_t arow_bytes = PREC == MOE_PREC_MXFP4 ? a.f / 2 : static_cast<size_t>(a.f) * (Q8 ? 1 : 2);
 
   GemmArgs g1{};
-  g1.A = a.Xp;
+  g1.A = a.src_tok ? a.Xs : a.Xp;
+  g1.gather = a.src_tok;
   g1.A_sh = a.Xs;
   g1.a_scale = a.xp_scale;
   g1.a_scale_sh = a.xs_scale;
@@ -1809,6 +1818,7 @@ hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream) {
+  if (a.src_tok && !ffn_gathers(a.precision, a.T, a.h, a.E, a.k, a.f)) return hipErrorInvalidValue;
   const int rows = a.T * a.k;
   if (a.precision == MOE_PREC_F32) {
     const int T_sh = a.has_shared ? a.T : 0;

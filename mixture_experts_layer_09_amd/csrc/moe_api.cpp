@@ -281,6 +281,10 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
     RouteArgs r = route_args(shape, opts, X, Wg, expert_ids, gate_weights, nullptr, ws);
     e = launch_route(r, stream);
   }
+  // Where Linear1 can gather its token rows from X by the row -> token map,
+  // the dispatch writes the row maps only and no permuted copy of X.
+  const bool gather = ffn_gathers(shape->precision, shape->tokens, shape->hidden, shape->experts,
+                                  shape->topk, shape->inter);
   if (e == hipSuccess) {
     PermuteArgs p = permute_args(shape, expert_ids, X, at<int32_t>(ws, L.counts),
                                  at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.dst_row),
@@ -288,6 +292,7 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
                                  fp8 ? at<void>(ws, L.xp_scale) : nullptr,
                                  fp8 ? at<void>(ws, L.Xq) : nullptr,
                                  fp8 ? at<void>(ws, L.x_scale) : nullptr, ws);
+    p.maps_only = gather ? 1 : 0;
     e = launch_permute(p, stream);
   }
   if (e == hipSuccess) {
@@ -295,6 +300,7 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
                          at<int32_t>(ws, L.offsets), fp8 ? at<void>(ws, L.Xq) : X,
                          fp8 ? at<void>(ws, L.x_scale) : nullptr, weights, at<void>(ws, L.Yp),
                          shape->has_shared ? at<void>(ws, L.Ys) : nullptr, ws);
+    if (gather) f.src_tok = at<int32_t>(ws, L.src_tok);
     e = launch_expert_ffn(f, stream);
   }
   if (e == hipSuccess) {

@@ -214,6 +214,7 @@ struct PermuteArgs {
   int32_t* blk_cnt;
   int32_t* local_rank;
   int32_t* flag;
+  int maps_only;  // 1: the row maps dst_row and src_tok only, no rows copied (Xp unused)
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 // launch_permute with the flag, per-block counts and ranks in the library's
@@ -234,8 +235,15 @@ struct FfnArgs {
   void* Aq;
   void* a_scale;
   int32_t* tile_off;
+  // Non-null: Linear1 reads routed row r as token row src_tok[r] of Xs (the
+  // layer input) instead of row r of Xp; only where ffn_gathers() allows it.
+  const int32_t* src_tok;
 };
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream);
+// Whether launch_expert_ffn can take its Linear1 rows from the layer input by
+// the row -> token map (FfnArgs::src_tok) for this shape: bf16 where Linear1
+// runs on the DMA kernel, with every byte offset into X below 2^32.
+bool ffn_gathers(int precision, int T, int h, int E, int k, int f);
 
 struct CombineArgs {
   int T, h, k, precision;

@@ -314,6 +314,26 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   }
 }
 
+// The row maps alone (the dispatch without its row copies, for a consumer
+// that gathers the token rows itself): one thread per assignment i = t k + j,
+// the same destination row as scatter_kernel gives it.
+__global__ __launch_bounds__(256) void row_maps_kernel(int n, int k, int E,
+                                                       const int32_t* __restrict__ ids,
+                                                       const int32_t* __restrict__ blk_base,
+                                                       const int32_t* __restrict__ local_rank,
+                                                       int32_t* __restrict__ dst_row,
+                                                       int32_t* __restrict__ src_tok) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = ids[i];
+  int d = -1;
+  if (e >= 0 && e < E) {
+    d = blk_base[static_cast<size_t>(i / kPermChunk) * E + e] + local_rank[i];
+    src_tok[d] = i / k;
+  }
+  dst_row[i] = d;
+}
+
 __global__ void clear_flag_kernel(int32_t* flag) { flag[0] = 0; }
 
 // The device address of this device's `scratch` (in host code the array's
@@ -373,6 +393,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
                      a.E, a.blk_cnt, a.local_rank, a.flag);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.nblk, a.E, a.blk_cnt,
                      a.counts, a.offsets);
+  if (a.maps_only) {
+    hipLaunchKernelGGL(row_maps_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, a.k, a.E,
+                       a.ids, a.blk_cnt, a.local_rank, a.dst_row, a.src_tok);
+    return hipGetLastError();
+  }
   switch (a.precision) {
     case MOE_PREC_F32:
       hipLaunchKernelGGL(scatter_kernel<MOE_PREC_F32>, dim3(a.T), dim3(256), 0, stream, a.T, a.h,

@@ -13,7 +13,8 @@ tokens the shared expert's Ys, each against the oracle's expert FFN with one
 expert's weights copied to the host at a time.  Checked on sampled tokens:
 the layer output against the oracle, with samples chosen to cover the
 hottest expert's last (ragged) tile, the coldest active experts and the
-shared expert.  A second moe_forward must give bit-identical outputs.
+shared expert.  A second moe_forward must give bit-identical outputs, and
+the same bits as the four entry points chained.
 """
 from __future__ import annotations
 
@@ -194,6 +195,7 @@ def test_full_size_forward(name):
          f"{' and ' + str(len(toks_sh)) + ' shared rows' if wl.shared else ''}: "
          f"max row-relative error {err_rows:.3e}")
     assert err_rows <= TOL[wl.precision]
+    Y_staged = L.combine(Yp, p["dst_row"], G_g, Ys)
     del Yp, Ys
 
     # the whole layer as the benchmark runs it
@@ -207,6 +209,10 @@ def test_full_size_forward(name):
     assert torch.equal(ids_2, ids_f) and torch.equal(G_2, G_f)
     assert torch.equal(Y2.view(torch.uint8), Y.view(torch.uint8))
     del Y2
+    # and the same bits as the four entry points chained (moe_forward of bf16
+    # gathers Linear1's token rows from X instead of writing permuted rows)
+    assert torch.equal(Y.view(torch.uint8), Y_staged.view(torch.uint8))
+    del Y_staged
     counts = d["counts"]
     toks = _sample_tokens(ids, counts)
     _log(f"[full] {name}: oracle on {len(toks)} sampled tokens")

@@ -228,6 +228,27 @@ def test_forward(name):
     assert err <= TOL[wl.precision]
 
 
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_matches_the_four_entry_points(name):
+    """moe_forward against moe_route -> moe_permute -> moe_expert_ffn ->
+    moe_combine on the same inputs: bit-identical.  Where the shape allows it
+    (bf16 on the DMA GEMM), moe_forward writes no permuted rows and Linear1
+    reads the token rows of X through the row -> token map instead, which
+    must change no bit."""
+    _need_gpu()
+    cpu, gpu, L = case(name)
+    _log(f"[forward vs staged] {name}")
+    ids, G, _ = L.route()
+    p = L.permute(ids)
+    Yp, Ys = L.expert_ffn(p)
+    Y_staged = L.combine(Yp, p["dst_row"], G, Ys)
+    Y, ids_f, G_f = L.forward()
+    torch.cuda.synchronize()
+    assert L.device_error() == 0
+    assert torch.equal(ids_f, ids) and torch.equal(G_f, G)
+    assert torch.equal(Y.view(torch.uint8), Y_staged.view(torch.uint8))
+
+
 @pytest.mark.parametrize("name", ["v4pro_small", "tiny_fp32", "v4pro_fp8_small",
                                   "v4pro_int8_small", "v4pro_mxfp8_small", "v4pro_mxfp4_small"])
 def test_forward_with_given_routing(name):

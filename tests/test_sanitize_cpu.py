@@ -1,7 +1,7 @@
 """Sanitizer builds of the host code (no GPU).
 
 - The host side of the C ABI (argument validation, the workspace layout, the
-  router's launch plan) built with AddressSanitizer and UndefinedBehavior-
+  router's launch plan, the expert FFN's gather rule) built with AddressSanitizer and UndefinedBehavior-
   Sanitizer against launcher stubs that read the first and last byte of every
   buffer a launch touches, every "device" buffer a host allocation of the
   size the header documents (tests/sanitize/abi_host_check.cpp).  A planted
@@ -37,6 +37,7 @@ def _build_abi_check(root, out):
            "-fno-omit-frame-pointer", *SAN, "-I", os.path.join(root, "include"),
            os.path.join(root, "mixture_experts_layer_09_amd", "csrc", "moe_api.cpp"),
            os.path.join(root, "mixture_experts_layer_09_amd", "csrc", "route_plan.cpp"),
+           os.path.join(root, "mixture_experts_layer_09_amd", "csrc", "ffn_plan.cpp"),
            os.path.join(root, "tests", "sanitize", "abi_host_check.cpp"), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
@@ -64,6 +65,7 @@ def test_abi_host_check_catches_an_overlapping_region(tmp_path):
     root = tmp_path / "tree"
     for rel in ("include/moe.h", "mixture_experts_layer_09_amd/csrc/moe_api.cpp",
                 "mixture_experts_layer_09_amd/csrc/route_plan.cpp",
+                "mixture_experts_layer_09_amd/csrc/ffn_plan.cpp",
                 "mixture_experts_layer_09_amd/csrc/moe_internal.h",
                 "tests/sanitize/abi_host_check.cpp"):
         dst = root / rel
