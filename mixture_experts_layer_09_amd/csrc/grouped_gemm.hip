@@ -783,13 +783,12 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: DMA targets are SGPRs
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
   // ------------------------------------------------ tile -> segment (as above)
   const int E = g.E;
-  const int NT = g.n_tiles;
   int seg, mtile, nt;
   if (!block_item<BM>(g, seg, mtile, nt)) return;
 
@@ -895,18 +894,26 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     bs_voff = static_cast<uint32_t>(lane / CPR) * static_cast<uint32_t>(g.Nw) + col;
     ops_sc = (wave <= AS_INSTS) ? 1 : 0;
   }
-  const int ops_w = a_live + B_OPS + ops_sc;
+  // Without MX scales every wave issues the same number of DMAs per stage:
+  // A blocks past the segment's last row are fetched too (their rows clamp
+  // to that row, one L2 line), so the vmcnt waits below are constants.
+  constexpr bool CONST_OPS = !MX;
+  constexpr int OPS = A_OPS + B_OPS;
+  const int ops_w = (CONST_OPS ? A_OPS : a_live) + B_OPS + ops_sc;
+  const uint32_t lds0 = lds_address(smem);
   auto issue = [&](int kt, int slot) {
     char* st = smem + slot * STAGE;
+    const uint32_t sl = lds0 + slot * STAGE;
 #pragma unroll
     for (int q = 0; q < A_OPS; ++q) {
       const int blk = (wave * A_OPS + q) % A_INSTS;
-      if (q < a_live) dma16(a_base + static_cast<size_t>(kt) * A_ROW, a_voff[q], st + blk * 1024);
+      if (CONST_OPS || q < a_live)
+        dma16_at(a_base + static_cast<size_t>(kt) * A_ROW, a_voff[q], sl + blk * 1024);
     }
 #pragma unroll
     for (int q = 0; q < B_OPS; ++q) {
       const int blk = wave * B_OPS + q;
-      dma16(b_base + static_cast<size_t>(kt) * BK * w_ld, b_voff[q], st + A_BYTES + blk * 1024);
+      dma16_at(b_base + static_cast<size_t>(kt) * BK * w_ld, b_voff[q], sl + A_BYTES + blk * 1024);
     }
     if constexpr (MX) {
       if (wave < AS_INSTS)
@@ -917,6 +924,17 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     }
   };
 
+  // one of this wave's DMAs of stage kt (q < A_OPS: A, else B)
+  auto issue_op = [&](int kt, int slot, int q) {
+    const uint32_t sl = lds0 + slot * STAGE;
+    if (q < A_OPS) {
+      const int blk = (wave * A_OPS + q) % A_INSTS;
+      dma16_at(a_base + static_cast<size_t>(kt) * A_ROW, a_voff[q], sl + blk * 1024);
+    } else {
+      const int blk = wave * B_OPS + (q - A_OPS);
+      dma16_at(b_base + static_cast<size_t>(kt) * BK * w_ld, b_voff[q - A_OPS], sl + A_BYTES + blk * 1024);
+    }
+  };
   typename O::acc_t acc[MT][NTW];  // fp32, or int32 for INT8
 #pragma unroll
   for (int i = 0; i < MT; ++i)
@@ -980,6 +998,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     }
   };
 
+
   // The K loop is unrolled by STAGES so that every stage slot is a constant
   // LDS range: the compiler then sees DMA targets and operand reads as
   // disjoint and leaves the waiting to the explicit vmcnt below.
@@ -994,9 +1013,13 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
     //   phase 1: half 0 reads stage kt, half 1 multiplies stage kt - 1;
     //   phase 2: half 0 multiplies stage kt, half 1 reads stage kt.
     // Stage kt must be in LDS before phase 1 (vmcnt wait + barrier, as
-    // above); the slot that half 1 read in phase 2 is refilled right after
-    // the next phase-1 barrier, so half 1 waits for its reads (lgkmcnt(0))
-    // before that barrier.
+    // above); the slot that half 1 read in phase 2 is refilled after the
+    // next phase-1 barrier, so half 1 waits for its reads (lgkmcnt(0))
+    // before that barrier.  A wave's DMAs of stage kt + STAGES - 1 go out
+    // one by one between its MFMAs (half 1 in phase 1, half 0 in phase 2):
+    // a DMA can stall at issue while the memory pipeline is full, and a
+    // block of them issued ahead of the MFMAs held those back.
+    static_assert(CONST_OPS, "ping-pong schedule: constant DMA count per wave");
     typename O::frag pb[NTW];
     typename O::frag pa[MT];
     auto load_frags = [&](int slot) {
@@ -1012,6 +1035,20 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
     };
+    // the MFMAs, with this wave's DMAs of stage ikt (slot islot; none if
+    // !more) one after each of the first OPS tile products (measured
+    // against spreading them over all products: 1.5% faster on V4-Pro)
+    static_assert(MT * NTW >= OPS, "a tile product per DMA");
+    auto mma_issue = [&](bool more, int ikt, int islot) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
+          const int idx = i * NTW + j;
+          if (idx < OPS && more) issue_op(ikt, islot, idx);
+        }
+    };
     // each half runs its own copy of the loop (the same barriers in the same
     // order), so that fragments flow from reads to MFMAs without merges
     const bool live = mt_live > 0;
@@ -1021,14 +1058,17 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
         for (int s = 0; s < STAGES; ++s) {
           const int kt = k0 + s;
           if (kt < KT) {
-            wait_vmcnt_rt(min(STAGES - 2, KT - 1 - kt) * ops_w);
+            wait_after<OPS, STAGES - 2>(KT - 1 - kt);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            const bool more = kt + STAGES - 1 < KT;
             if (live) load_frags(s);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (live) mma_frags();
+            if (live)
+              mma_issue(more, kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            else if (more)
+              issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
           }
         }
       }
@@ -1038,11 +1078,15 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
         for (int s = 0; s < STAGES; ++s) {
           const int kt = k0 + s;
           if (kt < KT) {
-            wait_vmcnt_rt(min(STAGES - 2, KT - 1 - kt) * ops_w);
+            wait_after<OPS, STAGES - 2>(KT - 1 - kt);
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
-            if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-            if (live && kt > 0) mma_frags();
+            const bool more = kt + STAGES - 1 < KT;
+            if (live && kt > 0) {
+              mma_issue(more, kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            } else if (more) {
+              issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            }
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             if (live) {
@@ -1061,8 +1105,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
       const int kt = k0 + s;
       if (kt < KT) {
         // stage kt is in LDS once at most the stages issued after it are in flight
-        const int after = min(STAGES - 2, KT - 1 - kt);
-        wait_vmcnt_rt(after * ops_w);
+        if constexpr (CONST_OPS)
+          wait_after<OPS, STAGES - 2>(KT - 1 - kt);
+        else
+          wait_vmcnt_rt(min(STAGES - 2, KT - 1 - kt) * ops_w);
         __builtin_amdgcn_s_barrier();
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
         compute(s, kt);

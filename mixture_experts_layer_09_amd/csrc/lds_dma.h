@@ -103,6 +103,21 @@ __device__ __forceinline__ void wait_vmcnt_rt(int n) {
   }
 }
 
+// Wait until at most min(MAXA, after) * OPS DMAs of this wave are in flight,
+// for a wave-uniform `after` >= 0: the first test is the steady state, so a
+// K-loop stage takes one scalar branch.
+template <int OPS, int MAXA>
+__device__ __forceinline__ void wait_after(int after) {
+  if constexpr (MAXA <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= MAXA)
+      wait_vmcnt<MAXA * OPS>();
+    else
+      wait_after<OPS, MAXA - 1>(after);
+  }
+}
+
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 __device__ __forceinline__ i16x4_t ds_read_tr16(const char* p) {
