@@ -318,16 +318,22 @@ void dgrad_kernel(DgradArgs g) {
     const int r = (wave * B_OPS + q) * 16 + lane / 4;
     b_voff[q] = static_cast<uint32_t>(r) * static_cast<uint32_t>(ld) + ((lane % 4) ^ swz(r)) * 16;
   }
-  const int a_live = __builtin_amdgcn_readfirstlane(max(0, min(A_OPS, (rows_valid + 15) / 16 - wave * A_OPS)));
-  const int ops_w = a_live + B_OPS;
+  // every wave issues OPS DMAs per stage (A blocks past the segment's last
+  // row fetch that row again), so the vmcnt waits are constants; the LDS
+  // targets are scalar
+  constexpr int OPS = A_OPS + B_OPS;
+  const uint32_t lds0 = lds_address(smem);
+  auto issue_op = [&](int kt, int slot, int q) {
+    const uint32_t st = lds0 + slot * STAGE;
+    if (q < A_OPS)
+      dma16_at(a_base + static_cast<size_t>(kt) * ROWB, a_voff[q], st + (wave * A_OPS + q) * 1024);
+    else
+      dma16_at(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q - A_OPS],
+               st + A_BYTES + (wave * B_OPS + q - A_OPS) * 1024);
+  };
   auto issue = [&](int kt, int slot) {
-    char* st = smem + slot * STAGE;
 #pragma unroll
-    for (int q = 0; q < A_OPS; ++q)
-      if (q < a_live) dma16(a_base + static_cast<size_t>(kt) * ROWB, a_voff[q], st + (wave * A_OPS + q) * 1024);
-#pragma unroll
-    for (int q = 0; q < B_OPS; ++q)
-      dma16(b_base + static_cast<size_t>(kt) * ROWB, b_voff[q], st + A_BYTES + (wave * B_OPS + q) * 1024);
+    for (int q = 0; q < OPS; ++q) issue_op(kt, slot, q);
   };
 
   f32x16_t acc[MT][NTW];
@@ -354,6 +360,7 @@ void dgrad_kernel(DgradArgs g) {
       b_off[j][kh] = A_BYTES + r * ROWB + ((ch ^ swz(r)) << 4);
     }
   }
+  static_assert(2 * MT * NTW >= OPS, "an MFMA per DMA");
   auto compute = [&](int slot) {
     if (mt_live == 0) return;
     const char* st = smem + slot * STAGE;
@@ -365,13 +372,20 @@ void dgrad_kernel(DgradArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) af[i][kh] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][kh]);
     }
+    // Without the SwiGLU backward, the transposed product (weight fragment
+    // first): element v of lane l is row l % 32 of the tile and column
+    // 8 (v / 4) + 4 (l / 32) + v % 4, stored 4 columns at a time.  With it,
+    // element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
+    // l % 32: the H1 reads and dH1 writes of a wave instruction then cover 2
+    // rows x 64 bytes instead of 32 rows x 16 bytes (measured 17% faster).
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][kh], bfr[j][kh], acc[i][j], 0, 0, 0);
+          acc[i][j] = SWB ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][kh], bfr[j][kh], acc[i][j], 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][kh], af[i][kh], acc[i][j], 0, 0, 0);
   };
 
   const int KT = g.K / 32;
@@ -384,8 +398,7 @@ void dgrad_kernel(DgradArgs g) {
       const int kt = k0 + s;
       if (kt < KT) {
         // stage kt is in LDS once at most the stages issued after it are in flight
-        const int after = min(STAGES - 2, KT - 1 - kt);
-        wait_vmcnt_rt(after * ops_w);
+        wait_after<OPS, STAGES - 2>(KT - 1 - kt);
         __builtin_amdgcn_s_barrier();
         if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
         compute(s);
@@ -395,20 +408,20 @@ void dgrad_kernel(DgradArgs g) {
 
   // ------------------------------------------------ epilogue
   uint16_t* obase = static_cast<uint16_t*>(shared ? g.out_sh : g.out);
-  const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
-  const int col_in = lane & 31;
+  if constexpr (SWB) {
+    const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
+    const int col_in = lane & 31;
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    if (i >= mt_live) continue;
+    for (int i = 0; i < MT; ++i) {
+      if (i >= mt_live) continue;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = row0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (row >= row_end) continue;
+      for (int v = 0; v < 16; ++v) {
+        const int row = row0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row >= row_end) continue;
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        const int n = nt * BN + wn * WN + j * 32 + col_in;
-        const float d = acc[i][j][v];
-        if constexpr (SWB) {
+        for (int j = 0; j < NTW; ++j) {
+          const int n = nt * BN + wn * WN + j * 32 + col_in;
+          const float d = acc[i][j][v];
           // dH = d; H1 = (gate G, up U); A = SiLU(G): dU = dH * A and
           // dG = dH * U * (sigma(G) + A (1 - sigma(G)))
           const size_t rb = static_cast<size_t>(row) * 2 * g.N;
@@ -417,9 +430,29 @@ void dgrad_kernel(DgradArgs g) {
           const float act = gt * sg;
           obase[rb + n] = f32_to_bf16(d * up * (sg + act * (1.0f - sg)));
           obase[rb + g.N + n] = f32_to_bf16(d * act);
-        } else {
-          obase[static_cast<size_t>(row) * g.N + n] = f32_to_bf16(d);
         }
+      }
+    }
+    return;
+  }
+  // lane l holds row l % 32 of row tile i; 4 consecutive columns
+  // 8 q + 4 (l / 32) + 0..3 of each n-tile leave as one 8-byte store
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    if (i >= mt_live) continue;  // wave-uniform
+    const int row = row0 + wm * WM + i * 32 + (lane & 31);
+    if (row >= row_end) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int j = 0; j < NTW; ++j) {
+        const int n = nt * BN + wn * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+        uint32_t w[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          w[e] = static_cast<uint32_t>(f32_to_bf16(acc[i][j][4 * q + 2 * e])) |
+                 (static_cast<uint32_t>(f32_to_bf16(acc[i][j][4 * q + 2 * e + 1])) << 16);
+        *reinterpret_cast<uint2*>(obase + static_cast<size_t>(row) * g.N + n) = make_uint2(w[0], w[1]);
       }
     }
   }
