@@ -778,11 +778,6 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   // ping-pong K loop for two row halves of 4 waves (see the K loop); bf16
   // only (measured: V4-Pro bf16 0.7% faster, e4m3 0.6% slower)
   constexpr bool PP = (NW == 8) && (WAVES_M == 2) && PREC == MOE_PREC_BF16;
-  // bf16 multiplies the transposed tile (weight fragment as the MFMA's first
-  // operand): a lane then holds one row and 4 groups of 4 consecutive
-  // columns, which leave as 8-byte stores (measured: the 2-byte stores of
-  // the other layout cost the V4-Pro stage about 1 ms)
-  constexpr bool TRANS = PREC == MOE_PREC_BF16;
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
@@ -999,8 +994,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = TRANS ? O::mma(bfr[j], af[i], acc[i][j]) : O::mma(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -1039,8 +1033,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
-          acc[i][j] = TRANS ? O::mma(pb[j], pa[i], acc[i][j]) : O::mma(pa[i], pb[j], acc[i][j]);
+        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
     };
     // the MFMAs, with this wave's DMAs of stage ikt (slot islot; none if
     // !more) one after each of the first OPS tile products (measured
@@ -1051,7 +1044,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          acc[i][j] = TRANS ? O::mma(pb[j], pa[i], acc[i][j]) : O::mma(pa[i], pb[j], acc[i][j]);
+          acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
           const int idx = i * NTW + j;
           if (idx < OPS && more) issue_op(ikt, islot, idx);
         }
@@ -1124,17 +1117,6 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------ epilogue
-#ifdef MOE_EXP_NOEPI
-  {
-    float t = 0.f;
-#pragma unroll
-    for (int a = 0; a < MT; ++a)
-#pragma unroll
-      for (int b = 0; b < NTW; ++b) t += static_cast<float>(acc[a][b][0]);
-    if (t == 1.2345e30f) reinterpret_cast<float*>(obase)[lane] = t;
-    return;
-  }
-#endif
   const int col_in = O::col_of(lane);
   if constexpr (MX && SWIGLU && TM == 32) {
     // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
@@ -1192,46 +1174,6 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
             orow[c0 + 16 + col_in] = static_cast<uint8_t>(f32_to_e4m3(u1 * inv));
             if (col_in == 0)
               osc8[static_cast<size_t>(row) * (g.Nout / 32) + c0 / 32] = static_cast<uint8_t>(code);
-          }
-        }
-      }
-    }
-    return;
-  }
-  if constexpr (TRANS) {
-    // element v of lane l: row l % 32 of the tile, column O::row_of(l, v)
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      if (i >= mt_live) continue;  // wave-uniform
-      const int row = row0 + wm * WM + i * TM + (lane & 31);
-      if (row >= row_end) continue;
-      uint16_t* orow = reinterpret_cast<uint16_t*>(obase) + static_cast<size_t>(row) * g.Nout;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {  // columns 8 q + 4 (l / 32) + 0..3 of each tile
-        const int c = 8 * q + 4 * (lane >> 5);
-        if (SWIGLU) {
-#pragma unroll
-          for (int j = 0; j < NTW / 2; ++j) {
-            uint32_t w[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const float u0 = silu(acc[i][j][4 * q + 2 * e]) * acc[i][j + NTW / 2][4 * q + 2 * e];
-              const float u1 =
-                  silu(acc[i][j][4 * q + 2 * e + 1]) * acc[i][j + NTW / 2][4 * q + 2 * e + 1];
-              w[e] = static_cast<uint32_t>(f32_to_bf16(u0)) |
-                     (static_cast<uint32_t>(f32_to_bf16(u1)) << 16);
-            }
-            *reinterpret_cast<uint2*>(orow + nt * (BN / 2) + bcol(j) + c) = make_uint2(w[0], w[1]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) {
-            uint32_t w[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-              w[e] = static_cast<uint32_t>(f32_to_bf16(acc[i][j][4 * q + 2 * e])) |
-                     (static_cast<uint32_t>(f32_to_bf16(acc[i][j][4 * q + 2 * e + 1])) << 16);
-            *reinterpret_cast<uint2*>(orow + nt * BN + bcol(j) + c) = make_uint2(w[0], w[1]);
           }
         }
       }
@@ -1877,10 +1819,6 @@ hipError_t dispatch_ffn(const FfnArgs& a, hipStream_t stream) {
     // stage in flight (measured: decode 3.8% faster, V4-Pro prefill 2% slower).
     if (w512 && static_cast<long>(rows) < 16L * a.E)
       return run_ffn<PREC, 128, 512, 2, 4, 4>(a, stream);
-#ifdef MOE_EXP_ST4
-    if (w512 && static_cast<long>(rows) < 256L * a.E)
-      return run_ffn<PREC, 128, 512, 2, 4, 4>(a, stream);
-#endif
     if (w512 && static_cast<long>(rows) < 256L * a.E)
       return run_ffn<PREC, 128, 512, 2, 4, 3>(a, stream);
     return run_ffn<PREC, 128, 256, 2, 2, 3>(a, stream);
