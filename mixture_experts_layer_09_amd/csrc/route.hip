@@ -408,17 +408,23 @@ void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
       ++ops;
     }
   }
-  auto issue = [&](int kt, int slot) {
-    char* st = smem + slot * STAGE;
-#pragma unroll
-    for (int i = 0; i < MAX_OPS; ++i) {
-      const int q = wave + i * NW;
-      if (q < A_INSTS)
-        dma16(a_base + static_cast<size_t>(kt) * A_ROW, voff[i], st + q * 1024);
-      else if (q < INSTS)
-        dma16(b_base + static_cast<size_t>(kt) * BK * w_ld, voff[i], st + q * 1024);
-    }
+  // DMA i of this wave for stage kt into ring slot `slot` (scalar LDS target)
+  const uint32_t lds0 = lds_address(smem);
+  auto issue_op = [&](int kt, int slot, int i) {
+    const uint32_t st = lds0 + slot * STAGE;
+    const int q = wave + i * NW;
+    if (q < A_INSTS)
+      dma16_at(a_base + static_cast<size_t>(kt) * A_ROW, voff[i], st + q * 1024);
+    else if (q < INSTS)
+      dma16_at(b_base + static_cast<size_t>(kt) * BK * w_ld, voff[i], st + q * 1024);
   };
+  auto issue = [&](int kt, int slot) {
+#pragma unroll
+    for (int i = 0; i < MAX_OPS; ++i) issue_op(kt, slot, i);
+  };
+  // with INSTS a multiple of the wave count every wave issues MAX_OPS DMAs
+  // per stage and the vmcnt waits are constants
+  constexpr bool EVEN = INSTS % NW == 0;
   // fragment offsets (within a stage): A rows wm * BM / 2 + 32 i + lane % 32;
   // B columns of this wave's NTW tiles
   int a_off[MT][2];
@@ -456,7 +462,12 @@ void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
     const i16x8_t v = i16x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     return __builtin_bit_cast(bf16x8_t, v);
   };
-  auto compute = [&](int slot) {
+  // the stage's MFMAs; with EVEN, this wave's DMAs of stage ikt (slot islot;
+  // none if !more) go out one after each of the first MAX_OPS tile products:
+  // a DMA can stall at issue while the memory pipeline is full, and ahead
+  // of the MFMAs it would hold them back
+  auto compute = [&](int slot, bool more, int ikt, int islot) {
+    if (!EVEN && more) issue(ikt, islot);
     const char* st = smem + slot * STAGE;
     bf16x8_t bk0[NTW], bk1[NTW];
 #pragma unroll
@@ -472,9 +483,12 @@ void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
       for (int j = 0; j < NTW; ++j) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak0, bk0[j], acc[i][j], 0, 0, 0);
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak1, bk1[j], acc[i][j], 0, 0, 0);
+        const int idx = i * NTW + j;
+        if (EVEN && idx < MAX_OPS && more) issue_op(ikt, islot, idx);
       }
     }
   };
+  static_assert(!EVEN || MT * NTW >= MAX_OPS, "a tile product per DMA");
   // K loop, unrolled by STAGES so that every slot is a constant LDS range
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
@@ -484,11 +498,12 @@ void gate_dma_kernel(RouteArgs a, int kchunk, float* __restrict__ part) {
     for (int s = 0; s < STAGES; ++s) {
       const int kt = kt0 + s;
       if (kt < KT) {
-        const int after = min(STAGES - 2, KT - 1 - kt);
-        wait_vmcnt_rt(after * ops);
+        if constexpr (EVEN)
+          wait_after<MAX_OPS, STAGES - 2>(KT - 1 - kt);
+        else
+          wait_vmcnt_rt(min(STAGES - 2, KT - 1 - kt) * ops);
         __builtin_amdgcn_s_barrier();
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-        compute(s);
+        compute(s, kt + STAGES - 1 < KT, kt + STAGES - 1, (s + STAGES - 1) % STAGES);
       }
     }
   }
