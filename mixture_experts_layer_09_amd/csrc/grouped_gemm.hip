@@ -1033,7 +1033,7 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
+        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(pb[j], pa[i], acc[i][j]);
     };
     // the MFMAs, with this wave's DMAs of stage ikt (slot islot; none if
     // !more) one after each of the first OPS tile products (measured
@@ -1044,13 +1044,17 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          acc[i][j] = O::mma(pa[i], pb[j], acc[i][j]);
+          acc[i][j] = O::mma(pb[j], pa[i], acc[i][j]);
           const int idx = i * NTW + j;
           if (idx < OPS && more) issue_op(ikt, islot, idx);
         }
     };
-    // each half runs its own copy of the loop (the same barriers in the same
-    // order), so that fragments flow from reads to MFMAs without merges
+    // The products are transposed (weight fragment first): element v of lane
+    // l is row l % 32 of the row tile and column O::row_of(l, v) of the
+    // n-tile, i.e. 4 groups of 4 consecutive columns, for the staged
+    // epilogue below.  Each half runs its own copy of the loop (the same
+    // barriers in the same order), so that fragments flow from reads to
+    // MFMAs without merges.
     const bool live = mt_live > 0;
     if (__builtin_amdgcn_readfirstlane(wm) == 0) {
       for (int k0 = 0; k0 < KT; k0 += STAGES) {
@@ -1117,6 +1121,59 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------ epilogue
+  if constexpr (PP) {
+    // Staged through LDS so that the tile leaves as whole 128-byte lines.
+    // Once a wave is past the first barrier of the last stage, no wave reads
+    // the ring slots of stages KT - 2 and KT - 3 again and no DMA writes
+    // them: waves 0-3 stage in the first, waves 4-7 in the second, 8 KB
+    // each (64 rows x 64 columns of bf16; 16-byte chunk c of row r at
+    // c ^ ((r >> 1) & 7), which keeps the 8-byte writes and the 16-byte
+    // reads free of bank conflicts).  A pass writes 64 columns: the SwiGLU
+    // output of the wave's gate/up tile pairs, or two of its n-tiles.
+    static_assert(WM == 64 && TM == 32 && MT == 2 && (SWIGLU ? NTW == 4 : NTW % 2 == 0), "wave tile");
+    if (mt_live == 0) return;
+    const int sslot = ((KT - 2 - (wave >> 2)) % STAGES + STAGES) % STAGES;
+    char* wst = smem + sslot * STAGE + (wave & 3) * 8192;
+    const int ml = lane & 31;
+    constexpr int PASSES = SWIGLU ? 1 : NTW / 2;
+#pragma unroll
+    for (int pass = 0; pass < PASSES; ++pass) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int r = i * TM + ml;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = SWIGLU ? jj : 2 * pass + jj;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float v4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[i][j][4 * q + e];
+              v4[e] = SWIGLU ? silu(x) * acc[i][j + NTW / 2][4 * q + e] : x;
+            }
+            const int c = 4 * jj + q;  // 16-byte chunk: columns 8 c .. 8 c + 7 of the pass
+            *reinterpret_cast<uint2*>(wst + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + (lane >> 5) * 8) =
+                make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+          }
+        }
+      }
+      // a wave's LDS operations run in order: its reads see its writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int cbase = SWIGLU ? nt * (BN / 2) + bcol(0) : nt * BN + bcol(2 * pass);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = (lane >> 3) + 8 * k, ch = lane & 7;
+        const uint4 w = *reinterpret_cast<const uint4*>(wst + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
+        const int row = row0 + wm * WM + r;
+        if (row < row_end)
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(obase) + static_cast<size_t>(row) * g.Nout +
+                                    cbase + ch * 8) = w;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
+    }
+    return;
+  }
   const int col_in = O::col_of(lane);
   if constexpr (MX && SWIGLU && TM == 32) {
     // SwiGLU, then MX quantisation in groups of 32 output columns: a group is
