@@ -778,6 +778,10 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   // ping-pong K loop for two row halves of 4 waves (see the K loop); bf16
   // only (measured: V4-Pro bf16 0.7% faster, e4m3 0.6% slower)
   constexpr bool PP = (NW == 8) && (WAVES_M == 2) && PREC == MOE_PREC_BF16;
+  // the ping-pong tile, and the 8-bit A8W8 128 x 512 tile: transposed
+  // products and an epilogue staged through LDS (see the epilogue)
+  constexpr bool STAGED =
+      PP || (A8W8 && BM == 128 && BN == 512 && NW == 8 && WAVES_M == 2 && O::TM == 32);
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
@@ -994,7 +998,8 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) acc[i][j] = O::mma(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < NTW; ++j)
+          acc[i][j] = STAGED ? O::mma(bfr[j], af[i], acc[i][j]) : O::mma(af[i], bfr[j], acc[i][j]);
     }
   };
 
@@ -1121,54 +1126,84 @@ void grouped_gemm_dma_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------ epilogue
-  if constexpr (PP) {
+  if constexpr (STAGED) {
     // Staged through LDS so that the tile leaves as whole 128-byte lines.
     // Once a wave is past the first barrier of the last stage, no wave reads
     // the ring slots of stages KT - 2 and KT - 3 again and no DMA writes
     // them: waves 0-3 stage in the first, waves 4-7 in the second, 8 KB
-    // each (64 rows x 64 columns of bf16; 16-byte chunk c of row r at
-    // c ^ ((r >> 1) & 7), which keeps the 8-byte writes and the 16-byte
-    // reads free of bank conflicts).  A pass writes 64 columns: the SwiGLU
-    // output of the wave's gate/up tile pairs, or two of its n-tiles.
-    static_assert(WM == 64 && TM == 32 && MT == 2 && (SWIGLU ? NTW == 4 : NTW % 2 == 0), "wave tile");
+    // each (64 rows x 128 bytes; 16-byte chunk c of row r at
+    // c ^ ((r >> 1) & 7), which keeps the writes and the 16-byte reads free
+    // of bank conflicts).  A pass is 128 bytes of each of the wave's 64
+    // rows: 64 bf16 columns (the SwiGLU output of its gate/up tile pairs,
+    // or two of its n-tiles) or 32 fp32 columns (the A8W8 SwiGLU output of
+    // one gate/up pair).
+    static_assert(WM == 64 && TM == 32 && MT == 2 && NTW == 4, "wave tile");
     if (mt_live == 0) return;
     const int sslot = ((KT - 2 - (wave >> 2)) % STAGES + STAGES) % STAGES;
     char* wst = smem + sslot * STAGE + (wave & 3) * 8192;
     const int ml = lane & 31;
-    constexpr int PASSES = SWIGLU ? 1 : NTW / 2;
+    constexpr bool F32OUT = A8W8 && SWIGLU;
+    constexpr int PASSES = SWIGLU ? (F32OUT ? 2 : 1) : 2;
+    float rs[MT];  // A8W8: the rows' activation scales
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = min(row0 + wm * WM + i * TM + ml, row_end - 1);
+      rs[i] = A8W8 ? asc[row] : 1.0f;
+    }
 #pragma unroll
     for (int pass = 0; pass < PASSES; ++pass) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         const int r = i * TM + ml;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = SWIGLU ? jj : 2 * pass + jj;
+        for (int jj = 0; jj < (F32OUT ? 1 : 2); ++jj) {
+          const int j = F32OUT ? pass : (SWIGLU ? jj : 2 * pass + jj);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
+            // columns 8 q + 4 (l / 32) + 0..3 of tile j
             float v4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float x = acc[i][j][4 * q + e];
-              v4[e] = SWIGLU ? silu(x) * acc[i][j + NTW / 2][4 * q + e] : x;
+              float x = static_cast<float>(acc[i][j][4 * q + e]);
+              if (SWIGLU) {
+                float u = static_cast<float>(acc[i][j + NTW / 2][4 * q + e]);
+                if (A8W8) {
+                  const int ncol = nt * (BN / 2) + bcol(j) + 8 * q + 4 * (lane >> 5) + e;
+                  x *= wsc[ncol] * rs[i];
+                  u *= wsc[g.f + ncol] * rs[i];
+                }
+                v4[e] = silu(x) * u;
+              } else {
+                if (A8W8) x *= wsc[nt * BN + bcol(j) + 8 * q + 4 * (lane >> 5) + e] * rs[i];
+                v4[e] = x;
+              }
             }
-            const int c = 4 * jj + q;  // 16-byte chunk: columns 8 c .. 8 c + 7 of the pass
-            *reinterpret_cast<uint2*>(wst + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + (lane >> 5) * 8) =
-                make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+            if constexpr (F32OUT) {
+              const int c = 2 * q + (lane >> 5);  // 16-byte chunk of the pass's 128 bytes
+              *reinterpret_cast<float4*>(wst + r * 128 + ((c ^ ((r >> 1) & 7)) << 4)) =
+                  make_float4(v4[0], v4[1], v4[2], v4[3]);
+            } else {
+              const int c = 4 * jj + q;
+              *reinterpret_cast<uint2*>(wst + r * 128 + ((c ^ ((r >> 1) & 7)) << 4) + (lane >> 5) * 8) =
+                  make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+            }
           }
         }
       }
       // a wave's LDS operations run in order: its reads see its writes
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      const int cbase = SWIGLU ? nt * (BN / 2) + bcol(0) : nt * BN + bcol(2 * pass);
+      // first output column of the pass and bytes per output element
+      const int cbase = F32OUT ? nt * (BN / 2) + bcol(pass)
+                               : (SWIGLU ? nt * (BN / 2) + bcol(0) : nt * BN + bcol(2 * pass));
+      constexpr int OB = F32OUT ? 4 : 2;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int r = (lane >> 3) + 8 * k, ch = lane & 7;
         const uint4 w = *reinterpret_cast<const uint4*>(wst + r * 128 + ((ch ^ ((r >> 1) & 7)) << 4));
         const int row = row0 + wm * WM + r;
         if (row < row_end)
-          *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(obase) + static_cast<size_t>(row) * g.Nout +
-                                    cbase + ch * 8) = w;
+          *reinterpret_cast<uint4*>(static_cast<char*>(obase) +
+                                    (static_cast<size_t>(row) * g.Nout + cbase) * OB + ch * 16) = w;
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
     }
