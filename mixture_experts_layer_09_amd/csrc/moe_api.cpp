@@ -198,9 +198,8 @@ int moe_permute(const moe_shape* shape, const int32_t* expert_ids, const void* X
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
   PermuteArgs a = permute_args(shape, expert_ids, X, counts, offsets, dst_row, src_tok, Xp,
                                xp_scale, Xq, x_scale, workspace);
-  hipError_t e = launch_clear_flag(a.flag, stream);
-  if (e == hipSuccess) e = launch_permute(a, stream);
-  return hip_status(e);
+  a.clear_flag = 1;  // the call's only step that can raise the flag
+  return hip_status(launch_permute(a, stream));
 }
 
 int moe_permute_no_alloc(const moe_shape* shape, const int32_t* expert_ids, const void* X,
@@ -275,9 +274,10 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
   const Layout L = make_layout(*shape);
   void* ws = workspace;
   const bool fp8 = shape->precision >= MOE_PREC_FP8;  // quantised activations
-  int32_t* flag = at<int32_t>(ws, L.flag);
-  hipError_t e = launch_clear_flag(flag, stream);
-  if (e == hipSuccess && opts) {
+  // the router clears the error flag when it starts; without it the
+  // dispatch is the first step that can raise it and writes it whole
+  hipError_t e = hipSuccess;
+  if (opts) {
     RouteArgs r = route_args(shape, opts, X, Wg, expert_ids, gate_weights, nullptr, ws);
     e = launch_route(r, stream);
   }
@@ -293,6 +293,7 @@ int moe_forward(const moe_shape* shape, const moe_route_opts* opts, const void* 
                                  fp8 ? at<void>(ws, L.Xq) : nullptr,
                                  fp8 ? at<void>(ws, L.x_scale) : nullptr, ws);
     p.maps_only = gather ? 1 : 0;
+    p.clear_flag = opts ? 0 : 1;
     e = launch_permute(p, stream);
   }
   if (e == hipSuccess) {

@@ -129,7 +129,7 @@ size_t route_partial_bytes(int T, int h, int E, int precision);
 
 // Byte offsets of every region inside the caller's workspace.
 struct Layout {
-  size_t flag;        // int32 error flag (+ padding to 256 B)
+  size_t flag;        // int32 error flag, then one error byte per counting block (padded to 256 B)
   size_t part;        // router: fp32 partial logits [splits, T, E]
   size_t blk_cnt;     // [nblk, E] int32 per-block expert counts
   size_t local_rank;  // [T*k] int32 rank of an assignment inside its block
@@ -154,7 +154,7 @@ inline Layout make_layout(const moe_shape& s) {
     o = align_up(o + bytes);
     return at;
   };
-  L.flag = take(kAlign);
+  L.flag = take(4 + static_cast<size_t>(L.nblk));  // flag word + the dispatch's per-block error bytes
   L.part = take(route_partial_bytes(s.tokens, s.hidden, s.experts, s.precision));
   L.blk_cnt = take(static_cast<size_t>(L.nblk) * E * 4);
   L.local_rank = take(rows * 4);
@@ -215,6 +215,7 @@ struct PermuteArgs {
   int32_t* local_rank;
   int32_t* flag;
   int maps_only;  // 1: the row maps dst_row and src_tok only, no rows copied (Xp unused)
+  int clear_flag;  // 1: the dispatch writes the error flag (clear unless a bad id); 0: only sets it
 };
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 // launch_permute with the flag, per-block counts and ranks in the library's

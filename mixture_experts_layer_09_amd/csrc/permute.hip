@@ -46,15 +46,17 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t*
                                                                   int n, int E,
                                                                   int32_t* __restrict__ blk_cnt,
                                                                   int32_t* __restrict__ local_rank,
-                                                                  int32_t* __restrict__ flag) {
+                                                                  uint8_t* __restrict__ blk_err) {
   constexpr int kGroups = kPermChunk / 64;  // groups of 64 assignments
   constexpr int kRounds = kPermChunk / kPermThreads;
   __shared__ int32_t s_cnt[kGroups][kMaxExperts];
+  __shared__ int s_err;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int base = blockIdx.x * kPermChunk;
   for (int x = tid; x < kGroups * kMaxExperts; x += kPermThreads) (&s_cnt[0][0])[x] = 0;
+  if (tid == 0) s_err = 0;
   int e[kRounds], rank[kRounds];
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -62,14 +64,14 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t*
     int v = -1;
     if (i < n) {
       v = ids[i];
-      if (v < 0 || v >= E) {
-        flag[0] = 1;  // every writer stores the same value
-        v = -1;
-      }
+      if (v < 0 || v >= E) v = -1;
     }
     e[r] = v;
   }
-  __syncthreads();  // s_cnt cleared
+  __syncthreads();  // s_cnt and s_err cleared
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r)
+    if (e[r] < 0 && base + r * kPermThreads + tid < n) s_err = 1;  // every writer stores 1
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     // rank among the group's earlier lanes with the same expert, and the
@@ -86,6 +88,8 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t*
     if (e[r] >= 0 && rk == cnt - 1) s_cnt[r * (kPermThreads / 64) + wave][e[r]] = cnt;
   }
   __syncthreads();
+  // this block's error byte (an expert id outside [0, E)), for the scan
+  if (tid == 0) blk_err[blockIdx.x] = static_cast<uint8_t>(s_err);
   // per expert: exclusive scan over the groups, in group order
   for (int x = tid; x < E; x += kPermThreads) {
     int run = 0;
@@ -107,13 +111,24 @@ __global__ __launch_bounds__(kPermThreads) void count_rank_kernel(const int32_t*
 
 // One block of 512 threads; E <= 512, one thread per expert.  The loops over
 // the per-block counts load 8 blocks at a time so that the loads overlap.
+// The prefix over the experts is a shuffle scan inside each wave plus the
+// earlier waves' totals.  The device error flag: set when a counting block
+// saw an expert id outside [0, E); with `clear` it is written either way
+// (the dispatch is then the first step of its call that can raise it).
 __global__ __launch_bounds__(kMaxExperts) void scan_kernel(int nblk, int E,
                                                            int32_t* __restrict__ blk_cnt,
                                                            int32_t* __restrict__ counts,
-                                                           int32_t* __restrict__ offsets) {
-  __shared__ int32_t s[kMaxExperts];
+                                                           int32_t* __restrict__ offsets,
+                                                           const uint8_t* __restrict__ blk_err,
+                                                           int32_t* __restrict__ flag, int clear) {
+  __shared__ int32_t s_wave[kMaxExperts / 64];
   constexpr int U = 8;
   const int e = threadIdx.x;
+  const int lane = e & 63, wave = e >> 6;
+  int my_err = 0;
+  for (int b = e; b < nblk; b += kMaxExperts) my_err |= blk_err[b];
+  const int err = __syncthreads_or(my_err);
+  if (e == 0 && (clear || err)) flag[0] = err ? 1 : 0;
   int total = 0;
   if (e < E) {
     int b = 0;
@@ -126,20 +141,21 @@ __global__ __launch_bounds__(kMaxExperts) void scan_kernel(int nblk, int E,
     }
     for (; b < nblk; ++b) total += blk_cnt[static_cast<size_t>(b) * E + e];
   }
-  s[e] = (e < E) ? total : 0;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over the experts
-  for (int o = 1; o < kMaxExperts; o <<= 1) {
-    int v = (e >= o) ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
+  // inclusive scan over the experts: inside the wave, then the waves before
+  int incl = total;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
   }
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) incl += s_wave[w];
   if (e < E) {
-    int off = s[e] - total;
+    int off = incl - total;
     counts[e] = total;
     offsets[e] = off;
-    if (e == E - 1) offsets[E] = s[e];
+    if (e == E - 1) offsets[E] = incl;
     int run = off;
     int b = 0;
     for (; b + U <= nblk; b += U) {
@@ -375,11 +391,11 @@ hipError_t launch_permute_no_alloc(PermuteArgs a, hipStream_t stream) {
   a.flag = reinterpret_cast<int32_t*>(s);
   a.blk_cnt = reinterpret_cast<int32_t*>(s + kNoAllocFlagBytes);
   a.local_rank = reinterpret_cast<int32_t*>(s + kNoAllocFlagBytes + kNoAllocBlkBytes);
-  // the flag is cleared by a kernel (no memset node under graph capture);
-  // the counts and ranks are written whole by every call before they are read
-  e = launch_clear_flag(a.flag, stream);
-  if (e == hipSuccess) e = launch_permute(a, stream);
-  return e;
+  // the flag is written by the scan kernel (no memset node under graph
+  // capture); the counts, ranks and error bytes are written whole by every
+  // call before they are read
+  a.clear_flag = 1;
+  return launch_permute(a, stream);
 }
 
 hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
@@ -389,10 +405,12 @@ hipError_t launch_clear_flag(int32_t* flag, hipStream_t stream) {
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const int n = a.T * a.k;
+  // the per-block error bytes follow the flag word in its region
+  uint8_t* blk_err = reinterpret_cast<uint8_t*>(a.flag + 1);
   hipLaunchKernelGGL(count_rank_kernel, dim3(a.nblk), dim3(kPermThreads), 0, stream, a.ids, n,
-                     a.E, a.blk_cnt, a.local_rank, a.flag);
+                     a.E, a.blk_cnt, a.local_rank, blk_err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kMaxExperts), 0, stream, a.nblk, a.E, a.blk_cnt,
-                     a.counts, a.offsets);
+                     a.counts, a.offsets, blk_err, a.flag, a.clear_flag);
   if (a.maps_only) {
     hipLaunchKernelGGL(row_maps_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n, a.k, a.E,
                        a.ids, a.blk_cnt, a.local_rank, a.dst_row, a.src_tok);

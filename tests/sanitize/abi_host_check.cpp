@@ -105,18 +105,20 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t) {
   }
   touch(a.blk_cnt, static_cast<size_t>(a.nblk) * E * 4);
   touch(a.local_rank, n * 4);
-  touch(a.flag, 4);
+  touch(a.flag, 4 + static_cast<size_t>(a.nblk));  // flag word + per-block error bytes
+  if (a.clear_flag) *a.flag = 0;  // what the scan kernel writes when no id was bad
   ++g_launches;
   return hipSuccess;
 }
 
 hipError_t launch_permute_no_alloc(PermuteArgs a, hipStream_t stream) {
   // the kernels' scratch is the library's static array, not a workspace
-  static int32_t flag;
-  static std::vector<int32_t> blk, rank;
+  static std::vector<int32_t> flag, blk, rank;
+  flag.assign(1 + (static_cast<size_t>(a.nblk) + 3) / 4, 0);  // flag word + error bytes
   blk.assign(static_cast<size_t>(a.nblk) * a.E, 0);
   rank.assign(static_cast<size_t>(a.T) * a.k, 0);
-  a.flag = &flag;
+  a.flag = flag.data();
+  a.clear_flag = 1;
   a.blk_cnt = blk.data();
   a.local_rank = rank.data();
   return launch_permute(a, stream);
