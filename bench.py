@@ -251,15 +251,16 @@ def copy_probe(nbytes: int, reps: int = 5):
 
 
 def backward_work(wl, counts):
-    """FLOPs and HBM bytes the local backward must do: the recomputed forward
-    (Linear1 and Linear2 over every row), the dgrad and wgrad of both linears
-    (each the forward's FLOPs again) and the router's two GEMMs; bytes: the
-    active experts' weights read once and their gradients written once, X
-    and dY read, dX written, the router's gradient."""
+    """FLOPs and HBM bytes the local backward must do: the recomputed Linear1
+    over every row (dG comes out of Linear2's dgrad, so Linear2's forward is
+    not recomputed), the dgrad and wgrad of both linears (each the forward's
+    FLOPs again) and the router's two GEMMs; bytes: the active experts'
+    weights read once and their gradients written once, X and dY read, dX
+    written, the router's gradient."""
     h, f, k, T, E = wl.hidden, wl.inter, wl.topk, wl.T, wl.experts
     rows = T * k + (T if wl.shared else 0)
     fwd = 2.0 * rows * (h * 2 * f + f * h)
-    flops = 3.0 * fwd + 2 * (2.0 * T * h * E)
+    flops = 2.0 * rows * h * 2 * f + 2.0 * fwd + 2 * (2.0 * T * h * E)
     active = int((counts > 0).sum()) + (1 if wl.shared else 0)
     nbytes = 2 * active * 3.0 * h * f * 2 + 3 * T * h * 2 + 2 * h * E * 2
     return flops, nbytes

@@ -290,16 +290,18 @@ size_t moe_backward_workspace_size(const moe_shape* shape);
  * (expert_ids, gate_weights as moe_route wrote them, or as the caller gave
  * them) and the upstream gradient dY [T, hidden], writes the gradients in
  * `grads`.  It recomputes the dispatch and the expert activations (Linear1
- * pre-activations, SwiGLU output, Yp) in the workspace, then: unpermute
- * backward (dYp[row(t,j)] = G[t,j] dY[t], dG[t,j] = dY[t] . Yp[row]), Linear2
- * dgrad with the SwiGLU backward of "Megatron 分布式训练全维度并行技术文档"
- * §1.8, dW2 = Aᵀ dYp, Linear1 dgrad, dW1 = Xpᵀ dH1 (per expert; the shared
- * expert with upstream dY), permute backward (dX[t] = sum of its k rows'
- * gradients + the shared expert's).  With opts (the options of the forward's
- * router) the router is differentiated too: only the chosen experts'
- * continuous affinities carry gradient (the selection is discrete, beta gets
- * none); dWg = Xᵀ dl, dgate_bias = column sums of dl and dl Wgᵀ is added to
- * dX.  With opts == NULL, gate_weights are treated as inputs and dG is their
+ * pre-activations H1 and the SwiGLU output A) in the workspace, then:
+ * unpermute backward (dY[t] to each of the token's rows), Linear2 dgrad of
+ * those rows U = dY[t] W2ᵀ with, in its epilogue, dA = G[t,j] U, the SwiGLU
+ * backward of "Megatron 分布式训练全维度并行技术文档" §1.8 and dG[t,j] = U . A
+ * (which equals dY[t] . Yp[row], Yp being A W2, so the expert outputs are
+ * not recomputed), dW2 = (G A)ᵀ dY, Linear1 dgrad, dW1 = Xpᵀ dH1 (per
+ * expert; the shared expert with upstream dY), permute backward (dX[t] = sum
+ * of its k rows' gradients + the shared expert's).  With opts (the options of
+ * the forward's router) the router is differentiated too: only the chosen
+ * experts' continuous affinities carry gradient (the selection is discrete,
+ * beta gets none); dWg = Xᵀ dl, dgate_bias = column sums of dl and dl Wgᵀ is
+ * added to dX.  With opts == NULL, gate_weights are treated as inputs and dG is their
  * gradient.  Weight gradients are fp32 sums rounded once to bf16; dX sums
  * its parts in fp32.  BF16 layers only (MOE_ERR_UNSUPPORTED otherwise); hidden
  * a multiple of 256, inter of 128, and with opts experts a multiple of 64. */
@@ -310,12 +312,13 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
 
 /* Training forward: steps 1-5 as moe_forward, for the layers and shapes
  * that moe_backward takes, on a backward workspace (moe_backward_workspace_size
- * bytes), keeping there what the backward reads: the dispatch, Linear1's
- * pre-activations H1 (gate, up) and the SwiGLU output A of every routed and
- * shared row, the routed experts' outputs Yp and, with opts, the router's
- * keys.  H1 is written out in bf16 and SwiGLU applied to it (the values the
- * backward differentiates), not fused into Linear1's epilogue as in
- * moe_forward, so Y agrees with moe_forward to bf16 rounding of H1.
+ * bytes), keeping there what the backward reads: the dispatch, the gate
+ * weight of each dispatched row, Linear1's pre-activations H1 (gate, up) and
+ * the SwiGLU output A of every routed and shared row times its gate weight
+ * and, with opts, the router's keys.  H1 is written out in bf16 and SwiGLU
+ * applied to it (the values the backward differentiates), not fused into
+ * Linear1's epilogue as in moe_forward, so Y agrees with moe_forward to bf16
+ * rounding of H1.
  * Arguments and errors as moe_forward, plus those of moe_backward's shape
  * limits. */
 int moe_forward_train(const moe_shape* shape, const moe_route_opts* opts, const void* X,
@@ -324,7 +327,7 @@ int moe_forward_train(const moe_shape* shape, const moe_route_opts* opts, const 
                       hipStream_t stream);
 
 /* moe_backward on saved activations: the same gradients, without the
- * recompute (dispatch, router keys, Linear1, SwiGLU, Linear2).  The
+ * recompute (dispatch, router keys, Linear1, SwiGLU).  The
  * workspace must hold the moe_forward_train of the same shape, X, weights,
  * routing and opts, unchanged since (the library cannot check this; anything
  * else gives wrong gradients, not an error).  Arguments and errors as

@@ -8,6 +8,13 @@
 // dgrad, the permute backward summing the k copies, and the router's
 // backward through the chosen experts' continuous affinities.
 //
+// The gate weight is moved off the gradient rows: with U = dY[t] W2[e]ᵀ (the
+// Linear2 dgrad of the unweighted row), dA = G U, and since Yp = A W2[e],
+// dG = dY[t] . (A W2[e]) = U . A, a row sum that the Linear2 dgrad epilogue
+// takes while it holds U and recomputes A for the SwiGLU backward; dW2 =
+// Aᵀ (G dY) = (G A)ᵀ dY.  So the backward needs neither Yp nor the Linear2
+// forward that makes it, and the rows of dY are copied, not scaled.
+//
 // Kernels:
 //   dgrad_kernel  out[r] = dO[r] W[e]ᵀ over the expert blocks (ragged rows,
 //                 as in the forward).  Both operands are K-contiguous rows
@@ -36,72 +43,76 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 __device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // ---------------------------------------------------------------- elementwise
-// A = SiLU(H1[:, :f]) * H1[:, f:], 8 columns per thread.
+// A = SiLU(H1[:, :f]) * H1[:, f:], 8 columns per thread, for `arows` rows:
+// Aw = A * grow[r] on the first `rows` (dispatched) rows and A on the rest
+// (the shared expert's); Af (may be NULL) = A.
 __global__ __launch_bounds__(256) void swiglu_fwd_kernel(const uint16_t* __restrict__ H1, int f,
-                                                         long rows, uint16_t* __restrict__ A) {
+                                                         long rows, long arows,
+                                                         const float* __restrict__ grow,
+                                                         uint16_t* __restrict__ Aw,
+                                                         uint16_t* __restrict__ Af) {
   const long i = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;  // 8-column group
   const long per = f / 8;
-  if (i >= rows * per) return;
+  if (i >= arows * per) return;
   const long r = i / per;
   const int c = static_cast<int>(i % per) * 8;
+  const float gw = r < rows ? grow[r] : 1.0f;
   const uint4 g = *reinterpret_cast<const uint4*>(H1 + r * 2 * f + c);
   const uint4 u = *reinterpret_cast<const uint4*>(H1 + r * 2 * f + f + c);
-  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
-  uint32_t o[4];
+  const uint32_t gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+  uint32_t ow[4], of[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const float a0 = silu(bfv(gw[q] & 0xFFFF)) * bfv(uw[q] & 0xFFFF);
-    const float a1 = silu(bfv(gw[q] >> 16)) * bfv(uw[q] >> 16);
-    o[q] = f32_to_bf16(a0) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
+    const float a0 = silu(bfv(gv[q] & 0xFFFF)) * bfv(uv[q] & 0xFFFF);
+    const float a1 = silu(bfv(gv[q] >> 16)) * bfv(uv[q] >> 16);
+    ow[q] = f32_to_bf16(gw * a0) | (static_cast<uint32_t>(f32_to_bf16(gw * a1)) << 16);
+    of[q] = f32_to_bf16(a0) | (static_cast<uint32_t>(f32_to_bf16(a1)) << 16);
   }
-  *reinterpret_cast<uint4*>(A + r * f + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(Aw + r * f + c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+  if (Af) *reinterpret_cast<uint4*>(Af + r * f + c) = make_uint4(of[0], of[1], of[2], of[3]);
 }
 
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+// The gate weight of each dispatched row: grow[dst_row[i]] = G[i].
+__global__ __launch_bounds__(256) void row_gate_kernel(const int32_t* __restrict__ dst_row,
+                                                       const float* __restrict__ G, int n,
+                                                       float* __restrict__ grow) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = dst_row[i];
+  if (r >= 0) grow[r] = G[i];
 }
 
 // Unpermute backward, one block (256 threads) per token: dYp[row(t,j)] =
-// G[t,j] dY[t] and dG[t,j] = dY[t] . Yp[row(t,j)] (fp32 sums in a fixed
-// order).  h % 8 == 0.
-__global__ __launch_bounds__(256) void combine_backward_kernel(
-    int h, int k, const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Yp,
-    const int32_t* __restrict__ dst_row, const float* __restrict__ G, uint16_t* __restrict__ dYp,
-    float* __restrict__ dG) {
-  __shared__ float red[4];
+// dY[t] for each of its k rows (unweighted: the gate weight goes onto A, and
+// dG comes out of the Linear2 dgrad).  h % 8 == 0.
+__global__ __launch_bounds__(256) void unpermute_backward_kernel(
+    int h, int k, const uint16_t* __restrict__ dY, const int32_t* __restrict__ dst_row,
+    uint16_t* __restrict__ dYp) {
   const int t = blockIdx.x;
   const uint16_t* dy = dY + static_cast<size_t>(t) * h;
-  for (int j = 0; j < k; ++j) {
-    const int r = dst_row[static_cast<size_t>(t) * k + j];
-    if (r < 0) {  // skipped assignment (uniform over the block)
-      if (threadIdx.x == 0) dG[static_cast<size_t>(t) * k + j] = 0.0f;
-      continue;
+  for (int c = threadIdx.x * 8; c < h; c += 256 * 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(dy + c);
+    for (int j = 0; j < k; ++j) {
+      const int r = dst_row[static_cast<size_t>(t) * k + j];
+      if (r >= 0) *reinterpret_cast<uint4*>(dYp + static_cast<size_t>(r) * h + c) = v;
     }
-    const float g = G[static_cast<size_t>(t) * k + j];
-    const uint16_t* y = Yp + static_cast<size_t>(r) * h;
-    uint16_t* o = dYp + static_cast<size_t>(r) * h;
-    float s = 0.0f;
-    for (int c = threadIdx.x * 8; c < h; c += 256 * 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(dy + c);
-      const uint4 b = *reinterpret_cast<const uint4*>(y + c);
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-      uint32_t ow[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = bfv(aw[q] & 0xFFFF), a1 = bfv(aw[q] >> 16);
-        s = fmaf(a0, bfv(bw[q] & 0xFFFF), s);
-        s = fmaf(a1, bfv(bw[q] >> 16), s);
-        ow[q] = f32_to_bf16(g * a0) | (static_cast<uint32_t>(f32_to_bf16(g * a1)) << 16);
-      }
-      *reinterpret_cast<uint4*>(o + c) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-    }
-    s = block_sum(s, red);
-    if (threadIdx.x == 0) dG[static_cast<size_t>(t) * k + j] = s;
   }
+}
+
+// dG[t,j] = the sum of row(t,j)'s P partials, in column order (0 for a
+// skipped assignment).
+__global__ __launch_bounds__(256) void dg_reduce_kernel(int n, int P, const int32_t* __restrict__ dst_row,
+                                                        const float* __restrict__ dgp,
+                                                        float* __restrict__ dG) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r = dst_row[i];
+  float s = 0.0f;
+  if (r >= 0) {
+    const float* p = dgp + static_cast<size_t>(r) * P;
+    for (int q = 0; q < P; ++q) s += p[q];
+  }
+  dG[i] = s;
 }
 
 // Router backward, one wave per token: affinities a from the recomputed keys
@@ -230,6 +241,8 @@ struct DgradArgs {
   void* out_sh;
   const void* h1;     // SWB: [rows, 2N] bf16 pre-activations (gate, up)
   const void* h1_sh;
+  const float* grow;  // SWB: [rows] gate weight of each routed row
+  float* dgp;         // SWB: [rows, N / 64] partial dG per row and 64 columns
   const int32_t* offsets;
   const int32_t* tile_off;
   int E, K, N, T, n_tiles;
@@ -265,6 +278,19 @@ __device__ __forceinline__ bool dgrad_item(const DgradArgs& g, int& seg, int& mt
   nt = rin / gsz;
   mtile = grp * GROUP_M + rin % gsz;
   return true;
+}
+
+// One halving step of a sum across lanes: lanes whose bit BIT is clear keep
+// values 0..W-1 and hand W..2W-1 to the lane BIT away, which keeps those.
+template <int W, int BIT>
+__device__ __forceinline__ void fold_half(float (&p)[16], int lane) {
+  const bool hi = (lane & BIT) != 0;
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const float keep = hi ? p[q + W] : p[q];
+    const float send = hi ? p[q] : p[q + W];
+    p[q] = keep + __shfl_xor(send, BIT);
+  }
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool SWB>
@@ -409,29 +435,52 @@ void dgrad_kernel(DgradArgs g) {
   // ------------------------------------------------ epilogue
   uint16_t* obase = static_cast<uint16_t*>(shared ? g.out_sh : g.out);
   if constexpr (SWB) {
+    // acc = U (the unweighted rows' dgrad); dA = G U, and this wave's part
+    // of dG = U . A over its WN = 64 columns of each row
+    static_assert(WN == 64, "one dG partial per 64 columns");
     const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
     const int col_in = lane & 31;
+    const int P = g.N / 64, pcol = (nt * BN + wn * WN) / 64;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
-      if (i >= mt_live) continue;
+      if (i >= mt_live) continue;  // wave-uniform
+      float part[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
+        part[v] = 0.0f;
         const int row = row0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row >= row_end) continue;
+        const float gw = shared ? 1.0f : g.grow[row];
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const int n = nt * BN + wn * WN + j * 32 + col_in;
-          const float d = acc[i][j][v];
-          // dH = d; H1 = (gate G, up U); A = SiLU(G): dU = dH * A and
-          // dG = dH * U * (sigma(G) + A (1 - sigma(G)))
+          const float u = acc[i][j][v];
+          const float d = gw * u;
+          // dH = d; H1 = (gate G, up U); A = SiLU(G) U: dU = dH SiLU(G) and
+          // dG = dH * U * (sigma(G) + SiLU(G) (1 - sigma(G)))
           const size_t rb = static_cast<size_t>(row) * 2 * g.N;
           const float gt = bfv(hbase[rb + n]), up = bfv(hbase[rb + g.N + n]);
           const float sg = 1.0f / (1.0f + expf(-gt));
           const float act = gt * sg;
           obase[rb + n] = f32_to_bf16(d * up * (sg + act * (1.0f - sg)));
           obase[rb + g.N + n] = f32_to_bf16(d * act);
+          // A as the forward's Linear2 multiplied it (bf16)
+          part[v] = fmaf(u, bfv(f32_to_bf16(act * up)), part[v]);
         }
       }
+      if (shared) continue;  // the shared expert has no gate weight
+      // sum each row's partial over the 32 lanes of its half-wave: halve the
+      // values at each xor step (16 -> 8 -> 4 -> 2 -> 1, then the pair), so
+      // lane l ends with row value v = 8 b4 + 4 b3 + 2 b2 + b1 of l's bits
+      fold_half<8, 16>(part, lane);
+      fold_half<4, 8>(part, lane);
+      fold_half<2, 4>(part, lane);
+      fold_half<1, 2>(part, lane);
+      part[0] += __shfl_xor(part[0], 1);
+      const int vv = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) +
+                     ((lane >> 1) & 1);
+      const int row = row0 + wm * WM + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
+      if ((lane & 1) == 0 && row < row_end) g.dgp[static_cast<size_t>(row) * P + pcol] = part[0];
     }
     return;
   }
@@ -1128,11 +1177,21 @@ hipError_t wgrad(const WgradArgs& in, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, void* A, hipStream_t stream) {
-  const long n = rows * (f / 8);
+hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, long arows, const float* grow,
+                              void* Aw, void* Af, hipStream_t stream) {
+  const long n = arows * (f / 8);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(swiglu_fwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(H1), f, rows, static_cast<uint16_t*>(A));
+                     stream, static_cast<const uint16_t*>(H1), f, rows, arows, grow,
+                     static_cast<uint16_t*>(Aw), static_cast<uint16_t*>(Af));
+  return hipGetLastError();
+}
+
+hipError_t launch_row_gate(const int32_t* dst_row, const float* G, int n, float* grow,
+                           hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(row_gate_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, dst_row, G, n,
+                     grow);
   return hipGetLastError();
 }
 
@@ -1141,13 +1200,15 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   const int T_sh = a.has_shared ? a.T : 0;
   const size_t h = a.h, f = a.f;
   hipError_t e;
-  // unpermute backward: dYp and dG
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(a.T), dim3(256), 0, stream, a.h, a.k,
-                     static_cast<const uint16_t*>(a.dY), static_cast<const uint16_t*>(a.Yp),
-                     a.dst_row, a.G, static_cast<uint16_t*>(a.dYp), a.dG);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // Linear2 dgrad with the SwiGLU backward: dH1 (the shared expert's
-  // upstream gradient is dY itself)
+  // unpermute backward: dY copied to each of its token's rows
+  if (rows > 0) {
+    hipLaunchKernelGGL(unpermute_backward_kernel, dim3(a.T), dim3(256), 0, stream, a.h, a.k,
+                       static_cast<const uint16_t*>(a.dY), a.dst_row, static_cast<uint16_t*>(a.dYp));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // Linear2 dgrad of the unweighted rows with the SwiGLU backward: dH1 and
+  // the partial dG of every routed row (the shared expert's upstream
+  // gradient is dY itself)
   DgradArgs d2{};
   d2.A = a.dYp;
   d2.A_sh = a.dY;
@@ -1157,6 +1218,8 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   d2.out_sh = static_cast<char*>(a.dH1) + static_cast<size_t>(rows) * 2 * f * 2;
   d2.h1 = a.H1;
   d2.h1_sh = static_cast<const char*>(a.H1) + static_cast<size_t>(rows) * 2 * f * 2;
+  d2.grow = a.grow;
+  d2.dgp = a.dGp;
   d2.offsets = a.offsets;
   d2.tile_off = a.tile_b;
   d2.E = a.E;
@@ -1164,7 +1227,13 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream) {
   d2.N = a.f;
   d2.T = a.T;
   if ((e = dgrad(d2, rows, T_sh, true, stream)) != hipSuccess) return e;
-  // Linear2 wgrad: dW2[e] = A_eᵀ dYp_e (shared: Aᵀ dY)
+  // dG = the sum of each row's partials
+  if (rows > 0) {
+    hipLaunchKernelGGL(dg_reduce_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, rows,
+                       a.f / 64, a.dst_row, static_cast<const float*>(a.dGp), a.dG);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // Linear2 wgrad: dW2[e] = (G A)_eᵀ dYp_e (shared: Aᵀ dY)
   WgradArgs w2{};
   w2.A = a.Aact;
   w2.A_sh = static_cast<const char*>(a.Aact) + static_cast<size_t>(rows) * f * 2;

@@ -355,14 +355,18 @@ int check_backward(const moe_shape* shape, const moe_route_opts* opts, const voi
   return MOE_OK;
 }
 
-// The dispatch, the router keys (with opts) and H1 = Xp W1 (routed and shared
-// rows), A = SwiGLU(H1), into a backward workspace; Yp = A W2 for the routed
-// rows and, with Ys != NULL, the shared expert's output too.  Routing: with
-// route_out the router runs and writes it (the training forward), else it
-// runs into scratch for its keys only (the recompute).
+// The dispatch, the router keys (with opts), the gate weight of each row,
+// H1 = Xp W1 (routed and shared rows) and A = SwiGLU(H1) weighted by the
+// row's gate weight (what the backward reads) into a backward workspace.
+// Routing: with ids_out the router runs and writes it and G (the training
+// forward), else it runs into scratch for its keys only and G is the
+// caller's (the recompute).  The training forward (train) also keeps A
+// unweighted and runs Linear2: Yp = A W2 for the routed rows and, with Ys !=
+// NULL, the shared expert's output.
 hipError_t recompute(const moe_shape* shape, const moe_route_opts* opts, const void* X, const void* Wg,
                      const moe_expert_weights* weights, const int32_t* expert_ids,
-                     int32_t* ids_out, float* g_out, void* Ys, void* ws, hipStream_t stream) {
+                     const float* G, int32_t* ids_out, float* g_out, bool train, void* Ys,
+                     void* ws, hipStream_t stream) {
   const Layout L = make_layout(*shape);
   const BwdLayout B = make_bwd_layout(*shape);
   const int T = shape->tokens, k = shape->topk, E = shape->experts;
@@ -402,13 +406,17 @@ hipError_t recompute(const moe_shape* shape, const moe_route_opts* opts, const v
     e = launch_grouped_linear_bf16(l1, stream);
   }
   if (e == hipSuccess)
-    e = launch_swiglu_bf16(at<void>(ws, B.H1), shape->inter,
+    e = launch_row_gate(at<int32_t>(ws, L.dst_row), g_out ? g_out : G, rows,
+                        at<float>(ws, B.grow), stream);
+  if (e == hipSuccess)
+    e = launch_swiglu_bf16(at<void>(ws, B.H1), shape->inter, rows,
                            static_cast<long>(rows) + (shape->has_shared ? T : 0),
-                           at<void>(ws, B.Aact), stream);
-  if (e == hipSuccess) {
+                           at<float>(ws, B.grow), at<void>(ws, B.Aact),
+                           train ? at<void>(ws, B.Afwd) : nullptr, stream);
+  if (e == hipSuccess && train) {
     LinearArgs l2{};
-    l2.A = at<void>(ws, B.Aact);
-    l2.A_sh = at<char>(ws, B.Aact) + static_cast<size_t>(rows) * f * 2;
+    l2.A = at<void>(ws, B.Afwd);
+    l2.A_sh = at<char>(ws, B.Afwd) + static_cast<size_t>(rows) * f * 2;
     l2.W = weights->W2;
     l2.W_sh = weights->Ws2;
     l2.out = at<void>(ws, L.Yp);
@@ -460,9 +468,10 @@ hipError_t backward_from_saved(const moe_shape* shape, const moe_route_opts* opt
   b.offsets = at<int32_t>(ws, L.offsets);
   b.dst_row = at<int32_t>(ws, L.dst_row);
   b.Xp = at<void>(ws, L.Xp);
-  b.Yp = at<void>(ws, L.Yp);
+  b.grow = at<float>(ws, B.grow);
   b.H1 = at<void>(ws, B.H1);
   b.Aact = at<void>(ws, B.Aact);
+  b.dGp = at<float>(ws, B.dGp);
   b.dYp = at<void>(ws, B.dYp);
   b.dH1 = at<void>(ws, B.dH1);
   b.dXp = at<void>(ws, B.dXp);
@@ -496,8 +505,8 @@ int moe_backward(const moe_shape* shape, const moe_route_opts* opts, const void*
   const Layout L = make_layout(*shape);
   hipError_t e = launch_clear_flag(at<int32_t>(workspace, L.flag), stream);
   if (e == hipSuccess)
-    e = recompute(shape, opts, X, Wg, weights, expert_ids, nullptr, nullptr, nullptr, workspace,
-                  stream);
+    e = recompute(shape, opts, X, Wg, weights, expert_ids, gate_weights, nullptr, nullptr, false,
+                  nullptr, workspace, stream);
   if (e == hipSuccess)
     e = backward_from_saved(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY, grads,
                             workspace, stream);
@@ -526,9 +535,9 @@ int moe_forward_train(const moe_shape* shape, const moe_route_opts* opts, const 
   void* ws = workspace;
   hipError_t e = launch_clear_flag(at<int32_t>(ws, L.flag), stream);
   if (e == hipSuccess)
-    e = recompute(shape, opts, X, Wg, weights, expert_ids, opts ? expert_ids : nullptr,
-                  opts ? gate_weights : nullptr, shape->has_shared ? at<void>(ws, L.Ys) : nullptr,
-                  ws, stream);
+    e = recompute(shape, opts, X, Wg, weights, expert_ids, gate_weights,
+                  opts ? expert_ids : nullptr, opts ? gate_weights : nullptr, true,
+                  shape->has_shared ? at<void>(ws, L.Ys) : nullptr, ws, stream);
   if (e == hipSuccess) {
     CombineArgs c{};
     c.T = shape->tokens;

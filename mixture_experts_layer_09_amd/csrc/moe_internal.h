@@ -279,8 +279,12 @@ hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t stream);
 // the recomputed activations and the gradients in flight.
 struct BwdLayout {
   size_t H1;       // [arows, 2f] bf16: Linear1 pre-activations (gate, up)
-  size_t Aact;     // [arows, f] bf16: SwiGLU output
-  size_t dYp;      // [rows, h] bf16: G-weighted upstream gradient per assignment
+  size_t Aact;     // [arows, f] bf16: SwiGLU output times the row's gate weight
+                   // (shared rows: 1), the left operand of dW2
+  size_t Afwd;     // [arows, f] bf16: SwiGLU output, the training forward's Linear2 input
+  size_t grow;     // [rows] fp32: gate weight of each dispatched row
+  size_t dGp;      // [rows, f/64] fp32: partial dG of each row per 64 columns of Linear2's dgrad
+  size_t dYp;      // [rows, h] bf16: upstream gradient dY[t] copied to each row of token t
   size_t dH1;      // [arows, 2f] bf16: gradient of the pre-activations
   size_t dXp;      // [arows, h] bf16: dgrad of the dispatched rows (+ shared)
   size_t dXr;      // [T, h] bf16: router part of dX
@@ -307,6 +311,9 @@ inline BwdLayout make_bwd_layout(const moe_shape& s) {
   };
   B.H1 = take(arows * 2 * f * 2);
   B.Aact = take(arows * f * 2);
+  B.Afwd = take(arows * f * 2);
+  B.grow = take(rows * 4);
+  B.dGp = take(rows * (f / 64) * 4);
   B.dYp = take(rows * h * 2);
   B.dH1 = take(arows * 2 * f * 2);
   B.dXp = take(arows * h * 2);
@@ -342,10 +349,11 @@ struct BackwardArgs {
   const int32_t* offsets;
   const int32_t* dst_row;
   const void* Xp;
-  const void* Yp;     // [rows, h] bf16
+  const float* grow;  // [rows] gate weight of each dispatched row
   // workspace regions (BwdLayout)
   void* H1;
   void* Aact;
+  float* dGp;
   void* dYp;
   void* dH1;
   void* dXp;
@@ -366,10 +374,17 @@ struct BackwardArgs {
   void* dWs1;
   void* dWs2;
 };
-// Everything after the forward recompute: combine backward, router backward
-// (when route), the experts' dgrad and wgrad, permute backward.
+// Everything after the forward recompute: unpermute backward, the experts'
+// dgrad and wgrad, router backward (when route), permute backward.
 hipError_t launch_backward(const BackwardArgs& a, hipStream_t stream);
-// A = SiLU(H1[:, :f]) * H1[:, f:] for `rows` rows (bf16).
-hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, void* A, hipStream_t stream);
+// grow[dst_row[i]] = G[i] for the n dispatched assignments (skipped ones have
+// no row).
+hipError_t launch_row_gate(const int32_t* dst_row, const float* G, int n, float* grow,
+                           hipStream_t stream);
+// A = SiLU(H1[:, :f]) * H1[:, f:] for `arows` rows (bf16): Aw gets A times
+// grow[r] for the first `rows` rows and A itself for the rest; Af (if not
+// NULL) gets A.
+hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, long arows, const float* grow,
+                              void* Aw, void* Af, hipStream_t stream);
 
 }  // namespace moe

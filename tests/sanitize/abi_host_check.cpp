@@ -192,10 +192,22 @@ hipError_t launch_grouped_linear_bf16(const LinearArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
-hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, void* A, hipStream_t) {
+hipError_t launch_swiglu_bf16(const void* H1, int f, long rows, long arows, const float* grow,
+                              void* Aw, void* Af, hipStream_t) {
   new_launch();
-  touch(H1, static_cast<size_t>(rows) * 2 * f * 2);
-  touch(A, static_cast<size_t>(rows) * f * 2);
+  touch(H1, static_cast<size_t>(arows) * 2 * f * 2);
+  touch(grow, static_cast<size_t>(rows) * 4);
+  touch(Aw, static_cast<size_t>(arows) * f * 2);
+  touch(Af, Af ? static_cast<size_t>(arows) * f * 2 : 0);
+  ++g_launches;
+  return hipSuccess;
+}
+
+hipError_t launch_row_gate(const int32_t* dst_row, const float* G, int n, float* grow, hipStream_t) {
+  new_launch();
+  touch(dst_row, static_cast<size_t>(n) * 4);
+  touch(G, static_cast<size_t>(n) * 4);
+  touch(grow, static_cast<size_t>(n) * 4);
   ++g_launches;
   return hipSuccess;
 }
@@ -213,9 +225,10 @@ hipError_t launch_backward(const BackwardArgs& a, hipStream_t) {
   touch(a.offsets, (E + 1) * 4);
   touch(a.dst_row, rows * 4);
   touch(a.Xp, rows * h * 2);
-  touch(a.Yp, rows * h * 2);
+  touch(a.grow, rows * 4);
   touch(a.H1, arows * 2 * f * 2);
   touch(a.Aact, arows * f * 2);
+  touch(a.dGp, rows * (f / 64) * 4);
   touch(a.dYp, rows * h * 2);
   touch(a.dH1, arows * 2 * f * 2);
   touch(a.dXp, arows * h * 2);

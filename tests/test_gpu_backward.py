@@ -20,7 +20,7 @@ from tests.helpers import bits, f64, row_rel_err
 
 pytestmark = pytest.mark.gpu
 
-# The GPU chain rounds four intermediates to bf16 (dYp, H1, A, dH1; 2^-9
+# The GPU chain rounds its intermediates to bf16 (H1, A and G A, dH1; 2^-9
 # relative each) and its outputs; the weight gradients are sums over an
 # expert's rows, with cancellation, compared per row against the row's
 # largest magnitude.  Measured: 0.4e-2 .. 1.5e-2.
