@@ -280,19 +280,6 @@ __device__ __forceinline__ bool dgrad_item(const DgradArgs& g, int& seg, int& mt
   return true;
 }
 
-// One halving step of a sum across lanes: lanes whose bit BIT is clear keep
-// values 0..W-1 and hand W..2W-1 to the lane BIT away, which keeps those.
-template <int W, int BIT>
-__device__ __forceinline__ void fold_half(float (&p)[16], int lane) {
-  const bool hi = (lane & BIT) != 0;
-#pragma unroll
-  for (int q = 0; q < W; ++q) {
-    const float keep = hi ? p[q + W] : p[q];
-    const float send = hi ? p[q] : p[q + W];
-    p[q] = keep + __shfl_xor(send, BIT);
-  }
-}
-
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, bool SWB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) __attribute__((amdgpu_waves_per_eu(2)))
 void dgrad_kernel(DgradArgs g) {
@@ -435,52 +422,79 @@ void dgrad_kernel(DgradArgs g) {
   // ------------------------------------------------ epilogue
   uint16_t* obase = static_cast<uint16_t*>(shared ? g.out_sh : g.out);
   if constexpr (SWB) {
-    // acc = U (the unweighted rows' dgrad); dA = G U, and this wave's part
-    // of dG = U . A over its WN = 64 columns of each row
-    static_assert(WN == 64, "one dG partial per 64 columns");
+    // acc = U, the dgrad of the unweighted rows.  Each wave stages its 64 x
+    // 64 part of U in LDS (fp32), 32 rows at a time, and reads it back as 8
+    // consecutive columns per lane, 8 lanes per row, so that H1 is read and
+    // dH1 written in 16-byte pieces of whole 128-byte lines.  Then dA = G U,
+    // the SwiGLU backward, and this wave's part of dG = U . A over its 64
+    // columns of each row.  Element (r, c) of a staged 32 x 64 block is float
+    // r * 64 + (c ^ 32 ((r >> 2) & 1)): the two half-waves of a write, rows
+    // r and r + 4, then fall in different banks.
+    static_assert(WN == 64 && NW * 8192 <= STAGES * STAGE, "staging: 32 x 64 fp32 per wave");
+    __syncthreads();  // every wave is done with the ring
+    float* wst = reinterpret_cast<float*>(smem + wave * 8192);
     const uint16_t* hbase = static_cast<const uint16_t*>(shared ? g.h1_sh : g.h1);
-    const int col_in = lane & 31;
     const int P = g.N / 64, pcol = (nt * BN + wn * WN) / 64;
+    const int cg = lane & 7;
+    const int n0 = nt * BN + wn * WN + 8 * cg;
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       if (i >= mt_live) continue;  // wave-uniform
-      float part[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        part[v] = 0.0f;
-        const int row = row0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row >= row_end) continue;
-        const float gw = shared ? 1.0f : g.grow[row];
+      for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          const int n = nt * BN + wn * WN + j * 32 + col_in;
-          const float u = acc[i][j][v];
-          const float d = gw * u;
-          // dH = d; H1 = (gate G, up U); A = SiLU(G) U: dU = dH SiLU(G) and
-          // dG = dH * U * (sigma(G) + SiLU(G) (1 - sigma(G)))
-          const size_t rb = static_cast<size_t>(row) * 2 * g.N;
-          const float gt = bfv(hbase[rb + n]), up = bfv(hbase[rb + g.N + n]);
-          const float sg = 1.0f / (1.0f + expf(-gt));
-          const float act = gt * sg;
-          obase[rb + n] = f32_to_bf16(d * up * (sg + act * (1.0f - sg)));
-          obase[rb + g.N + n] = f32_to_bf16(d * act);
-          // A as the forward's Linear2 multiplied it (bf16)
-          part[v] = fmaf(u, bfv(f32_to_bf16(act * up)), part[v]);
+        for (int v = 0; v < 16; ++v) {
+          const int r = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), c = 32 * j + (lane & 31);
+          wst[r * 64 + (c ^ (((r >> 2) & 1) << 5))] = acc[i][j][v];
         }
+      // the wave's LDS operations run in order: once its writes are done,
+      // its reads see them (the memory clobber keeps the compiler's order)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = (lane >> 3) + 8 * q;
+        const float4* src = reinterpret_cast<const float4*>(wst + rr * 64 + ((8 * cg) ^ (((rr >> 2) & 1) << 5)));
+        const float4 u0 = src[0], u1 = src[1];
+        const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const int row = row0 + wm * WM + i * 32 + rr;
+        float part = 0.0f;
+        if (row < row_end) {
+          const float gw = shared ? 1.0f : g.grow[row];
+          const size_t rb = static_cast<size_t>(row) * 2 * g.N;
+          const uint4 gv = *reinterpret_cast<const uint4*>(hbase + rb + n0);
+          const uint4 uv = *reinterpret_cast<const uint4*>(hbase + rb + g.N + n0);
+          const uint32_t gq[4] = {gv.x, gv.y, gv.z, gv.w}, uq[4] = {uv.x, uv.y, uv.z, uv.w};
+          uint32_t dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float og[2], ou[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              // dH = G U; H1 = (gate x, up y); A = SiLU(x) y: dy = dH SiLU(x)
+              // and dx = dH y (sigma(x) + SiLU(x) (1 - sigma(x)))
+              const float x = bfv(static_cast<uint16_t>(gq[e] >> (16 * hh)));
+              const float y = bfv(static_cast<uint16_t>(uq[e] >> (16 * hh)));
+              const float un = u[2 * e + hh], d = gw * un;
+              const float sg = 1.0f / (1.0f + expf(-x));
+              const float act = x * sg;
+              og[hh] = d * y * (sg + act * (1.0f - sg));
+              ou[hh] = d * act;
+              // A as the forward's Linear2 multiplied it (bf16)
+              part = fmaf(un, bfv(f32_to_bf16(act * y)), part);
+            }
+            dg[e] = pack_bf16x2(og[0], og[1]);
+            du[e] = pack_bf16x2(ou[0], ou[1]);
+          }
+          *reinterpret_cast<uint4*>(obase + rb + n0) = make_uint4(dg[0], dg[1], dg[2], dg[3]);
+          *reinterpret_cast<uint4*>(obase + rb + g.N + n0) = make_uint4(du[0], du[1], du[2], du[3]);
+        }
+        // the row's partial over its 8 lanes (every lane takes part)
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 4);
+        if (!shared && cg == 0 && row < row_end) g.dgp[static_cast<size_t>(row) * P + pcol] = part;
       }
-      if (shared) continue;  // the shared expert has no gate weight
-      // sum each row's partial over the 32 lanes of its half-wave: halve the
-      // values at each xor step (16 -> 8 -> 4 -> 2 -> 1, then the pair), so
-      // lane l ends with row value v = 8 b4 + 4 b3 + 2 b2 + b1 of l's bits
-      fold_half<8, 16>(part, lane);
-      fold_half<4, 8>(part, lane);
-      fold_half<2, 4>(part, lane);
-      fold_half<1, 2>(part, lane);
-      part[0] += __shfl_xor(part[0], 1);
-      const int vv = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) +
-                     ((lane >> 1) & 1);
-      const int row = row0 + wm * WM + i * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
-      if ((lane & 1) == 0 && row < row_end) g.dgp[static_cast<size_t>(row) * P + pcol] = part[0];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next writes
     }
     return;
   }
