@@ -374,10 +374,9 @@ void dgrad_kernel(DgradArgs g) {
     }
   }
   static_assert(2 * MT * NTW >= OPS, "an MFMA per DMA");
-  auto compute = [&](int slot) {
-    if (mt_live == 0) return;
+  bf16x8_t bfr[NTW][2], af[MT][2];
+  auto load_frags = [&](int slot) {
     const char* st = smem + slot * STAGE;
-    bf16x8_t bfr[NTW][2], af[MT][2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
@@ -385,36 +384,102 @@ void dgrad_kernel(DgradArgs g) {
 #pragma unroll
       for (int i = 0; i < MT; ++i) af[i][kh] = *reinterpret_cast<const bf16x8_t*>(st + a_off[i][kh]);
     }
-    // Without the SwiGLU backward, the transposed product (weight fragment
-    // first): element v of lane l is row l % 32 of the tile and column
-    // 8 (v / 4) + 4 (l / 32) + v % 4, stored 4 columns at a time.  With it,
-    // element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
-    // l % 32: the H1 reads and dH1 writes of a wave instruction then cover 2
-    // rows x 64 bytes instead of 32 rows x 16 bytes (measured 17% faster).
+  };
+  // Without the SwiGLU backward, the transposed product (weight fragment
+  // first): element v of lane l is row l % 32 of the tile and column
+  // 8 (v / 4) + 4 (l / 32) + v % 4, stored 4 columns at a time.  With it,
+  // element v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4, column
+  // l % 32, the layout the staged SwiGLU-backward epilogue writes to LDS.
+  // DMA idx of stage ikt (slot islot; none if !more) goes out after product
+  // idx: a DMA can stall at issue while the memory pipeline is full, and
+  // ahead of the MFMAs it would hold them back.
+  auto mma_issue = [&](bool more, int ikt, int islot) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
+        for (int j = 0; j < NTW; ++j) {
           acc[i][j] = SWB ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i][kh], bfr[j][kh], acc[i][j], 0, 0, 0)
                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j][kh], af[i][kh], acc[i][j], 0, 0, 0);
+          const int idx = (kh * MT + i) * NTW + j;
+          if (idx < OPS && more) issue_op(ikt, islot, idx);
+        }
   };
 
   const int KT = g.K / 32;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < KT) issue(s, s);
-  for (int k0 = 0; k0 < KT; k0 += STAGES) {
+  const bool live = mt_live > 0;
+  // Eight waves: ping-pong.  The two row halves (4 waves each, one of each
+  // per SIMD) alternate: half 0 reads stage kt's fragments while half 1
+  // multiplies stage kt - 1, then half 0 multiplies while half 1 reads, with
+  // two barriers per stage; each half runs its own copy of the loop (the
+  // same barriers in the same order).  Half 1 has read stage kt - 1 (and
+  // waited for its reads) before the barrier after which that slot is
+  // refilled.
+  if constexpr (NW == 8 && WAVES_M == 2) {
+    if (__builtin_amdgcn_readfirstlane(wm) == 0) {
+      for (int k0 = 0; k0 < KT; k0 += STAGES) {
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) {
-      const int kt = k0 + s;
-      if (kt < KT) {
-        // stage kt is in LDS once at most the stages issued after it are in flight
-        wait_after<OPS, STAGES - 2>(KT - 1 - kt);
-        __builtin_amdgcn_s_barrier();
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
-        compute(s);
+        for (int s = 0; s < STAGES; ++s) {
+          const int kt = k0 + s;
+          if (kt < KT) {
+            wait_after<OPS, STAGES - 2>(KT - 1 - kt);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const bool more = kt + STAGES - 1 < KT;
+            if (live) load_frags(s);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (live)
+              mma_issue(more, kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            else if (more)
+              issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+          }
+        }
+      }
+    } else {
+      for (int k0 = 0; k0 < KT; k0 += STAGES) {
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+          const int kt = k0 + s;
+          if (kt < KT) {
+            wait_after<OPS, STAGES - 2>(KT - 1 - kt);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            const bool more = kt + STAGES - 1 < KT;
+            if (live && kt > 0)
+              mma_issue(more, kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            else if (more)
+              issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (live) {
+              load_frags(s);
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+          }
+        }
+      }
+      if (live) mma_issue(false, 0, 0);
+    }
+  } else {
+    for (int k0 = 0; k0 < KT; k0 += STAGES) {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) {
+        const int kt = k0 + s;
+        if (kt < KT) {
+          // stage kt is in LDS once at most the stages issued after it are in flight
+          wait_after<OPS, STAGES - 2>(KT - 1 - kt);
+          __builtin_amdgcn_s_barrier();
+          if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (s + STAGES - 1) % STAGES);
+          if (live) {
+            load_frags(s);
+            mma_issue(false, 0, 0);
+          }
+        }
       }
     }
   }
