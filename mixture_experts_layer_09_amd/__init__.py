@@ -235,8 +235,8 @@ def moe_backward_saved(shape, opts, X, Wg, weights, expert_ids, gate_weights, dY
 
 def moe_check_device_error(workspace, stream=None) -> int:
     """Returns the status (0 or MOE_ERR_DEVICE_DATA) of the most recent call on
-    this workspace that can flag bad ids (each such call clears the flag when it
-    starts); raises on other errors."""
+    this workspace that can flag bad ids (each such call resets the flag);
+    raises on other errors."""
     st = lib().moe_check_device_error(_ptr(workspace), workspace.numel(), _stream(stream))
     if st not in (0, -5):
         raise MoeError("moe_check_device_error", st)

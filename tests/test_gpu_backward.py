@@ -310,3 +310,66 @@ def test_backward_full_size_v4pro():
     del inp, g, g2, wsb, ws
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_backward_skips_bad_expert_ids():
+    """Caller-given routing with two assignments out of contract (expert id -1
+    and E): moe_backward flags them, gives them dG = 0 and leaves them out of
+    every gradient.  Reference: the oracle's backward of the same layer with
+    those assignments' gate weights set to 0 (their ids replaced by a valid
+    expert), which contribute nothing to dX or dW; dG is compared on the
+    valid assignments."""
+    _need_gpu()
+    cpu = synth.make_inputs("v4pro_bf16", T=96, hidden=256, experts=64, inter=128)
+    wl = cpu["workload"]
+    gpu = to_device(cpu)
+    T, h, E, k, f = wl.T, wl.hidden, wl.experts, wl.topk, wl.inter
+    shape = moe.make_shape(T, h, E, k, f, wl.shared, "bf16")
+    opts = moe.make_route_opts(wl.score, wl.renorm, wl.alpha, gpu["beta"], gpu["gate_bias"])
+    weights = moe.make_weights(gpu["W1"], gpu["W2"], None, None, gpu["Ws1"], gpu["Ws2"])
+    ws = moe.alloc_workspace(shape)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    G = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(shape, opts, gpu["X"], gpu["Wg"], ids, G, None, ws)
+    bad = [(5, 2, -1), (70, 0, E)]
+    for t, j, v in bad:
+        ids[t, j] = v
+    dY = torch.randn((T, h), generator=torch.Generator().manual_seed(99)).to(torch.bfloat16)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    g = dict(dX=torch.empty((T, h), **bf), dW1=torch.empty((E, h, 2 * f), **bf),
+             dW2=torch.empty((E, f, h), **bf), dWs1=torch.empty((h, 2 * f), **bf),
+             dWs2=torch.empty((f, h), **bf),
+             dG=torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda"))
+    wsb = moe.alloc_workspace(shape, backward=True)
+    _log(f"[backward] bad ids {bad}: moe_backward T={T} h={h} E={E} k={k} f={f}")
+    moe.moe_backward(shape, None, gpu["X"], gpu["Wg"], weights, ids, G, dY.cuda(),
+                     moe.make_grads(**g), wsb)
+    torch.cuda.synchronize()
+    assert moe.moe_check_device_error(wsb) == -5   # MOE_ERR_DEVICE_DATA
+    ids_h = ids.cpu().numpy().copy()
+    G_h = G.cpu().double().numpy().copy()
+    valid = np.ones((T, k), bool)
+    for t, j, _ in bad:
+        ids_h[t, j] = 0 if 0 not in ids_h[t] else int(np.setdiff1d(np.arange(E), ids_h[t])[0])
+        G_h[t, j] = 0.0
+        valid[t, j] = False
+    L = oracle.Layer("bf16", bits(cpu["X"]), bits(cpu["W1"]), bits(cpu["W2"]), Ws1=bits(cpu["Ws1"]),
+                     Ws2=bits(cpu["Ws2"]), k=k)
+    dX, dG = L.backward_tokens(ids_h, G_h, dY.double().numpy())
+    gdG = f64(g["dG"])
+    assert (gdG[~valid] == 0).all()
+    err = {"dX": row_rel_err(f64(g["dX"]), dX),
+           "dG": float(np.abs(gdG[valid] - dG[valid]).max() / np.abs(dG[valid]).max())}
+    experts = list(range(E)) + [E]
+    dW1, dW2 = L.backward_weights(ids_h, G_h, dY.double().numpy(), experts)
+    gw1 = np.concatenate([f64(g["dW1"]), f64(g["dWs1"])[None]])
+    gw2 = np.concatenate([f64(g["dW2"]), f64(g["dWs2"])[None]])
+    used = np.zeros(E + 1, bool)
+    used[np.unique(ids_h[valid])] = True
+    used[-1] = True
+    assert not gw1[~used].any() and not gw2[~used].any()
+    err["dW1"] = row_rel_err(gw1[used].reshape(-1, 2 * f), dW1[used].reshape(-1, 2 * f))
+    err["dW2"] = row_rel_err(gw2[used].reshape(-1, h), dW2[used].reshape(-1, h))
+    _log("[backward] bad ids: " + ", ".join(f"{n} {v:.3e}" for n, v in err.items()))
+    for n, v in err.items():
+        assert v <= TOL, (n, v)
